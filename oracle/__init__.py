@@ -1,0 +1,229 @@
+"""CPU oracle for the MoE layer forward pass -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The product library never loads it,
+and it imports nothing from the product package: the two share no code.
+
+The arithmetic lives in ``moe_oracle.c`` (plain C loops, IEEE double
+accumulation, OpenMP over tokens or rows); this module only marshals numpy
+arrays.  bf16 tensors are passed as ``numpy.uint16`` arrays of raw bits.
+
+Sources, cited by page title and section:
+  * "Mixture-of-Experts (MoE) Architecture and Expert Parallelism",
+    section 2 "The Gating Network Formulation" -- logits, KeepTopK, softmax,
+    and the weighted sum of expert outputs.
+  * "EP Math -- Expert Parallelism (MoE)" -- notation (T, d, k, D), dispatch
+    and combine volumes, capacity factor, token drop, expert placement.
+  * "MoE Expert Parallelism Sizing: Traffic, Capacity, Fabric" -- the
+    gated three-matrix expert, drop-before-exchange, per-destination chunks.
+
+Every function is pinned by tests in ``tests/test_oracle_pins.py`` against
+values the pages print, closed forms, invariants and brute force.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "moe_oracle.c")
+_SO = os.path.join(_HERE, "liboracle.so")
+
+STAT_NAMES = (
+    "assignments",
+    "kept",
+    "dropped",
+    "padded",
+    "capacity",
+    "send_rows",
+    "dispatch_bytes",
+    "dispatch_wire_bytes",
+    "dispatch_remote_bytes",
+    "combine_bytes",
+    "max_expert_count",
+    "invalid_index",
+)
+
+_lib = None
+
+
+def build() -> str:
+    """Compile the oracle with gcc (no fast-math, no FMA contraction)."""
+    cmd = [
+        "gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
+        "-ffp-contract=off", "-fno-fast-math",
+        _SRC, "-o", _SO + ".tmp", "-lm",
+    ]
+    subprocess.run(cmd, check=True)
+    os.replace(_SO + ".tmp", _SO)
+    return _SO
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_SO) or os.path.getmtime(_SO) < os.path.getmtime(_SRC):
+        build()
+    lib = ctypes.CDLL(_SO)
+    P = ctypes.c_void_p
+    i32 = ctypes.c_int
+    lib.oracle_bf16_from_double.argtypes = [ctypes.c_double]
+    lib.oracle_bf16_from_double.restype = ctypes.c_uint16
+    lib.oracle_logits.argtypes = [i32, i32, i32, P, P, P, P]
+    lib.oracle_logits.restype = None
+    lib.oracle_topk.argtypes = [i32, i32, i32, P, P, P, P]
+    lib.oracle_topk.restype = None
+    lib.oracle_capacity.argtypes = [i32, i32, i32, ctypes.c_double]
+    lib.oracle_capacity.restype = ctypes.c_int64
+    lib.oracle_dispatch.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.c_double,
+                                    P, P, P, P, P, P, P, P, P]
+    lib.oracle_dispatch.restype = ctypes.c_int
+    lib.oracle_expert_ffn.argtypes = [i32, i32, i32, P, P, P, P, P]
+    lib.oracle_expert_ffn.restype = None
+    lib.oracle_combine.argtypes = [i32, i32, i32, P, P, P, P]
+    lib.oracle_combine.restype = None
+    lib.oracle_num_threads.argtypes = []
+    lib.oracle_num_threads.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _ptr(a: np.ndarray | None):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def num_threads() -> int:
+    return int(_load().oracle_num_threads())
+
+
+def bf16_from_double(v: float) -> int:
+    """Raw bits of the bf16 nearest to ``v`` (ties to even)."""
+    return int(_load().oracle_bf16_from_double(float(v)))
+
+
+def logits(x: np.ndarray, w_gate: np.ndarray, bias: np.ndarray | None = None) -> np.ndarray:
+    """H = x W_g (+ b), fp32 [T, E].  x [T, d] bf16 bits, w_gate [d, E] bf16 bits."""
+    x = _c(x, np.uint16)
+    w_gate = _c(w_gate, np.uint16)
+    T, d = x.shape
+    d2, E = w_gate.shape
+    assert d == d2
+    b = None if bias is None else _c(bias, np.float32)
+    out = np.empty((T, E), np.float32)
+    _load().oracle_logits(T, d, E, _ptr(x), _ptr(w_gate), _ptr(b), _ptr(out))
+    return out
+
+
+def topk(lg: np.ndarray, k: int):
+    """KeepTopK + softmax on fp32 logits [T, E] -> (idx int32 [T,k], w fp32 [T,k], gap f64 [T])."""
+    lg = _c(lg, np.float32)
+    T, E = lg.shape
+    assert 1 <= k <= E
+    idx = np.empty((T, k), np.int32)
+    w = np.empty((T, k), np.float32)
+    gap = np.empty((T,), np.float64)
+    _load().oracle_topk(T, E, k, _ptr(lg), _ptr(idx), _ptr(w), _ptr(gap))
+    return idx, w, gap
+
+
+def capacity(T: int, k: int, E: int, cf: float) -> int:
+    return int(_load().oracle_capacity(T, k, E, float(cf)))
+
+
+def dispatch(x: np.ndarray | None, topk_idx: np.ndarray, *, T: int, d: int, E: int,
+             D: int, my_rank: int = 0, cf: float = float("inf"),
+             with_send_buf: bool = True) -> dict:
+    """Histogram, capacity, token-order positions, slots and the send buffer."""
+    topk_idx = _c(topk_idx, np.int32)
+    k = topk_idx.shape[1]
+    assert topk_idx.shape[0] == T
+    C = capacity(T, k, E, cf)
+    send_rows = T * k if C < 0 else E * C
+    send_buf = None
+    if with_send_buf:
+        x = _c(x, np.uint16)
+        assert x.shape == (T, d)
+        send_buf = np.empty((send_rows, d), np.uint16)
+    out = dict(
+        slot=np.empty((T, k), np.int32),
+        expert_count=np.empty((E,), np.int32),
+        expert_kept=np.empty((E,), np.int32),
+        expert_offset=np.empty((E + 1,), np.int64),
+        rank_rows=np.empty((D,), np.int64),
+    )
+    stats = np.empty((len(STAT_NAMES),), np.int64)
+    rc = _load().oracle_dispatch(
+        T, d, E, k, D, my_rank, float(cf),
+        _ptr(x) if with_send_buf else None, _ptr(topk_idx), _ptr(send_buf),
+        _ptr(out["slot"]), _ptr(out["expert_count"]), _ptr(out["expert_kept"]),
+        _ptr(out["expert_offset"]), _ptr(out["rank_rows"]), _ptr(stats))
+    if rc != 0:
+        raise ValueError(f"oracle_dispatch rejected the shape (rc={rc})")
+    out["send_buf"] = send_buf
+    out["stats"] = {n: int(v) for n, v in zip(STAT_NAMES, stats)}
+    return out
+
+
+def expert_ffn(rows: np.ndarray, w1: np.ndarray, w3: np.ndarray, w2: np.ndarray) -> np.ndarray:
+    """One expert's SwiGLU FFN: rows [n, d], w1/w3 [H, d], w2 [d, H] (bf16 bits) -> [n, d]."""
+    rows = _c(rows, np.uint16)
+    w1 = _c(w1, np.uint16)
+    w3 = _c(w3, np.uint16)
+    w2 = _c(w2, np.uint16)
+    n, d = rows.shape
+    H = w1.shape[0]
+    assert w1.shape == (H, d) and w3.shape == (H, d) and w2.shape == (d, H)
+    out = np.empty((n, d), np.uint16)
+    if n:
+        _load().oracle_expert_ffn(n, d, H, _ptr(rows), _ptr(w1), _ptr(w3), _ptr(w2), _ptr(out))
+    return out
+
+
+def combine(expert_out: np.ndarray, slot: np.ndarray, topk_w: np.ndarray) -> np.ndarray:
+    """y[t] = bf16(sum_s G[t,s] * expert_out[slot[t,s]]) over kept s; dropped -> 0."""
+    expert_out = _c(expert_out, np.uint16)
+    slot = _c(slot, np.int32)
+    topk_w = _c(topk_w, np.float32)
+    T, k = slot.shape
+    d = expert_out.shape[1]
+    assert topk_w.shape == (T, k)
+    assert slot.max(initial=-1) < expert_out.shape[0]
+    y = np.empty((T, d), np.uint16)
+    _load().oracle_combine(T, d, k, _ptr(expert_out), _ptr(slot), _ptr(topk_w), _ptr(y))
+    return y
+
+
+def expert_ffn_all(send_buf: np.ndarray, expert_offset: np.ndarray, expert_kept: np.ndarray,
+                   w1: np.ndarray, w3: np.ndarray, w2: np.ndarray) -> np.ndarray:
+    """Every expert's FFN on its kept rows; rows that no assignment fills stay zero."""
+    out = np.zeros_like(send_buf)
+    E = expert_kept.shape[0]
+    for e in range(E):
+        lo, n = int(expert_offset[e]), int(expert_kept[e])
+        if n:
+            out[lo:lo + n] = expert_ffn(send_buf[lo:lo + n], w1[e], w3[e], w2[e])
+    return out
+
+
+def layer_fwd(x, w_gate, w1, w3, w2, *, k: int, D: int, cf: float, my_rank: int = 0,
+              bias=None) -> dict:
+    """The whole forward pass, stage by stage, returning every intermediate."""
+    T, d = x.shape
+    E = w_gate.shape[1]
+    lg = logits(x, w_gate, bias)
+    idx, w, gap = topk(lg, k)
+    disp = dispatch(x, idx, T=T, d=d, E=E, D=D, my_rank=my_rank, cf=cf)
+    eo = expert_ffn_all(disp["send_buf"], disp["expert_offset"], disp["expert_kept"], w1, w3, w2)
+    y = combine(eo, disp["slot"], w)
+    return dict(logits=lg, topk_idx=idx, topk_w=w, gap=gap, expert_out=eo, y=y, **disp)

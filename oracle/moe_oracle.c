@@ -1,0 +1,367 @@
+/*
+ * moe_oracle.c -- plain, slow CPU oracle for the MoE layer forward pass.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or
+ * call this file; only the test suite, the smoke check and the CPU-baseline
+ * leg of the benchmark do.  It shares no code, header, table or helper with
+ * the GPU library: it is written from the page definitions alone.
+ *
+ * Arithmetic: every accumulation is in IEEE double.  Values are rounded to
+ * fp32 or bf16 (round-to-nearest-even, computed from the exact double) only
+ * at the points where the method stores a tensor:
+ *   logits            -> fp32
+ *   gate weights      -> fp32
+ *   SwiGLU hidden h   -> bf16
+ *   expert output     -> bf16
+ *   layer output y    -> bf16
+ *
+ * Sources (page title, section):
+ *   [G]  "Mixture-of-Experts (MoE) Architecture and Expert Parallelism",
+ *        section 2 "The Gating Network Formulation": H(x) = x W_g + eps,
+ *        G(x) = Softmax(KeepTopK(H(x), K)), KeepTopK keeps the K largest
+ *        coordinates and sets the rest to -inf, y = sum_{i in TopK} G_i Expert_i(x).
+ *   [N]  "EP Math -- Expert Parallelism (MoE)", "Notation": T tokens per
+ *        device, d hidden size, T*k assignments per device.
+ *   [DA] same page, "The dispatch all-to-all": T*k*d*2 bytes produced,
+ *        (D-1)/D of it leaves the device.
+ *   [CA] same page, "The combine all-to-all": the exact reverse of dispatch,
+ *        weighted by the gate values and summed at the token's home device.
+ *   [CF] same page, "Capacity factor": C = f * tokens * k / E, rounded up;
+ *        buffer [E, C, d]; under-full experts padded up to C.
+ *   [TD] same page, "Token drop": assignments beyond C are dropped and the
+ *        token passes as if that expert's output were zero.
+ *   [PL] same page, "Placing experts across devices": E/D whole experts per
+ *        device, E divisible by D.
+ *   [M]  "MoE Expert Parallelism Sizing: Traffic, Capacity, Fabric",
+ *        "Memory residency for the same shape": gated three-matrix expert
+ *        (3*d*H parameters); "Capacity semantics decide what crosses the
+ *        wire": dropping happens before the exchange; "First-order dispatch
+ *        and combine bytes": one input chunk per destination rank.
+ *
+ * Readings taken where the pages are silent (each also listed in the design
+ * notes): eps = 0 at inference; an optional per-expert logit bias b is added
+ * to H and enters both selection and softmax; ties in KeepTopK go to the
+ * lower expert index; the kept experts are reported in descending-logit
+ * order; capacity uses the per-device token count T, computed as
+ * ceil(cf*T*k/E) in double; overflow is dropped in token order (the first
+ * C assignments of an expert, by token index, are kept); gates are not
+ * renormalised after a drop; the expert is SwiGLU, W2 (SiLU(W1 x) * (W3 x))
+ * with no biases; placement is contiguous: rank r owns experts
+ * [r*E/D, (r+1)*E/D).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ------------------------------------------------------------------ */
+/* Number formats.                                                     */
+/* ------------------------------------------------------------------ */
+
+/* bf16 is the upper 16 bits of an IEEE binary32. */
+static double bf16_value(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* Round a finite double to the nearest bf16 (ties to even) in one step.
+ * bf16 keeps 8 significant bits and fp32's exponent range, so its spacing
+ * near |v| in [2^e, 2^(e+1)) is 2^(e-7), and 2^-133 below 2^-126. */
+uint16_t oracle_bf16_from_double(double v)
+{
+    uint16_t sign = signbit(v) ? 0x8000u : 0u;
+    if (isnan(v))
+        return 0x7FC0u;
+    if (v == 0.0)
+        return sign;
+    int ex;
+    frexp(v, &ex); /* |v| = m * 2^ex with m in [0.5, 1) */
+    int q = ex - 8; /* spacing exponent for 8 significant bits */
+    if (q < -133)
+        q = -133;
+    double r = ldexp(nearbyint(ldexp(v, -q)), q); /* exact scaling, RNE */
+    if (isinf(r) || fabs(r) >= ldexp(1.0, 128))
+        return (uint16_t)(sign | 0x7F80u);
+    float f = (float)r; /* exact: r has at most 8 significant bits */
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return (uint16_t)(u >> 16);
+}
+
+/* ------------------------------------------------------------------ */
+/* Step 1: router logits  H = x W_g (+ b),  eps = 0.        [G]        */
+/* x [T, d] bf16, w_gate [d, E] bf16 (d_model x E as on the page),     */
+/* bias [E] fp32 or NULL, logits [T, E] fp32.                          */
+/* ------------------------------------------------------------------ */
+void oracle_logits(int T, int d, int E, const uint16_t *x, const uint16_t *w_gate,
+                   const float *bias, float *logits)
+{
+#pragma omp parallel for schedule(static)
+    for (int t = 0; t < T; ++t) {
+        for (int e = 0; e < E; ++e) {
+            double acc = 0.0;
+            for (int j = 0; j < d; ++j)
+                acc += bf16_value(x[(size_t)t * d + j]) * bf16_value(w_gate[(size_t)j * E + e]);
+            if (bias)
+                acc += (double)bias[e];
+            logits[(size_t)t * E + e] = (float)acc;
+        }
+    }
+}
+
+/* ------------------------------------------------------------------ */
+/* Step 2: G = Softmax(KeepTopK(H, k)).                      [G]       */
+/* KeepTopK by rank: rank(e) = #{e' : h_e' > h_e, or h_e' == h_e and   */
+/* e' < e}.  Expert e is kept iff rank(e) < k; it is written to output */
+/* position rank(e).  The softmax over the kept logits equals the      */
+/* softmax over the KeepTopK vector, whose other entries are -inf and  */
+/* contribute exp(-inf) = 0.  gap[t] = h_(k) - h_(k+1), the distance   */
+/* between the last kept and the first rejected order statistic        */
+/* (+inf when k == E).                                                 */
+/* ------------------------------------------------------------------ */
+void oracle_topk(int T, int E, int k, const float *logits, int32_t *topk_idx,
+                 float *topk_w, double *gap)
+{
+#pragma omp parallel for schedule(static)
+    for (int t = 0; t < T; ++t) {
+        const float *h = logits + (size_t)t * E;
+        double first_rejected = -INFINITY;
+        int have_rejected = 0;
+        for (int e = 0; e < E; ++e) {
+            int rank = 0;
+            for (int e2 = 0; e2 < E; ++e2)
+                if (h[e2] > h[e] || (h[e2] == h[e] && e2 < e))
+                    ++rank;
+            if (rank < k) {
+                topk_idx[(size_t)t * k + rank] = e;
+            } else if (rank == k) {
+                first_rejected = (double)h[e];
+                have_rejected = 1;
+            }
+        }
+        /* softmax over the kept logits, max-subtracted (the maximum is the
+         * rank-0 entry); mathematically identical to the plain softmax */
+        double hmax = (double)h[topk_idx[(size_t)t * k]];
+        double denom = 0.0;
+        for (int s = 0; s < k; ++s)
+            denom += exp((double)h[topk_idx[(size_t)t * k + s]] - hmax);
+        for (int s = 0; s < k; ++s)
+            topk_w[(size_t)t * k + s] =
+                (float)(exp((double)h[topk_idx[(size_t)t * k + s]] - hmax) / denom);
+        if (gap) {
+            double last_kept = (double)h[topk_idx[(size_t)t * k + k - 1]];
+            gap[t] = have_rejected ? last_kept - first_rejected : INFINITY;
+        }
+    }
+}
+
+/* ------------------------------------------------------------------ */
+/* Step 3: capacity.                                         [CF]      */
+/* C = ceil(cf * T * k / E) evaluated left to right in IEEE double.    */
+/* cf = +inf means dropless; returns -1 then.                          */
+/* ------------------------------------------------------------------ */
+int64_t oracle_capacity(int T, int k, int E, double cf)
+{
+    if (isinf(cf))
+        return -1;
+    return (int64_t)ceil(cf * (double)T * (double)k / (double)E);
+}
+
+/* Indices into the stats vector filled by oracle_dispatch. */
+enum {
+    ST_ASSIGNMENTS = 0, /* T*k                                          [N]  */
+    ST_KEPT,            /* assignments that reach an expert                   */
+    ST_DROPPED,         /* assignments - kept                            [TD] */
+    ST_PADDED,          /* E*C - kept in capacity mode, else 0           [CF] */
+    ST_CAPACITY,        /* C, or -1 when dropless                        [CF] */
+    ST_SEND_ROWS,       /* rows of the send buffer: E*C, or T*k               */
+    ST_DISPATCH_BYTES,  /* kept * d * 2: token vectors that travel       [DA] */
+    ST_WIRE_BYTES,      /* send_rows * d * 2 in capacity mode (pads
+                           included), kept*d*2 when dropless             [CF] */
+    ST_REMOTE_BYTES,    /* kept rows bound for ranks != my_rank, *d*2    [DA] */
+    ST_COMBINE_BYTES,   /* = dispatch bytes: combine reverses dispatch   [CA] */
+    ST_MAX_COUNT,       /* max_e n_e                                          */
+    ST_INVALID,         /* indices outside [0, E): counted, then dropped      */
+    ST_COUNT
+};
+
+/* ------------------------------------------------------------------ */
+/* Step 3/4: histogram, capacity, positions and the dispatch layout.   */
+/*                                                   [N][CF][TD][PL][M] */
+/* Positions: assignments are visited in ascending token order; the    */
+/* position of (t, s) in expert e is the number of earlier tokens       */
+/* routed to e (a token's k experts are distinct, so the slot order    */
+/* inside one token never matters).  An assignment is kept iff its     */
+/* position is below C.  Layout: capacity mode gives expert e the rows */
+/* [e*C, (e+1)*C) (pads left zero); dropless packs experts back to     */
+/* back, offset_e = n_0 + ... + n_(e-1).  Experts are in ascending     */
+/* order, so rank r's chunk -- the part the dispatch all-to-all sends  */
+/* to rank r -- is rows [offset[r*E/D], offset[(r+1)*E/D]).            */
+/* send_buf [send_rows, d] may be NULL (accounting only).              */
+/* ------------------------------------------------------------------ */
+int oracle_dispatch(int T, int d, int E, int k, int D, int my_rank, double cf,
+                    const uint16_t *x, const int32_t *topk_idx, uint16_t *send_buf,
+                    int32_t *slot, int32_t *expert_count, int32_t *expert_kept,
+                    int64_t *expert_offset, int64_t *rank_rows, int64_t *stats)
+{
+    if (D <= 0 || E % D != 0 || my_rank < 0 || my_rank >= D)
+        return -1;
+    int64_t C = oracle_capacity(T, k, E, cf);
+    int32_t *running = calloc((size_t)E, sizeof *running);
+    int32_t *position = malloc((size_t)T * k * sizeof *position);
+    if (!running || !position) {
+        free(running);
+        free(position);
+        return -2;
+    }
+    int64_t invalid = 0;
+    for (int e = 0; e < E; ++e)
+        expert_count[e] = 0;
+    /* histogram and token-order positions */
+    for (int t = 0; t < T; ++t) {
+        for (int s = 0; s < k; ++s) {
+            int32_t e = topk_idx[(size_t)t * k + s];
+            if (e < 0 || e >= E) {
+                position[(size_t)t * k + s] = -1;
+                ++invalid;
+                continue;
+            }
+            position[(size_t)t * k + s] = running[e]++;
+            expert_count[e]++;
+        }
+    }
+    /* kept counts and offsets */
+    int64_t kept_total = 0, max_count = 0;
+    int64_t acc = 0;
+    for (int e = 0; e < E; ++e) {
+        int64_t n = expert_count[e];
+        int64_t kept = (C < 0 || n < C) ? n : C;
+        expert_kept[e] = (int32_t)kept;
+        kept_total += kept;
+        if (n > max_count)
+            max_count = n;
+        expert_offset[e] = (C < 0) ? acc : (int64_t)e * C;
+        acc += n;
+    }
+    int64_t send_rows = (C < 0) ? (int64_t)T * k : (int64_t)E * C;
+    expert_offset[E] = (C < 0) ? acc : (int64_t)E * C;
+    /* slots and the send buffer */
+    if (send_buf)
+        memset(send_buf, 0, (size_t)send_rows * d * sizeof *send_buf);
+    for (int t = 0; t < T; ++t) {
+        for (int s = 0; s < k; ++s) {
+            int32_t e = topk_idx[(size_t)t * k + s];
+            int32_t p = position[(size_t)t * k + s];
+            int32_t sl = -1;
+            if (p >= 0 && (C < 0 || p < C))
+                sl = (int32_t)(expert_offset[e] + p);
+            slot[(size_t)t * k + s] = sl;
+            if (sl >= 0 && send_buf)
+                memcpy(send_buf + (size_t)sl * d, x + (size_t)t * d, (size_t)d * sizeof *x);
+        }
+    }
+    /* per-rank rows (kept token vectors per destination) */
+    int epr = E / D;
+    int64_t remote_rows = 0;
+    for (int r = 0; r < D; ++r) {
+        int64_t rows = 0;
+        for (int e = r * epr; e < (r + 1) * epr; ++e)
+            rows += expert_kept[e];
+        rank_rows[r] = rows;
+        if (r != my_rank)
+            remote_rows += rows;
+    }
+    stats[ST_ASSIGNMENTS] = (int64_t)T * k;
+    stats[ST_KEPT] = kept_total;
+    stats[ST_DROPPED] = (int64_t)T * k - kept_total;
+    stats[ST_PADDED] = (C < 0) ? 0 : (int64_t)E * C - kept_total;
+    stats[ST_CAPACITY] = C;
+    stats[ST_SEND_ROWS] = send_rows;
+    stats[ST_DISPATCH_BYTES] = kept_total * d * 2;
+    stats[ST_WIRE_BYTES] = (C < 0) ? kept_total * d * 2 : send_rows * d * 2;
+    stats[ST_REMOTE_BYTES] = remote_rows * d * 2;
+    stats[ST_COMBINE_BYTES] = kept_total * d * 2;
+    stats[ST_MAX_COUNT] = max_count;
+    stats[ST_INVALID] = invalid;
+    free(running);
+    free(position);
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* Step 5: one expert's SwiGLU FFN on n rows.                 [M]      */
+/* rows [n, d] bf16; w1, w3 [H, d] bf16; w2 [d, H] bf16; out [n, d].   */
+/* g = W1 x, u = W3 x (double), h = bf16(SiLU(g) * u) with             */
+/* SiLU(z) = z / (1 + exp(-z)), out = bf16(W2 h).                      */
+/* ------------------------------------------------------------------ */
+void oracle_expert_ffn(int n, int d, int H, const uint16_t *rows, const uint16_t *w1,
+                       const uint16_t *w3, const uint16_t *w2, uint16_t *out)
+{
+#pragma omp parallel
+    {
+        double *xr = malloc((size_t)d * sizeof *xr);
+        double *h = malloc((size_t)H * sizeof *h);
+#pragma omp for schedule(dynamic, 1)
+        for (int r = 0; r < n; ++r) {
+            for (int i = 0; i < d; ++i)
+                xr[i] = bf16_value(rows[(size_t)r * d + i]);
+            for (int j = 0; j < H; ++j) {
+                double g = 0.0, u = 0.0;
+                for (int i = 0; i < d; ++i) {
+                    g += xr[i] * bf16_value(w1[(size_t)j * d + i]);
+                    u += xr[i] * bf16_value(w3[(size_t)j * d + i]);
+                }
+                double silu = g / (1.0 + exp(-g));
+                h[j] = bf16_value(oracle_bf16_from_double(silu * u));
+            }
+            for (int m = 0; m < d; ++m) {
+                double o = 0.0;
+                for (int j = 0; j < H; ++j)
+                    o += h[j] * bf16_value(w2[(size_t)m * H + j]);
+                out[(size_t)r * d + m] = oracle_bf16_from_double(o);
+            }
+        }
+        free(xr);
+        free(h);
+    }
+}
+
+/* ------------------------------------------------------------------ */
+/* Step 6: combine.                                     [G][CA][TD]    */
+/* y[t] = bf16( sum over kept s, in rank order, of G[t,s] * O[slot] ). */
+/* A dropped assignment (slot < 0) adds nothing; the residual is the   */
+/* caller's.  expert_out [*, d] bf16, slot/topk_w [T, k], y [T, d].    */
+/* ------------------------------------------------------------------ */
+void oracle_combine(int T, int d, int k, const uint16_t *expert_out, const int32_t *slot,
+                    const float *topk_w, uint16_t *y)
+{
+#pragma omp parallel for schedule(static)
+    for (int t = 0; t < T; ++t) {
+        for (int m = 0; m < d; ++m) {
+            double acc = 0.0;
+            for (int s = 0; s < k; ++s) {
+                int32_t sl = slot[(size_t)t * k + s];
+                if (sl < 0)
+                    continue;
+                acc += (double)topk_w[(size_t)t * k + s] *
+                       bf16_value(expert_out[(size_t)sl * d + m]);
+            }
+            y[(size_t)t * d + m] = oracle_bf16_from_double(acc);
+        }
+    }
+}
+
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
