@@ -1,0 +1,234 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoE layer forward on one MI355X.
+
+One step is one pass of the whole path over one batch: route (logit GEMM +
+KeepTopK/softmax), dispatch (histogram, capacity, permute), the SwiGLU
+grouped GEMMs (gate/up, then down) and the combine, each through its C-ABI
+entry point on one stream.  HIP events recorded on that stream around every
+stage give per-stage durations over the timed region; the dominant kernel's
+roofline is computed from its algorithmic bytes and flops.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores, TFLOP/s
+METRIC = "MoE layer tokens/s + grouped-GEMM MFMA util, DeepSeek-V3-shaped T=4096"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def stage_traffic(cfg, st, touched):
+    """Algorithmic HBM bytes and flops of each stage for one call."""
+    T, d, E, k, H = cfg.T, cfg.d, cfg.E, cfg.k, cfg.H
+    kept, send_rows = st["kept"], st["send_rows"]
+    return {
+        "route": dict(bytes=T * d * 2 + d * E * 2 + T * k * 8, flops=2 * T * d * E),
+        "dispatch": dict(bytes=T * d * 2 + send_rows * d * 2 + T * k * 8, flops=0),
+        "gate_up": dict(bytes=touched * 2 * H * d * 2 + kept * d * 2 + kept * H * 2,
+                        flops=4 * kept * d * H),
+        "down": dict(bytes=touched * d * H * 2 + kept * H * 2 + kept * d * 2,
+                     flops=2 * kept * d * H),
+        "combine": dict(bytes=kept * d * 2 + T * d * 2 + T * k * 8, flops=0),
+    }
+
+
+def kernel_source_digest():
+    h = hashlib.sha256()
+    for name in ("ffn.hip", "moe_internal.hpp"):
+        with open(os.path.join(ROOT, "expert_token_routing_moe_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    ent = rec.get(workload, {}).get(kernel)
+    if not ent or ent.get("source_digest") != kernel_source_digest():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(cfg, inp, budget_s):
+    """The oracle as it stands, on the first tokens of the same workload."""
+    import numpy as np
+
+    import oracle
+    from expert_token_routing_moe_amd.inputs import bf16_bits
+
+    x = bf16_bits(inp["x"])
+    wg = bf16_bits(inp["w_gate"])
+    bias = None if inp["bias"] is None else inp["bias"].cpu().numpy()
+    experts = {}
+    batch = 16
+    done, spent = 0, 0.0
+    while done < cfg.T and spent < budget_s:
+        xb = x[done:done + batch]
+        tb = xb.shape[0]
+        t0 = time.perf_counter()
+        lg = oracle.logits(xb, wg, bias)
+        idx, w, _ = oracle.topk(lg, cfg.k)
+        r = oracle.dispatch(xb, idx, T=tb, d=cfg.d, E=cfg.E, D=cfg.D, cf=cfg.cf)
+        spent += time.perf_counter() - t0
+        need = [e for e in range(cfg.E) if r["expert_kept"][e] and e not in experts]
+        for e in need:  # weight copies to the host are not oracle work: not timed
+            experts[e] = tuple(bf16_bits(inp[n][e]) for n in ("w1", "w3", "w2"))
+        t0 = time.perf_counter()
+        eo = np.zeros_like(r["send_buf"])
+        for e in range(cfg.E):
+            lo, n = int(r["expert_offset"][e]), int(r["expert_kept"][e])
+            if n:
+                eo[lo:lo + n] = oracle.expert_ffn(r["send_buf"][lo:lo + n], *experts[e])
+        oracle.combine(eo, r["slot"], w)
+        spent += time.perf_counter() - t0
+        done += tb
+        log(f"  cpu oracle: {done} tokens in {spent:.1f} s")
+    return dict(value=done / spent, unit="tokens/s", cores=oracle.num_threads(), kind="oracle",
+                sample=f"first {done} of {cfg.T} tokens of the {cfg.name} workload, in batches "
+                       f"of {batch}: route, dispatch, SwiGLU experts and combine in fp64 "
+                       f"({spent:.1f} s of oracle compute)")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="dsv3_prefill")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs the single-GPU share of the MoE layer only: every box here has "
+              "one GPU and this build has no multi-GPU path; use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from expert_token_routing_moe_amd import api
+    from expert_token_routing_moe_amd.inputs import CONFIGS, make_inputs
+
+    cfg = CONFIGS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"bench: {cfg.name} T={cfg.T} d={cfg.d} E={cfg.E} k={cfg.k} H={cfg.H} cf={cfg.cf}")
+    inp = make_inputs(cfg, dev)
+    shape = api.Shape.from_config(cfg)
+    buf = api.LayerBuffers.allocate(shape, dev, keep_logits=False)
+    h = torch.empty(max(buf.send_buf.shape[0], 0), cfg.H, dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+    stages = ["route", "dispatch", "gate_up", "down", "combine"]
+
+    def step(ev=None):
+        rec = (lambda i: ev[i].record(stream)) if ev else (lambda i: None)
+        rec(0)
+        api.moe_route(shape, inp["x"], inp["w_gate"], inp["bias"], None, buf.topk_idx,
+                      buf.topk_w, buf.workspace, stream)
+        rec(1)
+        api.moe_dispatch(shape, inp["x"], buf.topk_idx, buf.send_buf, buf.slot,
+                         buf.expert_count, buf.expert_kept, buf.expert_offset, buf.rank_rows,
+                         buf.stats, buf.workspace, stream)
+        rec(2)
+        api.moe_expert_gate_up(shape, buf.send_buf, buf.expert_offset, buf.expert_kept,
+                               inp["w1"], inp["w3"], h, stream)
+        rec(3)
+        api.moe_expert_down(shape, h, buf.expert_offset, buf.expert_kept, inp["w2"],
+                            buf.expert_out, stream)
+        rec(4)
+        api.moe_combine(shape, buf.expert_out, buf.slot, buf.topk_w, buf.y, stream)
+        rec(5)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"bench: warmup {args.warmup} done")
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    stage_ms = {s: sum(events[i][j].elapsed_time(events[i][j + 1]) for i in range(args.steps))
+                / args.steps for j, s in enumerate(stages)}
+    log(f"bench: {args.steps} steps, {ms_step:.3f} ms/step; stages (ms): "
+        + ", ".join(f"{s}={v:.4f}" for s, v in stage_ms.items()))
+
+    st = api.stats_dict(buf.stats)
+    touched = int((buf.expert_kept > 0).sum().item())
+    traffic = stage_traffic(cfg, st, touched)
+    per_stage = {}
+    for s in stages:
+        t = stage_ms[s] / 1e3
+        per_stage[s] = dict(ms=round(stage_ms[s], 5),
+                            gbs=round(traffic[s]["bytes"] / t / 1e9, 1),
+                            hbm_frac=round(traffic[s]["bytes"] / t / 1e9 / HBM_PEAK_GBS, 4),
+                            tflops=round(traffic[s]["flops"] / t / 1e12, 2))
+    dom = max(("gate_up", "down"), key=lambda s: stage_ms[s])
+    t_dom = stage_ms[dom] / 1e3
+    intensity = traffic[dom]["flops"] / traffic[dom]["bytes"]
+    ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if intensity < ridge:
+        achieved = traffic[dom]["bytes"] / t_dom / 1e9
+        roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s")
+    else:
+        achieved = traffic[dom]["flops"] / t_dom / 1e12
+        roof = dict(bound="mfma", achieved=round(achieved, 1), peak=MFMA_BF16_PEAK_TFLOPS,
+                    unit="TFLOP/s")
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = measured_traffic(dom, cfg.name)
+    roof["kernel"] = f"grouped_gemm {dom}"
+    gemm_flops = traffic["gate_up"]["flops"] + traffic["down"]["flops"]
+    gemm_s = (stage_ms["gate_up"] + stage_ms["down"]) / 1e3
+    out = {
+        "metric": METRIC,
+        "value": round(cfg.T / (ms_step / 1e3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "E": cfg.E, "k": cfg.k,
+                   "H": cfg.H, "capacity_factor": None if cfg.cf == float("inf") else cfg.cf,
+                   "D": cfg.D, "parallelism": "single GPU share (EP rank-local layout)"},
+        "grouped_gemm": {"tflops": round(gemm_flops / gemm_s / 1e12, 1),
+                         "mfma_util": round(gemm_flops / gemm_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                         "touched_experts": touched},
+        "stages": per_stage,
+        "counts": {k: st[k] for k in ("kept", "dropped", "padded", "max_expert_count")},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        log("bench: timing the CPU oracle on a bounded sample")
+        out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

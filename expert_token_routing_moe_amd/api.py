@@ -1,0 +1,245 @@
+"""Python binding of the C ABI in ``include/moe.h`` (argument marshalling only).
+
+Every function here has the name of the C entry point it calls and forwards
+``torch`` tensor data pointers to it; all computation happens in the gfx950
+kernels of ``libmoe_mi355x.so``.  There is no fallback: if the library is not
+built, or a call returns an error status, a ``MoEError`` is raised.
+
+bf16 tensors are ``torch.bfloat16``; index tensors ``torch.int32``; gates and
+logits ``torch.float32``.  Every tensor must be contiguous and on the GPU
+(except for ``moe_query``, which is host-only).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_mi355x.so")
+
+MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = 0, -1, -2, -3, -4
+
+STAT_NAMES = (
+    "assignments", "kept", "dropped", "padded", "capacity", "send_rows",
+    "dispatch_bytes", "dispatch_wire_bytes", "dispatch_remote_bytes",
+    "combine_bytes", "max_expert_count", "invalid_index",
+)
+
+
+class MoEError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed with status {status}: {msg}")
+        self.status = status
+
+
+class moe_shape(ctypes.Structure):
+    _fields_ = [
+        ("T", ctypes.c_int32), ("d", ctypes.c_int32), ("E", ctypes.c_int32),
+        ("k", ctypes.c_int32), ("H", ctypes.c_int32), ("D", ctypes.c_int32),
+        ("my_rank", ctypes.c_int32), ("drop_policy", ctypes.c_int32),
+        ("capacity_factor", ctypes.c_double),
+    ]
+
+
+_lib = None
+
+
+def lib():
+    """Load the built library; raise if it is missing (there is no fallback)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise MoEError("load", MOE_EHIP,
+                       f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+    L = ctypes.CDLL(LIB_PATH)
+    P, S, I, SZ = ctypes.c_void_p, ctypes.POINTER(moe_shape), ctypes.c_int, ctypes.c_size_t
+    sig = {
+        "moe_query": [S, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64),
+                      ctypes.POINTER(ctypes.c_size_t)],
+        "moe_route": [S, P, P, P, P, P, P, P, SZ, P],
+        "moe_topk_from_logits": [S, P, P, P, P],
+        "moe_dispatch": [S, P, P, P, P, P, P, P, P, P, P, SZ, P],
+        "moe_expert_ffn": [S, P, P, P, P, P, P, P, P, SZ, P],
+        "moe_expert_gate_up": [S, P, P, P, P, P, P, P],
+        "moe_expert_down": [S, P, P, P, P, P, P],
+        "moe_combine": [S, P, P, P, P, P],
+        "moe_layer_fwd": [S] + [P] * 19 + [SZ, P],
+    }
+    for name, argtypes in sig.items():
+        f = getattr(L, name)
+        f.argtypes = argtypes
+        f.restype = I
+    L.moe_status_str.argtypes = [I]
+    L.moe_status_str.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def _check(fn: str, rc: int):
+    if rc != MOE_OK:
+        raise MoEError(fn, rc, lib().moe_status_str(rc).decode())
+
+
+@dataclass(frozen=True)
+class Shape:
+    """Python mirror of ``moe_shape`` (pages' notation)."""
+
+    T: int
+    d: int
+    E: int
+    k: int
+    H: int
+    D: int = 1
+    my_rank: int = 0
+    capacity_factor: float = math.inf
+    drop_policy: int = 0
+
+    def c(self) -> moe_shape:
+        return moe_shape(self.T, self.d, self.E, self.k, self.H, self.D, self.my_rank,
+                         self.drop_policy, float(self.capacity_factor))
+
+    @classmethod
+    def from_config(cls, cfg) -> "Shape":
+        return cls(cfg.T, cfg.d, cfg.E, cfg.k, cfg.H, cfg.D, cfg.my_rank, cfg.cf)
+
+
+def _p(t: torch.Tensor | None, dtype=None):
+    if t is None:
+        return None
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"expected {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    if not t.is_cuda:
+        raise ValueError("tensor must be on the GPU")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+BF16, I32, F32 = torch.bfloat16, torch.int32, torch.float32
+
+
+def moe_query(shape: Shape):
+    """-> (send_rows, capacity, workspace_bytes); host only."""
+    sr, cap, ws = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_size_t()
+    s = shape.c()
+    _check("moe_query", lib().moe_query(ctypes.byref(s), ctypes.byref(sr), ctypes.byref(cap),
+                                        ctypes.byref(ws)))
+    return sr.value, cap.value, ws.value
+
+
+def moe_route(shape, x, w_gate, logit_bias, logits_out, topk_idx, topk_w, workspace,
+              stream=None):
+    s = shape.c()
+    _check("moe_route", lib().moe_route(
+        ctypes.byref(s), _p(x, BF16), _p(w_gate, BF16), _p(logit_bias, F32),
+        _p(logits_out, F32), _p(topk_idx, I32), _p(topk_w, F32), _p(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def moe_topk_from_logits(shape, logits, topk_idx, topk_w, stream=None):
+    s = shape.c()
+    _check("moe_topk_from_logits", lib().moe_topk_from_logits(
+        ctypes.byref(s), _p(logits, F32), _p(topk_idx, I32), _p(topk_w, F32), _stream(stream)))
+
+
+def moe_dispatch(shape, x, topk_idx, send_buf, slot, expert_count, expert_kept, expert_offset,
+                 rank_rows, stats, workspace, stream=None):
+    s = shape.c()
+    _check("moe_dispatch", lib().moe_dispatch(
+        ctypes.byref(s), _p(x, BF16), _p(topk_idx, I32), _p(send_buf, BF16), _p(slot, I32),
+        _p(expert_count, I32), _p(expert_kept, I32), _p(expert_offset, I32),
+        _p(rank_rows, I32), _p(stats, torch.int64), _p(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def moe_expert_ffn(shape, send_buf, expert_offset, expert_kept, w1, w3, w2, expert_out,
+                   workspace, stream=None):
+    s = shape.c()
+    _check("moe_expert_ffn", lib().moe_expert_ffn(
+        ctypes.byref(s), _p(send_buf, BF16), _p(expert_offset, I32), _p(expert_kept, I32),
+        _p(w1, BF16), _p(w3, BF16), _p(w2, BF16), _p(expert_out, BF16), _p(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def moe_expert_gate_up(shape, send_buf, expert_offset, expert_kept, w1, w3, h, stream=None):
+    s = shape.c()
+    _check("moe_expert_gate_up", lib().moe_expert_gate_up(
+        ctypes.byref(s), _p(send_buf, BF16), _p(expert_offset, I32), _p(expert_kept, I32),
+        _p(w1, BF16), _p(w3, BF16), _p(h, BF16), _stream(stream)))
+
+
+def moe_expert_down(shape, h, expert_offset, expert_kept, w2, expert_out, stream=None):
+    s = shape.c()
+    _check("moe_expert_down", lib().moe_expert_down(
+        ctypes.byref(s), _p(h, BF16), _p(expert_offset, I32), _p(expert_kept, I32),
+        _p(w2, BF16), _p(expert_out, BF16), _stream(stream)))
+
+
+def moe_combine(shape, expert_out, slot, topk_w, y, stream=None):
+    s = shape.c()
+    _check("moe_combine", lib().moe_combine(
+        ctypes.byref(s), _p(expert_out, BF16), _p(slot, I32), _p(topk_w, F32), _p(y, BF16),
+        _stream(stream)))
+
+
+def moe_layer_fwd(shape, x, w_gate, logit_bias, w1, w3, w2, buf: "LayerBuffers", stream=None):
+    s = shape.c()
+    _check("moe_layer_fwd", lib().moe_layer_fwd(
+        ctypes.byref(s), _p(x, BF16), _p(w_gate, BF16), _p(logit_bias, F32), _p(w1, BF16),
+        _p(w3, BF16), _p(w2, BF16), _p(buf.y, BF16), _p(buf.logits, F32),
+        _p(buf.topk_idx, I32), _p(buf.topk_w, F32), _p(buf.send_buf, BF16), _p(buf.slot, I32),
+        _p(buf.expert_count, I32), _p(buf.expert_kept, I32), _p(buf.expert_offset, I32),
+        _p(buf.rank_rows, I32), _p(buf.stats, torch.int64), _p(buf.expert_out, BF16),
+        _p(buf.workspace), buf.workspace.numel(), _stream(stream)))
+
+
+@dataclass
+class LayerBuffers:
+    """Every output and intermediate of one layer call, plus the workspace."""
+
+    y: torch.Tensor
+    logits: torch.Tensor | None
+    topk_idx: torch.Tensor
+    topk_w: torch.Tensor
+    send_buf: torch.Tensor
+    slot: torch.Tensor
+    expert_count: torch.Tensor
+    expert_kept: torch.Tensor
+    expert_offset: torch.Tensor
+    rank_rows: torch.Tensor
+    stats: torch.Tensor
+    expert_out: torch.Tensor
+    workspace: torch.Tensor
+
+    @classmethod
+    def allocate(cls, shape: Shape, device="cuda", keep_logits: bool = True) -> "LayerBuffers":
+        send_rows, _, ws = moe_query(shape)
+        dev = torch.device(device)
+        T, d, E, k, D = shape.T, shape.d, shape.E, shape.k, shape.D
+        z = lambda *s, dt: torch.empty(s, dtype=dt, device=dev)
+        return cls(
+            y=z(T, d, dt=BF16),
+            logits=z(T, E, dt=F32) if keep_logits else None,
+            topk_idx=z(T, k, dt=I32), topk_w=z(T, k, dt=F32),
+            send_buf=z(send_rows, d, dt=BF16), slot=z(T, k, dt=I32),
+            expert_count=z(E, dt=I32), expert_kept=z(E, dt=I32),
+            expert_offset=z(E + 1, dt=I32), rank_rows=z(D, dt=I32),
+            stats=z(len(STAT_NAMES), dt=torch.int64),
+            expert_out=z(send_rows, d, dt=BF16),
+            workspace=z(ws, dt=torch.uint8),
+        )
+
+
+def stats_dict(stats: torch.Tensor) -> dict:
+    return {n: int(v) for n, v in zip(STAT_NAMES, stats.cpu().tolist())}

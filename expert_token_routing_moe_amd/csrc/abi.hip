@@ -1,0 +1,304 @@
+// C ABI of the library (declared in include/moe.h): host-side validation,
+// workspace carving and stream-ordered launch sequencing.  No allocation, no
+// host synchronisation, no state kept between calls.
+#include <math.h>
+
+#include <algorithm>
+
+#include "moe_internal.hpp"
+
+#define MOE_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace moe {
+
+static size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
+
+Workspace workspace_layout(const Dims &dm)
+{
+    Workspace w{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off = align_up(off + bytes);
+        return at;
+    };
+    w.logits = take((size_t)dm.T * dm.E * sizeof(float));
+    w.chunk_counts = take((size_t)dm.nchunks * dm.E * sizeof(int32_t));
+    w.chunk_base = take((size_t)dm.nchunks * dm.E * sizeof(int32_t));
+    w.chunk_invalid = take((size_t)dm.nchunks * sizeof(int32_t));
+    w.h = take((size_t)dm.send_rows * dm.H * sizeof(uint16_t));
+    w.total = std::max<size_t>(off, 256);
+    return w;
+}
+
+// Validates the shape and derives the per-call facts; MOE_OK or an error.
+static int make_dims(const moe_shape *s, Dims *dm)
+{
+    if (!s)
+        return MOE_EINVAL;
+    if (s->T < 0 || s->d <= 0 || s->E <= 0 || s->k <= 0 || s->H <= 0 || s->D <= 0)
+        return MOE_EINVAL;
+    if (s->k > s->E || s->E % s->D != 0 || s->my_rank < 0 || s->my_rank >= s->D)
+        return MOE_EINVAL;
+    const double cf = s->capacity_factor;
+    if (isnan(cf) || cf <= 0.0)
+        return MOE_EINVAL;
+    if (s->d % 8 != 0)
+        return MOE_EINVAL;
+    if (s->drop_policy != 0)
+        return MOE_EUNSUPPORTED;
+    if (s->d % 64 != 0 || s->H % 64 != 0 || s->E > kMaxExperts)
+        return MOE_EUNSUPPORTED;
+    const long long assignments = (long long)s->T * s->k;
+    if (assignments > INT32_MAX)
+        return MOE_EUNSUPPORTED;
+    long long C = -1, send_rows = assignments;
+    if (!isinf(cf)) {
+        // C = ceil(cf * T * k / E), evaluated left to right in double
+        const double c = ceil(cf * (double)s->T * (double)s->k / (double)s->E);
+        if (c > (double)INT32_MAX)
+            return MOE_EUNSUPPORTED;
+        C = (long long)c;
+        send_rows = (long long)s->E * C;
+    }
+    if (send_rows > INT32_MAX)
+        return MOE_EUNSUPPORTED;
+    // grouped-GEMM grids: (row tiles + E) * N tiles must fit a 1-D grid
+    const long long mtiles = (send_rows + 127) / 128 + s->E;
+    if (mtiles * (s->H / 64) > INT32_MAX / 2 || mtiles * (s->d / 64) > INT32_MAX / 2)
+        return MOE_EUNSUPPORTED;
+    dm->T = s->T;
+    dm->d = s->d;
+    dm->E = s->E;
+    dm->k = s->k;
+    dm->H = s->H;
+    dm->D = s->D;
+    dm->my_rank = s->my_rank;
+    dm->capacity = C;
+    dm->send_rows = send_rows;
+    dm->nchunks = (s->T + kChunk - 1) / kChunk;
+    return MOE_OK;
+}
+
+// A required pointer may be NULL only when its tensor has no elements.
+static bool bad_ptr(const void *p, long long elems = 1)
+{
+    return (p == nullptr && elems > 0) || ((uintptr_t)p & 15u) != 0;
+}
+static bool bad_opt_ptr(const void *p) { return p != nullptr && ((uintptr_t)p & 15u) != 0; }
+
+static int check_ws(const Dims &dm, const void *ws, size_t ws_bytes, Workspace *wl)
+{
+    *wl = workspace_layout(dm);
+    if (ws == nullptr || ((uintptr_t)ws & 255u) != 0 || ws_bytes < wl->total)
+        return MOE_EWORKSPACE;
+    return MOE_OK;
+}
+
+static int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
+
+} // namespace moe
+
+using namespace moe;
+
+MOE_EXPORT int moe_query(const moe_shape *shape, int64_t *send_rows, int64_t *capacity,
+                         size_t *workspace_bytes)
+{
+    Dims dm;
+    const int rc = make_dims(shape, &dm);
+    if (rc != MOE_OK)
+        return rc;
+    if (send_rows)
+        *send_rows = dm.send_rows;
+    if (capacity)
+        *capacity = dm.capacity;
+    if (workspace_bytes)
+        *workspace_bytes = workspace_layout(dm).total;
+    return MOE_OK;
+}
+
+MOE_EXPORT int moe_route(const moe_shape *shape, const uint16_t *x, const uint16_t *w_gate,
+                         const float *logit_bias, float *logits_out, int32_t *topk_idx,
+                         float *topk_w, void *workspace, size_t workspace_bytes, void *stream)
+{
+    Dims dm;
+    int rc = make_dims(shape, &dm);
+    if (rc != MOE_OK)
+        return rc;
+    if (bad_ptr(x, dm.T) || bad_ptr(w_gate) || bad_ptr(topk_idx, dm.T) ||
+        bad_ptr(topk_w, dm.T) || bad_opt_ptr(logit_bias) || bad_opt_ptr(logits_out))
+        return MOE_EINVAL;
+    Workspace wl;
+    if ((rc = check_ws(dm, workspace, workspace_bytes, &wl)) != MOE_OK)
+        return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    float *lg = logits_out ? logits_out : reinterpret_cast<float *>((char *)workspace + wl.logits);
+    hipError_t e = launch_router_logits(dm, x, w_gate, logit_bias, lg, st);
+    if (e == hipSuccess)
+        e = launch_topk_softmax(dm, lg, topk_idx, topk_w, st);
+    return hip_status(e);
+}
+
+MOE_EXPORT int moe_topk_from_logits(const moe_shape *shape, const float *logits,
+                                    int32_t *topk_idx, float *topk_w, void *stream)
+{
+    Dims dm;
+    const int rc = make_dims(shape, &dm);
+    if (rc != MOE_OK)
+        return rc;
+    if (bad_ptr(logits, dm.T) || bad_ptr(topk_idx, dm.T) || bad_ptr(topk_w, dm.T))
+        return MOE_EINVAL;
+    return hip_status(launch_topk_softmax(dm, logits, topk_idx, topk_w,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+MOE_EXPORT int moe_dispatch(const moe_shape *shape, const uint16_t *x, const int32_t *topk_idx,
+                            uint16_t *send_buf, int32_t *slot, int32_t *expert_count,
+                            int32_t *expert_kept, int32_t *expert_offset, int32_t *rank_rows,
+                            moe_stats *stats, void *workspace, size_t workspace_bytes,
+                            void *stream)
+{
+    Dims dm;
+    int rc = make_dims(shape, &dm);
+    if (rc != MOE_OK)
+        return rc;
+    if (bad_ptr(x, dm.T) || bad_ptr(topk_idx, dm.T) || bad_ptr(send_buf, dm.send_rows) ||
+        bad_ptr(slot, dm.T) || bad_ptr(expert_count) || bad_ptr(expert_kept) ||
+        bad_ptr(expert_offset) || bad_ptr(rank_rows) || bad_ptr(stats))
+        return MOE_EINVAL;
+    Workspace wl;
+    if ((rc = check_ws(dm, workspace, workspace_bytes, &wl)) != MOE_OK)
+        return rc;
+    return hip_status(launch_dispatch(dm, x, topk_idx, send_buf, slot, expert_count, expert_kept,
+                                      expert_offset, rank_rows, stats, (char *)workspace, wl,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+MOE_EXPORT int moe_expert_ffn(const moe_shape *shape, const uint16_t *send_buf,
+                              const int32_t *expert_offset, const int32_t *expert_kept,
+                              const uint16_t *w1, const uint16_t *w3, const uint16_t *w2,
+                              uint16_t *expert_out, void *workspace, size_t workspace_bytes,
+                              void *stream)
+{
+    Dims dm;
+    int rc = make_dims(shape, &dm);
+    if (rc != MOE_OK)
+        return rc;
+    if (bad_ptr(send_buf, dm.send_rows) || bad_ptr(expert_offset) || bad_ptr(expert_kept) ||
+        bad_ptr(w1) || bad_ptr(w3) || bad_ptr(w2) || bad_ptr(expert_out, dm.send_rows))
+        return MOE_EINVAL;
+    Workspace wl;
+    if ((rc = check_ws(dm, workspace, workspace_bytes, &wl)) != MOE_OK)
+        return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    uint16_t *h = reinterpret_cast<uint16_t *>((char *)workspace + wl.h);
+    hipError_t e = launch_gate_up(dm, send_buf, expert_offset, expert_kept, w1, w3, h, st);
+    if (e == hipSuccess)
+        e = launch_down(dm, h, expert_offset, expert_kept, w2, expert_out, st);
+    return hip_status(e);
+}
+
+MOE_EXPORT int moe_expert_gate_up(const moe_shape *shape, const uint16_t *send_buf,
+                                  const int32_t *expert_offset, const int32_t *expert_kept,
+                                  const uint16_t *w1, const uint16_t *w3, uint16_t *h,
+                                  void *stream)
+{
+    Dims dm;
+    const int rc = make_dims(shape, &dm);
+    if (rc != MOE_OK)
+        return rc;
+    if (bad_ptr(send_buf, dm.send_rows) || bad_ptr(expert_offset) || bad_ptr(expert_kept) ||
+        bad_ptr(w1) || bad_ptr(w3) || bad_ptr(h, dm.send_rows))
+        return MOE_EINVAL;
+    return hip_status(launch_gate_up(dm, send_buf, expert_offset, expert_kept, w1, w3, h,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+MOE_EXPORT int moe_expert_down(const moe_shape *shape, const uint16_t *h,
+                               const int32_t *expert_offset, const int32_t *expert_kept,
+                               const uint16_t *w2, uint16_t *expert_out, void *stream)
+{
+    Dims dm;
+    const int rc = make_dims(shape, &dm);
+    if (rc != MOE_OK)
+        return rc;
+    if (bad_ptr(h, dm.send_rows) || bad_ptr(expert_offset) || bad_ptr(expert_kept) ||
+        bad_ptr(w2) || bad_ptr(expert_out, dm.send_rows))
+        return MOE_EINVAL;
+    return hip_status(launch_down(dm, h, expert_offset, expert_kept, w2, expert_out,
+                                  static_cast<hipStream_t>(stream)));
+}
+
+MOE_EXPORT int moe_combine(const moe_shape *shape, const uint16_t *expert_out,
+                           const int32_t *slot, const float *topk_w, uint16_t *y, void *stream)
+{
+    Dims dm;
+    const int rc = make_dims(shape, &dm);
+    if (rc != MOE_OK)
+        return rc;
+    if (bad_ptr(expert_out, dm.send_rows) || bad_ptr(slot, dm.T) || bad_ptr(topk_w, dm.T) ||
+        bad_ptr(y, dm.T))
+        return MOE_EINVAL;
+    return hip_status(
+        launch_combine(dm, expert_out, slot, topk_w, y, static_cast<hipStream_t>(stream)));
+}
+
+MOE_EXPORT int moe_layer_fwd(const moe_shape *shape, const uint16_t *x, const uint16_t *w_gate,
+                             const float *logit_bias, const uint16_t *w1, const uint16_t *w3,
+                             const uint16_t *w2, uint16_t *y, float *logits_out,
+                             int32_t *topk_idx, float *topk_w, uint16_t *send_buf, int32_t *slot,
+                             int32_t *expert_count, int32_t *expert_kept, int32_t *expert_offset,
+                             int32_t *rank_rows, moe_stats *stats, uint16_t *expert_out,
+                             void *workspace, size_t workspace_bytes, void *stream)
+{
+    Dims dm;
+    int rc = make_dims(shape, &dm);
+    if (rc != MOE_OK)
+        return rc;
+    if (bad_ptr(x, dm.T) || bad_ptr(w_gate) || bad_ptr(w1) || bad_ptr(w3) || bad_ptr(w2) ||
+        bad_ptr(y, dm.T) || bad_ptr(topk_idx, dm.T) || bad_ptr(topk_w, dm.T) ||
+        bad_ptr(send_buf, dm.send_rows) || bad_ptr(slot, dm.T) || bad_ptr(expert_count) ||
+        bad_ptr(expert_kept) || bad_ptr(expert_offset) || bad_ptr(rank_rows) ||
+        bad_ptr(stats) || bad_ptr(expert_out, dm.send_rows) || bad_opt_ptr(logit_bias) ||
+        bad_opt_ptr(logits_out))
+        return MOE_EINVAL;
+    Workspace wl;
+    if ((rc = check_ws(dm, workspace, workspace_bytes, &wl)) != MOE_OK)
+        return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    char *ws = (char *)workspace;
+    float *lg = logits_out ? logits_out : reinterpret_cast<float *>(ws + wl.logits);
+    hipError_t e = launch_router_logits(dm, x, w_gate, logit_bias, lg, st);
+    if (e == hipSuccess)
+        e = launch_topk_softmax(dm, lg, topk_idx, topk_w, st);
+    if (e == hipSuccess)
+        e = launch_dispatch(dm, x, topk_idx, send_buf, slot, expert_count, expert_kept,
+                            expert_offset, rank_rows, stats, ws, wl, st);
+    if (e == hipSuccess)
+        e = launch_gate_up(dm, send_buf, expert_offset, expert_kept, w1, w3,
+                           reinterpret_cast<uint16_t *>(ws + wl.h), st);
+    if (e == hipSuccess)
+        e = launch_down(dm, reinterpret_cast<const uint16_t *>(ws + wl.h), expert_offset,
+                        expert_kept, w2, expert_out, st);
+    if (e == hipSuccess)
+        e = launch_combine(dm, expert_out, slot, topk_w, y, st);
+    return hip_status(e);
+}
+
+MOE_EXPORT const char *moe_status_str(int status)
+{
+    switch (status) {
+    case MOE_OK:
+        return "ok";
+    case MOE_EINVAL:
+        return "invalid argument";
+    case MOE_EUNSUPPORTED:
+        return "unsupported shape";
+    case MOE_EWORKSPACE:
+        return "workspace missing or too small";
+    case MOE_EHIP:
+        return "HIP launch error";
+    default:
+        return "unknown status";
+    }
+}

@@ -1,0 +1,103 @@
+// Internal declarations of the gfx950 MoE library: device helpers, the
+// workspace layout and the kernel launchers called by the C ABI (abi.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// Vector types and bf16 helpers (device side)
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16)
+{
+    return __uint_as_float(bits16 << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest even; NaN stays a (quiet) NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u)
+        return (u >> 16) | 0x40u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// Pack two fp32 values as two bf16 in one 32-bit word (lo first in memory).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+
+// ---------------------------------------------------------------------------
+// Sizes shared by host and kernels
+// ---------------------------------------------------------------------------
+constexpr int kChunk = 256;      // tokens per histogram chunk (one per thread)
+constexpr int kMaxExperts = 1024; // E limit of the LDS bitmaps and scans
+
+// Derived per-call shape facts (host side).
+struct Dims {
+    int T, d, E, k, H, D, my_rank;
+    int64_t capacity;  // C, or -1 when dropless
+    int64_t send_rows; // E*C or T*k
+    int nchunks;       // ceil(T / kChunk)
+};
+
+// Byte offsets of each region inside the caller's workspace.
+struct Workspace {
+    size_t logits;        // fp32 [T, E]        route scratch when logits_out == NULL
+    size_t chunk_counts;  // int32 [nchunks, E] per-chunk expert counts
+    size_t chunk_base;    // int32 [nchunks, E] exclusive scan of the counts over chunks
+    size_t chunk_invalid; // int32 [nchunks]    invalid entries per chunk
+    size_t h;             // bf16 [send_rows, H] SwiGLU hidden activations
+    size_t total;
+};
+
+Workspace workspace_layout(const Dims &dm);
+
+// ---------------------------------------------------------------------------
+// Launchers (return hipGetLastError() of their launches)
+// ---------------------------------------------------------------------------
+hipError_t launch_router_logits(const Dims &dm, const uint16_t *x, const uint16_t *w_gate,
+                                const float *bias, float *logits, hipStream_t st);
+hipError_t launch_topk_softmax(const Dims &dm, const float *logits, int32_t *topk_idx,
+                               float *topk_w, hipStream_t st);
+hipError_t launch_dispatch(const Dims &dm, const uint16_t *x, const int32_t *topk_idx,
+                           uint16_t *send_buf, int32_t *slot, int32_t *expert_count,
+                           int32_t *expert_kept, int32_t *expert_offset, int32_t *rank_rows,
+                           moe_stats *stats, char *ws, const Workspace &wl, hipStream_t st);
+hipError_t launch_gate_up(const Dims &dm, const uint16_t *send_buf, const int32_t *expert_offset,
+                          const int32_t *expert_kept, const uint16_t *w1, const uint16_t *w3,
+                          uint16_t *h, hipStream_t st);
+hipError_t launch_down(const Dims &dm, const uint16_t *h, const int32_t *expert_offset,
+                       const int32_t *expert_kept, const uint16_t *w2, uint16_t *expert_out,
+                       hipStream_t st);
+hipError_t launch_combine(const Dims &dm, const uint16_t *expert_out, const int32_t *slot,
+                          const float *topk_w, uint16_t *y, hipStream_t st);
+
+// XCD-aware block remap: the chip dispatches consecutive workgroups to its 8
+// XCDs round robin; this turns block b into a logical work index so that each
+// XCD walks one contiguous range of the work list (neighbouring tiles, which
+// share operands, then meet in the same L2).  Returns -1 for surplus blocks.
+// The grid must hold at least 8 * ceil(total / 8) blocks.
+__device__ __forceinline__ int xcd_remap(int b, int total)
+{
+    const int per = (total + 7) >> 3;
+    const int idx = b >> 3;
+    if (idx >= per)
+        return -1;
+    const int w = (b & 7) * per + idx;
+    return w < total ? w : -1;
+}
+
+inline int xcd_grid(int total) { return ((total + 7) / 8) * 8; }
+
+} // namespace moe

@@ -1,0 +1,218 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) MoE layer forward library.
+ *
+ * One MoE layer's forward pass on one GPU's share of the work:
+ *
+ *   route     H = x W_g (+ b),  G = Softmax(KeepTopK(H, k))
+ *   dispatch  per-expert histogram, capacity, token-order positions, and the
+ *             expert-contiguous send buffer the dispatch all-to-all would send
+ *   expert    SwiGLU FFN of every expert on its rows (grouped GEMM)
+ *   combine   y[t] = sum over kept s of G[t,s] * Expert_{idx[t,s]}(x[t])
+ *
+ * Sources (page title, section):
+ *   [G]  "Mixture-of-Experts (MoE) Architecture and Expert Parallelism",
+ *        section 2 "The Gating Network Formulation".
+ *   [N]  "EP Math -- Expert Parallelism (MoE)", "Notation": T tokens on one
+ *        device, d hidden size, k experts per token, D devices, T*k
+ *        assignments per device.
+ *   [DA] same page, "The dispatch all-to-all"; [CA] "The combine all-to-all";
+ *   [CF] "Capacity factor"; [TD] "Token drop"; [PL] "Placing experts across
+ *        devices".
+ *   [M]  "MoE Expert Parallelism Sizing: Traffic, Capacity, Fabric":
+ *        "Memory residency for the same shape" (gated three-matrix expert),
+ *        "Capacity semantics decide what crosses the wire" (drop before the
+ *        exchange), "First-order dispatch and combine bytes" (one input chunk
+ *        per destination rank).
+ *
+ * Conventions for every call
+ *   - Tensor pointers are DEVICE pointers (HIP global memory) unless marked
+ *     "host".  bf16 tensors are passed as raw 16-bit patterns (uint16_t).
+ *     All tensors are dense row-major with the shapes given.  Every device
+ *     pointer must be 16-byte aligned; the workspace 256-byte aligned.  A
+ *     pointer to a tensor with no elements (T = 0, or send_rows = 0) may be
+ *     NULL; every other required pointer must not be.
+ *   - The caller owns every buffer, including the workspace sized by
+ *     moe_query.  The library allocates nothing, frees nothing, keeps no
+ *     state between calls and never synchronises the host with the device.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
+ *     and runs in stream order.  Calls that share a workspace must not
+ *     overlap in time.
+ *   - Arguments are validated on the host before anything is enqueued; on
+ *     an error nothing is enqueued and no output is touched.
+ *   - Inputs must be finite.  Non-finite x, W_g or bias give unspecified
+ *     routing.
+ *   - Results are deterministic: the same inputs give bitwise-identical
+ *     outputs on every run.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every call. */
+#define MOE_OK 0
+#define MOE_EINVAL (-1)       /* bad argument: null/misaligned pointer, bad size */
+#define MOE_EUNSUPPORTED (-2) /* valid shape that no kernel here handles         */
+#define MOE_EWORKSPACE (-3)   /* workspace NULL or smaller than moe_query says  */
+#define MOE_EHIP (-4)         /* a HIP launch reported an error                 */
+
+/* Shape of one layer on one device, in the pages' notation [N][CF][PL].
+ *   T        tokens on this device (T >= 0; T = 0 enqueues nothing)
+ *   d        hidden size (d > 0, d % 64 == 0)
+ *   E        routed experts (1 <= E <= 1024, E % D == 0)
+ *   k        experts per token (1 <= k <= E)
+ *   H        SwiGLU hidden size of one expert (H > 0, H % 64 == 0)
+ *   D        logical destination ranks (D >= 1); rank r owns the contiguous
+ *            experts [r*E/D, (r+1)*E/D)  [PL]
+ *   my_rank  this device's rank, 0 <= my_rank < D (only for byte accounting)
+ *   drop_policy  0: overflow is dropped in token order (the first C
+ *            assignments of an expert by token index are kept).  Other
+ *            values are rejected with MOE_EUNSUPPORTED.
+ *   capacity_factor  f > 0: capacity C = ceil(f*T*k/E), evaluated left to
+ *            right in IEEE double [CF]; +INFINITY: dropless (no capacity).
+ *            NaN, zero, negative -> MOE_EINVAL.
+ */
+typedef struct moe_shape {
+    int32_t T, d, E, k, H, D, my_rank;
+    int32_t drop_policy;
+    double capacity_factor;
+} moe_shape;
+
+/* Device-resident counters written by moe_dispatch (and moe_layer_fwd).
+ *   assignments           T*k  [N]
+ *   kept                  assignments that reach an expert
+ *   dropped               assignments - kept  [TD]
+ *   padded                E*C - kept in capacity mode, 0 when dropless  [CF]
+ *   capacity              C, or -1 when dropless
+ *   send_rows             rows of the send buffer: E*C, or T*k when dropless
+ *   dispatch_bytes        kept*d*2: bf16 token vectors that travel  [DA]
+ *   dispatch_wire_bytes   send_rows*d*2 in capacity mode (pads included,
+ *                         the static [E, C, d] buffer), kept*d*2 dropless
+ *   dispatch_remote_bytes kept rows bound for ranks other than my_rank, *d*2
+ *   combine_bytes         = dispatch_bytes (combine reverses dispatch) [CA]
+ *   max_expert_count      max over experts of the routed count n_e
+ *   invalid_index         topk_idx entries outside [0, E), or repeating an
+ *                         expert listed earlier for the same token; each is
+ *                         treated as dropped (slot -1), never as an error
+ */
+typedef struct moe_stats {
+    int64_t assignments, kept, dropped, padded, capacity, send_rows;
+    int64_t dispatch_bytes, dispatch_wire_bytes, dispatch_remote_bytes;
+    int64_t combine_bytes, max_expert_count, invalid_index;
+} moe_stats;
+
+/* Host-only size query.  Writes (host pointers, each may be NULL):
+ *   send_rows        rows of send_buf / expert_out: E*C, or T*k if dropless
+ *   capacity         C, or -1 if dropless  [CF]
+ *   workspace_bytes  bytes of device workspace every call below needs
+ *                    (one size serves them all)
+ * Returns MOE_OK, or MOE_EINVAL / MOE_EUNSUPPORTED for a bad shape. */
+int moe_query(const moe_shape *shape, int64_t *send_rows, int64_t *capacity,
+              size_t *workspace_bytes);
+
+/* Router [G]: logits H = x W_g (+ bias), fp32 accumulation of exact bf16
+ * products; then KeepTopK + softmax over the kept logits.
+ *   x           [T, d] bf16
+ *   w_gate      [d, E] bf16 (d_model x E, as W_g is written on the page)
+ *   logit_bias  [E] fp32 or NULL; added to H, so it enters selection and
+ *               softmax alike
+ *   logits_out  [T, E] fp32 or NULL (the fp32 logits the selection used)
+ *   topk_idx    [T, k] int32 out: kept experts, descending logit, ties to
+ *               the lower expert index
+ *   topk_w      [T, k] fp32 out: gates G, summing to 1 per token
+ *   workspace   device, workspace_bytes >= moe_query's size */
+int moe_route(const moe_shape *shape, const uint16_t *x, const uint16_t *w_gate,
+              const float *logit_bias, float *logits_out, int32_t *topk_idx, float *topk_w,
+              void *workspace, size_t workspace_bytes, void *stream);
+
+/* KeepTopK + softmax alone, on caller-given fp32 logits [T, E] [G].  Same
+ * selection and gates as moe_route; lets routing be compared on identical
+ * logits. */
+int moe_topk_from_logits(const moe_shape *shape, const float *logits, int32_t *topk_idx,
+                         float *topk_w, void *stream);
+
+/* Dispatch [N][CF][TD][PL][M]: histogram n_e, capacity, token-order
+ * positions, slots and the send buffer.
+ *   x             [T, d] bf16
+ *   topk_idx      [T, k] int32 (entries outside [0, E), and repeats of an
+ *                 expert already listed for the token, are counted in
+ *                 stats->invalid_index and dropped)
+ *   send_buf      [send_rows, d] bf16 out.  Expert e's kept rows are
+ *                 [expert_offset[e], expert_offset[e] + expert_kept[e]), in
+ *                 ascending token order; capacity mode gives expert e the
+ *                 rows [e*C, (e+1)*C) and zero-fills the pad rows.  Experts
+ *                 are in ascending order, so rank r's chunk -- what the
+ *                 dispatch all-to-all sends to rank r -- is rows
+ *                 [expert_offset[r*E/D], expert_offset[(r+1)*E/D]).
+ *   slot          [T, k] int32 out: send_buf row of assignment (t, s), or -1
+ *                 if dropped
+ *   expert_count  [E] int32 out: n_e, assignments routed to expert e
+ *   expert_kept   [E] int32 out: min(n_e, C) (n_e when dropless)
+ *   expert_offset [E+1] int32 out: first send_buf row of each expert
+ *   rank_rows     [D] int32 out: kept rows per destination rank
+ *   stats         one moe_stats, device memory, out
+ *   workspace     device, >= moe_query's size */
+int moe_dispatch(const moe_shape *shape, const uint16_t *x, const int32_t *topk_idx,
+                 uint16_t *send_buf, int32_t *slot, int32_t *expert_count, int32_t *expert_kept,
+                 int32_t *expert_offset, int32_t *rank_rows, moe_stats *stats, void *workspace,
+                 size_t workspace_bytes, void *stream);
+
+/* Expert FFN [M]: for every expert e, on its kept rows X_e of send_buf,
+ *   h = bf16(SiLU(X_e W1_e^T) * (X_e W3_e^T)),  out = bf16(h W2_e^T),
+ * SiLU(z) = z / (1 + exp(-z)), fp32 accumulation on bf16 matrix cores.
+ *   send_buf       [send_rows, d] bf16
+ *   expert_offset  [E+1] int32, expert_kept [E] int32 (as moe_dispatch
+ *                  writes them; kept rows must lie inside send_buf)
+ *   w1, w3         [E, H, d] bf16;  w2 [E, d, H] bf16
+ *   expert_out     [send_rows, d] bf16 out; only kept rows are written
+ *   workspace      device, >= moe_query's size (holds h) */
+int moe_expert_ffn(const moe_shape *shape, const uint16_t *send_buf, const int32_t *expert_offset,
+                   const int32_t *expert_kept, const uint16_t *w1, const uint16_t *w3,
+                   const uint16_t *w2, uint16_t *expert_out, void *workspace,
+                   size_t workspace_bytes, void *stream);
+
+/* The two halves of moe_expert_ffn, for callers that keep h themselves.
+ * moe_expert_gate_up:  h = bf16(SiLU(X_e W1_e^T) * (X_e W3_e^T)) for every
+ *   expert's kept rows; h is [send_rows, H] bf16, row r of h belongs to row r
+ *   of send_buf; only kept rows are written.
+ * moe_expert_down:     expert_out = bf16(h W2_e^T) on the same rows.
+ * Arguments as in moe_expert_ffn; neither needs a workspace. */
+int moe_expert_gate_up(const moe_shape *shape, const uint16_t *send_buf,
+                       const int32_t *expert_offset, const int32_t *expert_kept,
+                       const uint16_t *w1, const uint16_t *w3, uint16_t *h, void *stream);
+int moe_expert_down(const moe_shape *shape, const uint16_t *h, const int32_t *expert_offset,
+                    const int32_t *expert_kept, const uint16_t *w2, uint16_t *expert_out,
+                    void *stream);
+
+/* Combine [G][CA][TD]: y[t] = bf16(sum over s with slot[t,s] >= 0, in s
+ * order, of topk_w[t,s] * expert_out[slot[t,s]]) with fp32 accumulation.
+ * Dropped assignments add nothing; the residual is the caller's to add.
+ *   expert_out  [send_rows, d] bf16;  slot, topk_w [T, k];  y [T, d] bf16 out */
+int moe_combine(const moe_shape *shape, const uint16_t *expert_out, const int32_t *slot,
+                const float *topk_w, uint16_t *y, void *stream);
+
+/* The whole forward pass: moe_route, moe_dispatch, moe_expert_ffn and
+ * moe_combine enqueued back to back on `stream`, with no host
+ * synchronisation; every intermediate lands in the caller's buffers with the
+ * meaning given above.  logit_bias and logits_out may be NULL. */
+int moe_layer_fwd(const moe_shape *shape, const uint16_t *x, const uint16_t *w_gate,
+                  const float *logit_bias, const uint16_t *w1, const uint16_t *w3,
+                  const uint16_t *w2, uint16_t *y, float *logits_out, int32_t *topk_idx,
+                  float *topk_w, uint16_t *send_buf, int32_t *slot, int32_t *expert_count,
+                  int32_t *expert_kept, int32_t *expert_offset, int32_t *rank_rows,
+                  moe_stats *stats, uint16_t *expert_out, void *workspace,
+                  size_t workspace_bytes, void *stream);
+
+/* Static string naming a status code (never NULL). */
+const char *moe_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

@@ -45,7 +45,9 @@
  * order; capacity uses the per-device token count T, computed as
  * ceil(cf*T*k/E) in double; overflow is dropped in token order (the first
  * C assignments of an expert, by token index, are kept); gates are not
- * renormalised after a drop; the expert is SwiGLU, W2 (SiLU(W1 x) * (W3 x))
+ * renormalised after a drop; a routing entry outside [0, E) or repeating
+ * an expert already listed for its token is invalid (counted, dropped),
+ * since KeepTopK yields k distinct experts; the expert is SwiGLU, W2 (SiLU(W1 x) * (W3 x))
  * with no biases; placement is contiguous: rank r owns experts
  * [r*E/D, (r+1)*E/D).
  */
@@ -187,7 +189,8 @@ enum {
     ST_REMOTE_BYTES,    /* kept rows bound for ranks != my_rank, *d*2    [DA] */
     ST_COMBINE_BYTES,   /* = dispatch bytes: combine reverses dispatch   [CA] */
     ST_MAX_COUNT,       /* max_e n_e                                          */
-    ST_INVALID,         /* indices outside [0, E): counted, then dropped      */
+    ST_INVALID,         /* indices outside [0, E), or repeating an expert
+                           already listed for the token: counted, dropped     */
     ST_COUNT
 };
 
@@ -227,7 +230,11 @@ int oracle_dispatch(int T, int d, int E, int k, int D, int my_rank, double cf,
     for (int t = 0; t < T; ++t) {
         for (int s = 0; s < k; ++s) {
             int32_t e = topk_idx[(size_t)t * k + s];
-            if (e < 0 || e >= E) {
+            int repeated = 0;
+            for (int s2 = 0; s2 < s; ++s2)
+                if (topk_idx[(size_t)t * k + s2] == e)
+                    repeated = 1;
+            if (e < 0 || e >= E || repeated) {
                 position[(size_t)t * k + s] = -1;
                 ++invalid;
                 continue;

@@ -1,0 +1,349 @@
+"""GPU parity: every stage of the HIP path against the CPU oracle, through the
+C ABI, on identical seeded inputs.
+
+Acceptance:
+  * expert indices bit-exact on identical fp32 logits; on the full path a flip
+    is accepted only where the oracle's top-k boundary gap is below 1e-5;
+  * counts, offsets, slots, per-rank rows, counters and the send buffer
+    bit-exact (fed the same routing);
+  * bf16 outputs within 2e-2 * (|ref| + rms(ref)) elementwise and 5e-3
+    relative Frobenius.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from expert_token_routing_moe_amd import api
+from expert_token_routing_moe_amd.inputs import CONFIGS, MoEConfig, bf16_bits, make_inputs
+from parity_util import GAP, assert_bf16_close, bits_to_f64, logit_tolerance, t2f
+
+pytestmark = pytest.mark.gpu
+INF = math.inf
+
+# Oracle-sized cases spanning several tiles and ragged tails.
+SMALL = {
+    "tiny": CONFIGS["tiny"],
+    # T not a multiple of the 256-token chunk, E not a multiple of 8, capacity drops
+    "ragged_e6": MoEConfig("ragged_e6", T=300, d=192, E=6, k=3, H=128, cf=1.0, D=3,
+                           x_std=1.0, wg_std=0.1, w_std=0.05, seed=11),
+    "dropless_e16": MoEConfig("dropless_e16", T=517, d=256, E=16, k=4, H=192, cf=INF, D=4,
+                              x_std=1.0, wg_std=0.0625, w_std=0.05, seed=12),
+    "e64_skew": MoEConfig("e64_skew", T=700, d=128, E=64, k=2, H=256, cf=1.25, D=8,
+                          x_std=1.0, wg_std=1 / math.sqrt(128), w_std=0.05,
+                          bias={2: 3.0}, seed=13),
+    "e256_k8": MoEConfig("e256_k8", T=130, d=256, E=256, k=8, H=128, cf=INF, D=8,
+                         x_std=1.0, wg_std=1 / 16, w_std=0.05, seed=14),
+    "k_eq_E": MoEConfig("k_eq_E", T=64, d=64, E=4, k=4, H=64, cf=INF, D=2,
+                        x_std=1.0, wg_std=0.125, w_std=0.05, seed=15),
+    "one_token": MoEConfig("one_token", T=1, d=128, E=8, k=2, H=128, cf=1.0, D=2,
+                           x_std=1.0, wg_std=0.1, w_std=0.05, seed=16),
+}
+
+DEV = "cuda"
+
+
+def _host(inp):
+    return {k: (bf16_bits(v) if v is not None and v.dtype == torch.bfloat16 else v)
+            for k, v in inp.items()}
+
+
+def _i32(a):
+    return torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(DEV)
+
+
+def _f32(a):
+    return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(DEV)
+
+
+@pytest.fixture(scope="module", params=list(SMALL))
+def case(request):
+    cfg = SMALL[request.param]
+    print(f"\n[case {cfg.name}] T={cfg.T} d={cfg.d} E={cfg.E} k={cfg.k} H={cfg.H} "
+          f"cf={cfg.cf} D={cfg.D}", flush=True)
+    inp = make_inputs(cfg, DEV)
+    h = _host(inp)
+    bias = None if inp["bias"] is None else inp["bias"].cpu().numpy()
+    ref = oracle.layer_fwd(h["x"], h["w_gate"], h["w1"], h["w3"], h["w2"], k=cfg.k, D=cfg.D,
+                           cf=cfg.cf, my_rank=cfg.my_rank, bias=bias)
+    shape = api.Shape.from_config(cfg)
+    buf = api.LayerBuffers.allocate(shape, DEV)
+    return cfg, inp, h, bias, ref, shape, buf
+
+
+def test_router_logits_and_selection(case):
+    cfg, inp, h, bias, ref, shape, buf = case
+    api.moe_route(shape, inp["x"], inp["w_gate"], inp["bias"], buf.logits, buf.topk_idx,
+                  buf.topk_w, buf.workspace)
+    torch.cuda.synchronize()
+    lg = buf.logits.cpu().numpy()
+    tol = logit_tolerance(bits_to_f64(h["x"]), bits_to_f64(h["w_gate"]))
+    assert np.all(np.abs(lg.astype(np.float64) - ref["logits"]) <= tol)
+    # selection on the GPU's own logits is exactly the oracle's KeepTopK
+    o_idx, o_w, _ = oracle.topk(lg, cfg.k)
+    np.testing.assert_array_equal(buf.topk_idx.cpu().numpy(), o_idx)
+    np.testing.assert_allclose(buf.topk_w.cpu().numpy(), o_w, rtol=4e-6, atol=1e-7)
+    # against the oracle's own routing, flips only at near-ties
+    flips = np.any(buf.topk_idx.cpu().numpy() != ref["topk_idx"], axis=1)
+    assert np.all(ref["gap"][flips] < GAP)
+
+
+@pytest.mark.parametrize("E,k", [(8, 2), (6, 3), (64, 2), (256, 8), (5, 5), (300, 7)])
+def test_topk_on_identical_logits_with_ties(E, k):
+    rng = np.random.default_rng(E * 7 + k)
+    T = 333
+    lg = np.concatenate([rng.integers(-3, 4, (T // 2, E)).astype(np.float32),   # many ties
+                         rng.standard_normal((T - T // 2, E)).astype(np.float32)])
+    lg[0, :] = 0.0
+    lg[1, ::2] = -0.0                                                           # signed zeros tie
+    shape = api.Shape(T=T, d=64, E=E, k=k, H=64)
+    idx = torch.empty(T, k, dtype=torch.int32, device=DEV)
+    w = torch.empty(T, k, dtype=torch.float32, device=DEV)
+    api.moe_topk_from_logits(shape, _f32(lg), idx, w)
+    torch.cuda.synchronize()
+    o_idx, o_w, _ = oracle.topk(lg, k)
+    np.testing.assert_array_equal(idx.cpu().numpy(), o_idx)
+    np.testing.assert_allclose(w.cpu().numpy(), o_w, rtol=4e-6, atol=1e-7)
+
+
+def _run_dispatch(shape, x, topk_idx, buf):
+    api.moe_dispatch(shape, x, topk_idx, buf.send_buf, buf.slot, buf.expert_count,
+                     buf.expert_kept, buf.expert_offset, buf.rank_rows, buf.stats, buf.workspace)
+    torch.cuda.synchronize()
+
+
+def _assert_dispatch_equal(buf, r, send_rows):
+    np.testing.assert_array_equal(buf.expert_count.cpu().numpy(), r["expert_count"])
+    np.testing.assert_array_equal(buf.expert_kept.cpu().numpy(), r["expert_kept"])
+    np.testing.assert_array_equal(buf.expert_offset.cpu().numpy(), r["expert_offset"])
+    np.testing.assert_array_equal(buf.rank_rows.cpu().numpy(), r["rank_rows"])
+    np.testing.assert_array_equal(buf.slot.cpu().numpy(), r["slot"])
+    assert api.stats_dict(buf.stats) == r["stats"]
+    if r["send_buf"] is not None and send_rows:
+        np.testing.assert_array_equal(bf16_bits(buf.send_buf[:send_rows]), r["send_buf"])
+
+
+def test_dispatch_bit_exact(case):
+    cfg, inp, h, bias, ref, shape, buf = case
+    idx = _i32(ref["topk_idx"])
+    _run_dispatch(shape, inp["x"], idx, buf)
+    r = oracle.dispatch(h["x"], ref["topk_idx"], T=cfg.T, d=cfg.d, E=cfg.E, D=cfg.D,
+                        my_rank=cfg.my_rank, cf=cfg.cf)
+    _assert_dispatch_equal(buf, r, r["stats"]["send_rows"])
+
+
+def test_dispatch_invalid_and_repeated_entries(case):
+    cfg, inp, h, bias, ref, shape, buf = case
+    idx = ref["topk_idx"].copy()
+    rng = np.random.default_rng(5)
+    n_bad = max(1, cfg.T // 10)
+    rows = rng.integers(0, cfg.T, n_bad)
+    cols = rng.integers(0, cfg.k, n_bad)
+    idx[rows, cols] = rng.choice([-1, cfg.E, cfg.E + 7, -100], n_bad)
+    if cfg.k > 1:
+        idx[rows[0], 1] = idx[rows[0], 0]   # a repeated expert within one token
+    _run_dispatch(shape, inp["x"], _i32(idx), buf)
+    r = oracle.dispatch(h["x"], idx, T=cfg.T, d=cfg.d, E=cfg.E, D=cfg.D, my_rank=cfg.my_rank,
+                        cf=cfg.cf)
+    assert r["stats"]["invalid_index"] > 0
+    _assert_dispatch_equal(buf, r, r["stats"]["send_rows"])
+
+
+def test_expert_ffn_stage(case):
+    cfg, inp, h, bias, ref, shape, buf = case
+    # feed the oracle's dispatch so both sides see identical rows
+    send = torch.from_numpy(ref["send_buf"].view(np.int16)).view(torch.bfloat16).to(DEV)
+    off = _i32(ref["expert_offset"])
+    kept = _i32(ref["expert_kept"])
+    out = torch.zeros_like(send)
+    api.moe_expert_ffn(shape, send, off, kept, inp["w1"], inp["w3"], inp["w2"], out,
+                       buf.workspace)
+    torch.cuda.synchronize()
+    got = bf16_bits(out)
+    for e in range(cfg.E):
+        lo, n = int(ref["expert_offset"][e]), int(ref["expert_kept"][e])
+        if n:
+            assert_bf16_close(bits_to_f64(got[lo:lo + n]),
+                              bits_to_f64(ref["expert_out"][lo:lo + n]), f"expert {e}")
+
+
+def test_combine_stage(case):
+    cfg, inp, h, bias, ref, shape, buf = case
+    eo = torch.from_numpy(ref["expert_out"].view(np.int16)).view(torch.bfloat16).to(DEV)
+    y = torch.empty(cfg.T, cfg.d, dtype=torch.bfloat16, device=DEV)
+    api.moe_combine(shape, eo, _i32(ref["slot"]), _f32(ref["topk_w"]), y)
+    torch.cuda.synchronize()
+    got, want = t2f(y), bits_to_f64(ref["y"])
+    res = assert_bf16_close(got, want, "combine")
+    # same inputs, fp32 vs double accumulation: at most one bf16 ulp apart
+    ulp = np.ldexp(1.0, np.frexp(np.abs(want))[1] - 8)
+    assert np.all(np.abs(got - want) <= np.maximum(ulp, 2.0 ** -133))
+    assert res is None or res["exact"] > 0.95
+
+
+def test_layer_fwd_end_to_end(case):
+    cfg, inp, h, bias, ref, shape, buf = case
+    api.moe_layer_fwd(shape, inp["x"], inp["w_gate"], inp["bias"], inp["w1"], inp["w3"],
+                      inp["w2"], buf)
+    torch.cuda.synchronize()
+    idx = buf.topk_idx.cpu().numpy()
+    flips = np.any(idx != ref["topk_idx"], axis=1)
+    assert np.all(ref["gap"][flips] < GAP)
+    if flips.any():
+        # a legitimate near-tie flip: judge the rest on the GPU's own routing
+        w = buf.topk_w.cpu().numpy()
+        r = oracle.dispatch(h["x"], idx, T=cfg.T, d=cfg.d, E=cfg.E, D=cfg.D,
+                            my_rank=cfg.my_rank, cf=cfg.cf)
+        eo = oracle.expert_ffn_all(r["send_buf"], r["expert_offset"], r["expert_kept"],
+                                   h["w1"], h["w3"], h["w2"])
+        yref = oracle.combine(eo, r["slot"], w)
+    else:
+        r, yref = ref, ref["y"]
+    _assert_dispatch_equal(buf, r, r["stats"]["send_rows"])
+    assert_bf16_close(t2f(buf.y), bits_to_f64(yref), "y")
+    # determinism: a second run is bitwise identical
+    y1 = buf.y.clone()
+    eo1 = buf.expert_out.clone()
+    api.moe_layer_fwd(shape, inp["x"], inp["w_gate"], inp["bias"], inp["w1"], inp["w3"],
+                      inp["w2"], buf)
+    torch.cuda.synchronize()
+    assert torch.equal(buf.y.view(torch.int16), y1.view(torch.int16))
+    n = r["stats"]["send_rows"]
+    kept_rows = np.zeros(n, bool)
+    for e in range(cfg.E):
+        lo = int(r["expert_offset"][e])
+        kept_rows[lo:lo + int(r["expert_kept"][e])] = True
+    kr = torch.from_numpy(kept_rows).to(DEV)
+    assert torch.equal(buf.expert_out[:n][kr].view(torch.int16), eo1[:n][kr].view(torch.int16))
+
+
+@pytest.mark.parametrize("k", [2, 8])
+def test_identity_experts_round_trip_on_gpu(k):
+    """Dispatch then combine with identity experts and nothing dropped gives x
+    back bit for bit (k = E = 8 included)."""
+    cfg = CONFIGS["tiny"].with_(k=k, cf=INF)
+    inp = make_inputs(cfg, DEV, experts=False)
+    shape = api.Shape.from_config(cfg)
+    buf = api.LayerBuffers.allocate(shape, DEV)
+    api.moe_route(shape, inp["x"], inp["w_gate"], None, buf.logits, buf.topk_idx, buf.topk_w,
+                  buf.workspace)
+    _run_dispatch(shape, inp["x"], buf.topk_idx, buf)
+    api.moe_combine(shape, buf.send_buf, buf.slot, buf.topk_w, buf.y)
+    torch.cuda.synchronize()
+    assert torch.equal(buf.y.view(torch.int16), inp["x"].view(torch.int16))
+
+
+def test_zero_tokens():
+    """T = 0: nothing to route; dispatch still writes zero counts and counters."""
+    shape = api.Shape(T=0, d=128, E=8, k=2, H=128, D=2, capacity_factor=1.25)
+    buf = api.LayerBuffers.allocate(shape, DEV)
+    buf.expert_count.fill_(-7)
+    buf.expert_offset.fill_(-7)
+    buf.stats.fill_(-7)
+    x = torch.empty(0, 128, dtype=torch.bfloat16, device=DEV)
+    idx = torch.empty(0, 2, dtype=torch.int32, device=DEV)
+    _run_dispatch(shape, x, idx, buf)
+    assert buf.expert_count.cpu().tolist() == [0] * 8
+    assert buf.expert_offset.cpu().tolist() == [0] * 9
+    st = api.stats_dict(buf.stats)
+    assert st["assignments"] == 0 and st["kept"] == 0 and st["capacity"] == 0
+    inp = make_inputs(CONFIGS["tiny"].with_(T=0, d=128, H=128), DEV)
+    api.moe_layer_fwd(shape, inp["x"], inp["w_gate"], None, inp["w1"], inp["w3"], inp["w2"], buf)
+    torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------
+# Full-size workloads: the whole path at its real shape, checked on the parts
+# the oracle can compute one by one (all routing and accounting; a sample of
+# experts and tokens for the FFN and the combine).
+# ---------------------------------------------------------------------------
+
+def _expert_weights(inp, e):
+    return (bf16_bits(inp["w1"][e]), bf16_bits(inp["w3"][e]), bf16_bits(inp["w2"][e]))
+
+
+@pytest.mark.parametrize("name", ["mixtral", "dsv3_prefill", "dsv3_decode", "skewed"])
+def test_full_size_config(name):
+    cfg = CONFIGS[name]
+    print(f"\n[full {name}] T={cfg.T} d={cfg.d} E={cfg.E} k={cfg.k} H={cfg.H}", flush=True)
+    inp = make_inputs(cfg, DEV)
+    shape = api.Shape.from_config(cfg)
+    buf = api.LayerBuffers.allocate(shape, DEV)
+    api.moe_layer_fwd(shape, inp["x"], inp["w_gate"], inp["bias"], inp["w1"], inp["w3"],
+                      inp["w2"], buf)
+    torch.cuda.synchronize()
+    x = bf16_bits(inp["x"])
+    wg = bf16_bits(inp["w_gate"])
+    bias = None if inp["bias"] is None else inp["bias"].cpu().numpy()
+    # routing: every token
+    lg_ref = oracle.logits(x, wg, bias)
+    lg = buf.logits.cpu().numpy()
+    assert np.all(np.abs(lg.astype(np.float64) - lg_ref) <= logit_tolerance(
+        bits_to_f64(x), bits_to_f64(wg)))
+    idx = buf.topk_idx.cpu().numpy()
+    w = buf.topk_w.cpu().numpy()
+    o_idx, o_w, _ = oracle.topk(lg, cfg.k)
+    np.testing.assert_array_equal(idx, o_idx)
+    np.testing.assert_allclose(w, o_w, rtol=4e-6, atol=1e-7)
+    r_idx, _, gap = oracle.topk(lg_ref, cfg.k)
+    flips = np.any(idx != r_idx, axis=1)
+    print(f"  routing flips vs oracle logits: {int(flips.sum())}", flush=True)
+    assert np.all(gap[flips] < GAP)
+    # accounting and layout: bit-exact on the GPU's routing (send buffer sampled)
+    r = oracle.dispatch(x, idx, T=cfg.T, d=cfg.d, E=cfg.E, D=cfg.D, my_rank=cfg.my_rank,
+                        cf=cfg.cf, with_send_buf=False)
+    for key in ("expert_count", "expert_kept", "expert_offset", "rank_rows", "slot"):
+        np.testing.assert_array_equal(getattr(buf, key).cpu().numpy(), r[key], err_msg=key)
+    st = api.stats_dict(buf.stats)
+    assert st == r["stats"]
+    print(f"  stats: {st}", flush=True)
+    rng = np.random.default_rng(0)
+    slot = r["slot"]
+    for t in rng.choice(cfg.T, min(cfg.T, 64), replace=False):
+        for s in range(cfg.k):
+            if slot[t, s] >= 0:
+                assert torch.equal(buf.send_buf[slot[t, s]].view(torch.int16),
+                                   inp["x"][t].view(torch.int16))
+    if r["stats"]["capacity"] > 0:
+        kept = r["expert_kept"]
+        C = r["stats"]["capacity"]
+        for e in rng.choice(cfg.E, min(cfg.E, 8), replace=False):
+            pads = buf.send_buf[e * C + kept[e]:(e + 1) * C]
+            assert torch.count_nonzero(pads.view(torch.int16)) == 0
+    # expert FFN: sampled experts (busiest, quietest non-empty, one more), sampled rows
+    eo = bf16_bits(buf.expert_out)
+    sb = bf16_bits(buf.send_buf)
+    kept = r["expert_kept"]
+    nz = np.nonzero(kept)[0]
+    experts = sorted({int(nz[np.argmax(kept[nz])]), int(nz[np.argmin(kept[nz])]),
+                      int(rng.choice(nz))})
+    max_rows = 48 if cfg.d * cfg.H > 20e6 else 160
+    for e in experts:
+        lo, n = int(r["expert_offset"][e]), int(kept[e])
+        rows = np.sort(rng.choice(n, min(n, max_rows), replace=False)) + lo
+        got = oracle.expert_ffn(sb[rows], *_expert_weights(inp, e))
+        assert_bf16_close(bits_to_f64(eo[rows]), bits_to_f64(got), f"{name} expert {e}")
+    # combine: sampled tokens on the GPU's expert outputs (stage parity)
+    toks = np.sort(rng.choice(cfg.T, min(cfg.T, 256), replace=False))
+    yref = oracle.combine(eo, slot[toks], w[toks])
+    y = bf16_bits(buf.y)
+    assert_bf16_close(bits_to_f64(y[toks]), bits_to_f64(yref), f"{name} combine")
+    # end to end for a few tokens, every step by the oracle from x
+    for t in toks[:2]:
+        acc = []
+        for s in range(cfg.k):
+            if slot[t, s] < 0:
+                continue
+            e = int(idx[t, s])
+            acc.append((float(w[t, s]), oracle.expert_ffn(x[t:t + 1], *_expert_weights(inp, e))))
+        yt = np.zeros(cfg.d)
+        for g, o in acc:
+            yt += g * bits_to_f64(o[0])
+        ref_row = np.array([oracle.bf16_from_double(v) for v in yt], np.uint16)
+        assert_bf16_close(bits_to_f64(y[t]), bits_to_f64(ref_row), f"{name} token {t}")
+    del inp, buf
+    torch.cuda.empty_cache()

@@ -317,10 +317,13 @@ def test_dispatch_invalid_indices_counted_and_dropped():
     idx = HAND_IDX.copy()
     idx[1, 0] = -1
     idx[3, 1] = 3
+    idx[5, 1] = 1     # repeats token 5's first expert
     r = oracle.dispatch(None, idx, T=6, d=8, E=3, D=1, cf=INF, with_send_buf=False)
-    assert r["stats"]["invalid_index"] == 2
-    assert r["slot"][1, 0] == -1 and r["slot"][3, 1] == -1
-    assert r["stats"]["kept"] == 10 and r["stats"]["dropped"] == 2
+    assert r["stats"]["invalid_index"] == 3
+    assert r["slot"][1, 0] == -1 and r["slot"][3, 1] == -1 and r["slot"][5, 1] == -1
+    assert r["slot"][5, 0] >= 0
+    assert r["stats"]["kept"] == 9 and r["stats"]["dropped"] == 3
+    assert r["expert_count"].sum() == 9
 
 
 def test_dispatch_rejects_indivisible_placement():
