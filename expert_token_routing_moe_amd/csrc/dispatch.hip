@@ -234,6 +234,17 @@ __global__ __launch_bounds__(256) void permute_kernel(
                         reinterpret_cast<uint4 *>(send_buf + (size_t)dst[q] * d)[c] = v;
             }
         }
+    } else if (C < 0) {
+        // dropless: rows [offset[E], T*k) hold no token (they exist only when
+        // entries were invalid); zero them so the whole buffer is defined
+        const long long lo = expert_offset[E], hi = (long long)T * k;
+        const int b = blockIdx.x - tok_blocks;
+        const uint4 z = make_uint4(0, 0, 0, 0);
+        for (long long r = lo + b * 4 + wave; r < hi; r += (long long)pad_parts * 4) {
+            uint4 *dstp = reinterpret_cast<uint4 *>(send_buf + (size_t)r * d);
+            for (int c = lane; c < nvec; c += 64)
+                dstp[c] = z;
+        }
     } else {
         // zero the pad rows [e*C + kept_e, (e+1)*C) of capacity mode
         const int b = blockIdx.x - tok_blocks;
@@ -272,11 +283,17 @@ hipError_t launch_dispatch(const Dims &dm, const uint16_t *x, const int32_t *top
                                            expert_offset, rank_rows, stats);
     const int tok_blocks = (dm.T + 3) / 4;
     int pad_parts = 0;
+    long long pad_blocks = 0;
     if (dm.capacity > 0) {
         // split each expert's C rows so that the pad zeroing spreads over ~1024 workgroups
         pad_parts = (int)std::max<long long>(1, std::min<long long>(dm.capacity, 1024 / dm.E));
+        pad_blocks = (long long)dm.E * pad_parts;
+    } else if (dm.capacity < 0 && dm.T > 0) {
+        // dropless tail: a few grid-stride workgroups (idle unless entries were invalid)
+        pad_parts = 16;
+        pad_blocks = pad_parts;
     }
-    const long long blocks = (long long)tok_blocks + (long long)dm.E * pad_parts;
+    const long long blocks = (long long)tok_blocks + pad_blocks;
     if (blocks > 0)
         permute_kernel<<<(unsigned)blocks, 256, 0, st>>>(
             x, topk_idx, slot, chunk_base, expert_offset, expert_kept, send_buf, dm.T, dm.d,

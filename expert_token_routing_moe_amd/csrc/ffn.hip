@@ -79,6 +79,44 @@ __device__ __forceinline__ void decode_work(const int32_t *__restrict__ rows, in
     }
 }
 
+// Global -> register staging of one K step.  Every thread owns the same
+// 16-byte chunks at every step (chunk c = tid + 256*j covers row c/8, column
+// piece c%8), so its source rows are fixed and set up once.
+template <int A_PT, int B_PT>
+struct StageRegs {
+    uint4 a[A_PT];
+    uint4 b[B_PT];
+};
+
+template <int A_PT, int B_PT>
+__device__ __forceinline__ void stage_load(StageRegs<A_PT, B_PT> &r,
+                                           const uint16_t *const (&asrc)[A_PT],
+                                           const uint16_t *const (&bsrc)[B_PT], int k0)
+{
+#pragma unroll
+    for (int j = 0; j < A_PT; ++j)
+        r.a[j] = asrc[j] ? *reinterpret_cast<const uint4 *>(asrc[j] + k0) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < B_PT; ++j)
+        r.b[j] = *reinterpret_cast<const uint4 *>(bsrc[j] + k0);
+}
+
+template <int A_PT, int B_PT>
+__device__ __forceinline__ void stage_store(const StageRegs<A_PT, B_PT> &r, uint16_t *As,
+                                            uint16_t *Bs, int tid)
+{
+#pragma unroll
+    for (int j = 0; j < A_PT; ++j) {
+        const int c = tid + 256 * j;
+        *reinterpret_cast<uint4 *>(As + (c >> 3) * GLD + (c & 7) * 8) = r.a[j];
+    }
+#pragma unroll
+    for (int j = 0; j < B_PT; ++j) {
+        const int c = tid + 256 * j;
+        *reinterpret_cast<uint4 *>(Bs + (c >> 3) * GLD + (c & 7) * 8) = r.b[j];
+    }
+}
+
 template <int BM, int BN, int WM, int WN, bool DUAL>
 __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs g)
 {
@@ -114,40 +152,21 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs g)
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
 
-    const uint16_t *Ab = g.A + row0 * K;
-    const uint16_t *B0e = g.B0 + ((size_t)e * N + n0) * K;
-    const uint16_t *B1e = DUAL ? g.B1 + ((size_t)e * N + n0) * K : nullptr;
-
-    uint4 ra[A_PT], rb[B_PT];
-    auto load = [&](int k0) {
+    // per-thread source rows (A rows past the expert's last row read as zero)
+    const uint16_t *asrc[A_PT];
+    const uint16_t *bsrc[B_PT];
 #pragma unroll
-        for (int j = 0; j < A_PT; ++j) {
-            const int c = tid + 256 * j, r = c >> 3, kc = c & 7;
-            ra[j] = (r < rows_valid)
-                        ? *reinterpret_cast<const uint4 *>(Ab + (size_t)r * K + k0 + kc * 8)
-                        : make_uint4(0, 0, 0, 0);
-        }
+    for (int j = 0; j < A_PT; ++j) {
+        const int c = tid + 256 * j, r = c >> 3;
+        asrc[j] = (r < rows_valid) ? g.A + (row0 + r) * K + (c & 7) * 8 : nullptr;
+    }
 #pragma unroll
-        for (int j = 0; j < B_PT; ++j) {
-            const int c = tid + 256 * j, r = c >> 3, kc = c & 7;
-            const uint16_t *src = (!DUAL || r < BN) ? B0e + (size_t)r * K
-                                                    : B1e + (size_t)(r - BN) * K;
-            rb[j] = *reinterpret_cast<const uint4 *>(src + k0 + kc * 8);
-        }
-    };
-    auto store = [&](int s) {
-        uint16_t *As = lds + s * STAGE, *Bs = As + BM * GLD;
-#pragma unroll
-        for (int j = 0; j < A_PT; ++j) {
-            const int c = tid + 256 * j, r = c >> 3, kc = c & 7;
-            *reinterpret_cast<uint4 *>(As + r * GLD + kc * 8) = ra[j];
-        }
-#pragma unroll
-        for (int j = 0; j < B_PT; ++j) {
-            const int c = tid + 256 * j, r = c >> 3, kc = c & 7;
-            *reinterpret_cast<uint4 *>(Bs + r * GLD + kc * 8) = rb[j];
-        }
-    };
+    for (int j = 0; j < B_PT; ++j) {
+        const int c = tid + 256 * j, r = c >> 3;
+        const uint16_t *base = (DUAL && r >= BN) ? g.B1 : g.B0;
+        const int rr = (DUAL && r >= BN) ? r - BN : r;
+        bsrc[j] = base + ((size_t)e * N + n0 + rr) * K + (c & 7) * 8;
+    }
 
     floatx4 acc0[RT][CT], acc1[DUAL ? RT : 1][DUAL ? CT : 1];
 #pragma unroll
@@ -159,15 +178,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs g)
                 acc1[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
         }
 
-    const int nsteps = K / GBK;
-    load(0);
-    store(0);
-    __syncthreads();
-    for (int step = 0; step < nsteps; ++step) {
-        const int s = step & 1;
-        if (step + 1 < nsteps)
-            load((step + 1) * GBK);
-        const uint16_t *As = lds + s * STAGE, *Bs = As + BM * GLD;
+    auto compute = [&](const uint16_t *As, const uint16_t *Bs) {
 #pragma unroll
         for (int kk = 0; kk < GBK; kk += 32) {
             const int koff = kk + 8 * (lane >> 4);
@@ -193,9 +204,36 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs g)
                 }
             }
         }
-        if (step + 1 < nsteps)
-            store(s ^ 1);
+    };
+
+    // Pipeline: LDS holds steps i (being multiplied) and i+1 (being filled);
+    // two register sets hold the loads of steps i+1 and i+2 in flight.
+    const int nsteps = K / GBK;
+    StageRegs<A_PT, B_PT> r0, r1;
+    stage_load(r0, asrc, bsrc, 0);
+    if (nsteps > 1)
+        stage_load(r1, asrc, bsrc, GBK);
+    stage_store(r0, lds, lds + BM * GLD, tid);
+    __syncthreads();
+    if (nsteps > 2)
+        stage_load(r0, asrc, bsrc, 2 * GBK);
+    for (int i = 0; i < nsteps; i += 2) {
+        // step i: its tile is in buffer 0; step i+1 arrives in r1
+        compute(lds, lds + BM * GLD);
+        if (i + 1 < nsteps)
+            stage_store(r1, lds + STAGE, lds + STAGE + BM * GLD, tid);
         __syncthreads();
+        if (i + 3 < nsteps)
+            stage_load(r1, asrc, bsrc, (i + 3) * GBK);
+        if (i + 1 >= nsteps)
+            break;
+        // step i+1: buffer 1; step i+2 arrives in r0
+        compute(lds + STAGE, lds + STAGE + BM * GLD);
+        if (i + 2 < nsteps)
+            stage_store(r0, lds, lds + BM * GLD, tid);
+        __syncthreads();
+        if (i + 4 < nsteps)
+            stage_load(r0, asrc, bsrc, (i + 4) * GBK);
     }
 
     // Epilogue through LDS so that global stores are whole 16-byte row pieces.

@@ -145,7 +145,9 @@ int moe_topk_from_logits(const moe_shape *shape, const float *logits, int32_t *t
  *   send_buf      [send_rows, d] bf16 out.  Expert e's kept rows are
  *                 [expert_offset[e], expert_offset[e] + expert_kept[e]), in
  *                 ascending token order; capacity mode gives expert e the
- *                 rows [e*C, (e+1)*C) and zero-fills the pad rows.  Experts
+ *                 rows [e*C, (e+1)*C) and zero-fills the pad rows; when
+ *                 dropless, rows [expert_offset[E], T*k) -- present only if
+ *                 entries were invalid -- are zero-filled too.  Experts
  *                 are in ascending order, so rank r's chunk -- what the
  *                 dispatch all-to-all sends to rank r -- is rows
  *                 [expert_offset[r*E/D], expert_offset[(r+1)*E/D]).
