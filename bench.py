@@ -117,6 +117,8 @@ def main():
     ap.add_argument("--workload", default="dsv3_prefill")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a 1 GiB device copy (scale reference for HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs the single-GPU share of the MoE layer only: every box here has "
@@ -224,6 +226,17 @@ def main():
         "counts": {k: st[k] for k in ("kept", "dropped", "padded", "max_expert_count")},
         "roofline": roof,
     }
+    if args.copy_calibration:
+        # a plain device copy of known size: its FETCH_SIZE / WRITE_SIZE counter
+        # readings give the scale factor for the counters of the kernels above
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = n
+        del src, dst
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)

@@ -5,25 +5,41 @@
 // same shape"): h = SiLU(X W1^T) * (X W3^T), out = h W2^T.
 //
 //  gate/up GEMM  A = send_buf rows of expert e [M_e, d], B = W1_e and W3_e
-//                [H, d] side by side; epilogue applies SiLU(g) * u and stores
-//                h as bf16.
-//  down GEMM     A = h [M_e, H], B = W2_e [d, H]; epilogue stores bf16.
+//                [H, d] side by side; the epilogue applies SiLU(g) * u and
+//                stores h as bf16.
+//  down GEMM     A = h [M_e, H], B = W2_e [d, H]; the epilogue stores bf16.
 //
-// Both operands are K-contiguous ("NT"), so tiles go global -> registers ->
-// LDS with 16-byte accesses and MFMA fragments are read from LDS rows padded
-// by 16 bytes (no bank conflicts).  Ragged M: each workgroup scans the
+// Memory path.  Both operands are K-contiguous ("NT").  Tiles move global ->
+// LDS with direct-to-LDS loads (global_load_lds_dwordx4): no staging
+// registers, no LDS write instructions.  LDS is a ring of S stages, S chosen
+// per tile from its row count (fewer rows, more stages); a stage is
+// issued S-1 steps before it is multiplied, and each wave waits on its own
+// load counter (s_waitcnt vmcnt) for exactly the stages it needs, then one
+// workgroup barrier per step publishes the stage.  Rows are stored unpadded
+// with an XOR swizzle of their 16-byte pieces, so the MFMA fragment reads are
+// free of bank conflicts.
+//
+// Tiles.  An M tile holds up to 256 rows, so every expert with at most 256
+// rows streams each weight tile from HBM exactly once; the 16-row slices of
+// the tile are interleaved across the waves and empty slices are skipped
+// (neither loaded nor multiplied).  Ragged M: each workgroup scans the
 // device-resident kept counts (one wavefront, E values) into a prefix of tile
 // work per expert and finds its own (expert, N tile, M tile), so nothing waits
-// on the host and no planning launch is needed.  The work order is expert-major, then N tile, then M
-// tile: the M tiles that share a weight tile run side by side, and an XCD
-// walks a contiguous range of experts (its L2 sees each expert's rows).
+// on the host.  The work order is expert-major, then N tile, then M tile, and
+// the XCD remap gives each XCD a contiguous range of it: the N tiles of one
+// expert run side by side and share that expert's rows in one L2.
+#include <type_traits>
+
 #include "moe_internal.hpp"
 
 namespace moe {
 namespace {
 
-constexpr int GBK = 64;         // K step
-constexpr int GLD = GBK + 8;    // padded LDS row (elements)
+#define LDS_AS __attribute__((address_space(3)))
+
+#ifndef MOE_GEMM_MIN_BLOCKS
+#define MOE_GEMM_MIN_BLOCKS 1 // workgroups per CU the register budget must allow
+#endif
 
 struct GemmArgs {
     const uint16_t *A;          // [rows, K]
@@ -79,193 +95,287 @@ __device__ __forceinline__ void decode_work(const int32_t *__restrict__ rows, in
     }
 }
 
-// Global -> register staging of one K step.  Every thread owns the same
-// 16-byte chunks at every step (chunk c = tid + 256*j covers row c/8, column
-// piece c%8), so its source rows are fixed and set up once.
-template <int A_PT, int B_PT>
-struct StageRegs {
-    uint4 a[A_PT];
-    uint4 b[B_PT];
-};
-
-template <int A_PT, int B_PT>
-__device__ __forceinline__ void stage_load(StageRegs<A_PT, B_PT> &r,
-                                           const uint16_t *const (&asrc)[A_PT],
-                                           const uint16_t *const (&bsrc)[B_PT], int k0)
+// s_waitcnt with a run-time vector-memory count (the other counters left
+// unconstrained); the instruction takes an immediate, hence the switch.
+__device__ __forceinline__ void wait_vmcnt(int n)
 {
-#pragma unroll
-    for (int j = 0; j < A_PT; ++j)
-        r.a[j] = asrc[j] ? *reinterpret_cast<const uint4 *>(asrc[j] + k0) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-    for (int j = 0; j < B_PT; ++j)
-        r.b[j] = *reinterpret_cast<const uint4 *>(bsrc[j] + k0);
+#define MOE_VMCNT(N)                                                                       \
+    case N:                                                                                \
+        __builtin_amdgcn_s_waitcnt(((N) & 15) | (((N) >> 4) << 14) | (7 << 4) | (15 << 8)); \
+        break;
+    switch (n) {
+        MOE_VMCNT(0) MOE_VMCNT(1) MOE_VMCNT(2) MOE_VMCNT(3) MOE_VMCNT(4) MOE_VMCNT(5)
+        MOE_VMCNT(6) MOE_VMCNT(7) MOE_VMCNT(8) MOE_VMCNT(9) MOE_VMCNT(10) MOE_VMCNT(11)
+        MOE_VMCNT(12) MOE_VMCNT(13) MOE_VMCNT(14) MOE_VMCNT(15) MOE_VMCNT(16) MOE_VMCNT(17)
+        MOE_VMCNT(18) MOE_VMCNT(19) MOE_VMCNT(20) MOE_VMCNT(21) MOE_VMCNT(22) MOE_VMCNT(23)
+        MOE_VMCNT(24) MOE_VMCNT(25) MOE_VMCNT(26) MOE_VMCNT(27) MOE_VMCNT(28) MOE_VMCNT(29)
+        MOE_VMCNT(30) MOE_VMCNT(31) MOE_VMCNT(32) MOE_VMCNT(33) MOE_VMCNT(34) MOE_VMCNT(35)
+        MOE_VMCNT(36) MOE_VMCNT(37) MOE_VMCNT(38) MOE_VMCNT(39) MOE_VMCNT(40) MOE_VMCNT(41)
+        MOE_VMCNT(42) MOE_VMCNT(43) MOE_VMCNT(44) MOE_VMCNT(45) MOE_VMCNT(46) MOE_VMCNT(47)
+        MOE_VMCNT(48) MOE_VMCNT(49) MOE_VMCNT(50) MOE_VMCNT(51) MOE_VMCNT(52) MOE_VMCNT(53)
+        MOE_VMCNT(54) MOE_VMCNT(55) MOE_VMCNT(56) MOE_VMCNT(57) MOE_VMCNT(58) MOE_VMCNT(59)
+        MOE_VMCNT(60) MOE_VMCNT(61) MOE_VMCNT(62)
+    default:
+        __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (15 << 8));
+        break;
+    }
+#undef MOE_VMCNT
 }
 
-template <int A_PT, int B_PT>
-__device__ __forceinline__ void stage_store(const StageRegs<A_PT, B_PT> &r, uint16_t *As,
-                                            uint16_t *Bs, int tid)
+// Workgroup barrier for the LDS ring.  The wave's own LDS reads are drained
+// first (the slot they read is refilled right after the barrier), and the
+// empty asm statements keep the compiler from moving memory accesses across
+// it.  No fence: the load counter is managed explicitly with wait_vmcnt.
+__device__ __forceinline__ void ring_barrier()
 {
-#pragma unroll
-    for (int j = 0; j < A_PT; ++j) {
-        const int c = tid + 256 * j;
-        *reinterpret_cast<uint4 *>(As + (c >> 3) * GLD + (c & 7) * 8) = r.a[j];
-    }
-#pragma unroll
-    for (int j = 0; j < B_PT; ++j) {
-        const int c = tid + 256 * j;
-        *reinterpret_cast<uint4 *>(Bs + (c >> 3) * GLD + (c & 7) * 8) = r.b[j];
-    }
+    __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8)); // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 }
 
-template <int BM, int BN, int WM, int WN, bool DUAL>
-__global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs g)
+// One wave-wide direct-to-LDS load: every lane fetches 16 bytes from its own
+// global address and the wave's 64 pieces land contiguously at LDS byte
+// address lds_addr (wave-uniform, passed in M0).  Written as inline asm so
+// that the compiler, which cannot tell the ring's slots apart, does not drain
+// the whole load counter before every LDS read; the ring's waits are the
+// explicit wait_vmcnt calls.  M0 is restored afterwards.
+__device__ __forceinline__ void dma16(const void *gptr, uint32_t lds_addr)
+{
+    uint32_t saved;
+    asm volatile("s_mov_b32 %0, m0\n\t"
+                 "s_mov_b32 m0, %2\n\t"
+                 "global_load_lds_dwordx4 %1, off\n\t"
+                 "s_mov_b32 m0, %0"
+                 : "=&s"(saved)
+                 : "v"(gptr), "s"(lds_addr)
+                 : "memory");
+}
+
+// 16-byte piece p of row r is stored at piece p ^ swz(r) of that row.
+template <int RC>
+__device__ __forceinline__ int swz(int r)
+{
+    static_assert(RC == 4 || RC == 8, "rows of 64 or 128 bytes");
+    return RC == 8 ? (r & 7) : ((r >> 1) & 3);
+}
+
+template <int BM, int BN, int BK, int RING, int WM, int WN, bool DUAL>
+__global__ __launch_bounds__(256, MOE_GEMM_MIN_BLOCKS) void grouped_gemm_kernel(GemmArgs g)
 {
     static_assert(WM * WN == 4, "4 waves");
-    constexpr int NB = DUAL ? 2 * BN : BN;            // B rows staged per step
-    constexpr int WTM = BM / WM, WTN = BN / WN;       // wave tile
-    constexpr int RT = WTM / 16, CT = WTN / 16;       // 16x16 MFMA tiles per wave
-    constexpr int A_CH = BM * GBK / 8, B_CH = NB * GBK / 8;
-    static_assert(A_CH % 256 == 0 && B_CH % 256 == 0, "whole chunks per thread");
-    constexpr int A_PT = A_CH / 256, B_PT = B_CH / 256;
-    constexpr int STAGE = (BM + NB) * GLD;
-    constexpr int LDC = BN + 8;
-    static_assert(BM * LDC <= 2 * STAGE, "epilogue tile fits in the staging LDS");
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE];
-
+    constexpr int RC = BK / 8;                        // 16-byte pieces per row and step
+    constexpr int RPI = 64 / RC;                      // rows filled by one wave-wide load
+    constexpr int NB = DUAL ? 2 * BN : BN;            // B rows per stage
+    constexpr int A_PW = BM / RPI / 4, B_PW = NB / RPI / 4; // loads per wave per stage
+    static_assert(A_PW * RPI * 4 == BM && B_PW * RPI * 4 == NB, "whole loads per wave");
+    constexpr int B_BYTES = NB * BK * 2;
+    constexpr int WTN = BN / WN;                      // wave tile columns
+    constexpr int RT = BM / 16 / WM, CT = WTN / 16;   // 16x16 MFMA tiles per wave
+    constexpr int LDC = BN + 8;                       // epilogue row (elements)
+    static_assert(BM * LDC * 2 <= RING, "epilogue tile fits in the ring");
+    static_assert(2 * (BM * BK * 2 + B_BYTES) <= RING, "two full stages fit in the ring");
+    // Wave (wm, wn) owns the 16-row slices wm, wm+WM, wm+2*WM, ... of the tile
+    // (interleaved, so a partly filled tile keeps every wave busy) and the
+    // columns [wn*WTN, (wn+1)*WTN).
+    __shared__ __attribute__((aligned(1024))) char smem[RING];
     __shared__ int s_e, s_local;
+
     if (threadIdx.x < 64)
         decode_work<BM>(g.row_count, g.E, g.N / BN, &s_e, &s_local);
     __syncthreads();
-    const int e = s_e;
+    // tile facts are wave-uniform; readfirstlane lets the compiler keep them in
+    // scalar registers and branch on them without exec masking
+    const int e = __builtin_amdgcn_readfirstlane(s_e);
     if (e < 0)
         return;
-    const int local = s_local;
-    const int cnt = g.row_count[e];
+    const int local = __builtin_amdgcn_readfirstlane(s_local);
+    const int cnt = __builtin_amdgcn_readfirstlane(g.row_count[e]);
     const int mt = (cnt + BM - 1) / BM;
     const int n_tile = local / mt, m_tile = local % mt;
     const int m0 = m_tile * BM;
     const int rows_valid = min(BM, cnt - m0);
-    const size_t row0 = (size_t)g.row_offset[e] + m0;
+    const size_t row0 = (size_t)__builtin_amdgcn_readfirstlane(g.row_offset[e]) + m0;
     const int n0 = n_tile * BN;
     const int N = g.N, K = g.K;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WN, wn = wave % WN;
 
-    // per-thread source rows (A rows past the expert's last row read as zero)
-    const uint16_t *asrc[A_PT];
-    const uint16_t *bsrc[B_PT];
+    // Load descriptors.  Load j of wave w fills rows [(4j + w) * RPI, +RPI) of
+    // its region; lane l writes piece l % RC of row l / RC, i.e. it fetches
+    // source piece (l % RC) ^ swz(row).  A loads whose rows all lie past the
+    // expert's end are skipped (wave-uniform); a row past the end inside a
+    // partly valid load reads row 0 of the tile instead (never multiplied
+    // into a stored result).
+    const uint16_t *asrc[A_PW];
+    const uint16_t *bsrc[B_PW];
+    int a_loads = 0; // loads this wave issues per stage for A
 #pragma unroll
-    for (int j = 0; j < A_PT; ++j) {
-        const int c = tid + 256 * j, r = c >> 3;
-        asrc[j] = (r < rows_valid) ? g.A + (row0 + r) * K + (c & 7) * 8 : nullptr;
+    for (int j = 0; j < A_PW; ++j) {
+        const int grp = 4 * j + wave;
+        const int r = grp * RPI + lane / RC;
+        const int piece = (lane % RC) ^ swz<RC>(r);
+        const int rr = r < rows_valid ? r : 0;
+        asrc[j] = g.A + (row0 + rr) * K + piece * 8;
+        a_loads += (grp * RPI < rows_valid) ? 1 : 0;
     }
 #pragma unroll
-    for (int j = 0; j < B_PT; ++j) {
-        const int c = tid + 256 * j, r = c >> 3;
+    for (int j = 0; j < B_PW; ++j) {
+        const int grp = 4 * j + wave;
+        const int r = grp * RPI + lane / RC;
+        const int piece = (lane % RC) ^ swz<RC>(r);
         const uint16_t *base = (DUAL && r >= BN) ? g.B1 : g.B0;
         const int rr = (DUAL && r >= BN) ? r - BN : r;
-        bsrc[j] = base + ((size_t)e * N + n0 + rr) * K + (c & 7) * 8;
+        bsrc[j] = base + ((size_t)e * N + n0 + rr) * K + piece * 8;
     }
+    const int loads_per_stage = a_loads + B_PW;
+    // A stage holds only the A rows that carry data (whole 1 KB loads), then
+    // the B rows; the ring takes as many stages as fit (2 .. 8), so a tile
+    // with fewer rows keeps more K steps in flight.
+    const int a_bytes = ((rows_valid + RPI - 1) / RPI) * 1024;
+    const int stage = a_bytes + B_BYTES;
+    const int S = min(8, RING / stage);
 
-    floatx4 acc0[RT][CT], acc1[DUAL ? RT : 1][DUAL ? CT : 1];
+    const uint32_t lds_base = (uint32_t)(uintptr_t)(LDS_AS char *)smem;
+    auto issue = [&](int step, int slot) {
+        const uint32_t st = lds_base + slot * stage;
+        const int k0 = step * BK;
 #pragma unroll
-    for (int i = 0; i < RT; ++i)
+        for (int j = 0; j < A_PW; ++j)
+            if ((4 * j + wave) * RPI < rows_valid)
+                dma16(asrc[j] + k0, st + (4 * j + wave) * 1024);
 #pragma unroll
-        for (int j = 0; j < CT; ++j) {
-            acc0[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-            if constexpr (DUAL)
-                acc1[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-        }
+        for (int j = 0; j < B_PW; ++j)
+            dma16(bsrc[j] + k0, st + a_bytes + (4 * j + wave) * 1024);
+    };
 
-    auto compute = [&](const uint16_t *As, const uint16_t *Bs) {
+    const int nsteps = K / BK;
+    for (int u = 0; u < S - 1 && u < nsteps; ++u)
+        issue(u, u);
+
+    // The main loop and epilogue for a wave that multiplies NA 16-row slices
+    // (its first NA slices hold rows; the rest lie past the expert's end).
+    // NA is a compile-time constant, so no MFMA sits under a branch.
+    auto run = [&](auto na_const) {
+        constexpr int NA = decltype(na_const)::value;
+        floatx4 acc0[NA > 0 ? NA : 1][CT], acc1[(DUAL && NA > 0) ? NA : 1][DUAL ? CT : 1];
 #pragma unroll
-        for (int kk = 0; kk < GBK; kk += 32) {
-            const int koff = kk + 8 * (lane >> 4);
-            bf16x8 b0[CT], b1[DUAL ? CT : 1];
+        for (int i = 0; i < NA; ++i)
 #pragma unroll
             for (int j = 0; j < CT; ++j) {
-                const int col = wn * WTN + j * 16 + (lane & 15);
-                b0[j] = *reinterpret_cast<const bf16x8 *>(Bs + col * GLD + koff);
+                acc0[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
                 if constexpr (DUAL)
-                    b1[j] = *reinterpret_cast<const bf16x8 *>(Bs + (BN + col) * GLD + koff);
+                    acc1[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
             }
+        for (int st = 0; st < nsteps; ++st) {
+            // stages st+1 .. st+S-2 may stay in flight; stage st must have landed
+            const int ahead = min(S - 2, nsteps - 1 - st);
+            wait_vmcnt(ahead * loads_per_stage);
+            ring_barrier();
+            if (st + S - 1 < nsteps)
+                issue(st + S - 1, (st + S - 1) % S);
+            if constexpr (NA > 0) {
+                const char *As = smem + (st % S) * stage;
+                const char *Bs = As + a_bytes;
 #pragma unroll
-            for (int i = 0; i < RT; ++i) {
-                if (wm * WTM + i * 16 >= rows_valid)
-                    continue; // this 16-row slice is past the expert's last row
-                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(
-                    As + (wm * WTM + i * 16 + (lane & 15)) * GLD + koff);
+                for (int kc = 0; kc < RC; kc += 4) { // one 32-deep MFMA step = 4 pieces
+                    const int piece = kc + (lane >> 4);
+                    bf16x8 b0[CT], b1[DUAL ? CT : 1];
 #pragma unroll
-                for (int j = 0; j < CT; ++j) {
-                    acc0[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b0[j], acc0[i][j], 0, 0, 0);
-                    if constexpr (DUAL)
-                        acc1[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b1[j], acc1[i][j], 0, 0, 0);
+                    for (int j = 0; j < CT; ++j) {
+                        const int n = wn * WTN + j * 16 + (lane & 15);
+                        b0[j] = *reinterpret_cast<const bf16x8 *>(
+                            Bs + n * (BK * 2) + ((piece ^ swz<RC>(n)) << 4));
+                        if constexpr (DUAL) {
+                            const int n1 = BN + n;
+                            b1[j] = *reinterpret_cast<const bf16x8 *>(
+                                Bs + n1 * (BK * 2) + ((piece ^ swz<RC>(n1)) << 4));
+                        }
+                    }
+#pragma unroll
+                    for (int i = 0; i < NA; ++i) {
+                        const int r = (wm + WM * i) * 16 + (lane & 15);
+                        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(
+                            As + r * (BK * 2) + ((piece ^ swz<RC>(r)) << 4));
+#pragma unroll
+                        for (int j = 0; j < CT; ++j) {
+                            acc0[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                a, b0[j], acc0[i][j], 0, 0, 0);
+                            if constexpr (DUAL)
+                                acc1[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                    a, b1[j], acc1[i][j], 0, 0, 0);
+                        }
+                    }
                 }
             }
+        }
+
+        // Epilogue through LDS so that global stores are whole 16-byte row
+        // pieces.  D layout of a 16x16 MFMA tile: lane holds rows
+        // 4*(lane/16)+q, column lane%16.
+        __syncthreads();
+        uint16_t *Cs = reinterpret_cast<uint16_t *>(smem);
+#pragma unroll
+        for (int i = 0; i < NA; ++i)
+#pragma unroll
+            for (int j = 0; j < CT; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int m = (wm + WM * i) * 16 + 4 * (lane >> 4) + q;
+                    const int n = wn * WTN + j * 16 + (lane & 15);
+                    float v = acc0[i][j][q];
+                    if constexpr (DUAL) {
+                        const float gt = v, up = acc1[i][j][q];
+                        v = gt / (1.f + expf(-gt)) * up; // SiLU(g) * u
+                    }
+                    Cs[m * LDC + n] = (uint16_t)f32_to_bf16_rne(v);
+                }
+        __syncthreads();
+        constexpr int CPR = BN / 8; // 16-byte pieces per output row
+        for (int c = tid; c < BM * CPR; c += 256) {
+            const int r = c / CPR, cc = c % CPR;
+            if (r < rows_valid)
+                *reinterpret_cast<uint4 *>(g.out + (row0 + r) * N + n0 + cc * 8) =
+                    *reinterpret_cast<const uint4 *>(Cs + r * LDC + cc * 8);
         }
     };
 
-    // Pipeline: LDS holds steps i (being multiplied) and i+1 (being filled);
-    // two register sets hold the loads of steps i+1 and i+2 in flight.
-    const int nsteps = K / GBK;
-    StageRegs<A_PT, B_PT> r0, r1;
-    stage_load(r0, asrc, bsrc, 0);
-    if (nsteps > 1)
-        stage_load(r1, asrc, bsrc, GBK);
-    stage_store(r0, lds, lds + BM * GLD, tid);
-    __syncthreads();
-    if (nsteps > 2)
-        stage_load(r0, asrc, bsrc, 2 * GBK);
-    for (int i = 0; i < nsteps; i += 2) {
-        // step i: its tile is in buffer 0; step i+1 arrives in r1
-        compute(lds, lds + BM * GLD);
-        if (i + 1 < nsteps)
-            stage_store(r1, lds + STAGE, lds + STAGE + BM * GLD, tid);
-        __syncthreads();
-        if (i + 3 < nsteps)
-            stage_load(r1, asrc, bsrc, (i + 3) * GBK);
-        if (i + 1 >= nsteps)
-            break;
-        // step i+1: buffer 1; step i+2 arrives in r0
-        compute(lds + STAGE, lds + STAGE + BM * GLD);
-        if (i + 2 < nsteps)
-            stage_store(r0, lds, lds + BM * GLD, tid);
-        __syncthreads();
-        if (i + 4 < nsteps)
-            stage_load(r0, asrc, bsrc, (i + 4) * GBK);
-    }
-
-    // Epilogue through LDS so that global stores are whole 16-byte row pieces.
-    // D layout of a 16x16 MFMA tile: lane holds rows 4*(lane/16)+q, column lane%16.
-    uint16_t *Cs = lds;
-#pragma unroll
-    for (int i = 0; i < RT; ++i)
-#pragma unroll
-        for (int j = 0; j < CT; ++j)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int m = wm * WTM + i * 16 + 4 * (lane >> 4) + q;
-                const int n = wn * WTN + j * 16 + (lane & 15);
-                float v = acc0[i][j][q];
-                if constexpr (DUAL) {
-                    const float gt = v, up = acc1[i][j][q];
-                    v = gt / (1.f + expf(-gt)) * up; // SiLU(g) * u
-                }
-                Cs[m * LDC + n] = (uint16_t)f32_to_bf16_rne(v);
-            }
-    __syncthreads();
-    constexpr int CPR = BN / 8; // 16-byte pieces per output row
-    for (int c = tid; c < BM * CPR; c += 256) {
-        const int r = c / CPR, cc = c % CPR;
-        if (r < rows_valid)
-            *reinterpret_cast<uint4 *>(g.out + (row0 + r) * N + n0 + cc * 8) =
-                *reinterpret_cast<const uint4 *>(Cs + r * LDC + cc * 8);
+    // active slices of this wave: slices wm, wm+WM, ... below rows_valid
+    const int slices = (rows_valid + 15) / 16;
+    const int n_act = slices > wm ? min(RT, (slices - wm + WM - 1) / WM) : 0;
+    static_assert(RT <= 8, "dispatch covers up to 8 slices per wave");
+    switch (n_act) {
+    case 0: run(std::integral_constant<int, 0>{}); break;
+    case 1: run(std::integral_constant<int, (RT >= 1 ? 1 : 0)>{}); break;
+    case 2: run(std::integral_constant<int, (RT >= 2 ? 2 : 0)>{}); break;
+    case 3: run(std::integral_constant<int, (RT >= 3 ? 3 : 0)>{}); break;
+    case 4: run(std::integral_constant<int, (RT >= 4 ? 4 : 0)>{}); break;
+    case 5: run(std::integral_constant<int, (RT >= 5 ? 5 : 0)>{}); break;
+    case 6: run(std::integral_constant<int, (RT >= 6 ? 6 : 0)>{}); break;
+    case 7: run(std::integral_constant<int, (RT >= 7 ? 7 : 0)>{}); break;
+    default: run(std::integral_constant<int, RT>{}); break;
     }
 }
 
-constexpr int kBM = 128;  // M tile of both GEMMs
-constexpr int kBN1 = 64;  // h columns per gate/up tile (x2 for W1 and W3)
+#ifndef MOE_GEMM_BK
+#define MOE_GEMM_BK 64
+#endif
+#ifndef MOE_GEMM_RING
+#define MOE_GEMM_RING (156 * 1024)
+#endif
+#ifndef MOE_GEMM_BN1
+#define MOE_GEMM_BN1 128
+#endif
+#ifndef MOE_GEMM_BN2
+#define MOE_GEMM_BN2 256
+#endif
+constexpr int kBM = 256;             // M tile of both GEMMs
+constexpr int kBN1 = MOE_GEMM_BN1;   // h columns per gate/up tile (x2 for W1 and W3)
+constexpr int kBN2 = MOE_GEMM_BN2;   // output columns per down tile
+constexpr int kBK = MOE_GEMM_BK;     // K step
+constexpr int kRing = MOE_GEMM_RING; // LDS ring bytes (one workgroup per CU)
 
 } // namespace
 
@@ -275,10 +385,14 @@ hipError_t launch_gate_up(const Dims &dm, const uint16_t *send_buf, const int32_
 {
     if (dm.send_rows == 0)
         return hipSuccess;
-    const int nn = dm.H / kBN1;
     const long long mtiles_max = (dm.send_rows + kBM - 1) / kBM + dm.E;
     GemmArgs a{send_buf, expert_offset, expert_kept, w1, w3, h, dm.E, dm.H, dm.d};
-    grouped_gemm_kernel<kBM, kBN1, 2, 2, true><<<xcd_grid((int)(mtiles_max * nn)), 256, 0, st>>>(a);
+    if (dm.H % kBN1 == 0) // H is a multiple of 64; the wide tile needs a multiple of kBN1
+        grouped_gemm_kernel<kBM, kBN1, kBK, kRing, 2, 2, true>
+            <<<xcd_grid((int)(mtiles_max * (dm.H / kBN1))), 256, 0, st>>>(a);
+    else
+        grouped_gemm_kernel<kBM, 64, kBK, kRing, 2, 2, true>
+            <<<xcd_grid((int)(mtiles_max * (dm.H / 64))), 256, 0, st>>>(a);
     return hipGetLastError();
 }
 
@@ -290,11 +404,11 @@ hipError_t launch_down(const Dims &dm, const uint16_t *h, const int32_t *expert_
         return hipSuccess;
     const long long mtiles_max = (dm.send_rows + kBM - 1) / kBM + dm.E;
     GemmArgs a{h, expert_offset, expert_kept, w2, nullptr, expert_out, dm.E, dm.d, dm.H};
-    if (dm.d % 128 == 0)
-        grouped_gemm_kernel<kBM, 128, 2, 2, false>
-            <<<xcd_grid((int)(mtiles_max * (dm.d / 128))), 256, 0, st>>>(a);
+    if (dm.d % kBN2 == 0)
+        grouped_gemm_kernel<kBM, kBN2, kBK, kRing, 2, 2, false>
+            <<<xcd_grid((int)(mtiles_max * (dm.d / kBN2))), 256, 0, st>>>(a);
     else
-        grouped_gemm_kernel<kBM, 64, 2, 2, false>
+        grouped_gemm_kernel<kBM, 64, kBK, kRing, 2, 2, false>
             <<<xcd_grid((int)(mtiles_max * (dm.d / 64))), 256, 0, st>>>(a);
     return hipGetLastError();
 }
