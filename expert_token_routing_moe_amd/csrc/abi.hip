@@ -22,7 +22,8 @@ Workspace workspace_layout(const Dims &dm)
         off = align_up(off + bytes);
         return at;
     };
-    w.logits = take((size_t)dm.T * dm.E * sizeof(float));
+    w.logits = take((size_t)router_ksplit(dm.T, dm.E, dm.d) * dm.T * dm.E * sizeof(float));
+    w.wg_t = take((size_t)router_epad(dm.E) * dm.d * sizeof(uint16_t));
     w.chunk_counts = take((size_t)dm.nchunks * dm.E * sizeof(int32_t));
     w.chunk_base = take((size_t)dm.nchunks * dm.E * sizeof(int32_t));
     w.chunk_invalid = take((size_t)dm.nchunks * sizeof(int32_t));
@@ -131,12 +132,8 @@ MOE_EXPORT int moe_route(const moe_shape *shape, const uint16_t *x, const uint16
     Workspace wl;
     if ((rc = check_ws(dm, workspace, workspace_bytes, &wl)) != MOE_OK)
         return rc;
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    float *lg = logits_out ? logits_out : reinterpret_cast<float *>((char *)workspace + wl.logits);
-    hipError_t e = launch_router_logits(dm, x, w_gate, logit_bias, lg, st);
-    if (e == hipSuccess)
-        e = launch_topk_softmax(dm, lg, topk_idx, topk_w, st);
-    return hip_status(e);
+    return hip_status(launch_route(dm, x, w_gate, logit_bias, logits_out, topk_idx, topk_w,
+                                   (char *)workspace, wl, static_cast<hipStream_t>(stream)));
 }
 
 MOE_EXPORT int moe_topk_from_logits(const moe_shape *shape, const float *logits,
@@ -267,10 +264,8 @@ MOE_EXPORT int moe_layer_fwd(const moe_shape *shape, const uint16_t *x, const ui
         return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
     char *ws = (char *)workspace;
-    float *lg = logits_out ? logits_out : reinterpret_cast<float *>(ws + wl.logits);
-    hipError_t e = launch_router_logits(dm, x, w_gate, logit_bias, lg, st);
-    if (e == hipSuccess)
-        e = launch_topk_softmax(dm, lg, topk_idx, topk_w, st);
+    hipError_t e =
+        launch_route(dm, x, w_gate, logit_bias, logits_out, topk_idx, topk_w, ws, wl, st);
     if (e == hipSuccess)
         e = launch_dispatch(dm, x, topk_idx, send_buf, slot, expert_count, expert_kept,
                             expert_offset, rank_rows, stats, ws, wl, st);

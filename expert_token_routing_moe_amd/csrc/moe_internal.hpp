@@ -53,7 +53,8 @@ struct Dims {
 
 // Byte offsets of each region inside the caller's workspace.
 struct Workspace {
-    size_t logits;        // fp32 [T, E]        route scratch when logits_out == NULL
+    size_t logits;        // fp32 [SK, T, E]    router partial logits (SK = router_ksplit)
+    size_t wg_t;          // bf16 [E_pad, d]    W_g transposed for the logit GEMM
     size_t chunk_counts;  // int32 [nchunks, E] per-chunk expert counts
     size_t chunk_base;    // int32 [nchunks, E] exclusive scan of the counts over chunks
     size_t chunk_invalid; // int32 [nchunks]    invalid entries per chunk
@@ -66,8 +67,11 @@ Workspace workspace_layout(const Dims &dm);
 // ---------------------------------------------------------------------------
 // Launchers (return hipGetLastError() of their launches)
 // ---------------------------------------------------------------------------
-hipError_t launch_router_logits(const Dims &dm, const uint16_t *x, const uint16_t *w_gate,
-                                const float *bias, float *logits, hipStream_t st);
+int router_ksplit(int T, int E, int d); // K slices of the logit GEMM
+int router_epad(int E);                 // E rounded up to 64
+hipError_t launch_route(const Dims &dm, const uint16_t *x, const uint16_t *w_gate,
+                        const float *bias, float *logits_out, int32_t *topk_idx, float *topk_w,
+                        char *ws, const Workspace &wl, hipStream_t st);
 hipError_t launch_topk_softmax(const Dims &dm, const float *logits, int32_t *topk_idx,
                                float *topk_w, hipStream_t st);
 hipError_t launch_dispatch(const Dims &dm, const uint16_t *x, const int32_t *topk_idx,

@@ -3,105 +3,124 @@
 // Expert Parallelism", section 2 "The Gating Network Formulation"; the noise
 // term is zero at inference).
 //
-// The logit GEMM (M = T tokens, N = E experts, K = d) uses
-// v_mfma_f32_16x16x32_bf16: bf16 products are exact in fp32 and accumulate
-// in fp32.  A workgroup of 4 waves computes a BT x BE tile; x and W_g tiles
-// are staged through LDS, W_g transposed on the way in so that both MFMA
-// operands are read K-contiguous.  KeepTopK runs one wavefront per token on
-// order-preserving 64-bit keys (value bits, then E-1-e, so a tie goes to the
-// lower expert index).
+// Three launches:
+//  1. W_g [d, E] is transposed into the workspace as W_g^T [E_pad, d]
+//     (E_pad = E rounded up to 64, zero rows past E), so both operands of the
+//     logit GEMM are K-contiguous.
+//  2. The logit GEMM (M = T tokens, N = E_pad, K = d) on
+//     v_mfma_f32_16x16x32_bf16: bf16 products are exact in fp32 and
+//     accumulate in fp32.  A workgroup owns a 64-token x BE-expert tile and
+//     one of SK slices of K, fed through an LDS ring by direct-to-LDS loads;
+//     it writes fp32 partial logits [SK][T][E].  Splitting K fills the chip
+//     when T*E is small.
+//  3. KeepTopK + softmax, one wavefront per token: the SK partials are summed
+//     in slice order and the bias added (the logits), then k rounds of a
+//     wave-wide arg-max on order-preserving 64-bit keys (value bits, then
+//     E-1-e, so a tie goes to the lower expert index).
+#include <type_traits>
+
 #include "moe_internal.hpp"
+#include "ring.hpp"
 
 namespace moe {
+
+// Split of K for the logit GEMM: enough workgroups to cover the chip (~512),
+// at least four K steps per slice.  Shared by the workspace layout.
+int router_ksplit(int T, int E, int d)
+{
+    const int tiles = ((T + 63) / 64) * ((E + 127) / 128);
+    const int steps = d / 64;
+    if (tiles == 0)
+        return 1; // T = 0: nothing to split
+    int sk = (512 + tiles - 1) / tiles;
+    sk = std::min(sk, std::max(1, steps / 4));
+    return std::max(1, sk);
+}
+
+int router_epad(int E) { return (E + 63) / 64 * 64; }
+
 namespace {
 
-constexpr int RBK = 64;          // K step of the logit GEMM
-constexpr int RLD = RBK + 8;     // padded LDS row (elements): conflict-free 16 B reads
-
-template <int BT, int BE, int WT, int WE>
-__global__ __launch_bounds__(256) void router_logits_kernel(
-    const uint16_t *__restrict__ x, const uint16_t *__restrict__ wg,
-    const float *__restrict__ bias, float *__restrict__ logits, int T, int d, int E,
-    int n_et, int total_tiles)
+// W_g [d, E] -> W_g^T [E_pad, d], 64 x 64 tiles through LDS.
+__global__ __launch_bounds__(256) void transpose_wg_kernel(const uint16_t *__restrict__ wg,
+                                                           uint16_t *__restrict__ wgt, int d,
+                                                           int E)
 {
-    static_assert(WT * WE == 4, "4 waves");
-    constexpr int WTT = BT / WT; // tokens per wave
-    constexpr int WTE = BE / WE; // experts per wave
+    __shared__ uint16_t tile[64][65];
+    const int k0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
+    for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+        const int kr = i / 64, ec = i % 64;
+        const int e = e0 + ec;
+        tile[kr][ec] = (e < E) ? wg[(size_t)(k0 + kr) * E + e] : (uint16_t)0;
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+        const int er = i / 64, kc = i % 64;
+        wgt[(size_t)(e0 + er) * d + k0 + kc] = tile[kc][er];
+    }
+}
+
+constexpr int RBT = 64;   // tokens per tile
+constexpr int RBK = 64;   // K step
+constexpr int RRING = 78 * 1024;
+
+template <int BE>
+__global__ __launch_bounds__(256, 2) void router_logits_kernel(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ wgt,
+    float *__restrict__ partial, int T, int d, int E, int n_et, int sk_count, int total)
+{
+    constexpr int RC = RBK / 8, RPI = 64 / RC;     // 8 pieces per row, 8 rows per load
+    constexpr int A_PW = RBT / RPI / 4;            // x loads per wave per stage
+    constexpr int B_PW = BE / RPI / 4;             // W_g^T loads per wave per stage
+    constexpr int A_BYTES = RBT * RBK * 2, STAGE = (RBT + BE) * RBK * 2;
+    constexpr int S = RRING / STAGE < 8 ? RRING / STAGE : 8;
+    static_assert(S >= 2, "two stages fit");
+    constexpr int WTT = RBT / 2, WTE = BE / 2;     // 2 x 2 waves
     constexpr int RT = WTT / 16, CT = WTE / 16;
-    static_assert(RT >= 1 && CT >= 1, "wave tile must be a multiple of 16");
+    __shared__ __attribute__((aligned(1024))) char smem[S * STAGE];
 
-    __shared__ __attribute__((aligned(16))) uint16_t As[2][BT * RLD];
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BE * RLD];
-
-    const int w = xcd_remap(blockIdx.x, total_tiles);
+    const int w = xcd_remap(blockIdx.x, total);
     if (w < 0)
         return;
-    const int t0 = (w / n_et) * BT;
-    const int e0 = (w % n_et) * BE;
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int wt = wave / WE, we = wave % WE;
-    const bool vec_b = (E % 8) == 0;
+    // work order: token tile, then K slice, then expert tile (the expert tiles
+    // of one token tile and slice read the same x rows)
+    const int et = w % n_et;
+    const int sk = (w / n_et) % sk_count;
+    const int tt = w / (n_et * sk_count);
+    const int t0 = tt * RBT, e0 = et * BE;
+    const int steps = d / RBK;
+    const int s_lo = steps * sk / sk_count, s_hi = steps * (sk + 1) / sk_count;
+    const int nsteps = s_hi - s_lo;
 
-    // --- global -> register staging -------------------------------------
-    constexpr int A_CH = BT * RBK / 8;         // 16-byte chunks of the x tile
-    constexpr int A_PT = (A_CH + 255) / 256;
-    constexpr int B_CH = RBK * BE / 8;         // 16-byte chunks of the W_g tile
-    constexpr int B_PT = (B_CH + 255) / 256;
-    uint4 ra[A_PT], rb[B_PT];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wt = wave >> 1, we = wave & 1;
 
-    auto load = [&](int k0) {
+    const uint16_t *asrc[A_PW];
+    const uint16_t *bsrc[B_PW];
 #pragma unroll
-        for (int j = 0; j < A_PT; ++j) {
-            const int c = tid + 256 * j;
-            const int r = c / (RBK / 8), kc = c % (RBK / 8);
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (c < A_CH && t0 + r < T)
-                v = *reinterpret_cast<const uint4 *>(x + (size_t)(t0 + r) * d + k0 + kc * 8);
-            ra[j] = v;
-        }
+    for (int j = 0; j < A_PW; ++j) {
+        const int r = (4 * j + wave) * RPI + lane / RC;
+        const int piece = (lane % RC) ^ swz<RC>(r);
+        const int t = (t0 + r < T) ? t0 + r : t0; // rows past T read row t0 (never stored)
+        asrc[j] = x + (size_t)t * d + (size_t)s_lo * RBK + piece * 8;
+    }
 #pragma unroll
-        for (int j = 0; j < B_PT; ++j) {
-            const int c = tid + 256 * j;
-            const int kr = c / (BE / 8), ec = c % (BE / 8);
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (c < B_CH) {
-                const int e = e0 + ec * 8;
-                const uint16_t *src = wg + (size_t)(k0 + kr) * E + e;
-                if (vec_b && e + 8 <= E) {
-                    v = *reinterpret_cast<const uint4 *>(src);
-                } else {
-                    uint16_t tmp[8];
+    for (int j = 0; j < B_PW; ++j) {
+        const int r = (4 * j + wave) * RPI + lane / RC;
+        const int piece = (lane % RC) ^ swz<RC>(r);
+        bsrc[j] = wgt + (size_t)(e0 + r) * d + (size_t)s_lo * RBK + piece * 8;
+    }
+    const uint32_t lds_base = (uint32_t)(uintptr_t)(LDS_AS char *)smem;
+    auto issue = [&](int step, int slot) {
+        const uint32_t st = lds_base + slot * STAGE;
+        const int k0 = step * RBK;
 #pragma unroll
-                    for (int q = 0; q < 8; ++q)
-                        tmp[q] = (e + q < E) ? src[q] : (uint16_t)0;
-                    v = make_uint4(tmp[0] | (tmp[1] << 16), tmp[2] | (tmp[3] << 16),
-                                   tmp[4] | (tmp[5] << 16), tmp[6] | (tmp[7] << 16));
-                }
-            }
-            rb[j] = v;
-        }
-    };
-    auto store = [&](int s) {
+        for (int j = 0; j < A_PW; ++j)
+            dma16(asrc[j] + k0, st + (4 * j + wave) * 1024);
 #pragma unroll
-        for (int j = 0; j < A_PT; ++j) {
-            const int c = tid + 256 * j;
-            if (c < A_CH) {
-                const int r = c / (RBK / 8), kc = c % (RBK / 8);
-                *reinterpret_cast<uint4 *>(&As[s][r * RLD + kc * 8]) = ra[j];
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < B_PT; ++j) {
-            const int c = tid + 256 * j;
-            if (c < B_CH) {
-                const int kr = c / (BE / 8), ec = c % (BE / 8);
-                const uint32_t wv[4] = {rb[j].x, rb[j].y, rb[j].z, rb[j].w};
-#pragma unroll
-                for (int q = 0; q < 8; ++q)
-                    Bs[s][(ec * 8 + q) * RLD + kr] = (uint16_t)(wv[q >> 1] >> (16 * (q & 1)));
-            }
-        }
+        for (int j = 0; j < B_PW; ++j)
+            dma16(bsrc[j] + k0, st + A_BYTES + (4 * j + wave) * 1024);
     };
 
     floatx4 acc[RT][CT];
@@ -111,51 +130,55 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
         for (int j = 0; j < CT; ++j)
             acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    const int nsteps = d / RBK;
-    load(0);
-    store(0);
-    __syncthreads();
-    for (int step = 0; step < nsteps; ++step) {
-        const int s = step & 1;
-        if (step + 1 < nsteps)
-            load((step + 1) * RBK);
+    for (int u = 0; u < S - 1 && u < nsteps; ++u)
+        issue(u, u);
+    for (int st = 0; st < nsteps; ++st) {
+        const int ahead = min(S - 2, nsteps - 1 - st);
+        wait_vmcnt(ahead * (A_PW + B_PW));
+        ring_barrier();
+        if (st + S - 1 < nsteps)
+            issue(st + S - 1, (st + S - 1) % S);
+        const char *As = smem + (st % S) * STAGE;
+        const char *Bs = As + A_BYTES;
 #pragma unroll
-        for (int kk = 0; kk < RBK; kk += 32) {
-            bf16x8 af[RT], bfr[CT];
+        for (int kc = 0; kc < RC; kc += 4) {
+            const int piece = kc + (lane >> 4);
+            bf16x8 a[RT], b[CT];
 #pragma unroll
-            for (int i = 0; i < RT; ++i)
-                af[i] = *reinterpret_cast<const bf16x8 *>(
-                    &As[s][(wt * WTT + i * 16 + (lane & 15)) * RLD + kk + 8 * (lane >> 4)]);
+            for (int i = 0; i < RT; ++i) {
+                const int r = wt * WTT + i * 16 + (lane & 15);
+                a[i] = *reinterpret_cast<const bf16x8 *>(As + r * (RBK * 2) +
+                                                         ((piece ^ swz<RC>(r)) << 4));
+            }
 #pragma unroll
-            for (int j = 0; j < CT; ++j)
-                bfr[j] = *reinterpret_cast<const bf16x8 *>(
-                    &Bs[s][(we * WTE + j * 16 + (lane & 15)) * RLD + kk + 8 * (lane >> 4)]);
+            for (int j = 0; j < CT; ++j) {
+                const int n = we * WTE + j * 16 + (lane & 15);
+                b[j] = *reinterpret_cast<const bf16x8 *>(Bs + n * (RBK * 2) +
+                                                         ((piece ^ swz<RC>(n)) << 4));
+            }
 #pragma unroll
             for (int i = 0; i < RT; ++i)
 #pragma unroll
                 for (int j = 0; j < CT; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j],
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j],
                                                                          0, 0, 0);
         }
-        if (step + 1 < nsteps)
-            store(s ^ 1);
-        __syncthreads();
     }
 
     // D layout of a 16x16 MFMA tile: lane holds rows 4*(lane/16)+q, column lane%16.
+    float *out = partial + (size_t)sk * T * E;
 #pragma unroll
     for (int j = 0; j < CT; ++j) {
         const int e = e0 + we * WTE + j * 16 + (lane & 15);
         if (e >= E)
             continue;
-        const float b = bias ? bias[e] : 0.f;
 #pragma unroll
         for (int i = 0; i < RT; ++i)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int t = t0 + wt * WTT + i * 16 + 4 * (lane >> 4) + q;
                 if (t < T)
-                    logits[(size_t)t * E + e] = acc[i][j][q] + b;
+                    out[(size_t)t * E + e] = acc[i][j][q];
             }
     }
 }
@@ -189,22 +212,33 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v)
 }
 
 // One wavefront per token; lane l holds logits l, l+64, ... (V per lane).
+// The logit of (t, e) is the sum, in slice order, of the sk_count partials
+// plus the bias; it is written to logits_out when that is non-null.
 template <int V>
-__global__ __launch_bounds__(256) void topk_softmax_kernel(const float *__restrict__ logits,
-                                                           int32_t *__restrict__ topk_idx,
-                                                           float *__restrict__ topk_w, int T,
-                                                           int E, int k)
+__global__ __launch_bounds__(256) void topk_softmax_kernel(
+    const float *__restrict__ partial, int sk_count, const float *__restrict__ bias,
+    float *__restrict__ logits_out, int32_t *__restrict__ topk_idx, float *__restrict__ topk_w,
+    int T, int E, int k)
 {
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T)
         return;
-    const float *h = logits + (size_t)t * E;
     uint64_t key[V];
 #pragma unroll
     for (int j = 0; j < V; ++j) {
         const int e = lane + 64 * j;
-        key[j] = e < E ? topk_key(h[e], e, E) : 0ull; // 0 sorts below every real key
+        key[j] = 0ull; // sorts below every real key
+        if (e < E) {
+            float h = partial[(size_t)t * E + e];
+            for (int s = 1; s < sk_count; ++s)
+                h += partial[((size_t)s * T + t) * E + e];
+            if (bias)
+                h += bias[e];
+            if (logits_out)
+                logits_out[(size_t)t * E + e] = h;
+            key[j] = topk_key(h, e, E);
+        }
     }
     float hmax = 0.f, denom = 0.f;
     // k rounds of a wave-wide arg-max; the winner's key is retired.  Lane
@@ -237,50 +271,16 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(const float *__restri
     }
 }
 
-} // namespace
-
-hipError_t launch_router_logits(const Dims &dm, const uint16_t *x, const uint16_t *w_gate,
-                                const float *bias, float *logits, hipStream_t st)
-{
-    if (dm.T == 0)
-        return hipSuccess;
-    const int T = dm.T, E = dm.E, d = dm.d;
-    if (E <= 16) {
-        constexpr int BT = 64, BE = 16;
-        const int n_tt = (T + BT - 1) / BT, n_et = (E + BE - 1) / BE, tiles = n_tt * n_et;
-        router_logits_kernel<BT, BE, 4, 1><<<xcd_grid(tiles), 256, 0, st>>>(
-            x, w_gate, bias, logits, T, d, E, n_et, tiles);
-    } else if (E <= 32) {
-        constexpr int BT = 64, BE = 32;
-        const int n_tt = (T + BT - 1) / BT, n_et = (E + BE - 1) / BE, tiles = n_tt * n_et;
-        router_logits_kernel<BT, BE, 2, 2><<<xcd_grid(tiles), 256, 0, st>>>(
-            x, w_gate, bias, logits, T, d, E, n_et, tiles);
-    } else {
-        const int n_et = (E + 63) / 64;
-        if ((long)((T + 63) / 64) * n_et >= 256) {
-            constexpr int BT = 64, BE = 64;
-            const int n_tt = (T + BT - 1) / BT, tiles = n_tt * n_et;
-            router_logits_kernel<BT, BE, 2, 2><<<xcd_grid(tiles), 256, 0, st>>>(
-                x, w_gate, bias, logits, T, d, E, n_et, tiles);
-        } else {
-            constexpr int BT = 32, BE = 64;
-            const int n_tt = (T + BT - 1) / BT, tiles = n_tt * n_et;
-            router_logits_kernel<BT, BE, 2, 2><<<xcd_grid(tiles), 256, 0, st>>>(
-                x, w_gate, bias, logits, T, d, E, n_et, tiles);
-        }
-    }
-    return hipGetLastError();
-}
-
-hipError_t launch_topk_softmax(const Dims &dm, const float *logits, int32_t *topk_idx,
-                               float *topk_w, hipStream_t st)
+hipError_t launch_topk(const Dims &dm, const float *partial, int sk, const float *bias,
+                       float *logits_out, int32_t *topk_idx, float *topk_w, hipStream_t st)
 {
     if (dm.T == 0)
         return hipSuccess;
     const int blocks = (dm.T + 3) / 4;
     const int V = (dm.E + 63) / 64;
 #define MOE_TOPK(VV)                                                                       \
-    topk_softmax_kernel<VV><<<blocks, 256, 0, st>>>(logits, topk_idx, topk_w, dm.T, dm.E, dm.k)
+    topk_softmax_kernel<VV><<<blocks, 256, 0, st>>>(partial, sk, bias, logits_out, topk_idx,  \
+                                                   topk_w, dm.T, dm.E, dm.k)
     if (V <= 1)
         MOE_TOPK(1);
     else if (V <= 2)
@@ -293,6 +293,42 @@ hipError_t launch_topk_softmax(const Dims &dm, const float *logits, int32_t *top
         MOE_TOPK(16);
 #undef MOE_TOPK
     return hipGetLastError();
+}
+
+} // namespace
+
+hipError_t launch_route(const Dims &dm, const uint16_t *x, const uint16_t *w_gate,
+                        const float *bias, float *logits_out, int32_t *topk_idx, float *topk_w,
+                        char *ws, const Workspace &wl, hipStream_t st)
+{
+    if (dm.T == 0)
+        return hipSuccess;
+    const int T = dm.T, E = dm.E, d = dm.d;
+    const int epad = router_epad(E);
+    uint16_t *wgt = reinterpret_cast<uint16_t *>(ws + wl.wg_t);
+    float *partial = reinterpret_cast<float *>(ws + wl.logits);
+    transpose_wg_kernel<<<dim3(d / 64, epad / 64), 256, 0, st>>>(w_gate, wgt, d, E);
+    const int sk = router_ksplit(T, E, d);
+    const int n_tt = (T + RBT - 1) / RBT;
+    if (epad % 128 == 0) {
+        const int n_et = epad / 128, total = n_tt * n_et * sk;
+        router_logits_kernel<128><<<xcd_grid(total), 256, 0, st>>>(x, wgt, partial, T, d, E,
+                                                                   n_et, sk, total);
+    } else {
+        const int n_et = epad / 64, total = n_tt * n_et * sk;
+        router_logits_kernel<64><<<xcd_grid(total), 256, 0, st>>>(x, wgt, partial, T, d, E,
+                                                                  n_et, sk, total);
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    return launch_topk(dm, partial, sk, bias, logits_out, topk_idx, topk_w, st);
+}
+
+hipError_t launch_topk_softmax(const Dims &dm, const float *logits, int32_t *topk_idx,
+                               float *topk_w, hipStream_t st)
+{
+    return launch_topk(dm, logits, 1, nullptr, nullptr, topk_idx, topk_w, st);
 }
 
 } // namespace moe

@@ -40,6 +40,28 @@ def assert_bf16_close(got: np.ndarray, ref: np.ndarray, what: str):
     return dict(frob=frob, exact=float(np.mean(got == ref)))
 
 
+def routing_mismatch(idx: np.ndarray, ref_idx: np.ndarray, ref_logits: np.ndarray,
+                     gap: np.ndarray) -> np.ndarray:
+    """Tokens whose GPU routing differs from the oracle's beyond what fp32
+    rounding of the logits can explain.
+
+    The kept *set* may differ only where the oracle's boundary gap
+    h_(k) - h_(k+1) is below GAP.  With the same set, the *order* may differ
+    only between experts whose oracle logits lie within GAP of each other,
+    i.e. the oracle logits read in the GPU's order must still be the sorted
+    sequence to within GAP.
+    """
+    T, k = idx.shape
+    bad = np.zeros(T, bool)
+    same_set = np.all(np.sort(idx, 1) == np.sort(ref_idx, 1), axis=1)
+    bad |= ~same_set & ~(gap < GAP)
+    rows = np.arange(T)[:, None]
+    v_gpu = ref_logits[rows, idx].astype(np.float64)
+    v_ref = ref_logits[rows, ref_idx].astype(np.float64)
+    bad |= same_set & np.any(np.abs(v_gpu - v_ref) >= GAP, axis=1)
+    return bad
+
+
 def logit_tolerance(x_f64: np.ndarray, wg_f64: np.ndarray) -> np.ndarray:
     """Bound on fp32-accumulation error of x W_g: 8 sqrt(d) u sum_j |x_j w_je| + 1e-6."""
     d = x_f64.shape[1]

@@ -42,6 +42,14 @@ def test_query_matches_oracle_capacity(name):
     assert ws >= sr * cfg.H * 2
 
 
+@pytest.mark.parametrize("T,cf", [(0, 1.25), (0, math.inf), (1, 1.0), (1, math.inf)])
+def test_query_degenerate_token_counts(T, cf):
+    sr, cap, ws = api.moe_query(api.Shape(T=T, d=128, E=8, k=2, H=128, D=2, capacity_factor=cf))
+    assert cap == oracle.capacity(T, 2, 8, cf)
+    assert sr == (T * 2 if cap < 0 else 8 * cap)
+    assert ws > 0
+
+
 @pytest.mark.parametrize("kw,status", [
     (dict(k=0), api.MOE_EINVAL),
     (dict(k=9), api.MOE_EINVAL),                 # k > E

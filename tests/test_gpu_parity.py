@@ -2,8 +2,10 @@
 C ABI, on identical seeded inputs.
 
 Acceptance:
-  * expert indices bit-exact on identical fp32 logits; on the full path a flip
-    is accepted only where the oracle's top-k boundary gap is below 1e-5;
+  * expert indices bit-exact on identical fp32 logits; on the full path the
+    kept set may differ only where the oracle's top-k boundary gap is below
+    1e-5, and the order within it only between experts whose oracle logits
+    are within 1e-5 of each other;
   * counts, offsets, slots, per-rank rows, counters and the send buffer
     bit-exact (fed the same routing);
   * bf16 outputs within 2e-2 * (|ref| + rms(ref)) elementwise and 5e-3
@@ -20,7 +22,8 @@ import torch
 import oracle
 from expert_token_routing_moe_amd import api
 from expert_token_routing_moe_amd.inputs import CONFIGS, MoEConfig, bf16_bits, make_inputs
-from parity_util import GAP, assert_bf16_close, bits_to_f64, logit_tolerance, t2f
+from parity_util import (GAP, assert_bf16_close, bits_to_f64, logit_tolerance, routing_mismatch,
+                         t2f)
 
 pytestmark = pytest.mark.gpu
 INF = math.inf
@@ -87,9 +90,9 @@ def test_router_logits_and_selection(case):
     o_idx, o_w, _ = oracle.topk(lg, cfg.k)
     np.testing.assert_array_equal(buf.topk_idx.cpu().numpy(), o_idx)
     np.testing.assert_allclose(buf.topk_w.cpu().numpy(), o_w, rtol=4e-6, atol=1e-7)
-    # against the oracle's own routing, flips only at near-ties
-    flips = np.any(buf.topk_idx.cpu().numpy() != ref["topk_idx"], axis=1)
-    assert np.all(ref["gap"][flips] < GAP)
+    # against the oracle's own routing, differences only at near-ties
+    bad = routing_mismatch(buf.topk_idx.cpu().numpy(), ref["topk_idx"], ref["logits"], ref["gap"])
+    assert not bad.any(), f"routing differs beyond near-ties for tokens {np.nonzero(bad)[0][:8]}"
 
 
 @pytest.mark.parametrize("E,k", [(8, 2), (6, 3), (64, 2), (256, 8), (5, 5), (300, 7)])
@@ -192,7 +195,7 @@ def test_layer_fwd_end_to_end(case):
     torch.cuda.synchronize()
     idx = buf.topk_idx.cpu().numpy()
     flips = np.any(idx != ref["topk_idx"], axis=1)
-    assert np.all(ref["gap"][flips] < GAP)
+    assert not routing_mismatch(idx, ref["topk_idx"], ref["logits"], ref["gap"]).any()
     if flips.any():
         # a legitimate near-tie flip: judge the rest on the GPU's own routing
         w = buf.topk_w.cpu().numpy()
@@ -291,8 +294,10 @@ def test_full_size_config(name):
     np.testing.assert_allclose(w, o_w, rtol=4e-6, atol=1e-7)
     r_idx, _, gap = oracle.topk(lg_ref, cfg.k)
     flips = np.any(idx != r_idx, axis=1)
-    print(f"  routing flips vs oracle logits: {int(flips.sum())}", flush=True)
-    assert np.all(gap[flips] < GAP)
+    bad = routing_mismatch(idx, r_idx, lg_ref, gap)
+    print(f"  tokens routed differently from the oracle's logits: {int(flips.sum())} "
+          f"(beyond near-ties: {int(bad.sum())})", flush=True)
+    assert not bad.any()
     # accounting and layout: bit-exact on the GPU's routing (send buffer sampled)
     r = oracle.dispatch(x, idx, T=cfg.T, d=cfg.d, E=cfg.E, D=cfg.D, my_rank=cfg.my_rank,
                         cf=cfg.cf, with_send_buf=False)
