@@ -2,19 +2,67 @@
 // at the token's home device ("Mixture-of-Experts (MoE) Architecture and
 // Expert Parallelism", section 2; "EP Math -- Expert Parallelism (MoE)",
 // "The combine all-to-all").  A dropped assignment (slot -1) adds nothing
-// ("Token drop").  A wavefront per token gathers its k expert rows with
-// 16-byte loads, accumulates G * row in fp32 in rank order, and stores the
-// bf16 result (round to nearest even) with 16-byte stores.
+// ("Token drop").
+//
+// A wavefront per token.  Its slots and gates are read once into scalar
+// registers; for every 16-byte piece of the row, the lane issues all k
+// gathers before using any of them, accumulates G * row in fp32 in rank
+// order, and stores the bf16 result (round to nearest even).
 #include "moe_internal.hpp"
 
 namespace moe {
 namespace {
 
+template <int KM> // upper bound on k (compile time), so the gathers unroll
 __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict__ expert_out,
                                                       const int32_t *__restrict__ slot,
                                                       const float *__restrict__ topk_w,
                                                       uint16_t *__restrict__ y, int T, int d,
                                                       int k)
+{
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T)
+        return;
+    const int nvec = d / 8;
+    int rows[KM];
+    float g[KM];
+#pragma unroll
+    for (int s = 0; s < KM; ++s) {
+        rows[s] = s < k ? __builtin_amdgcn_readfirstlane(slot[(size_t)t * k + s]) : -1;
+        g[s] = s < k ? __int_as_float(__builtin_amdgcn_readfirstlane(
+                               __float_as_int(topk_w[(size_t)t * k + s])))
+                         : 0.f;
+    }
+    uint4 *dst = reinterpret_cast<uint4 *>(y + (size_t)t * d);
+    for (int c = lane; c < nvec; c += 64) {
+        uint4 v[KM];
+#pragma unroll
+        for (int s = 0; s < KM; ++s)
+            v[s] = rows[s] >= 0
+                       ? reinterpret_cast<const uint4 *>(expert_out + (size_t)rows[s] * d)[c]
+                       : make_uint4(0, 0, 0, 0);
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KM; ++s) {
+            if (rows[s] < 0)
+                continue;
+            const uint32_t p[4] = {v[s].x, v[s].y, v[s].z, v[s].w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                acc[2 * q] = fmaf(g[s], bf16_to_f32(p[q] & 0xffffu), acc[2 * q]);
+                acc[2 * q + 1] = fmaf(g[s], bf16_to_f32(p[q] >> 16), acc[2 * q + 1]);
+            }
+        }
+        dst[c] = make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                            pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
+    }
+}
+
+// Any k: the slots are walked in rank order, one gather at a time.
+__global__ __launch_bounds__(256) void combine_kernel_any_k(
+    const uint16_t *__restrict__ expert_out, const int32_t *__restrict__ slot,
+    const float *__restrict__ topk_w, uint16_t *__restrict__ y, int T, int d, int k)
 {
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -51,7 +99,16 @@ hipError_t launch_combine(const Dims &dm, const uint16_t *expert_out, const int3
 {
     if (dm.T == 0)
         return hipSuccess;
-    combine_kernel<<<(dm.T + 3) / 4, 256, 0, st>>>(expert_out, slot, topk_w, y, dm.T, dm.d, dm.k);
+    const int blocks = (dm.T + 3) / 4;
+    if (dm.k <= 2)
+        combine_kernel<2><<<blocks, 256, 0, st>>>(expert_out, slot, topk_w, y, dm.T, dm.d, dm.k);
+    else if (dm.k <= 4)
+        combine_kernel<4><<<blocks, 256, 0, st>>>(expert_out, slot, topk_w, y, dm.T, dm.d, dm.k);
+    else if (dm.k <= 8)
+        combine_kernel<8><<<blocks, 256, 0, st>>>(expert_out, slot, topk_w, y, dm.T, dm.d, dm.k);
+    else
+        combine_kernel_any_k<<<blocks, 256, 0, st>>>(expert_out, slot, topk_w, y, dm.T, dm.d,
+                                                     dm.k);
     return hipGetLastError();
 }
 

@@ -201,18 +201,21 @@ __global__ __launch_bounds__(256) void permute_kernel(
         const int32_t *base = chunk_base + (size_t)(t / kChunk) * E;
         const uint4 *src = reinterpret_cast<const uint4 *>(x + (size_t)t * d);
         for (int s0 = 0; s0 < k; s0 += kSlotGroup) {
+            // the slots are wave-uniform: resolve them in scalar registers
             int dst[kSlotGroup];
 #pragma unroll
             for (int q = 0; q < kSlotGroup; ++q) {
                 const int s = s0 + q;
                 int sl = -1;
                 if (s < k) {
-                    const int p = slot[(size_t)t * k + s]; // in-chunk position, or -1
+                    // in-chunk position, or -1
+                    const int p = __builtin_amdgcn_readfirstlane(slot[(size_t)t * k + s]);
                     if (p >= 0) {
-                        const int e = row[s];
-                        const long long pos = (long long)base[e] + p;
+                        const int e = __builtin_amdgcn_readfirstlane(row[s]);
+                        const long long pos =
+                            (long long)__builtin_amdgcn_readfirstlane(base[e]) + p;
                         if (C < 0 || pos < C)
-                            sl = expert_offset[e] + (int)pos;
+                            sl = __builtin_amdgcn_readfirstlane(expert_offset[e]) + (int)pos;
                     }
                 }
                 dst[q] = sl;
@@ -226,12 +229,22 @@ __global__ __launch_bounds__(256) void permute_kernel(
                     v = (lane == q) ? dst[q] : v;
                 slot[(size_t)t * k + s0 + lane] = v;
             }
-            for (int c = lane; c < nvec; c += 64) {
-                const uint4 v = src[c];
+            // four row pieces in flight per lane before their stores
+            for (int c0 = lane; c0 < nvec; c0 += 256) {
+                uint4 v[4];
 #pragma unroll
-                for (int q = 0; q < kSlotGroup; ++q)
-                    if (dst[q] >= 0)
-                        reinterpret_cast<uint4 *>(send_buf + (size_t)dst[q] * d)[c] = v;
+                for (int u = 0; u < 4; ++u)
+                    v[u] = (c0 + 64 * u < nvec) ? src[c0 + 64 * u] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+                for (int q = 0; q < kSlotGroup; ++q) {
+                    if (dst[q] < 0)
+                        continue;
+                    uint4 *out = reinterpret_cast<uint4 *>(send_buf + (size_t)dst[q] * d);
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        if (c0 + 64 * u < nvec)
+                            out[c0 + 64 * u] = v[u];
+                }
             }
         }
     } else if (C < 0) {
