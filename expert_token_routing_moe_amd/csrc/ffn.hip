@@ -213,36 +213,71 @@ __global__ __launch_bounds__(256, MOE_GEMM_MIN_BLOCKS) void grouped_gemm_kernel(
             if constexpr (NA > 0) {
                 const char *As = smem + (st % S) * stage;
                 const char *Bs = As + a_bytes;
-#pragma unroll
-                for (int kc = 0; kc < RC; kc += 4) { // one 32-deep MFMA step = 4 pieces
-                    const int piece = kc + (lane >> 4);
-                    bf16x8 b0[CT], b1[DUAL ? CT : 1];
+                // Fragment reads are software-pipelined: the A fragment of the
+                // next slice (and, before the last slice of a 32-deep step,
+                // the B fragments of the next step) is read while the MFMAs of
+                // the current slice run, so LDS latency hides under them.
+                constexpr int KC = RC / 4;           // 32-deep MFMA steps per stage
+                constexpr int NBF = DUAL ? 2 * CT : CT; // B fragments per MFMA step
+                auto read_b = [&](int kc, bf16x8 *dst) {
+                    const int piece = 4 * kc + (lane >> 4);
 #pragma unroll
                     for (int j = 0; j < CT; ++j) {
                         const int n = wn * WTN + j * 16 + (lane & 15);
-                        b0[j] = *reinterpret_cast<const bf16x8 *>(
+                        dst[j] = *reinterpret_cast<const bf16x8 *>(
                             Bs + n * (BK * 2) + ((piece ^ swz<RC>(n)) << 4));
                         if constexpr (DUAL) {
                             const int n1 = BN + n;
-                            b1[j] = *reinterpret_cast<const bf16x8 *>(
+                            dst[CT + j] = *reinterpret_cast<const bf16x8 *>(
                                 Bs + n1 * (BK * 2) + ((piece ^ swz<RC>(n1)) << 4));
                         }
                     }
+                };
+                auto read_a = [&](int kc, int i) {
+                    const int piece = 4 * kc + (lane >> 4);
+                    const int r = (wm + WM * i) * 16 + (lane & 15);
+                    return *reinterpret_cast<const bf16x8 *>(As + r * (BK * 2) +
+                                                             ((piece ^ swz<RC>(r)) << 4));
+                };
+                bf16x8 bf[2][NBF], af[2];
+                read_b(0, bf[0]);
+                af[0] = read_a(0, 0);
+#pragma unroll
+                for (int kc = 0; kc < KC; ++kc) {
 #pragma unroll
                     for (int i = 0; i < NA; ++i) {
-                        const int r = (wm + WM * i) * 16 + (lane & 15);
-                        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(
-                            As + r * (BK * 2) + ((piece ^ swz<RC>(r)) << 4));
+                        const int cur = (kc * NA + i) & 1;
+                        if (i + 1 < NA) {
+                            af[cur ^ 1] = read_a(kc, i + 1);
+                        } else if (kc + 1 < KC) {
+                            read_b(kc + 1, bf[(kc + 1) & 1]);
+                            af[cur ^ 1] = read_a(kc + 1, 0);
+                        }
+                        const bf16x8 *b = bf[kc & 1];
 #pragma unroll
                         for (int j = 0; j < CT; ++j) {
                             acc0[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                a, b0[j], acc0[i][j], 0, 0, 0);
+                                af[cur], b[j], acc0[i][j], 0, 0, 0);
                             if constexpr (DUAL)
                                 acc1[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                    a, b1[j], acc1[i][j], 0, 0, 0);
+                                    af[cur], b[CT + j], acc1[i][j], 0, 0, 0);
                         }
                     }
                 }
+                // Pin that order for the scheduler, which would otherwise sink
+                // every fragment read next to its first use: the first reads,
+                // then per slice the prefetch reads followed by its MFMAs.
+                __builtin_amdgcn_sched_group_barrier(0x100, NBF + 1, 0);
+#pragma unroll
+                for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+                    for (int i = 0; i < NA; ++i) {
+                        if (i + 1 < NA)
+                            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                        else if (kc + 1 < KC)
+                            __builtin_amdgcn_sched_group_barrier(0x100, NBF + 1, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x008, NBF, 0);
+                    }
             }
         }
 
