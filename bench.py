@@ -8,6 +8,11 @@ entry point on one stream.  HIP events recorded on that stream around every
 stage give per-stage durations over the timed region; the dominant kernel's
 roofline is computed from its algorithmic bytes and flops.
 
+For a dropless workload spread over D > 1 ranks, the expert GEMMs are also
+timed on one rank's share under D-way expert parallelism (E/D experts, the
+rows of D batches), where the grouped GEMM is bound by the matrix cores
+rather than by streaming the weights.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -109,6 +114,78 @@ def cpu_baseline(cfg, inp, budget_s):
                        f"({spent:.1f} s of oracle compute)")
 
 
+def pct(v, q):
+    v = sorted(v)
+    return v[min(len(v) - 1, int(round(q * (len(v) - 1))))]
+
+
+def rank_local_gemm(cfg, inp, dev, steps, warmup):
+    """The expert GEMMs on one rank's share under D-way expert parallelism.
+
+    Every rank's batch (D * T tokens) is routed and dispatched; rank 0's E/D
+    experts then hold the rows that the dispatch all-to-all would deliver to
+    it (about D * T * k / E rows each), which is the shape one GPU multiplies
+    when the layer is spread over D GPUs.  Both grouped GEMMs run on those
+    rows through the same entry points with E/D experts.
+    """
+    import torch
+
+    from expert_token_routing_moe_amd import api
+    from expert_token_routing_moe_amd.inputs import make_inputs
+
+    big = cfg.with_(T=cfg.T * cfg.D)
+    xin = make_inputs(big, dev, experts=False)
+    shape = api.Shape.from_config(big)
+    buf = api.LayerBuffers.allocate(shape, dev, keep_logits=False)
+    stream = torch.cuda.current_stream()
+    api.moe_route(shape, xin["x"], xin["w_gate"], xin["bias"], None, buf.topk_idx, buf.topk_w,
+                  buf.workspace, stream)
+    api.moe_dispatch(shape, xin["x"], buf.topk_idx, buf.send_buf, buf.slot, buf.expert_count,
+                     buf.expert_kept, buf.expert_offset, buf.rank_rows, buf.stats,
+                     buf.workspace, stream)
+    el = cfg.E // cfg.D
+    loc = api.Shape(big.T, cfg.d, el, cfg.k, cfg.H, 1, 0, big.cf)
+    rows = int(buf.expert_offset[el].item())
+    h = torch.empty(buf.send_buf.shape[0], cfg.H, dtype=torch.bfloat16, device=dev)
+    w1, w3, w2 = inp["w1"][:el], inp["w3"][:el], inp["w2"][:el]
+
+    def run(ev=None):
+        if ev:
+            ev[0].record(stream)
+        api.moe_expert_gate_up(loc, buf.send_buf, buf.expert_offset, buf.expert_kept, w1, w3, h,
+                               stream)
+        if ev:
+            ev[1].record(stream)
+        api.moe_expert_down(loc, h, buf.expert_offset, buf.expert_kept, w2, buf.expert_out,
+                            stream)
+        if ev:
+            ev[2].record(stream)
+
+    for _ in range(warmup):
+        run()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for i in range(steps):
+        run(evs[i])
+    torch.cuda.synchronize()
+    gu = [e[0].elapsed_time(e[1]) for e in evs]
+    dn = [e[1].elapsed_time(e[2]) for e in evs]
+    tot = [a + b for a, b in zip(gu, dn)]
+    flops = 6 * cfg.d * cfg.H * rows
+    wbytes = 3 * el * cfg.d * cfg.H * 2
+    t = pct(tot, 0.5) / 1e3
+    res = dict(
+        experts=el, rows=rows, tokens_routed=big.T,
+        gate_up_ms=round(pct(gu, 0.5), 4), down_ms=round(pct(dn, 0.5), 4),
+        ms_p10=round(pct(tot, 0.1), 4), ms_p50=round(pct(tot, 0.5), 4),
+        ms_p90=round(pct(tot, 0.9), 4),
+        tflops=round(flops / t / 1e12, 1),
+        mfma_util=round(flops / t / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        weight_gbs=round(wbytes / t / 1e9, 1))
+    del buf, h, xin
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -117,6 +194,8 @@ def main():
     ap.add_argument("--workload", default="dsv3_prefill")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-rank-local", action="store_true",
+                    help="skip the expert-parallel rank-local GEMM measurement")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (scale reference for HBM counters)")
     args = ap.parse_args()
@@ -172,8 +251,9 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
-    stage_ms = {s: sum(events[i][j].elapsed_time(events[i][j + 1]) for i in range(args.steps))
-                / args.steps for j, s in enumerate(stages)}
+    samples = {s: [events[i][j].elapsed_time(events[i][j + 1]) for i in range(args.steps)]
+               for j, s in enumerate(stages)}
+    stage_ms = {s: sum(v) / len(v) for s, v in samples.items()}
     log(f"bench: {args.steps} steps, {ms_step:.3f} ms/step; stages (ms): "
         + ", ".join(f"{s}={v:.4f}" for s, v in stage_ms.items()))
 
@@ -184,6 +264,9 @@ def main():
     for s in stages:
         t = stage_ms[s] / 1e3
         per_stage[s] = dict(ms=round(stage_ms[s], 5),
+                            p10=round(pct(samples[s], 0.1), 5),
+                            p50=round(pct(samples[s], 0.5), 5),
+                            p90=round(pct(samples[s], 0.9), 5),
                             gbs=round(traffic[s]["bytes"] / t / 1e9, 1),
                             hbm_frac=round(traffic[s]["bytes"] / t / 1e9 / HBM_PEAK_GBS, 4),
                             tflops=round(traffic[s]["flops"] / t / 1e12, 2))
@@ -226,6 +309,9 @@ def main():
         "counts": {k: st[k] for k in ("kept", "dropped", "padded", "max_expert_count")},
         "roofline": roof,
     }
+    if cfg.D > 1 and cfg.cf == float("inf") and not args.no_rank_local:
+        log(f"bench: rank-local expert GEMMs ({cfg.E // cfg.D} experts, {cfg.D}x tokens routed)")
+        out["grouped_gemm_rank_local"] = rank_local_gemm(cfg, inp, dev, args.steps, args.warmup)
     if args.copy_calibration:
         # a plain device copy of known size: its FETCH_SIZE / WRITE_SIZE counter
         # readings give the scale factor for the counters of the kernels above

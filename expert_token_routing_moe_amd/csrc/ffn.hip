@@ -19,8 +19,9 @@
 // with an XOR swizzle of their 16-byte pieces, so the MFMA fragment reads are
 // free of bank conflicts.
 //
-// Tiles.  An M tile holds up to 256 rows, so every expert with at most 256
-// rows streams each weight tile from HBM exactly once; the 16-row slices of
+// Tiles.  An M tile holds up to 256 rows (an expert's rows are split into
+// equal tiles), so every expert with at most 256 rows streams each weight
+// tile from HBM exactly once; the 16-row slices of
 // the tile are interleaved across the waves and empty slices are skipped
 // (neither loaded nor multiplied).  Ragged M: each workgroup scans the
 // device-resident kept counts (one wavefront, E values) into a prefix of tile
@@ -125,10 +126,15 @@ __global__ __launch_bounds__(256, MOE_GEMM_MIN_BLOCKS) void grouped_gemm_kernel(
         return;
     const int local = __builtin_amdgcn_readfirstlane(s_local);
     const int cnt = __builtin_amdgcn_readfirstlane(g.row_count[e]);
+    // The expert's rows are cut into mt tiles of (nearly) equal size rather
+    // than full tiles plus a remainder: the M tiles that share a weight tile
+    // run side by side, and equal tiles keep them in step, so the weights
+    // they read are still in L2 when the others ask for them.
     const int mt = (cnt + BM - 1) / BM;
     const int n_tile = local / mt, m_tile = local % mt;
-    const int m0 = m_tile * BM;
-    const int rows_valid = min(BM, cnt - m0);
+    const int tile_rows = (cnt + mt - 1) / mt; // <= BM; the last tile is never empty
+    const int m0 = m_tile * tile_rows;
+    const int rows_valid = min(tile_rows, cnt - m0);
     const size_t row0 = (size_t)__builtin_amdgcn_readfirstlane(g.row_offset[e]) + m0;
     const int n0 = n_tile * BN;
     const int N = g.N, K = g.K;

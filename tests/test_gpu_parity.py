@@ -352,3 +352,47 @@ def test_full_size_config(name):
         assert_bf16_close(bits_to_f64(y[t]), bits_to_f64(ref_row), f"{name} token {t}")
     del inp, buf
     torch.cuda.empty_cache()
+
+
+def test_rank_local_expert_share():
+    """The expert GEMMs on one rank's share under 8-way expert parallelism:
+    8 * 4096 DeepSeek-V3-shaped tokens are routed and dispatched, and the two
+    grouped GEMMs run with E/D = 32 experts on the rows of experts 0..31
+    (about 1024 each, several full 256-row tiles).  Sampled rows match the
+    oracle; rows of other experts are left untouched."""
+    base = CONFIGS["dsv3_prefill"]
+    cfg = base.with_(T=base.T * base.D)
+    print(f"\n[rank-local] T={cfg.T} d={cfg.d} E={cfg.E} k={cfg.k} H={cfg.H}", flush=True)
+    inp = make_inputs(cfg, DEV, experts=False)
+    el = cfg.E // cfg.D
+    w = make_inputs(base.with_(E=el, T=1), DEV)  # weights of experts 0..31
+    shape = api.Shape.from_config(cfg)
+    buf = api.LayerBuffers.allocate(shape, DEV, keep_logits=False)
+    api.moe_route(shape, inp["x"], inp["w_gate"], None, None, buf.topk_idx, buf.topk_w,
+                  buf.workspace)
+    _run_dispatch(shape, inp["x"], buf.topk_idx, buf)
+    torch.cuda.synchronize()
+    kept = buf.expert_kept.cpu().numpy()
+    off = buf.expert_offset.cpu().numpy()
+    rows = int(off[el])
+    assert rows == int(kept[:el].sum()) and kept[:el].max() > 256
+    loc = api.Shape(cfg.T, cfg.d, el, cfg.k, cfg.H, 1, 0, INF)
+    h = torch.empty(buf.send_buf.shape[0], cfg.H, dtype=torch.bfloat16, device=DEV)
+    out = torch.full(buf.send_buf.shape, 0x1234, dtype=torch.int16, device=DEV)
+    api.moe_expert_gate_up(loc, buf.send_buf, buf.expert_offset, buf.expert_kept, w["w1"],
+                           w["w3"], h)
+    api.moe_expert_down(loc, h, buf.expert_offset, buf.expert_kept, w["w2"],
+                        out.view(torch.bfloat16))
+    torch.cuda.synchronize()
+    tail = out[rows:rows + 4096]
+    assert torch.all(tail == 0x1234), "rows past the share were written"
+    rng = np.random.default_rng(1)
+    sb = bf16_bits(buf.send_buf[:rows])
+    eo = bf16_bits(out[:rows].view(torch.bfloat16))
+    for e in sorted({int(np.argmax(kept[:el])), int(np.argmin(kept[:el])), int(rng.integers(el))}):
+        lo, n = int(off[e]), int(kept[e])
+        r = np.sort(rng.choice(n, min(n, 48), replace=False)) + lo
+        got = oracle.expert_ffn(sb[r], *_expert_weights(w, e))
+        assert_bf16_close(bits_to_f64(eo[r]), bits_to_f64(got), f"rank-local expert {e}")
+    del inp, w, buf, h, out
+    torch.cuda.empty_cache()
