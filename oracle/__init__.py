@@ -77,10 +77,10 @@ def _load():
     lib.oracle_logits.restype = None
     lib.oracle_topk.argtypes = [i32, i32, i32, P, P, P, P]
     lib.oracle_topk.restype = None
-    lib.oracle_capacity.argtypes = [i32, i32, i32, ctypes.c_double]
+    lib.oracle_capacity.argtypes = [i32, i32, i32, ctypes.c_double, i32]
     lib.oracle_capacity.restype = ctypes.c_int64
-    lib.oracle_dispatch.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.c_double,
-                                    P, P, P, P, P, P, P, P, P]
+    lib.oracle_dispatch.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.c_double, i32, i32,
+                                    P, P, P, P, P, P, P, P, P, P]
     lib.oracle_dispatch.restype = ctypes.c_int
     lib.oracle_expert_ffn.argtypes = [i32, i32, i32, P, P, P, P, P]
     lib.oracle_expert_ffn.restype = None
@@ -137,18 +137,25 @@ def topk(lg: np.ndarray, k: int):
     return idx, w, gap
 
 
-def capacity(T: int, k: int, E: int, cf: float) -> int:
-    return int(_load().oracle_capacity(T, k, E, float(cf)))
+def capacity(T: int, k: int, E: int, cf: float, min_capacity: int = 0) -> int:
+    return int(_load().oracle_capacity(T, k, E, float(cf), int(min_capacity)))
 
 
 def dispatch(x: np.ndarray | None, topk_idx: np.ndarray, *, T: int, d: int, E: int,
              D: int, my_rank: int = 0, cf: float = float("inf"),
-             with_send_buf: bool = True) -> dict:
-    """Histogram, capacity, token-order positions, slots and the send buffer."""
+             with_send_buf: bool = True, drop_policy: int = 0, topk_w=None,
+             min_capacity: int = 0) -> dict:
+    """Histogram, capacity, positions, slots and the send buffer.
+
+    drop_policy 0 keeps an overflowing expert's first C assignments in token
+    order; 1 keeps its C largest gate values (topk_w, fp32 [T, k])."""
     topk_idx = _c(topk_idx, np.int32)
     k = topk_idx.shape[1]
     assert topk_idx.shape[0] == T
-    C = capacity(T, k, E, cf)
+    if topk_w is not None:
+        topk_w = _c(topk_w, np.float32)
+        assert topk_w.shape == topk_idx.shape
+    C = capacity(T, k, E, cf, min_capacity)
     send_rows = T * k if C < 0 else E * C
     send_buf = None
     if with_send_buf:
@@ -164,8 +171,8 @@ def dispatch(x: np.ndarray | None, topk_idx: np.ndarray, *, T: int, d: int, E: i
     )
     stats = np.empty((len(STAT_NAMES),), np.int64)
     rc = _load().oracle_dispatch(
-        T, d, E, k, D, my_rank, float(cf),
-        _ptr(x) if with_send_buf else None, _ptr(topk_idx), _ptr(send_buf),
+        T, d, E, k, D, my_rank, float(cf), int(min_capacity), int(drop_policy),
+        _ptr(x) if with_send_buf else None, _ptr(topk_idx), _ptr(topk_w), _ptr(send_buf),
         _ptr(out["slot"]), _ptr(out["expert_count"]), _ptr(out["expert_kept"]),
         _ptr(out["expert_offset"]), _ptr(out["rank_rows"]), _ptr(stats))
     if rc != 0:
@@ -217,13 +224,14 @@ def expert_ffn_all(send_buf: np.ndarray, expert_offset: np.ndarray, expert_kept:
 
 
 def layer_fwd(x, w_gate, w1, w3, w2, *, k: int, D: int, cf: float, my_rank: int = 0,
-              bias=None) -> dict:
+              bias=None, drop_policy: int = 0, min_capacity: int = 0) -> dict:
     """The whole forward pass, stage by stage, returning every intermediate."""
     T, d = x.shape
     E = w_gate.shape[1]
     lg = logits(x, w_gate, bias)
     idx, w, gap = topk(lg, k)
-    disp = dispatch(x, idx, T=T, d=d, E=E, D=D, my_rank=my_rank, cf=cf)
+    disp = dispatch(x, idx, T=T, d=d, E=E, D=D, my_rank=my_rank, cf=cf,
+                    drop_policy=drop_policy, topk_w=w, min_capacity=min_capacity)
     eo = expert_ffn_all(disp["send_buf"], disp["expert_offset"], disp["expert_kept"], w1, w3, w2)
     y = combine(eo, disp["slot"], w)
     return dict(logits=lg, topk_idx=idx, topk_w=w, gap=gap, expert_out=eo, y=y, **disp)

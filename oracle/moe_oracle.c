@@ -37,14 +37,24 @@
  *        (3*d*H parameters); "Capacity semantics decide what crosses the
  *        wire": dropping happens before the exchange; "First-order dispatch
  *        and combine bytes": one input chunk per destination rank.
+ *   [DP] same page, "Capacity semantics decide what crosses the wire", and
+ *        its question on the capacity factor: with a capacity factor set,
+ *        the tokens beyond an expert's capacity are dropped by their
+ *        selected (gate) probability, the default strategy drops nothing.
+ *   [MC] same page, the DeepSpeed paragraph: a minimum capacity per expert
+ *        that holds regardless of the capacity factor.
  *
  * Readings taken where the pages are silent (each also listed in the design
  * notes): eps = 0 at inference; an optional per-expert logit bias b is added
  * to H and enters both selection and softmax; ties in KeepTopK go to the
  * lower expert index; the kept experts are reported in descending-logit
  * order; capacity uses the per-device token count T, computed as
- * ceil(cf*T*k/E) in double; overflow is dropped in token order (the first
- * C assignments of an expert, by token index, are kept); gates are not
+ * ceil(cf*T*k/E) in double, raised to a minimum capacity when one is given
+ * [MC]; overflow is dropped in token order (the first C assignments of an
+ * expert, by token index, are kept) under drop policy 0, or by gate
+ * probability under drop policy 1 [DP]: the C assignments with the largest
+ * gate value G stay, equal G going to the lower token index, and the kept
+ * rows keep token order inside the expert's block; gates are not
  * renormalised after a drop; a routing entry outside [0, E) or repeating
  * an expert already listed for its token is invalid (counted, dropped),
  * since KeepTopK yields k distinct experts; the expert is SwiGLU, W2 (SiLU(W1 x) * (W3 x))
@@ -164,15 +174,32 @@ void oracle_topk(int T, int E, int k, const float *logits, int32_t *topk_idx,
 }
 
 /* ------------------------------------------------------------------ */
-/* Step 3: capacity.                                         [CF]      */
-/* C = ceil(cf * T * k / E) evaluated left to right in IEEE double.    */
-/* cf = +inf means dropless; returns -1 then.                          */
+/* Step 3: capacity.                                     [CF][MC]      */
+/* C = ceil(cf * T * k / E) evaluated left to right in IEEE double,    */
+/* then C = max(C, min_capacity).  cf = +inf means dropless; returns   */
+/* -1 then (the minimum capacity does not apply).                      */
 /* ------------------------------------------------------------------ */
-int64_t oracle_capacity(int T, int k, int E, double cf)
+int64_t oracle_capacity(int T, int k, int E, double cf, int min_capacity)
 {
     if (isinf(cf))
         return -1;
-    return (int64_t)ceil(cf * (double)T * (double)k / (double)E);
+    int64_t C = (int64_t)ceil(cf * (double)T * (double)k / (double)E);
+    return C > min_capacity ? C : (int64_t)min_capacity;
+}
+
+/* Order of two assignments of one expert under drop policy 1: larger gate
+ * value first, then lower token index (a token lists an expert once, so
+ * the token decides every remaining tie).                       [DP]  */
+static const float *g_cmp_w;
+static int g_cmp_k;
+static int by_gate_then_token(const void *pa, const void *pb)
+{
+    int32_t a = *(const int32_t *)pa, b = *(const int32_t *)pb;
+    float ga = g_cmp_w[a], gb = g_cmp_w[b];
+    if (ga != gb)
+        return ga > gb ? -1 : 1;
+    int32_t ta = a / g_cmp_k, tb = b / g_cmp_k;
+    return (ta > tb) - (ta < tb);
 }
 
 /* Indices into the stats vector filled by oracle_dispatch. */
@@ -200,8 +227,13 @@ enum {
 /* Positions: assignments are visited in ascending token order; the    */
 /* position of (t, s) in expert e is the number of earlier tokens       */
 /* routed to e (a token's k experts are distinct, so the slot order    */
-/* inside one token never matters).  An assignment is kept iff its     */
-/* position is below C.  Layout: capacity mode gives expert e the rows */
+/* inside one token never matters).  Drop policy 0: an assignment is   */
+/* kept iff its position is below C.  Drop policy 1 [DP]: an expert    */
+/* with more than C assignments keeps the C first in the order of      */
+/* by_gate_then_token (topk_w holds G), and its kept assignments take  */
+/* positions 0..C-1 in ascending token order.  The counts, and so the  */
+/* offsets, bytes and per-rank rows, do not depend on the policy.      */
+/* Layout: capacity mode gives expert e the rows                        */
 /* [e*C, (e+1)*C) (pads left zero); dropless packs experts back to     */
 /* back, offset_e = n_0 + ... + n_(e-1).  Experts are in ascending     */
 /* order, so rank r's chunk -- the part the dispatch all-to-all sends  */
@@ -209,13 +241,18 @@ enum {
 /* send_buf [send_rows, d] may be NULL (accounting only).              */
 /* ------------------------------------------------------------------ */
 int oracle_dispatch(int T, int d, int E, int k, int D, int my_rank, double cf,
-                    const uint16_t *x, const int32_t *topk_idx, uint16_t *send_buf,
+                    int min_capacity, int drop_policy, const uint16_t *x,
+                    const int32_t *topk_idx, const float *topk_w, uint16_t *send_buf,
                     int32_t *slot, int32_t *expert_count, int32_t *expert_kept,
                     int64_t *expert_offset, int64_t *rank_rows, int64_t *stats)
 {
     if (D <= 0 || E % D != 0 || my_rank < 0 || my_rank >= D)
         return -1;
-    int64_t C = oracle_capacity(T, k, E, cf);
+    if (drop_policy != 0 && drop_policy != 1)
+        return -1;
+    if (drop_policy == 1 && !topk_w && (int64_t)T * k > 0)
+        return -1;
+    int64_t C = oracle_capacity(T, k, E, cf, min_capacity);
     int32_t *running = calloc((size_t)E, sizeof *running);
     int32_t *position = malloc((size_t)T * k * sizeof *position);
     if (!running || !position) {
@@ -258,6 +295,52 @@ int oracle_dispatch(int T, int d, int E, int k, int D, int my_rank, double cf,
     }
     int64_t send_rows = (C < 0) ? (int64_t)T * k : (int64_t)E * C;
     expert_offset[E] = (C < 0) ? acc : (int64_t)E * C;
+    /* drop policy 1: re-rank the assignments of every overflowing expert */
+    if (drop_policy == 1 && C >= 0) {
+        int32_t *list = malloc(((size_t)T * k + 1) * sizeof *list);
+        int64_t *start = malloc(((size_t)E + 1) * sizeof *start);
+        if (!list || !start) {
+            free(list);
+            free(start);
+            free(running);
+            free(position);
+            return -2;
+        }
+        start[0] = 0;
+        for (int e = 0; e < E; ++e)
+            start[e + 1] = start[e] + expert_count[e];
+        /* each expert's assignments, in ascending token order */
+        for (int64_t a = 0; a < (int64_t)T * k; ++a)
+            if (position[a] >= 0)
+                list[start[topk_idx[a]] + position[a]] = (int32_t)a;
+        g_cmp_w = topk_w;
+        g_cmp_k = k;
+        for (int e = 0; e < E; ++e) {
+            int64_t n = expert_count[e];
+            if (n <= C)
+                continue; /* everything fits: token-order positions stand */
+            int32_t *mine = list + start[e];
+            int32_t *ranked = malloc((size_t)n * sizeof *ranked);
+            if (!ranked) {
+                free(list);
+                free(start);
+                free(running);
+                free(position);
+                return -2;
+            }
+            memcpy(ranked, mine, (size_t)n * sizeof *ranked);
+            qsort(ranked, (size_t)n, sizeof *ranked, by_gate_then_token);
+            /* mark the C best; then number the kept ones in token order */
+            for (int64_t i = 0; i < n; ++i)
+                position[ranked[i]] = i < C ? 1 : 0;
+            int32_t next = 0;
+            for (int64_t i = 0; i < n; ++i) /* dropped: -1, no slot */
+                position[mine[i]] = position[mine[i]] == 1 ? next++ : -1;
+            free(ranked);
+        }
+        free(list);
+        free(start);
+    }
     /* slots and the send buffer */
     if (send_buf)
         memset(send_buf, 0, (size_t)send_rows * d * sizeof *send_buf);

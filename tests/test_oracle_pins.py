@@ -326,6 +326,116 @@ def test_dispatch_invalid_indices_counted_and_dropped():
     assert r["expert_count"].sum() == 9
 
 
+# ---------------------------------------------------------------------------
+# Drop by gate probability ("MoE Expert Parallelism Sizing: Traffic,
+# Capacity, Fabric", "Capacity semantics decide what crosses the wire") and
+# the minimum capacity per expert (same page, the DeepSpeed paragraph).
+# ---------------------------------------------------------------------------
+
+def test_capacity_with_minimum():
+    assert oracle.capacity(10, 2, 8, 1.0) == 3                     # 2.5 rounds up
+    assert oracle.capacity(10, 2, 8, 1.0, min_capacity=4) == 4     # raised to the minimum
+    assert oracle.capacity(10, 2, 8, 1.0, min_capacity=2) == 3     # minimum below C: no effect
+    assert oracle.capacity(10, 2, 8, 0.01, min_capacity=1) == 1    # ceil(0.025) = 1 already
+    assert oracle.capacity(4096, 2, 8, 1.0, min_capacity=1000) == 1024
+    assert oracle.capacity(4096, 8, 256, INF, min_capacity=64) == -1  # dropless: none applies
+
+
+# Worked by hand: T=5, E=3, k=2, cf 0.5 -> C = ceil(5*2*0.5/3) = ceil(1.67) = 2.
+PROB_IDX = np.array([[0, 1], [0, 2], [1, 0], [0, 1], [0, 2]], np.int32)
+PROB_W = np.array([[0.7, 0.3], [0.6, 0.4], [0.55, 0.45], [0.9, 0.1], [0.7, 0.3]], np.float32)
+
+
+def test_drop_by_probability_hand_example():
+    # expert 0: tokens 0 (0.7), 1 (0.6), 2 (0.45), 3 (0.9), 4 (0.7)
+    #   token order keeps 0, 1; by probability 3 (0.9) and 0 (0.7, tied with
+    #   token 4 and first by token), placed in token order: 0 -> row 0, 3 -> row 1
+    # expert 1: tokens 0 (0.3), 2 (0.55), 3 (0.1): keeps 2 and 0 -> rows 2, 3
+    # expert 2: tokens 1 (0.4), 4 (0.3): both fit -> rows 4, 5
+    x = np.arange(5 * 8, dtype=np.uint16).reshape(5, 8)
+    r0 = oracle.dispatch(x, PROB_IDX, T=5, d=8, E=3, D=1, cf=0.5, topk_w=PROB_W)
+    r1 = oracle.dispatch(x, PROB_IDX, T=5, d=8, E=3, D=1, cf=0.5, topk_w=PROB_W,
+                         drop_policy=1)
+    assert r0["stats"]["capacity"] == 2
+    np.testing.assert_array_equal(r0["slot"], [[0, 2], [1, 4], [3, -1], [-1, -1], [-1, 5]])
+    np.testing.assert_array_equal(r1["slot"], [[0, 2], [-1, 4], [3, -1], [1, -1], [-1, 5]])
+    np.testing.assert_array_equal(r1["send_buf"], x[[0, 3, 0, 2, 1, 4]])
+    # the counts, and everything derived from them, do not depend on the policy
+    for key in ("expert_count", "expert_kept", "expert_offset", "rank_rows"):
+        np.testing.assert_array_equal(r0[key], r1[key])
+    assert r0["stats"] == r1["stats"]
+
+
+def test_drop_by_probability_needs_gates():
+    with pytest.raises(ValueError):
+        oracle.dispatch(None, PROB_IDX, T=5, d=8, E=3, D=1, cf=0.5, drop_policy=1,
+                        with_send_buf=False)
+
+
+@pytest.mark.parametrize("T,E,k,cf,ties", [
+    (300, 8, 2, 0.8, False), (517, 16, 4, 1.0, True), (1000, 64, 2, 0.5, True),
+    (64, 4, 4, 1.0, False), (1, 8, 2, 0.1, False),
+])
+def test_drop_by_probability_invariants_random(T, E, k, cf, ties):
+    """Per expert: exactly min(n, C) kept; every kept gate >= every dropped
+    gate, and on equal gates the kept token comes first; kept rows in token
+    order; all counts equal to the token-order policy's."""
+    rng = np.random.default_rng(7 * T + E)
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    if ties:   # few distinct values: many exact ties
+        w = rng.integers(1, 5, (T, k)).astype(np.float32) / 8
+    else:
+        w = rng.random((T, k)).astype(np.float32)
+    d = 8
+    x = rng.integers(0, 65535, (T, d)).astype(np.uint16)
+    r0 = oracle.dispatch(x, idx, T=T, d=d, E=E, D=1, cf=cf, topk_w=w)
+    r1 = oracle.dispatch(x, idx, T=T, d=d, E=E, D=1, cf=cf, topk_w=w, drop_policy=1)
+    for key in ("expert_count", "expert_kept", "expert_offset", "rank_rows"):
+        np.testing.assert_array_equal(r0[key], r1[key])
+    assert r0["stats"] == r1["stats"]
+    C = r1["stats"]["capacity"]
+    for e in range(E):
+        t_, s_ = np.nonzero(idx == e)          # ascending token order
+        sl = r1["slot"][t_, s_]
+        g = w[t_, s_]
+        keep = sl >= 0
+        assert keep.sum() == min(len(t_), C)
+        if keep.any() and (~keep).any():
+            gk, gd = g[keep], g[~keep]
+            assert gk.min() >= gd.max()
+            tie = gk.min() == gd.max()
+            if tie:
+                assert t_[keep][gk == gk.min()].max() < t_[~keep][gd == gd.max()].min()
+        np.testing.assert_array_equal(sl[keep], r1["expert_offset"][e] + np.arange(keep.sum()))
+    for t in range(T):
+        for s in range(k):
+            if r1["slot"][t, s] >= 0:
+                np.testing.assert_array_equal(r1["send_buf"][r1["slot"][t, s]], x[t])
+
+
+def test_drop_by_probability_reduces_to_token_order_for_equal_gates():
+    """k = 1 gives G = 1 for every token: probability order is token order."""
+    rng = np.random.default_rng(3)
+    T, E = 400, 8
+    idx = rng.integers(0, E, (T, 1)).astype(np.int32)
+    w = np.ones((T, 1), np.float32)
+    x = rng.integers(0, 65535, (T, 16)).astype(np.uint16)
+    r0 = oracle.dispatch(x, idx, T=T, d=16, E=E, D=2, cf=0.7, topk_w=w)
+    r1 = oracle.dispatch(x, idx, T=T, d=16, E=E, D=2, cf=0.7, topk_w=w, drop_policy=1)
+    assert r0["stats"]["dropped"] > 0
+    np.testing.assert_array_equal(r0["slot"], r1["slot"])
+    np.testing.assert_array_equal(r0["send_buf"], r1["send_buf"])
+
+
+def test_minimum_capacity_prevents_drops_and_pads():
+    idx = PROB_IDX
+    r = oracle.dispatch(None, idx, T=5, d=8, E=3, D=1, cf=0.5, topk_w=PROB_W,
+                        drop_policy=1, min_capacity=5, with_send_buf=False)
+    st = r["stats"]
+    assert st["capacity"] == 5 and st["dropped"] == 0 and st["padded"] == 15 - 10
+    np.testing.assert_array_equal(r["expert_offset"], [0, 5, 10, 15])
+
+
 def test_dispatch_rejects_indivisible_placement():
     with pytest.raises(ValueError):
         oracle.dispatch(None, HAND_IDX, T=6, d=8, E=3, D=2, cf=INF, with_send_buf=False)
