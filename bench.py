@@ -93,7 +93,8 @@ def cpu_baseline(cfg, inp, budget_s):
         t0 = time.perf_counter()
         lg = oracle.logits(xb, wg, bias)
         idx, w, _ = oracle.topk(lg, cfg.k)
-        r = oracle.dispatch(xb, idx, T=tb, d=cfg.d, E=cfg.E, D=cfg.D, cf=cfg.cf)
+        r = oracle.dispatch(xb, idx, T=tb, d=cfg.d, E=cfg.E, D=cfg.D, cf=cfg.cf,
+                            drop_policy=cfg.drop_policy, topk_w=w, min_capacity=cfg.min_capacity)
         spent += time.perf_counter() - t0
         need = [e for e in range(cfg.E) if r["expert_kept"][e] and e not in experts]
         for e in need:  # weight copies to the host are not oracle work: not timed
@@ -140,7 +141,8 @@ def rank_local_gemm(cfg, inp, dev, steps, warmup):
     stream = torch.cuda.current_stream()
     api.moe_route(shape, xin["x"], xin["w_gate"], xin["bias"], None, buf.topk_idx, buf.topk_w,
                   buf.workspace, stream)
-    api.moe_dispatch(shape, xin["x"], buf.topk_idx, buf.send_buf, buf.slot, buf.expert_count,
+    api.moe_dispatch(shape, xin["x"], buf.topk_idx, buf.topk_w, buf.send_buf, buf.slot,
+                     buf.expert_count,
                      buf.expert_kept, buf.expert_offset, buf.rank_rows, buf.stats,
                      buf.workspace, stream)
     el = cfg.E // cfg.D
@@ -194,6 +196,10 @@ def main():
     ap.add_argument("--workload", default="dsv3_prefill")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--drop-policy", type=int, default=None, choices=(0, 1),
+                    help="capacity overflow: 0 token order, 1 by gate value (default: the workload's)")
+    ap.add_argument("--min-capacity", type=int, default=None,
+                    help="lower bound on the expert capacity (default: the workload's)")
     ap.add_argument("--no-rank-local", action="store_true",
                     help="skip the expert-parallel rank-local GEMM measurement")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -210,6 +216,10 @@ def main():
     from expert_token_routing_moe_amd.inputs import CONFIGS, make_inputs
 
     cfg = CONFIGS[args.workload]
+    if args.drop_policy is not None:
+        cfg = cfg.with_(drop_policy=args.drop_policy)
+    if args.min_capacity is not None:
+        cfg = cfg.with_(min_capacity=args.min_capacity)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     log(f"bench: {cfg.name} T={cfg.T} d={cfg.d} E={cfg.E} k={cfg.k} H={cfg.H} cf={cfg.cf}")
@@ -226,7 +236,7 @@ def main():
         api.moe_route(shape, inp["x"], inp["w_gate"], inp["bias"], None, buf.topk_idx,
                       buf.topk_w, buf.workspace, stream)
         rec(1)
-        api.moe_dispatch(shape, inp["x"], buf.topk_idx, buf.send_buf, buf.slot,
+        api.moe_dispatch(shape, inp["x"], buf.topk_idx, buf.topk_w, buf.send_buf, buf.slot,
                          buf.expert_count, buf.expert_kept, buf.expert_offset, buf.rank_rows,
                          buf.stats, buf.workspace, stream)
         rec(2)
@@ -301,6 +311,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "E": cfg.E, "k": cfg.k,
                    "H": cfg.H, "capacity_factor": None if cfg.cf == float("inf") else cfg.cf,
+                   "drop_policy": cfg.drop_policy, "min_capacity": cfg.min_capacity,
                    "D": cfg.D, "parallelism": "single GPU share (EP rank-local layout)"},
         "grouped_gemm": {"tflops": round(gemm_flops / gemm_s / 1e12, 1),
                          "mfma_util": round(gemm_flops / gemm_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),

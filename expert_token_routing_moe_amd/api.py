@@ -41,7 +41,7 @@ class moe_shape(ctypes.Structure):
         ("T", ctypes.c_int32), ("d", ctypes.c_int32), ("E", ctypes.c_int32),
         ("k", ctypes.c_int32), ("H", ctypes.c_int32), ("D", ctypes.c_int32),
         ("my_rank", ctypes.c_int32), ("drop_policy", ctypes.c_int32),
-        ("capacity_factor", ctypes.c_double),
+        ("min_capacity", ctypes.c_int32), ("capacity_factor", ctypes.c_double),
     ]
 
 
@@ -63,7 +63,7 @@ def lib():
                       ctypes.POINTER(ctypes.c_size_t)],
         "moe_route": [S, P, P, P, P, P, P, P, SZ, P],
         "moe_topk_from_logits": [S, P, P, P, P],
-        "moe_dispatch": [S, P, P, P, P, P, P, P, P, P, P, SZ, P],
+        "moe_dispatch": [S, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
         "moe_expert_ffn": [S, P, P, P, P, P, P, P, P, SZ, P],
         "moe_expert_gate_up": [S, P, P, P, P, P, P, P],
         "moe_expert_down": [S, P, P, P, P, P, P],
@@ -98,14 +98,16 @@ class Shape:
     my_rank: int = 0
     capacity_factor: float = math.inf
     drop_policy: int = 0
+    min_capacity: int = 0
 
     def c(self) -> moe_shape:
         return moe_shape(self.T, self.d, self.E, self.k, self.H, self.D, self.my_rank,
-                         self.drop_policy, float(self.capacity_factor))
+                         self.drop_policy, self.min_capacity, float(self.capacity_factor))
 
     @classmethod
     def from_config(cls, cfg) -> "Shape":
-        return cls(cfg.T, cfg.d, cfg.E, cfg.k, cfg.H, cfg.D, cfg.my_rank, cfg.cf)
+        return cls(cfg.T, cfg.d, cfg.E, cfg.k, cfg.H, cfg.D, cfg.my_rank, cfg.cf,
+                   cfg.drop_policy, cfg.min_capacity)
 
 
 def _p(t: torch.Tensor | None, dtype=None):
@@ -153,11 +155,13 @@ def moe_topk_from_logits(shape, logits, topk_idx, topk_w, stream=None):
         ctypes.byref(s), _p(logits, F32), _p(topk_idx, I32), _p(topk_w, F32), _stream(stream)))
 
 
-def moe_dispatch(shape, x, topk_idx, send_buf, slot, expert_count, expert_kept, expert_offset,
-                 rank_rows, stats, workspace, stream=None):
+def moe_dispatch(shape, x, topk_idx, topk_w, send_buf, slot, expert_count, expert_kept,
+                 expert_offset, rank_rows, stats, workspace, stream=None):
+    """topk_w is read only by drop policy 1 in capacity mode; may be None otherwise."""
     s = shape.c()
     _check("moe_dispatch", lib().moe_dispatch(
-        ctypes.byref(s), _p(x, BF16), _p(topk_idx, I32), _p(send_buf, BF16), _p(slot, I32),
+        ctypes.byref(s), _p(x, BF16), _p(topk_idx, I32), _p(topk_w, F32), _p(send_buf, BF16),
+        _p(slot, I32),
         _p(expert_count, I32), _p(expert_kept, I32), _p(expert_offset, I32),
         _p(rank_rows, I32), _p(stats, torch.int64), _p(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))

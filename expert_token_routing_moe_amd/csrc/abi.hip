@@ -27,6 +27,9 @@ Workspace workspace_layout(const Dims &dm)
     w.chunk_counts = take((size_t)dm.nchunks * dm.E * sizeof(int32_t));
     w.chunk_base = take((size_t)dm.nchunks * dm.E * sizeof(int32_t));
     w.chunk_invalid = take((size_t)dm.nchunks * sizeof(int32_t));
+    const bool by_gate = dm.drop_policy == 1 && dm.capacity >= 0;
+    w.all_offset = take(by_gate ? (size_t)dm.E * sizeof(int32_t) : 0);
+    w.by_expert = take(by_gate ? (size_t)dm.T * dm.k * sizeof(int32_t) : 0);
     w.h = take((size_t)dm.send_rows * dm.H * sizeof(uint16_t));
     w.total = std::max<size_t>(off, 256);
     return w;
@@ -46,8 +49,10 @@ static int make_dims(const moe_shape *s, Dims *dm)
         return MOE_EINVAL;
     if (s->d % 8 != 0)
         return MOE_EINVAL;
-    if (s->drop_policy != 0)
-        return MOE_EUNSUPPORTED;
+    if (s->drop_policy != 0 && s->drop_policy != 1)
+        return MOE_EINVAL;
+    if (s->min_capacity < 0)
+        return MOE_EINVAL;
     if (s->d % 64 != 0 || s->H % 64 != 0 || s->E > kMaxExperts)
         return MOE_EUNSUPPORTED;
     const long long assignments = (long long)s->T * s->k;
@@ -55,11 +60,12 @@ static int make_dims(const moe_shape *s, Dims *dm)
         return MOE_EUNSUPPORTED;
     long long C = -1, send_rows = assignments;
     if (!isinf(cf)) {
-        // C = ceil(cf * T * k / E), evaluated left to right in double
+        // C = ceil(cf * T * k / E), evaluated left to right in double, then
+        // raised to the minimum capacity
         const double c = ceil(cf * (double)s->T * (double)s->k / (double)s->E);
         if (c > (double)INT32_MAX)
             return MOE_EUNSUPPORTED;
-        C = (long long)c;
+        C = std::max<long long>((long long)c, s->min_capacity);
         send_rows = (long long)s->E * C;
     }
     if (send_rows > INT32_MAX)
@@ -75,6 +81,7 @@ static int make_dims(const moe_shape *s, Dims *dm)
     dm->H = s->H;
     dm->D = s->D;
     dm->my_rank = s->my_rank;
+    dm->drop_policy = s->drop_policy;
     dm->capacity = C;
     dm->send_rows = send_rows;
     dm->nchunks = (s->T + kChunk - 1) / kChunk;
@@ -150,15 +157,18 @@ MOE_EXPORT int moe_topk_from_logits(const moe_shape *shape, const float *logits,
 }
 
 MOE_EXPORT int moe_dispatch(const moe_shape *shape, const uint16_t *x, const int32_t *topk_idx,
-                            uint16_t *send_buf, int32_t *slot, int32_t *expert_count,
-                            int32_t *expert_kept, int32_t *expert_offset, int32_t *rank_rows,
-                            moe_stats *stats, void *workspace, size_t workspace_bytes,
-                            void *stream)
+                            const float *topk_w, uint16_t *send_buf, int32_t *slot,
+                            int32_t *expert_count, int32_t *expert_kept, int32_t *expert_offset,
+                            int32_t *rank_rows, moe_stats *stats, void *workspace,
+                            size_t workspace_bytes, void *stream)
 {
     Dims dm;
     int rc = make_dims(shape, &dm);
     if (rc != MOE_OK)
         return rc;
+    const bool need_w = dm.drop_policy == 1 && dm.capacity >= 0;
+    if (need_w ? bad_ptr(topk_w, dm.T) : bad_opt_ptr(topk_w))
+        return MOE_EINVAL;
     if (bad_ptr(x, dm.T) || bad_ptr(topk_idx, dm.T) || bad_ptr(send_buf, dm.send_rows) ||
         bad_ptr(slot, dm.T) || bad_ptr(expert_count) || bad_ptr(expert_kept) ||
         bad_ptr(expert_offset) || bad_ptr(rank_rows) || bad_ptr(stats))
@@ -166,7 +176,8 @@ MOE_EXPORT int moe_dispatch(const moe_shape *shape, const uint16_t *x, const int
     Workspace wl;
     if ((rc = check_ws(dm, workspace, workspace_bytes, &wl)) != MOE_OK)
         return rc;
-    return hip_status(launch_dispatch(dm, x, topk_idx, send_buf, slot, expert_count, expert_kept,
+    return hip_status(launch_dispatch(dm, x, topk_idx, topk_w, send_buf, slot, expert_count,
+                                      expert_kept,
                                       expert_offset, rank_rows, stats, (char *)workspace, wl,
                                       static_cast<hipStream_t>(stream)));
 }
@@ -267,8 +278,8 @@ MOE_EXPORT int moe_layer_fwd(const moe_shape *shape, const uint16_t *x, const ui
     hipError_t e =
         launch_route(dm, x, w_gate, logit_bias, logits_out, topk_idx, topk_w, ws, wl, st);
     if (e == hipSuccess)
-        e = launch_dispatch(dm, x, topk_idx, send_buf, slot, expert_count, expert_kept,
-                            expert_offset, rank_rows, stats, ws, wl, st);
+        e = launch_dispatch(dm, x, topk_idx, topk_w, send_buf, slot, expert_count,
+                            expert_kept, expert_offset, rank_rows, stats, ws, wl, st);
     if (e == hipSuccess)
         e = launch_gate_up(dm, send_buf, expert_offset, expert_kept, w1, w3,
                            reinterpret_cast<uint16_t *>(ws + wl.h), st);

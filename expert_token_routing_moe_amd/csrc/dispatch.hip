@@ -21,6 +21,20 @@
 //  3. permute: a wavefront per token turns positions into slots, reads the
 //     token row once and writes it to each kept slot with 16-byte stores;
 //     extra workgroups zero the pad rows of capacity mode.
+//
+// Drop by gate value (drop policy 1, capacity mode; "MoE Expert Parallelism
+// Sizing: Traffic, Capacity, Fabric", "Capacity semantics decide what
+// crosses the wire": overflow is dropped by selected probability) adds two
+// kernels between 2 and 3:
+//  a. group: every valid assignment writes its index into its expert's
+//     segment of a by-expert list, at its token-order position.
+//  b. select: a workgroup per expert.  If the expert holds more than C
+//     assignments, a radix select over the gate values finds the C-th
+//     largest one exactly; equal gates at that boundary go to the lower
+//     tokens, i.e. the first ones in the token-ordered list.  The kept
+//     assignments are then numbered in list (token) order by a block scan,
+//     and the final in-expert positions replace the in-chunk ones.
+// The counts do not change, so the scan's offsets and counters stand.
 #include "moe_internal.hpp"
 
 namespace moe {
@@ -100,7 +114,8 @@ __global__ __launch_bounds__(kMaxExperts) void scan_kernel(
     const int32_t *__restrict__ chunk_counts, int32_t *__restrict__ chunk_base,
     const int32_t *__restrict__ chunk_invalid, int32_t *__restrict__ expert_count,
     int32_t *__restrict__ expert_kept, int32_t *__restrict__ expert_offset,
-    int32_t *__restrict__ rank_rows, moe_stats *__restrict__ stats)
+    int32_t *__restrict__ rank_rows, moe_stats *__restrict__ stats,
+    int32_t *__restrict__ all_offset)
 {
     __shared__ int32_t s_n[kMaxExperts], s_kept[kMaxExperts];
     __shared__ int32_t s_wave_sum[kMaxExperts / 64];
@@ -142,6 +157,8 @@ __global__ __launch_bounds__(kMaxExperts) void scan_kernel(
     const int excl = wave_base + incl - n;
     if (e < E)
         expert_offset[e] = (C < 0) ? excl : (int)((long long)e * C);
+    if (all_offset && e < E)
+        all_offset[e] = excl; // where expert e's assignments start in the by-expert list
     if (e == E - 1)
         expert_offset[E] = (C < 0) ? excl + n : (int)((long long)E * C);
     // reductions
@@ -182,6 +199,153 @@ __global__ __launch_bounds__(kMaxExperts) void scan_kernel(
     }
 }
 
+// a. Assignment a = t*k + s of expert e goes to by_expert[all_offset[e] + its
+//    token-order position]: each expert's segment lists its assignments in
+//    ascending token order.
+__global__ __launch_bounds__(256) void group_by_expert_kernel(
+    const int32_t *__restrict__ topk_idx, const int32_t *__restrict__ pos_in_chunk,
+    const int32_t *__restrict__ chunk_base, const int32_t *__restrict__ all_offset, int T,
+    int k, int E, int32_t *__restrict__ by_expert)
+{
+    const long long a = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (a >= (long long)T * k)
+        return;
+    const int p = pos_in_chunk[a];
+    if (p < 0) // invalid entry
+        return;
+    const int t = (int)(a / k);
+    const int e = topk_idx[a];
+    by_expert[all_offset[e] + chunk_base[(size_t)(t / kChunk) * E + e] + p] = (int32_t)a;
+}
+
+// Order key of a gate value under drop policy 1: the fp32 bits mapped to an
+// unsigned integer with the same order (-0 taken as +0).
+__device__ __forceinline__ uint32_t gate_key(float g)
+{
+    uint32_t b = __float_as_uint(g);
+    if (b == 0x80000000u)
+        b = 0u;
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+constexpr int kSelCache = 16384; // gate keys an expert keeps in LDS (more: re-read)
+
+// b. One workgroup of 1024 threads per expert.  If the expert holds n > C
+// assignments, a most-significant-digit radix select (four 8-bit digits)
+// finds the gate key g* of the C-th largest gate and how many of the
+// assignments with gate exactly g* still fit (m >= 1).  Because the list is
+// in token order, the tie rule (equal gates: lower token first) keeps the
+// first m of those in list order.  The kept ones are then numbered in list
+// order: position = #(g > g*) before + min(#(g = g*) before, m), from one
+// block scan of the two packed counts.
+__global__ __launch_bounds__(1024) void gate_select_kernel(
+    const int32_t *__restrict__ by_expert, const int32_t *__restrict__ all_offset,
+    const int32_t *__restrict__ expert_count, const float *__restrict__ topk_w,
+    long long C, int32_t *__restrict__ slot)
+{
+    __shared__ uint32_t s_key[kSelCache];
+    __shared__ uint32_t hist[256];
+    __shared__ uint32_t s_wave[kMaxExperts / 64];
+    __shared__ uint32_t s_prefix;
+    __shared__ int s_want;
+    const int e = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n = expert_count[e];
+    const int32_t *list = by_expert + all_offset[e];
+    if (n <= C) { // everything fits: the token-order positions stand
+        for (int i = tid; i < n; i += 1024)
+            slot[list[i]] = i;
+        return;
+    }
+    const bool cached = n <= kSelCache;
+    if (cached)
+        for (int i = tid; i < n; i += 1024)
+            s_key[i] = gate_key(topk_w[list[i]]);
+    auto key_of = [&](int i) { return cached ? s_key[i] : gate_key(topk_w[list[i]]); };
+    uint32_t prefix = 0, mask = 0;
+    int want = (int)C; // rank, among keys matching prefix, of the wanted key
+    for (int shift = 24; shift >= 0; shift -= 8) {
+        if (tid < 256)
+            hist[tid] = 0u;
+        __syncthreads();
+        for (int i = tid; i < n; i += 1024) {
+            const uint32_t key = key_of(i);
+            if ((key & mask) == prefix)
+                atomicAdd(&hist[(key >> shift) & 255u], 1u);
+        }
+        __syncthreads();
+        if (wave == 0) {
+            // lane l holds digits 255-4l .. 252-4l (largest first)
+            uint32_t c[4];
+            int tot = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                c[j] = hist[255 - (4 * lane + j)];
+                tot += (int)c[j];
+            }
+            int incl = tot;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const int o = __shfl_up(incl, off, 64);
+                if (lane >= off)
+                    incl += o;
+            }
+            const unsigned long long hit = __ballot(incl >= want);
+            if (lane == __ffsll((long long)hit) - 1) {
+                int above = incl - tot;
+                int digit = 0;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    if (above + (int)c[j] >= want) {
+                        digit = 255 - (4 * lane + j);
+                        break;
+                    }
+                    above += (int)c[j];
+                }
+                s_want = want - above;
+                s_prefix = prefix | ((uint32_t)digit << shift);
+            }
+        }
+        __syncthreads();
+        want = s_want;
+        prefix = s_prefix;
+        mask |= 255u << shift;
+    }
+    const uint32_t thr = prefix; // g*; `want` of the keys equal to it are kept
+    int gt_carry = 0, eq_carry = 0;
+    for (int base = 0; base < n; base += 1024) {
+        const int i = base + tid;
+        const uint32_t key = i < n ? key_of(i) : 0u;
+        const uint32_t gt = (i < n && key > thr) ? 1u : 0u;
+        const uint32_t eq = (i < n && key == thr) ? 1u : 0u;
+        const uint32_t v = gt | (eq << 16); // per-tile counts stay below 2^16
+        uint32_t incl = v;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const uint32_t o = __shfl_up(incl, off, 64);
+            if (lane >= off)
+                incl += o;
+        }
+        if (lane == 63)
+            s_wave[wave] = incl;
+        __syncthreads();
+        uint32_t before = 0, total = 0;
+        for (int w = 0; w < kMaxExperts / 64; ++w) {
+            before += w < wave ? s_wave[w] : 0u;
+            total += s_wave[w];
+        }
+        const uint32_t ex = before + incl - v;
+        const int gt_before = gt_carry + (int)(ex & 0xffffu);
+        const int eq_before = eq_carry + (int)(ex >> 16);
+        if (i < n) {
+            const bool keep = gt || (eq && eq_before < want);
+            slot[list[i]] = keep ? gt_before + min(eq_before, want) : -1;
+        }
+        gt_carry += (int)(total & 0xffffu);
+        eq_carry += (int)(total >> 16);
+        __syncthreads();
+    }
+}
+
 constexpr int kSlotGroup = 8; // slots resolved per pass over a token row
 
 __global__ __launch_bounds__(256) void permute_kernel(
@@ -189,7 +353,7 @@ __global__ __launch_bounds__(256) void permute_kernel(
     int32_t *__restrict__ slot, const int32_t *__restrict__ chunk_base,
     const int32_t *__restrict__ expert_offset, const int32_t *__restrict__ expert_kept,
     uint16_t *__restrict__ send_buf, int T, int d, int k, int E, long long C, int tok_blocks,
-    int pad_parts)
+    int pad_parts, int pos_final)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int nvec = d / 8; // 16-byte vectors per row
@@ -208,12 +372,13 @@ __global__ __launch_bounds__(256) void permute_kernel(
                 const int s = s0 + q;
                 int sl = -1;
                 if (s < k) {
-                    // in-chunk position, or -1
+                    // in-chunk position (in-expert position if pos_final), or -1
                     const int p = __builtin_amdgcn_readfirstlane(slot[(size_t)t * k + s]);
                     if (p >= 0) {
                         const int e = __builtin_amdgcn_readfirstlane(row[s]);
                         const long long pos =
-                            (long long)__builtin_amdgcn_readfirstlane(base[e]) + p;
+                            pos_final ? p
+                                      : (long long)__builtin_amdgcn_readfirstlane(base[e]) + p;
                         if (C < 0 || pos < C)
                             sl = __builtin_amdgcn_readfirstlane(expert_offset[e]) + (int)pos;
                     }
@@ -278,13 +443,17 @@ __global__ __launch_bounds__(256) void permute_kernel(
 } // namespace
 
 hipError_t launch_dispatch(const Dims &dm, const uint16_t *x, const int32_t *topk_idx,
-                           uint16_t *send_buf, int32_t *slot, int32_t *expert_count,
-                           int32_t *expert_kept, int32_t *expert_offset, int32_t *rank_rows,
-                           moe_stats *stats, char *ws, const Workspace &wl, hipStream_t st)
+                           const float *topk_w, uint16_t *send_buf, int32_t *slot,
+                           int32_t *expert_count, int32_t *expert_kept, int32_t *expert_offset,
+                           int32_t *rank_rows, moe_stats *stats, char *ws, const Workspace &wl,
+                           hipStream_t st)
 {
     int32_t *chunk_counts = reinterpret_cast<int32_t *>(ws + wl.chunk_counts);
     int32_t *chunk_base = reinterpret_cast<int32_t *>(ws + wl.chunk_base);
     int32_t *chunk_invalid = reinterpret_cast<int32_t *>(ws + wl.chunk_invalid);
+    const bool by_gate = dm.drop_policy == 1 && dm.capacity >= 0;
+    int32_t *all_offset = by_gate ? reinterpret_cast<int32_t *>(ws + wl.all_offset) : nullptr;
+    int32_t *by_expert = reinterpret_cast<int32_t *>(ws + wl.by_expert);
     if (dm.nchunks > 0) {
         const size_t lds = (size_t)dm.E * kWords * sizeof(uint32_t);
         count_kernel<<<dm.nchunks, kChunk, lds, st>>>(topk_idx, dm.T, dm.k, dm.E, slot,
@@ -293,7 +462,14 @@ hipError_t launch_dispatch(const Dims &dm, const uint16_t *x, const int32_t *top
     scan_kernel<<<1, kMaxExperts, 0, st>>>(dm.T, dm.k, dm.E, dm.D, dm.my_rank, dm.d,
                                            (long long)dm.capacity, dm.nchunks, chunk_counts,
                                            chunk_base, chunk_invalid, expert_count, expert_kept,
-                                           expert_offset, rank_rows, stats);
+                                           expert_offset, rank_rows, stats, all_offset);
+    if (by_gate && dm.T > 0) {
+        const long long a = (long long)dm.T * dm.k;
+        group_by_expert_kernel<<<(unsigned)((a + 255) / 256), 256, 0, st>>>(
+            topk_idx, slot, chunk_base, all_offset, dm.T, dm.k, dm.E, by_expert);
+        gate_select_kernel<<<dm.E, 1024, 0, st>>>(by_expert, all_offset, expert_count, topk_w,
+                                                   (long long)dm.capacity, slot);
+    }
     const int tok_blocks = (dm.T + 3) / 4;
     int pad_parts = 0;
     long long pad_blocks = 0;
@@ -310,7 +486,7 @@ hipError_t launch_dispatch(const Dims &dm, const uint16_t *x, const int32_t *top
     if (blocks > 0)
         permute_kernel<<<(unsigned)blocks, 256, 0, st>>>(
             x, topk_idx, slot, chunk_base, expert_offset, expert_kept, send_buf, dm.T, dm.d,
-            dm.k, dm.E, (long long)dm.capacity, tok_blocks, pad_parts);
+            dm.k, dm.E, (long long)dm.capacity, tok_blocks, pad_parts, by_gate ? 1 : 0);
     return hipGetLastError();
 }
 

@@ -46,6 +46,7 @@ constexpr int kMaxExperts = 1024; // E limit of the LDS bitmaps and scans
 // Derived per-call shape facts (host side).
 struct Dims {
     int T, d, E, k, H, D, my_rank;
+    int drop_policy;   // 0: token order, 1: by gate value (capacity mode only)
     int64_t capacity;  // C, or -1 when dropless
     int64_t send_rows; // E*C or T*k
     int nchunks;       // ceil(T / kChunk)
@@ -58,6 +59,8 @@ struct Workspace {
     size_t chunk_counts;  // int32 [nchunks, E] per-chunk expert counts
     size_t chunk_base;    // int32 [nchunks, E] exclusive scan of the counts over chunks
     size_t chunk_invalid; // int32 [nchunks]    invalid entries per chunk
+    size_t all_offset;    // int32 [E]          exclusive scan of n_e (drop policy 1)
+    size_t by_expert;     // int32 [T*k]        assignments grouped by expert (drop policy 1)
     size_t h;             // bf16 [send_rows, H] SwiGLU hidden activations
     size_t total;
 };
@@ -75,7 +78,7 @@ hipError_t launch_route(const Dims &dm, const uint16_t *x, const uint16_t *w_gat
 hipError_t launch_topk_softmax(const Dims &dm, const float *logits, int32_t *topk_idx,
                                float *topk_w, hipStream_t st);
 hipError_t launch_dispatch(const Dims &dm, const uint16_t *x, const int32_t *topk_idx,
-                           uint16_t *send_buf, int32_t *slot, int32_t *expert_count,
+                           const float *topk_w, uint16_t *send_buf, int32_t *slot, int32_t *expert_count,
                            int32_t *expert_kept, int32_t *expert_offset, int32_t *rank_rows,
                            moe_stats *stats, char *ws, const Workspace &wl, hipStream_t st);
 hipError_t launch_gate_up(const Dims &dm, const uint16_t *send_buf, const int32_t *expert_offset,

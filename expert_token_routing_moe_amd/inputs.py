@@ -40,6 +40,8 @@ class MoEConfig:
     bias: dict = field(default_factory=dict)  # expert -> logit bias
     my_rank: int = 0
     seed: int = BASE_SEED
+    drop_policy: int = 0   # 0: overflow dropped in token order; 1: by gate value
+    min_capacity: int = 0  # lower bound on the capacity C (capacity mode)
 
     def with_(self, **kw) -> "MoEConfig":
         return replace(self, **kw)

@@ -23,6 +23,11 @@
  *        "Capacity semantics decide what crosses the wire" (drop before the
  *        exchange), "First-order dispatch and combine bytes" (one input chunk
  *        per destination rank).
+ *   [DP] same page, "Capacity semantics decide what crosses the wire" and its
+ *        question on the capacity factor: with a capacity factor set, tokens
+ *        beyond an expert's capacity are dropped by selected probability.
+ *   [MC] same page, the DeepSpeed paragraph: a minimum capacity per expert
+ *        regardless of the capacity factor.
  *
  * Conventions for every call
  *   - Tensor pointers are DEVICE pointers (HIP global memory) unless marked
@@ -61,7 +66,7 @@ extern "C" {
 #define MOE_EWORKSPACE (-3)   /* workspace NULL or smaller than moe_query says  */
 #define MOE_EHIP (-4)         /* a HIP launch reported an error                 */
 
-/* Shape of one layer on one device, in the pages' notation [N][CF][PL].
+/* Shape of one layer on one device, in the pages' notation [N][CF][PL][DP][MC].
  *   T        tokens on this device (T >= 0; T = 0 enqueues nothing)
  *   d        hidden size (d > 0, d % 64 == 0)
  *   E        routed experts (1 <= E <= 1024, E % D == 0)
@@ -70,9 +75,15 @@ extern "C" {
  *   D        logical destination ranks (D >= 1); rank r owns the contiguous
  *            experts [r*E/D, (r+1)*E/D)  [PL]
  *   my_rank  this device's rank, 0 <= my_rank < D (only for byte accounting)
- *   drop_policy  0: overflow is dropped in token order (the first C
- *            assignments of an expert by token index are kept).  Other
- *            values are rejected with MOE_EUNSUPPORTED.
+ *   drop_policy  which assignments an expert over capacity keeps:
+ *            0: the first C by token index (token order);
+ *            1: the C with the largest gate value G = topk_w[t,s], equal G
+ *               going to the lower token index [DP].
+ *            Either way the kept rows sit in ascending token order inside
+ *            the expert's block, and the counts (so offsets, bytes and
+ *            per-rank rows) are the same.  Other values -> MOE_EINVAL.
+ *   min_capacity  >= 0: in capacity mode C = max(ceil(f*T*k/E), min_capacity)
+ *            [MC]; 0 leaves C as computed.  Ignored when dropless.
  *   capacity_factor  f > 0: capacity C = ceil(f*T*k/E), evaluated left to
  *            right in IEEE double [CF]; +INFINITY: dropless (no capacity).
  *            NaN, zero, negative -> MOE_EINVAL.
@@ -80,6 +91,7 @@ extern "C" {
 typedef struct moe_shape {
     int32_t T, d, E, k, H, D, my_rank;
     int32_t drop_policy;
+    int32_t min_capacity;
     double capacity_factor;
 } moe_shape;
 
@@ -108,6 +120,7 @@ typedef struct moe_stats {
 
 /* Host-only size query.  Writes (host pointers, each may be NULL):
  *   send_rows        rows of send_buf / expert_out: E*C, or T*k if dropless
+ *                    (C includes the minimum capacity)
  *   capacity         C, or -1 if dropless  [CF]
  *   workspace_bytes  bytes of device workspace every call below needs
  *                    (one size serves them all)
@@ -136,12 +149,14 @@ int moe_route(const moe_shape *shape, const uint16_t *x, const uint16_t *w_gate,
 int moe_topk_from_logits(const moe_shape *shape, const float *logits, int32_t *topk_idx,
                          float *topk_w, void *stream);
 
-/* Dispatch [N][CF][TD][PL][M]: histogram n_e, capacity, token-order
- * positions, slots and the send buffer.
+/* Dispatch [N][CF][TD][PL][M][DP]: histogram n_e, capacity, positions,
+ * slots and the send buffer.
  *   x             [T, d] bf16
  *   topk_idx      [T, k] int32 (entries outside [0, E), and repeats of an
  *                 expert already listed for the token, are counted in
  *                 stats->invalid_index and dropped)
+ *   topk_w        [T, k] fp32 gates (as moe_route writes them): read only by
+ *                 drop policy 1 in capacity mode, may be NULL otherwise
  *   send_buf      [send_rows, d] bf16 out.  Expert e's kept rows are
  *                 [expert_offset[e], expert_offset[e] + expert_kept[e]), in
  *                 ascending token order; capacity mode gives expert e the
@@ -160,7 +175,7 @@ int moe_topk_from_logits(const moe_shape *shape, const float *logits, int32_t *t
  *   stats         one moe_stats, device memory, out
  *   workspace     device, >= moe_query's size */
 int moe_dispatch(const moe_shape *shape, const uint16_t *x, const int32_t *topk_idx,
-                 uint16_t *send_buf, int32_t *slot, int32_t *expert_count, int32_t *expert_kept,
+                 const float *topk_w, uint16_t *send_buf, int32_t *slot, int32_t *expert_count, int32_t *expert_kept,
                  int32_t *expert_offset, int32_t *rank_rows, moe_stats *stats, void *workspace,
                  size_t workspace_bytes, void *stream);
 

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 def test_query_matches_oracle_capacity(name):
     cfg = CONFIGS[name]
     sr, cap, ws = api.moe_query(api.Shape.from_config(cfg))
-    C = oracle.capacity(cfg.T, cfg.k, cfg.E, cfg.cf)
+    C = oracle.capacity(cfg.T, cfg.k, cfg.E, cfg.cf, cfg.min_capacity)
     assert cap == C
     assert sr == (cfg.T * cfg.k if C < 0 else cfg.E * C)
     # workspace holds at least the SwiGLU hidden activations h [send_rows, H] bf16
@@ -48,6 +48,27 @@ def test_query_degenerate_token_counts(T, cf):
     assert cap == oracle.capacity(T, 2, 8, cf)
     assert sr == (T * 2 if cap < 0 else 8 * cap)
     assert ws > 0
+
+
+@pytest.mark.parametrize("T,cf,mc", [(256, 1.25, 0), (256, 1.25, 80), (256, 1.25, 81),
+                                     (256, 0.01, 7), (1, 1.0, 3), (0, 1.0, 5),
+                                     (256, math.inf, 100)])
+def test_query_minimum_capacity_matches_oracle(T, cf, mc):
+    for policy in (0, 1):
+        sr, cap, _ = api.moe_query(api.Shape(T=T, d=128, E=8, k=2, H=128, D=2,
+                                             capacity_factor=cf, drop_policy=policy,
+                                             min_capacity=mc))
+        assert cap == oracle.capacity(T, 2, 8, cf, mc)
+        assert sr == (T * 2 if cap < 0 else 8 * cap)
+
+
+def test_query_workspace_grows_only_for_gate_order_drops():
+    base = dict(T=256, d=128, E=8, k=2, H=128, D=2, capacity_factor=1.25)
+    _, _, ws0 = api.moe_query(api.Shape(**base))
+    _, _, ws1 = api.moe_query(api.Shape(**base, drop_policy=1))
+    assert ws1 >= ws0 + 256 * 2 * 4          # the by-expert assignment list
+    base["capacity_factor"] = math.inf       # dropless: nothing to drop, no extra space
+    assert api.moe_query(api.Shape(**base, drop_policy=1))[2] == api.moe_query(api.Shape(**base))[2]
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -63,7 +84,9 @@ def test_query_degenerate_token_counts(T, cf):
     (dict(d=520), api.MOE_EUNSUPPORTED),         # multiple of 8, not of 64
     (dict(H=1000), api.MOE_EUNSUPPORTED),
     (dict(E=2048, D=1, k=2), api.MOE_EUNSUPPORTED),
-    (dict(drop_policy=1), api.MOE_EUNSUPPORTED),
+    (dict(drop_policy=2), api.MOE_EINVAL),
+    (dict(drop_policy=-1), api.MOE_EINVAL),
+    (dict(min_capacity=-1), api.MOE_EINVAL),
     (dict(capacity_factor=1e12), api.MOE_EUNSUPPORTED),  # E*C does not fit int32 rows
 ])
 def test_query_rejects_bad_shapes(kw, status):
@@ -90,9 +113,17 @@ def test_entry_points_reject_null_and_misaligned_pointers():
     assert _raw("moe_route", S, mis, good, nul, nul, good, good, good, 1 << 30, nul) == api.MOE_EINVAL
     assert _raw("moe_route", S, good, good, mis, nul, good, good, good, 1 << 30, nul) == api.MOE_EINVAL
     assert _raw("moe_topk_from_logits", S, good, nul, good, nul) == api.MOE_EINVAL
-    args = [good] * 9
-    args[3] = nul
+    args = [good] * 10   # x, topk_idx, topk_w, send_buf, slot, ..., stats
+    args[4] = nul        # slot is required
     assert _raw("moe_dispatch", S, *args, good, 1 << 30, nul) == api.MOE_EINVAL
+    args = [good] * 10
+    args[2] = mis        # topk_w is optional under drop policy 0, but must be aligned
+    assert _raw("moe_dispatch", S, *args, good, 1 << 30, nul) == api.MOE_EINVAL
+    s1 = api.Shape(T=256, d=512, E=8, k=2, H=1024, D=2, capacity_factor=1.25,
+                   drop_policy=1).c()
+    args = [good] * 10
+    args[2] = nul        # drop policy 1 needs the gates
+    assert _raw("moe_dispatch", ctypes.byref(s1), *args, good, 1 << 30, nul) == api.MOE_EINVAL
     assert _raw("moe_expert_ffn", S, good, good, good, good, good, mis, good, good, 1 << 30,
                 nul) == api.MOE_EINVAL
     assert _raw("moe_combine", S, good, good, good, nul, nul) == api.MOE_EINVAL
@@ -114,7 +145,7 @@ def test_entry_points_reject_small_or_missing_workspace():
     assert _raw("moe_route", S, good, good, None, None, good, good, None, ws, None) == api.MOE_EWORKSPACE
     assert _raw("moe_route", S, good, good, None, None, good, good, P((1 << 20) + 16), ws,
                 None) == api.MOE_EWORKSPACE   # workspace must be 256-byte aligned
-    assert _raw("moe_dispatch", S, *([good] * 9), good, ws - 256, None) == api.MOE_EWORKSPACE
+    assert _raw("moe_dispatch", S, *([good] * 10), good, ws - 256, None) == api.MOE_EWORKSPACE
     assert _raw("moe_expert_ffn", S, *([good] * 7), good, 0, None) == api.MOE_EWORKSPACE
 
 

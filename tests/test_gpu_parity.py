@@ -13,6 +13,7 @@ Acceptance:
 """
 from __future__ import annotations
 
+import dataclasses
 import math
 
 import numpy as np
@@ -113,8 +114,8 @@ def test_topk_on_identical_logits_with_ties(E, k):
     np.testing.assert_allclose(w.cpu().numpy(), o_w, rtol=4e-6, atol=1e-7)
 
 
-def _run_dispatch(shape, x, topk_idx, buf):
-    api.moe_dispatch(shape, x, topk_idx, buf.send_buf, buf.slot, buf.expert_count,
+def _run_dispatch(shape, x, topk_idx, buf, topk_w=None):
+    api.moe_dispatch(shape, x, topk_idx, topk_w, buf.send_buf, buf.slot, buf.expert_count,
                      buf.expert_kept, buf.expert_offset, buf.rank_rows, buf.stats, buf.workspace)
     torch.cuda.synchronize()
 
@@ -224,6 +225,95 @@ def test_layer_fwd_end_to_end(case):
     assert torch.equal(buf.expert_out[:n][kr].view(torch.int16), eo1[:n][kr].view(torch.int16))
 
 
+# ---------------------------------------------------------------------------
+# Drop by gate value (drop policy 1) and the minimum capacity.  The oracle is
+# fed the GPU's own fp32 gates, so both sides rank on identical values.
+# ---------------------------------------------------------------------------
+
+def test_dispatch_by_gate_bit_exact(case):
+    cfg, inp, h, bias, ref, shape, buf = case
+    sh1 = dataclasses.replace(shape, drop_policy=1)
+    b1 = api.LayerBuffers.allocate(sh1, DEV)
+    api.moe_route(sh1, inp["x"], inp["w_gate"], inp["bias"], None, b1.topk_idx, b1.topk_w,
+                  b1.workspace)
+    _run_dispatch(sh1, inp["x"], b1.topk_idx, b1, b1.topk_w)
+    idx, w = b1.topk_idx.cpu().numpy(), b1.topk_w.cpu().numpy()
+    r = oracle.dispatch(h["x"], idx, T=cfg.T, d=cfg.d, E=cfg.E, D=cfg.D, my_rank=cfg.my_rank,
+                        cf=cfg.cf, drop_policy=1, topk_w=w)
+    _assert_dispatch_equal(b1, r, r["stats"]["send_rows"])
+    r0 = oracle.dispatch(None, idx, T=cfg.T, d=cfg.d, E=cfg.E, D=cfg.D, my_rank=cfg.my_rank,
+                         cf=cfg.cf, with_send_buf=False)
+    assert r0["stats"] == r["stats"]
+    if r["stats"]["dropped"]:
+        print(f"  dropped {r['stats']['dropped']}; slots differing from token order: "
+              f"{int((r0['slot'] != r['slot']).sum())}", flush=True)
+
+
+@pytest.mark.parametrize("T,E,k,cf,levels,seed", [
+    (3000, 16, 4, 0.5, 4, 1),      # few gate levels: many exact ties across tokens
+    (2500, 8, 2, 0.3, 1, 2),       # one level: probability order is token order
+    (1000, 64, 8, 0.25, 1000, 3),  # near-distinct gates, heavy drops
+    (300, 6, 3, 1.0, 3, 4),
+])
+def test_dispatch_by_gate_ties_bit_exact(T, E, k, cf, levels, seed):
+    rng = np.random.default_rng(seed)
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    w = (rng.integers(1, levels + 1, (T, k)) / (levels + 1)).astype(np.float32)
+    d = 64
+    x = torch.from_numpy(rng.integers(0, 65535, (T, d)).astype(np.uint16).view(np.int16))
+    x = x.view(torch.bfloat16).to(DEV)
+    shape = api.Shape(T=T, d=d, E=E, k=k, H=64, D=2, capacity_factor=cf, drop_policy=1)
+    buf = api.LayerBuffers.allocate(shape, DEV)
+    _run_dispatch(shape, x, _i32(idx), buf, _f32(w))
+    r = oracle.dispatch(bf16_bits(x), idx, T=T, d=d, E=E, D=2, cf=cf, drop_policy=1, topk_w=w)
+    assert r["stats"]["dropped"] > 0
+    _assert_dispatch_equal(buf, r, r["stats"]["send_rows"])
+    if levels == 1:
+        r0 = oracle.dispatch(None, idx, T=T, d=d, E=E, D=2, cf=cf, with_send_buf=False)
+        np.testing.assert_array_equal(buf.slot.cpu().numpy(), r0["slot"])
+
+
+@pytest.mark.parametrize("mc", [0, 100, 1000])
+def test_dispatch_minimum_capacity(mc):
+    cfg = SMALL["e64_skew"]
+    inp = make_inputs(cfg, DEV, experts=False)
+    for policy in (0, 1):
+        shape = dataclasses.replace(api.Shape.from_config(cfg), drop_policy=policy,
+                                    min_capacity=mc)
+        buf = api.LayerBuffers.allocate(shape, DEV)
+        api.moe_route(shape, inp["x"], inp["w_gate"], inp["bias"], None, buf.topk_idx,
+                      buf.topk_w, buf.workspace)
+        _run_dispatch(shape, inp["x"], buf.topk_idx, buf, buf.topk_w)
+        idx, w = buf.topk_idx.cpu().numpy(), buf.topk_w.cpu().numpy()
+        r = oracle.dispatch(bf16_bits(inp["x"]), idx, T=cfg.T, d=cfg.d, E=cfg.E, D=cfg.D,
+                            cf=cfg.cf, drop_policy=policy, topk_w=w, min_capacity=mc)
+        assert r["stats"]["capacity"] == max(oracle.capacity(cfg.T, cfg.k, cfg.E, cfg.cf), mc)
+        _assert_dispatch_equal(buf, r, r["stats"]["send_rows"])
+        if mc >= 1000:
+            assert r["stats"]["dropped"] == 0
+
+
+@pytest.mark.parametrize("name", ["tiny", "ragged_e6", "e64_skew", "one_token"])
+def test_layer_fwd_by_gate_end_to_end(name):
+    cfg = SMALL[name].with_(drop_policy=1)
+    inp = make_inputs(cfg, DEV)
+    h = _host(inp)
+    shape = api.Shape.from_config(cfg)
+    buf = api.LayerBuffers.allocate(shape, DEV)
+    api.moe_layer_fwd(shape, inp["x"], inp["w_gate"], inp["bias"], inp["w1"], inp["w3"],
+                      inp["w2"], buf)
+    torch.cuda.synchronize()
+    # judged on the GPU's own routing (checked against the oracle elsewhere)
+    idx, w = buf.topk_idx.cpu().numpy(), buf.topk_w.cpu().numpy()
+    r = oracle.dispatch(h["x"], idx, T=cfg.T, d=cfg.d, E=cfg.E, D=cfg.D, cf=cfg.cf,
+                        drop_policy=1, topk_w=w)
+    _assert_dispatch_equal(buf, r, r["stats"]["send_rows"])
+    eo = oracle.expert_ffn_all(r["send_buf"], r["expert_offset"], r["expert_kept"], h["w1"],
+                               h["w3"], h["w2"])
+    yref = oracle.combine(eo, r["slot"], w)
+    assert_bf16_close(t2f(buf.y), bits_to_f64(yref), "y")
+
+
 @pytest.mark.parametrize("k", [2, 8])
 def test_identity_experts_round_trip_on_gpu(k):
     """Dispatch then combine with identity experts and nothing dropped gives x
@@ -269,9 +359,11 @@ def _expert_weights(inp, e):
     return (bf16_bits(inp["w1"][e]), bf16_bits(inp["w3"][e]), bf16_bits(inp["w2"][e]))
 
 
-@pytest.mark.parametrize("name", ["mixtral", "dsv3_prefill", "dsv3_decode", "skewed"])
+@pytest.mark.parametrize("name", ["mixtral", "dsv3_prefill", "dsv3_decode", "skewed",
+                                  "skewed_by_gate"])
 def test_full_size_config(name):
-    cfg = CONFIGS[name]
+    cfg = (CONFIGS["skewed"].with_(drop_policy=1) if name == "skewed_by_gate"
+           else CONFIGS[name])
     print(f"\n[full {name}] T={cfg.T} d={cfg.d} E={cfg.E} k={cfg.k} H={cfg.H}", flush=True)
     inp = make_inputs(cfg, DEV)
     shape = api.Shape.from_config(cfg)
@@ -300,7 +392,7 @@ def test_full_size_config(name):
     assert not bad.any()
     # accounting and layout: bit-exact on the GPU's routing (send buffer sampled)
     r = oracle.dispatch(x, idx, T=cfg.T, d=cfg.d, E=cfg.E, D=cfg.D, my_rank=cfg.my_rank,
-                        cf=cfg.cf, with_send_buf=False)
+                        cf=cfg.cf, with_send_buf=False, drop_policy=cfg.drop_policy, topk_w=w)
     for key in ("expert_count", "expert_kept", "expert_offset", "rank_rows", "slot"):
         np.testing.assert_array_equal(getattr(buf, key).cpu().numpy(), r[key], err_msg=key)
     st = api.stats_dict(buf.stats)
