@@ -80,7 +80,15 @@ def _load():
     lib.oracle_capacity.argtypes = [i32, i32, i32, ctypes.c_double, i32]
     lib.oracle_capacity.restype = ctypes.c_int64
     lib.oracle_dispatch.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.c_double, i32, i32,
-                                    P, P, P, P, P, P, P, P, P, P]
+                                    i32, P, P, P, P, P, P, P, P, P, P, P]
+    lib.oracle_fp8_value.argtypes = [ctypes.c_uint8]
+    lib.oracle_fp8_value.restype = ctypes.c_double
+    lib.oracle_fp8_from_float.argtypes = [ctypes.c_float]
+    lib.oracle_fp8_from_float.restype = ctypes.c_uint8
+    lib.oracle_fp8_quantize_rows.argtypes = [i32, i32, P, P, P]
+    lib.oracle_fp8_quantize_rows.restype = None
+    lib.oracle_expert_ffn_fp8.argtypes = [i32, i32, i32, P, P, P, P, P, P]
+    lib.oracle_expert_ffn_fp8.restype = None
     lib.oracle_dispatch.restype = ctypes.c_int
     lib.oracle_expert_ffn.argtypes = [i32, i32, i32, P, P, P, P, P]
     lib.oracle_expert_ffn.restype = None
@@ -141,14 +149,42 @@ def capacity(T: int, k: int, E: int, cf: float, min_capacity: int = 0) -> int:
     return int(_load().oracle_capacity(T, k, E, float(cf), int(min_capacity)))
 
 
+def fp8_value(code: int) -> float:
+    """Value of an E4M3 code (OCP: bias 7, max 448, 0x7F/0xFF NaN)."""
+    return float(_load().oracle_fp8_value(int(code)))
+
+
+def fp8_from_float(v: float) -> int:
+    """E4M3 code nearest to the fp32 value v (ties to even, saturating, sign kept)."""
+    return int(_load().oracle_fp8_from_float(float(v)))
+
+
+def fp8_quantize_rows(x: np.ndarray):
+    """bf16 rows [n, d] -> (E4M3 codes uint8 [n, d], fp32 scales [n])."""
+    x = _c(x, np.uint16)
+    n, d = x.shape
+    codes = np.empty((n, d), np.uint8)
+    scales = np.empty((n,), np.float32)
+    _load().oracle_fp8_quantize_rows(n, d, _ptr(x), _ptr(codes), _ptr(scales))
+    return codes, scales
+
+
+def fp8_values(codes: np.ndarray) -> np.ndarray:
+    """Vectorised E4M3 decode through the oracle's table of all 256 codes."""
+    table = np.array([fp8_value(c) for c in range(256)], np.float64)
+    return table[np.asarray(codes, np.uint8)]
+
+
 def dispatch(x: np.ndarray | None, topk_idx: np.ndarray, *, T: int, d: int, E: int,
              D: int, my_rank: int = 0, cf: float = float("inf"),
              with_send_buf: bool = True, drop_policy: int = 0, topk_w=None,
-             min_capacity: int = 0) -> dict:
+             min_capacity: int = 0, fp8: bool = False) -> dict:
     """Histogram, capacity, positions, slots and the send buffer.
 
     drop_policy 0 keeps an overflowing expert's first C assignments in token
-    order; 1 keeps its C largest gate values (topk_w, fp32 [T, k])."""
+    order; 1 keeps its C largest gate values (topk_w, fp32 [T, k]).
+    fp8: the send buffer holds E4M3 rows (uint8) with per-row fp32 scales
+    (out["send_scale"]); otherwise bf16 rows."""
     topk_idx = _c(topk_idx, np.int32)
     k = topk_idx.shape[1]
     assert topk_idx.shape[0] == T
@@ -157,11 +193,13 @@ def dispatch(x: np.ndarray | None, topk_idx: np.ndarray, *, T: int, d: int, E: i
         assert topk_w.shape == topk_idx.shape
     C = capacity(T, k, E, cf, min_capacity)
     send_rows = T * k if C < 0 else E * C
-    send_buf = None
+    send_buf = send_scale = None
     if with_send_buf:
         x = _c(x, np.uint16)
         assert x.shape == (T, d)
-        send_buf = np.empty((send_rows, d), np.uint16)
+        send_buf = np.empty((send_rows, d), np.uint8 if fp8 else np.uint16)
+        if fp8:
+            send_scale = np.empty((send_rows,), np.float32)
     out = dict(
         slot=np.empty((T, k), np.int32),
         expert_count=np.empty((E,), np.int32),
@@ -171,13 +209,14 @@ def dispatch(x: np.ndarray | None, topk_idx: np.ndarray, *, T: int, d: int, E: i
     )
     stats = np.empty((len(STAT_NAMES),), np.int64)
     rc = _load().oracle_dispatch(
-        T, d, E, k, D, my_rank, float(cf), int(min_capacity), int(drop_policy),
+        T, d, E, k, D, my_rank, float(cf), int(min_capacity), int(drop_policy), int(fp8),
         _ptr(x) if with_send_buf else None, _ptr(topk_idx), _ptr(topk_w), _ptr(send_buf),
-        _ptr(out["slot"]), _ptr(out["expert_count"]), _ptr(out["expert_kept"]),
+        _ptr(send_scale), _ptr(out["slot"]), _ptr(out["expert_count"]), _ptr(out["expert_kept"]),
         _ptr(out["expert_offset"]), _ptr(out["rank_rows"]), _ptr(stats))
     if rc != 0:
         raise ValueError(f"oracle_dispatch rejected the shape (rc={rc})")
     out["send_buf"] = send_buf
+    out["send_scale"] = send_scale
     out["stats"] = {n: int(v) for n, v in zip(STAT_NAMES, stats)}
     return out
 
@@ -197,6 +236,25 @@ def expert_ffn(rows: np.ndarray, w1: np.ndarray, w3: np.ndarray, w2: np.ndarray)
     return out
 
 
+def expert_ffn_fp8(codes: np.ndarray, scales: np.ndarray, w1: np.ndarray, w3: np.ndarray,
+                   w2: np.ndarray) -> np.ndarray:
+    """The SwiGLU FFN on E4M3 rows: codes [n, d] uint8, scales [n] fp32 -> bf16 [n, d]."""
+    codes = _c(codes, np.uint8)
+    scales = _c(scales, np.float32)
+    w1 = _c(w1, np.uint16)
+    w3 = _c(w3, np.uint16)
+    w2 = _c(w2, np.uint16)
+    n, d = codes.shape
+    H = w1.shape[0]
+    assert scales.shape == (n,)
+    assert w1.shape == (H, d) and w3.shape == (H, d) and w2.shape == (d, H)
+    out = np.empty((n, d), np.uint16)
+    if n:
+        _load().oracle_expert_ffn_fp8(n, d, H, _ptr(codes), _ptr(scales), _ptr(w1), _ptr(w3),
+                                      _ptr(w2), _ptr(out))
+    return out
+
+
 def combine(expert_out: np.ndarray, slot: np.ndarray, topk_w: np.ndarray) -> np.ndarray:
     """y[t] = bf16(sum_s G[t,s] * expert_out[slot[t,s]]) over kept s; dropped -> 0."""
     expert_out = _c(expert_out, np.uint16)
@@ -212,26 +270,34 @@ def combine(expert_out: np.ndarray, slot: np.ndarray, topk_w: np.ndarray) -> np.
 
 
 def expert_ffn_all(send_buf: np.ndarray, expert_offset: np.ndarray, expert_kept: np.ndarray,
-                   w1: np.ndarray, w3: np.ndarray, w2: np.ndarray) -> np.ndarray:
-    """Every expert's FFN on its kept rows; rows that no assignment fills stay zero."""
-    out = np.zeros_like(send_buf)
+                   w1: np.ndarray, w3: np.ndarray, w2: np.ndarray,
+                   send_scale: np.ndarray | None = None) -> np.ndarray:
+    """Every expert's FFN on its kept rows; rows that no assignment fills stay
+    zero.  With send_scale the rows are E4M3 codes (FP8 dispatch)."""
+    out = np.zeros(send_buf.shape, np.uint16)
     E = expert_kept.shape[0]
     for e in range(E):
         lo, n = int(expert_offset[e]), int(expert_kept[e])
-        if n:
+        if not n:
+            continue
+        if send_scale is None:
             out[lo:lo + n] = expert_ffn(send_buf[lo:lo + n], w1[e], w3[e], w2[e])
+        else:
+            out[lo:lo + n] = expert_ffn_fp8(send_buf[lo:lo + n], send_scale[lo:lo + n],
+                                            w1[e], w3[e], w2[e])
     return out
 
 
 def layer_fwd(x, w_gate, w1, w3, w2, *, k: int, D: int, cf: float, my_rank: int = 0,
-              bias=None, drop_policy: int = 0, min_capacity: int = 0) -> dict:
+              bias=None, drop_policy: int = 0, min_capacity: int = 0, fp8: bool = False) -> dict:
     """The whole forward pass, stage by stage, returning every intermediate."""
     T, d = x.shape
     E = w_gate.shape[1]
     lg = logits(x, w_gate, bias)
     idx, w, gap = topk(lg, k)
     disp = dispatch(x, idx, T=T, d=d, E=E, D=D, my_rank=my_rank, cf=cf,
-                    drop_policy=drop_policy, topk_w=w, min_capacity=min_capacity)
-    eo = expert_ffn_all(disp["send_buf"], disp["expert_offset"], disp["expert_kept"], w1, w3, w2)
+                    drop_policy=drop_policy, topk_w=w, min_capacity=min_capacity, fp8=fp8)
+    eo = expert_ffn_all(disp["send_buf"], disp["expert_offset"], disp["expert_kept"], w1, w3, w2,
+                        send_scale=disp["send_scale"])
     y = combine(eo, disp["slot"], w)
     return dict(logits=lg, topk_idx=idx, topk_w=w, gap=gap, expert_out=eo, y=y, **disp)

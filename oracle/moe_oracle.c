@@ -43,6 +43,10 @@
  *        selected (gate) probability, the default strategy drops nothing.
  *   [MC] same page, the DeepSpeed paragraph: a minimum capacity per expert
  *        that holds regardless of the capacity factor.
+ *   [F8] same page, "What the bounds omit": FP8 dispatch sends the token
+ *        rows in FP8 instead of BF16, halving the dispatch row, while the
+ *        combine path may stay wider; quantization scale tensors travel
+ *        with it.
  *
  * Readings taken where the pages are silent (each also listed in the design
  * notes): eps = 0 at inference; an optional per-expert logit bias b is added
@@ -54,7 +58,13 @@
  * expert, by token index, are kept) under drop policy 0, or by gate
  * probability under drop policy 1 [DP]: the C assignments with the largest
  * gate value G stay, equal G going to the lower token index, and the kept
- * rows keep token order inside the expert's block; gates are not
+ * rows keep token order inside the expert's block; FP8 dispatch [F8] uses
+ * the OCP E4M3 format (bias 7, max 448, no infinities) with one fp32 scale
+ * per row, s = amax/448 computed in fp32 (s = 1 for an all-zero row), each
+ * element encoded as E4M3(x/s) with x/s computed in fp32, rounded to the
+ * nearest E4M3 value (ties to even), saturated at +-448, sign kept (so -0
+ * and tiny negatives give 0x80); the expert sees code value * s, and the
+ * combine stays bf16; gates are not
  * renormalised after a drop; a routing entry outside [0, E) or repeating
  * an expert already listed for its token is invalid (counted, dropped),
  * since KeepTopK yields k distinct experts; the expert is SwiGLU, W2 (SiLU(W1 x) * (W3 x))
@@ -202,6 +212,64 @@ static int by_gate_then_token(const void *pa, const void *pb)
     return (ta > tb) - (ta < tb);
 }
 
+/* ------------------------------------------------------------------ */
+/* FP8 E4M3 (OCP) for the dispatch payload.                  [F8]      */
+/* Code bits: s eeee mmm, exponent bias 7.  e = 0: subnormal m * 2^-9; */
+/* e = 15, m = 7: NaN (never produced here); otherwise                 */
+/* 2^(e-7) * (1 + m/8).  Largest finite value 448 (0x7E).              */
+/* ------------------------------------------------------------------ */
+double oracle_fp8_value(uint8_t code)
+{
+    int sgn = code >> 7, e = (code >> 3) & 15, m = code & 7;
+    double v;
+    if (e == 15 && m == 7)
+        return NAN;
+    if (e == 0)
+        v = ldexp((double)m, -9);
+    else
+        v = ldexp(1.0 + m / 8.0, e - 7);
+    return sgn ? -v : v;
+}
+
+/* Nearest E4M3 value to v (|v| saturated at 448), ties to the code with an
+ * even mantissa, found by scanning every finite magnitude code. */
+uint8_t oracle_fp8_from_float(float v)
+{
+    double a = fabs((double)v);
+    if (a > 448.0)
+        a = 448.0;
+    int best = 0;
+    double best_d = INFINITY;
+    for (int c = 0; c <= 0x7E; ++c) {
+        double dist = fabs(oracle_fp8_value((uint8_t)c) - a);
+        if (dist < best_d || (dist == best_d && (c & 1) == 0 && (best & 1) == 1)) {
+            best = c;
+            best_d = dist;
+        }
+    }
+    return (uint8_t)(best | (signbit(v) ? 0x80 : 0));
+}
+
+/* Per-row quantization of n bf16 rows [n, d]: scale s = amax / 448 (fp32),
+ * code = E4M3(x / s) with the quotient in fp32.                      */
+void oracle_fp8_quantize_rows(int n, int d, const uint16_t *x, uint8_t *codes, float *scales)
+{
+    for (int r = 0; r < n; ++r) {
+        float amax = 0.0f;
+        for (int i = 0; i < d; ++i) {
+            float a = fabsf((float)bf16_value(x[(size_t)r * d + i]));
+            if (a > amax)
+                amax = a;
+        }
+        float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
+        scales[r] = sc;
+        for (int i = 0; i < d; ++i) {
+            float q = (float)bf16_value(x[(size_t)r * d + i]) / sc;
+            codes[(size_t)r * d + i] = oracle_fp8_from_float(q);
+        }
+    }
+}
+
 /* Indices into the stats vector filled by oracle_dispatch. */
 enum {
     ST_ASSIGNMENTS = 0, /* T*k                                          [N]  */
@@ -241,9 +309,9 @@ enum {
 /* send_buf [send_rows, d] may be NULL (accounting only).              */
 /* ------------------------------------------------------------------ */
 int oracle_dispatch(int T, int d, int E, int k, int D, int my_rank, double cf,
-                    int min_capacity, int drop_policy, const uint16_t *x,
-                    const int32_t *topk_idx, const float *topk_w, uint16_t *send_buf,
-                    int32_t *slot, int32_t *expert_count, int32_t *expert_kept,
+                    int min_capacity, int drop_policy, int fp8, const uint16_t *x,
+                    const int32_t *topk_idx, const float *topk_w, void *send_buf,
+                    float *send_scale, int32_t *slot, int32_t *expert_count, int32_t *expert_kept,
                     int64_t *expert_offset, int64_t *rank_rows, int64_t *stats)
 {
     if (D <= 0 || E % D != 0 || my_rank < 0 || my_rank >= D)
@@ -341,10 +409,24 @@ int oracle_dispatch(int T, int d, int E, int k, int D, int my_rank, double cf,
         free(list);
         free(start);
     }
-    /* slots and the send buffer */
+    /* slots and the send buffer: bf16 rows, or [F8] E4M3 rows + scales
+     * (pad rows: zero codes, scale 0) */
+    const size_t elem = fp8 ? 1 : 2;
+    uint8_t *qrow = NULL;
+    float qscale = 0.0f;
+    if (fp8 && send_buf && !(qrow = malloc((size_t)d))) {
+        free(running);
+        free(position);
+        return -2;
+    }
     if (send_buf)
-        memset(send_buf, 0, (size_t)send_rows * d * sizeof *send_buf);
+        memset(send_buf, 0, (size_t)send_rows * d * elem);
+    if (fp8 && send_buf)
+        for (int64_t r = 0; r < send_rows; ++r)
+            send_scale[r] = 0.0f;
     for (int t = 0; t < T; ++t) {
+        if (qrow)
+            oracle_fp8_quantize_rows(1, d, x + (size_t)t * d, qrow, &qscale);
         for (int s = 0; s < k; ++s) {
             int32_t e = topk_idx[(size_t)t * k + s];
             int32_t p = position[(size_t)t * k + s];
@@ -352,10 +434,17 @@ int oracle_dispatch(int T, int d, int E, int k, int D, int my_rank, double cf,
             if (p >= 0 && (C < 0 || p < C))
                 sl = (int32_t)(expert_offset[e] + p);
             slot[(size_t)t * k + s] = sl;
-            if (sl >= 0 && send_buf)
-                memcpy(send_buf + (size_t)sl * d, x + (size_t)t * d, (size_t)d * sizeof *x);
+            if (sl < 0 || !send_buf)
+                continue;
+            if (fp8) {
+                memcpy((uint8_t *)send_buf + (size_t)sl * d, qrow, (size_t)d);
+                send_scale[sl] = qscale;
+            } else {
+                memcpy((uint16_t *)send_buf + (size_t)sl * d, x + (size_t)t * d, (size_t)d * 2);
+            }
         }
     }
+    free(qrow);
     /* per-rank rows (kept token vectors per destination) */
     int epr = E / D;
     int64_t remote_rows = 0;
@@ -373,9 +462,11 @@ int oracle_dispatch(int T, int d, int E, int k, int D, int my_rank, double cf,
     stats[ST_PADDED] = (C < 0) ? 0 : (int64_t)E * C - kept_total;
     stats[ST_CAPACITY] = C;
     stats[ST_SEND_ROWS] = send_rows;
-    stats[ST_DISPATCH_BYTES] = kept_total * d * 2;
-    stats[ST_WIRE_BYTES] = (C < 0) ? kept_total * d * 2 : send_rows * d * 2;
-    stats[ST_REMOTE_BYTES] = remote_rows * d * 2;
+    /* a dispatched row: d bf16, or [F8] d E4M3 codes plus its fp32 scale */
+    const int64_t row_bytes = fp8 ? (int64_t)d + 4 : (int64_t)d * 2;
+    stats[ST_DISPATCH_BYTES] = kept_total * row_bytes;
+    stats[ST_WIRE_BYTES] = (C < 0) ? kept_total * row_bytes : send_rows * row_bytes;
+    stats[ST_REMOTE_BYTES] = remote_rows * row_bytes;
     stats[ST_COMBINE_BYTES] = kept_total * d * 2;
     stats[ST_MAX_COUNT] = max_count;
     stats[ST_INVALID] = invalid;
@@ -390,8 +481,11 @@ int oracle_dispatch(int T, int d, int E, int k, int D, int my_rank, double cf,
 /* g = W1 x, u = W3 x (double), h = bf16(SiLU(g) * u) with             */
 /* SiLU(z) = z / (1 + exp(-z)), out = bf16(W2 h).                      */
 /* ------------------------------------------------------------------ */
-void oracle_expert_ffn(int n, int d, int H, const uint16_t *rows, const uint16_t *w1,
-                       const uint16_t *w3, const uint16_t *w2, uint16_t *out)
+/* rows given either as bf16 (codes == NULL) or [F8] as E4M3 codes with a
+ * per-row scale: the row value is code value * scale (exact in double). */
+static void expert_ffn_rows(int n, int d, int H, const uint16_t *rows, const uint8_t *codes,
+                            const float *scales, const uint16_t *w1, const uint16_t *w3,
+                            const uint16_t *w2, uint16_t *out)
 {
 #pragma omp parallel
     {
@@ -400,7 +494,8 @@ void oracle_expert_ffn(int n, int d, int H, const uint16_t *rows, const uint16_t
 #pragma omp for schedule(dynamic, 1)
         for (int r = 0; r < n; ++r) {
             for (int i = 0; i < d; ++i)
-                xr[i] = bf16_value(rows[(size_t)r * d + i]);
+                xr[i] = codes ? oracle_fp8_value(codes[(size_t)r * d + i]) * (double)scales[r]
+                              : bf16_value(rows[(size_t)r * d + i]);
             for (int j = 0; j < H; ++j) {
                 double g = 0.0, u = 0.0;
                 for (int i = 0; i < d; ++i) {
@@ -420,6 +515,20 @@ void oracle_expert_ffn(int n, int d, int H, const uint16_t *rows, const uint16_t
         free(xr);
         free(h);
     }
+}
+
+void oracle_expert_ffn(int n, int d, int H, const uint16_t *rows, const uint16_t *w1,
+                       const uint16_t *w3, const uint16_t *w2, uint16_t *out)
+{
+    expert_ffn_rows(n, d, H, rows, NULL, NULL, w1, w3, w2, out);
+}
+
+/* The same FFN on FP8 rows (codes [n, d], scales [n]).          [F8]  */
+void oracle_expert_ffn_fp8(int n, int d, int H, const uint8_t *codes, const float *scales,
+                           const uint16_t *w1, const uint16_t *w3, const uint16_t *w2,
+                           uint16_t *out)
+{
+    expert_ffn_rows(n, d, H, NULL, codes, scales, w1, w3, w2, out);
 }
 
 /* ------------------------------------------------------------------ */

@@ -533,3 +533,134 @@ def test_layer_fwd_tiny_end_to_end_invariants():
     # a token all of whose assignments were dropped has y = 0
     dropped_all = np.all(out["slot"] < 0, axis=1)
     assert np.all(y[dropped_all] == 0)
+
+
+# ---------------------------------------------------------------------------
+# FP8 dispatch payload ("MoE Expert Parallelism Sizing: Traffic, Capacity,
+# Fabric", "What the bounds omit": FP8 dispatch halves the dispatch row, the
+# combine may stay wider, scale tensors travel with it).  Format: OCP E4M3.
+# ---------------------------------------------------------------------------
+
+def _torch_e4m3_decode():
+    return torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+
+
+def test_fp8_special_values():
+    assert oracle.fp8_value(0x7E) == 448.0          # largest finite
+    assert oracle.fp8_value(0x08) == 2.0 ** -6      # smallest normal
+    assert oracle.fp8_value(0x01) == 2.0 ** -9      # smallest subnormal
+    assert oracle.fp8_value(0x07) == 7 * 2.0 ** -9  # largest subnormal
+    assert oracle.fp8_value(0x38) == 1.0 and oracle.fp8_value(0x3C) == 1.5
+    assert oracle.fp8_value(0xB8) == -1.0
+    assert math.isnan(oracle.fp8_value(0x7F)) and math.isnan(oracle.fp8_value(0xFF))
+    assert math.copysign(1.0, oracle.fp8_value(0x80)) == -1.0
+
+
+def test_fp8_decode_matches_torch_for_every_code():
+    ours = np.array([oracle.fp8_value(c) for c in range(256)])
+    ref = _torch_e4m3_decode()
+    np.testing.assert_array_equal(np.isnan(ours), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    np.testing.assert_array_equal(ours[ok], ref[ok])
+    np.testing.assert_array_equal(np.signbit(ours[ok]), np.signbit(ref[ok]))
+
+
+def test_fp8_encode_round_trips_every_finite_code():
+    for c in range(256):
+        if c & 0x7F == 0x7F:
+            continue
+        assert oracle.fp8_from_float(oracle.fp8_value(c)) == c, hex(c)
+
+
+def test_fp8_encode_matches_torch_within_range():
+    """Nearest value, ties to even: agrees with torch's fp32 -> float8_e4m3fn
+    on random values and on every midpoint between neighbouring codes."""
+    rng = np.random.default_rng(5)
+    vals = [rng.uniform(-448, 448, 3000), rng.standard_normal(3000) * 0.01,
+            rng.standard_normal(3000) * 1e-3]
+    pos = np.array([oracle.fp8_value(c) for c in range(0x7F)])
+    vals.append((pos[:-1] + pos[1:]) / 2)          # ties
+    vals.append(-(pos[:-1] + pos[1:]) / 2)
+    v = np.concatenate(vals).astype(np.float32)
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    ours = np.array([oracle.fp8_from_float(x) for x in v], np.uint8)
+    np.testing.assert_array_equal(ours, ref)
+
+
+def test_fp8_encode_saturates_and_keeps_sign():
+    assert oracle.fp8_from_float(448.0) == 0x7E
+    assert oracle.fp8_from_float(460.0) == 0x7E     # beyond 448: saturate, not NaN
+    assert oracle.fp8_from_float(3e38) == 0x7E
+    assert oracle.fp8_from_float(-1e10) == 0xFE
+    assert oracle.fp8_from_float(2.0 ** -10) == 0x00   # tie between 0 and 2^-9: even
+    assert oracle.fp8_from_float(1.5 * 2.0 ** -10) == 0x01
+    assert oracle.fp8_from_float(-1e-30) == 0x80
+    assert oracle.fp8_from_float(-0.0) == 0x80
+
+
+def test_fp8_quantize_rows_scale_and_error_bound():
+    rng = np.random.default_rng(9)
+    n, d = 40, 96
+    x = bf16_bits((torch.randn(n, d) * torch.logspace(-3, 2, n)[:, None]).to(torch.bfloat16))
+    x[3] = 0                                    # all-zero row
+    x[4] = 0
+    x[4, 17] = bf16_bits(torch.tensor([-2.5], dtype=torch.bfloat16))[0]  # a single nonzero
+    codes, scales = oracle.fp8_quantize_rows(x)
+    xf = x.astype(np.uint32).__lshift__(16).view(np.float32)
+    for r in range(n):
+        amax = np.abs(xf[r]).max()
+        if amax == 0:
+            assert scales[r] == 1.0 and np.all(codes[r] == 0)
+            continue
+        assert scales[r] == np.float32(amax) / np.float32(448.0)
+        i = int(np.argmax(np.abs(xf[r])))
+        assert codes[r, i] == (0xFE if xf[r, i] < 0 else 0x7E)
+        deq = oracle.fp8_values(codes[r]) * np.float64(scales[r])
+        err = np.abs(deq - xf[r].astype(np.float64))
+        assert np.all(err <= 2.0 ** -4 * np.abs(xf[r]) + 2.0 ** -10 * scales[r] * 1.0001)
+        assert np.all(np.signbit(deq[xf[r] != 0]) == np.signbit(xf[r][xf[r] != 0]))
+
+
+def test_fp8_expert_ffn_reduces_to_bf16_on_exact_rows():
+    """Codes times a power-of-two scale are exact bf16 values: the FP8 FFN must
+    equal the (separately pinned) bf16 FFN on those values, bit for bit."""
+    rng = np.random.default_rng(11)
+    n, d, H = 5, 64, 48
+    codes = rng.integers(0, 256, (n, d)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x3A             # no NaN codes
+    scales = (2.0 ** rng.integers(-4, 3, n)).astype(np.float32)
+    vals = oracle.fp8_values(codes) * scales[:, None]
+    rows = bf16_bits(torch.from_numpy(vals.astype(np.float32)).to(torch.bfloat16))
+    assert np.array_equal(rows.astype(np.uint32).__lshift__(16).view(np.float32), vals.astype(np.float32))
+    w = [bf16_bits((torch.randn(*s) * 0.05).to(torch.bfloat16)) for s in ((H, d), (H, d), (d, H))]
+    np.testing.assert_array_equal(oracle.expert_ffn_fp8(codes, scales, *w),
+                                  oracle.expert_ffn(rows, *w))
+
+
+def test_fp8_dispatch_hand_example():
+    x = bf16_bits(torch.randn(6, 16).to(torch.bfloat16))
+    r = oracle.dispatch(x, HAND_IDX, T=6, d=16, E=3, D=3, my_rank=0, cf=0.5, fp8=True)
+    rb = oracle.dispatch(x, HAND_IDX, T=6, d=16, E=3, D=3, my_rank=0, cf=0.5)
+    np.testing.assert_array_equal(r["slot"], rb["slot"])
+    q, sc = oracle.fp8_quantize_rows(x)
+    rows = [0, 1, 0, 1, 2, 3]                       # tokens of send rows 0..5
+    np.testing.assert_array_equal(r["send_buf"], q[rows])
+    np.testing.assert_array_equal(r["send_scale"], sc[rows])
+    st, sb = r["stats"], rb["stats"]
+    assert st["dispatch_bytes"] == 6 * (16 + 4) and sb["dispatch_bytes"] == 6 * 16 * 2
+    assert st["combine_bytes"] == sb["combine_bytes"] == 6 * 16 * 2   # combine stays bf16
+    assert st["dispatch_remote_bytes"] == 4 * (16 + 4)
+
+
+def test_fp8_decode_example_page_bytes(sizing):
+    """The page's decode example with FP8 dispatch: 1,152 vectors at one byte
+    per element, about 8.3 MB (the per-row fp32 scales add 4.6 KB); the
+    combine of the same example stays at two bytes, about 16.5 MB."""
+    p = sizing["decode_dispatch_fp8"]
+    T, k, d = p["shape"]["T"], p["shape"]["k"], p["shape"]["d"]
+    idx = _balanced_routing(T, k, 288)
+    st = oracle.dispatch(None, idx, T=T, d=d, E=288, D=1, cf=INF, with_send_buf=False,
+                         fp8=True)["stats"]
+    assert st["kept"] == p["vectors"]
+    assert abs(st["dispatch_bytes"] / 1e6 - p["printed_MB"]) <= p["printed_precision_MB"]
+    assert abs(st["combine_bytes"] / 1e6 - sizing["decode_combine"]["printed_MB"]) <= 0.05
