@@ -41,10 +41,11 @@ def stage_traffic(cfg, st, touched):
     """Algorithmic HBM bytes and flops of each stage for one call."""
     T, d, E, k, H = cfg.T, cfg.d, cfg.E, cfg.k, cfg.H
     kept, send_rows = st["kept"], st["send_rows"]
+    row = d + 4 if cfg.dispatch_fp8 else d * 2   # a dispatched row: E4M3 + scale, or bf16
     return {
         "route": dict(bytes=T * d * 2 + d * E * 2 + T * k * 8, flops=2 * T * d * E),
-        "dispatch": dict(bytes=T * d * 2 + send_rows * d * 2 + T * k * 8, flops=0),
-        "gate_up": dict(bytes=touched * 2 * H * d * 2 + kept * d * 2 + kept * H * 2,
+        "dispatch": dict(bytes=T * d * 2 + send_rows * row + T * k * 8, flops=0),
+        "gate_up": dict(bytes=touched * 2 * H * d * 2 + kept * row + kept * H * 2,
                         flops=4 * kept * d * H),
         "down": dict(bytes=touched * d * H * 2 + kept * H * 2 + kept * d * 2,
                      flops=2 * kept * d * H),
@@ -94,17 +95,17 @@ def cpu_baseline(cfg, inp, budget_s):
         lg = oracle.logits(xb, wg, bias)
         idx, w, _ = oracle.topk(lg, cfg.k)
         r = oracle.dispatch(xb, idx, T=tb, d=cfg.d, E=cfg.E, D=cfg.D, cf=cfg.cf,
-                            drop_policy=cfg.drop_policy, topk_w=w, min_capacity=cfg.min_capacity)
+                            drop_policy=cfg.drop_policy, topk_w=w, min_capacity=cfg.min_capacity,
+                            fp8=bool(cfg.dispatch_fp8))
         spent += time.perf_counter() - t0
         need = [e for e in range(cfg.E) if r["expert_kept"][e] and e not in experts]
         for e in need:  # weight copies to the host are not oracle work: not timed
             experts[e] = tuple(bf16_bits(inp[n][e]) for n in ("w1", "w3", "w2"))
         t0 = time.perf_counter()
-        eo = np.zeros_like(r["send_buf"])
-        for e in range(cfg.E):
-            lo, n = int(r["expert_offset"][e]), int(r["expert_kept"][e])
-            if n:
-                eo[lo:lo + n] = oracle.expert_ffn(r["send_buf"][lo:lo + n], *experts[e])
+        # the experts' weights by index (only experts with kept rows are read)
+        w1, w3, w2 = ({e: v[i] for e, v in experts.items()} for i in range(3))
+        eo = oracle.expert_ffn_all(r["send_buf"], r["expert_offset"], r["expert_kept"],
+                                   w1, w3, w2, send_scale=r["send_scale"])
         oracle.combine(eo, r["slot"], w)
         spent += time.perf_counter() - t0
         done += tb
@@ -141,12 +142,13 @@ def rank_local_gemm(cfg, inp, dev, steps, warmup):
     stream = torch.cuda.current_stream()
     api.moe_route(shape, xin["x"], xin["w_gate"], xin["bias"], None, buf.topk_idx, buf.topk_w,
                   buf.workspace, stream)
-    api.moe_dispatch(shape, xin["x"], buf.topk_idx, buf.topk_w, buf.send_buf, buf.slot,
-                     buf.expert_count,
+    api.moe_dispatch(shape, xin["x"], buf.topk_idx, buf.topk_w, buf.send_buf, buf.send_scale,
+                     buf.slot, buf.expert_count,
                      buf.expert_kept, buf.expert_offset, buf.rank_rows, buf.stats,
                      buf.workspace, stream)
     el = cfg.E // cfg.D
-    loc = api.Shape(big.T, cfg.d, el, cfg.k, cfg.H, 1, 0, big.cf)
+    loc = api.Shape(big.T, cfg.d, el, cfg.k, cfg.H, 1, 0, big.cf,
+                    dispatch_fp8=big.dispatch_fp8)
     rows = int(buf.expert_offset[el].item())
     h = torch.empty(buf.send_buf.shape[0], cfg.H, dtype=torch.bfloat16, device=dev)
     w1, w3, w2 = inp["w1"][:el], inp["w3"][:el], inp["w2"][:el]
@@ -154,8 +156,8 @@ def rank_local_gemm(cfg, inp, dev, steps, warmup):
     def run(ev=None):
         if ev:
             ev[0].record(stream)
-        api.moe_expert_gate_up(loc, buf.send_buf, buf.expert_offset, buf.expert_kept, w1, w3, h,
-                               stream)
+        api.moe_expert_gate_up(loc, buf.send_buf, buf.send_scale, buf.expert_offset,
+                               buf.expert_kept, w1, w3, h, stream)
         if ev:
             ev[1].record(stream)
         api.moe_expert_down(loc, h, buf.expert_offset, buf.expert_kept, w2, buf.expert_out,
@@ -200,6 +202,8 @@ def main():
                     help="capacity overflow: 0 token order, 1 by gate value (default: the workload's)")
     ap.add_argument("--min-capacity", type=int, default=None,
                     help="lower bound on the expert capacity (default: the workload's)")
+    ap.add_argument("--dispatch-fp8", action="store_true",
+                    help="dispatch payload as E4M3 rows with fp32 row scales (combine stays bf16)")
     ap.add_argument("--no-rank-local", action="store_true",
                     help="skip the expert-parallel rank-local GEMM measurement")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -220,6 +224,8 @@ def main():
         cfg = cfg.with_(drop_policy=args.drop_policy)
     if args.min_capacity is not None:
         cfg = cfg.with_(min_capacity=args.min_capacity)
+    if args.dispatch_fp8:
+        cfg = cfg.with_(dispatch_fp8=1)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     log(f"bench: {cfg.name} T={cfg.T} d={cfg.d} E={cfg.E} k={cfg.k} H={cfg.H} cf={cfg.cf}")
@@ -236,12 +242,12 @@ def main():
         api.moe_route(shape, inp["x"], inp["w_gate"], inp["bias"], None, buf.topk_idx,
                       buf.topk_w, buf.workspace, stream)
         rec(1)
-        api.moe_dispatch(shape, inp["x"], buf.topk_idx, buf.topk_w, buf.send_buf, buf.slot,
-                         buf.expert_count, buf.expert_kept, buf.expert_offset, buf.rank_rows,
+        api.moe_dispatch(shape, inp["x"], buf.topk_idx, buf.topk_w, buf.send_buf,
+                         buf.send_scale, buf.slot, buf.expert_count, buf.expert_kept, buf.expert_offset, buf.rank_rows,
                          buf.stats, buf.workspace, stream)
         rec(2)
-        api.moe_expert_gate_up(shape, buf.send_buf, buf.expert_offset, buf.expert_kept,
-                               inp["w1"], inp["w3"], h, stream)
+        api.moe_expert_gate_up(shape, buf.send_buf, buf.send_scale, buf.expert_offset,
+                               buf.expert_kept, inp["w1"], inp["w3"], h, stream)
         rec(3)
         api.moe_expert_down(shape, h, buf.expert_offset, buf.expert_kept, inp["w2"],
                             buf.expert_out, stream)

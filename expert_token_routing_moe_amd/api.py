@@ -41,7 +41,8 @@ class moe_shape(ctypes.Structure):
         ("T", ctypes.c_int32), ("d", ctypes.c_int32), ("E", ctypes.c_int32),
         ("k", ctypes.c_int32), ("H", ctypes.c_int32), ("D", ctypes.c_int32),
         ("my_rank", ctypes.c_int32), ("drop_policy", ctypes.c_int32),
-        ("min_capacity", ctypes.c_int32), ("capacity_factor", ctypes.c_double),
+        ("min_capacity", ctypes.c_int32), ("dispatch_fp8", ctypes.c_int32),
+        ("capacity_factor", ctypes.c_double),
     ]
 
 
@@ -63,12 +64,13 @@ def lib():
                       ctypes.POINTER(ctypes.c_size_t)],
         "moe_route": [S, P, P, P, P, P, P, P, SZ, P],
         "moe_topk_from_logits": [S, P, P, P, P],
-        "moe_dispatch": [S, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
-        "moe_expert_ffn": [S, P, P, P, P, P, P, P, P, SZ, P],
-        "moe_expert_gate_up": [S, P, P, P, P, P, P, P],
+        "moe_dispatch": [S, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
+        "moe_expert_ffn": [S, P, P, P, P, P, P, P, P, P, SZ, P],
+        "moe_expert_gate_up": [S, P, P, P, P, P, P, P, P],
         "moe_expert_down": [S, P, P, P, P, P, P],
         "moe_combine": [S, P, P, P, P, P],
-        "moe_layer_fwd": [S] + [P] * 19 + [SZ, P],
+        "moe_layer_fwd": [S] + [P] * 20 + [SZ, P],
+        "moe_fp8_rows_to_bf16": [P, P, ctypes.c_int64, ctypes.c_int32, P, P],
     }
     for name, argtypes in sig.items():
         f = getattr(L, name)
@@ -99,15 +101,17 @@ class Shape:
     capacity_factor: float = math.inf
     drop_policy: int = 0
     min_capacity: int = 0
+    dispatch_fp8: int = 0
 
     def c(self) -> moe_shape:
         return moe_shape(self.T, self.d, self.E, self.k, self.H, self.D, self.my_rank,
-                         self.drop_policy, self.min_capacity, float(self.capacity_factor))
+                         self.drop_policy, self.min_capacity, self.dispatch_fp8,
+                         float(self.capacity_factor))
 
     @classmethod
     def from_config(cls, cfg) -> "Shape":
         return cls(cfg.T, cfg.d, cfg.E, cfg.k, cfg.H, cfg.D, cfg.my_rank, cfg.cf,
-                   cfg.drop_policy, cfg.min_capacity)
+                   cfg.drop_policy, cfg.min_capacity, cfg.dispatch_fp8)
 
 
 def _p(t: torch.Tensor | None, dtype=None):
@@ -129,6 +133,11 @@ def _stream(stream) -> ctypes.c_void_p:
 
 
 BF16, I32, F32 = torch.bfloat16, torch.int32, torch.float32
+
+
+def _send(shape, t):
+    """The send buffer: bf16 rows, or E4M3 codes (uint8) under FP8 dispatch."""
+    return _p(t, torch.uint8 if shape.dispatch_fp8 else BF16)
 
 
 def moe_query(shape: Shape):
@@ -155,31 +164,35 @@ def moe_topk_from_logits(shape, logits, topk_idx, topk_w, stream=None):
         ctypes.byref(s), _p(logits, F32), _p(topk_idx, I32), _p(topk_w, F32), _stream(stream)))
 
 
-def moe_dispatch(shape, x, topk_idx, topk_w, send_buf, slot, expert_count, expert_kept,
-                 expert_offset, rank_rows, stats, workspace, stream=None):
-    """topk_w is read only by drop policy 1 in capacity mode; may be None otherwise."""
+def moe_dispatch(shape, x, topk_idx, topk_w, send_buf, send_scale, slot, expert_count,
+                 expert_kept, expert_offset, rank_rows, stats, workspace, stream=None):
+    """topk_w is read only by drop policy 1 in capacity mode; send_scale only
+    under FP8 dispatch; either may be None otherwise."""
     s = shape.c()
     _check("moe_dispatch", lib().moe_dispatch(
-        ctypes.byref(s), _p(x, BF16), _p(topk_idx, I32), _p(topk_w, F32), _p(send_buf, BF16),
-        _p(slot, I32),
+        ctypes.byref(s), _p(x, BF16), _p(topk_idx, I32), _p(topk_w, F32), _send(shape, send_buf),
+        _p(send_scale, F32), _p(slot, I32),
         _p(expert_count, I32), _p(expert_kept, I32), _p(expert_offset, I32),
         _p(rank_rows, I32), _p(stats, torch.int64), _p(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
-def moe_expert_ffn(shape, send_buf, expert_offset, expert_kept, w1, w3, w2, expert_out,
-                   workspace, stream=None):
+def moe_expert_ffn(shape, send_buf, send_scale, expert_offset, expert_kept, w1, w3, w2,
+                   expert_out, workspace, stream=None):
     s = shape.c()
     _check("moe_expert_ffn", lib().moe_expert_ffn(
-        ctypes.byref(s), _p(send_buf, BF16), _p(expert_offset, I32), _p(expert_kept, I32),
+        ctypes.byref(s), _send(shape, send_buf), _p(send_scale, F32), _p(expert_offset, I32),
+        _p(expert_kept, I32),
         _p(w1, BF16), _p(w3, BF16), _p(w2, BF16), _p(expert_out, BF16), _p(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
-def moe_expert_gate_up(shape, send_buf, expert_offset, expert_kept, w1, w3, h, stream=None):
+def moe_expert_gate_up(shape, send_buf, send_scale, expert_offset, expert_kept, w1, w3, h,
+                       stream=None):
     s = shape.c()
     _check("moe_expert_gate_up", lib().moe_expert_gate_up(
-        ctypes.byref(s), _p(send_buf, BF16), _p(expert_offset, I32), _p(expert_kept, I32),
+        ctypes.byref(s), _send(shape, send_buf), _p(send_scale, F32), _p(expert_offset, I32),
+        _p(expert_kept, I32),
         _p(w1, BF16), _p(w3, BF16), _p(h, BF16), _stream(stream)))
 
 
@@ -202,10 +215,18 @@ def moe_layer_fwd(shape, x, w_gate, logit_bias, w1, w3, w2, buf: "LayerBuffers",
     _check("moe_layer_fwd", lib().moe_layer_fwd(
         ctypes.byref(s), _p(x, BF16), _p(w_gate, BF16), _p(logit_bias, F32), _p(w1, BF16),
         _p(w3, BF16), _p(w2, BF16), _p(buf.y, BF16), _p(buf.logits, F32),
-        _p(buf.topk_idx, I32), _p(buf.topk_w, F32), _p(buf.send_buf, BF16), _p(buf.slot, I32),
+        _p(buf.topk_idx, I32), _p(buf.topk_w, F32), _send(shape, buf.send_buf),
+        _p(buf.send_scale, F32), _p(buf.slot, I32),
         _p(buf.expert_count, I32), _p(buf.expert_kept, I32), _p(buf.expert_offset, I32),
         _p(buf.rank_rows, I32), _p(buf.stats, torch.int64), _p(buf.expert_out, BF16),
         _p(buf.workspace), buf.workspace.numel(), _stream(stream)))
+
+
+def moe_fp8_rows_to_bf16(codes, scales, out, stream=None):
+    """out = bf16(E4M3 value of codes * row scale), the expert GEMM's decode."""
+    rows, d = codes.shape
+    _check("moe_fp8_rows_to_bf16", lib().moe_fp8_rows_to_bf16(
+        _p(codes, torch.uint8), _p(scales, F32), rows, d, _p(out, BF16), _stream(stream)))
 
 
 @dataclass
@@ -217,6 +238,7 @@ class LayerBuffers:
     topk_idx: torch.Tensor
     topk_w: torch.Tensor
     send_buf: torch.Tensor
+    send_scale: torch.Tensor | None
     slot: torch.Tensor
     expert_count: torch.Tensor
     expert_kept: torch.Tensor
@@ -236,7 +258,9 @@ class LayerBuffers:
             y=z(T, d, dt=BF16),
             logits=z(T, E, dt=F32) if keep_logits else None,
             topk_idx=z(T, k, dt=I32), topk_w=z(T, k, dt=F32),
-            send_buf=z(send_rows, d, dt=BF16), slot=z(T, k, dt=I32),
+            send_buf=z(send_rows, d, dt=torch.uint8 if shape.dispatch_fp8 else BF16),
+            send_scale=z(send_rows, dt=F32) if shape.dispatch_fp8 else None,
+            slot=z(T, k, dt=I32),
             expert_count=z(E, dt=I32), expert_kept=z(E, dt=I32),
             expert_offset=z(E + 1, dt=I32), rank_rows=z(D, dt=I32),
             stats=z(len(STAT_NAMES), dt=torch.int64),

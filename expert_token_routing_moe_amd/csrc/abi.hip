@@ -53,6 +53,8 @@ static int make_dims(const moe_shape *s, Dims *dm)
         return MOE_EINVAL;
     if (s->min_capacity < 0)
         return MOE_EINVAL;
+    if (s->dispatch_fp8 != 0 && s->dispatch_fp8 != 1)
+        return MOE_EINVAL;
     if (s->d % 64 != 0 || s->H % 64 != 0 || s->E > kMaxExperts)
         return MOE_EUNSUPPORTED;
     const long long assignments = (long long)s->T * s->k;
@@ -82,6 +84,7 @@ static int make_dims(const moe_shape *s, Dims *dm)
     dm->D = s->D;
     dm->my_rank = s->my_rank;
     dm->drop_policy = s->drop_policy;
+    dm->fp8 = s->dispatch_fp8;
     dm->capacity = C;
     dm->send_rows = send_rows;
     dm->nchunks = (s->T + kChunk - 1) / kChunk;
@@ -156,11 +159,17 @@ MOE_EXPORT int moe_topk_from_logits(const moe_shape *shape, const float *logits,
                                           static_cast<hipStream_t>(stream)));
 }
 
+// The FP8 row scales: required (for a non-empty buffer) under FP8 dispatch.
+static bool bad_scale(const Dims &dm, const float *send_scale)
+{
+    return dm.fp8 ? bad_ptr(send_scale, dm.send_rows) : bad_opt_ptr(send_scale);
+}
+
 MOE_EXPORT int moe_dispatch(const moe_shape *shape, const uint16_t *x, const int32_t *topk_idx,
-                            const float *topk_w, uint16_t *send_buf, int32_t *slot,
-                            int32_t *expert_count, int32_t *expert_kept, int32_t *expert_offset,
-                            int32_t *rank_rows, moe_stats *stats, void *workspace,
-                            size_t workspace_bytes, void *stream)
+                            const float *topk_w, void *send_buf, float *send_scale,
+                            int32_t *slot, int32_t *expert_count, int32_t *expert_kept,
+                            int32_t *expert_offset, int32_t *rank_rows, moe_stats *stats,
+                            void *workspace, size_t workspace_bytes, void *stream)
 {
     Dims dm;
     int rc = make_dims(shape, &dm);
@@ -169,6 +178,8 @@ MOE_EXPORT int moe_dispatch(const moe_shape *shape, const uint16_t *x, const int
     const bool need_w = dm.drop_policy == 1 && dm.capacity >= 0;
     if (need_w ? bad_ptr(topk_w, dm.T) : bad_opt_ptr(topk_w))
         return MOE_EINVAL;
+    if (bad_scale(dm, send_scale))
+        return MOE_EINVAL;
     if (bad_ptr(x, dm.T) || bad_ptr(topk_idx, dm.T) || bad_ptr(send_buf, dm.send_rows) ||
         bad_ptr(slot, dm.T) || bad_ptr(expert_count) || bad_ptr(expert_kept) ||
         bad_ptr(expert_offset) || bad_ptr(rank_rows) || bad_ptr(stats))
@@ -176,14 +187,15 @@ MOE_EXPORT int moe_dispatch(const moe_shape *shape, const uint16_t *x, const int
     Workspace wl;
     if ((rc = check_ws(dm, workspace, workspace_bytes, &wl)) != MOE_OK)
         return rc;
-    return hip_status(launch_dispatch(dm, x, topk_idx, topk_w, send_buf, slot, expert_count,
-                                      expert_kept,
+    return hip_status(launch_dispatch(dm, x, topk_idx, topk_w, send_buf, send_scale, slot,
+                                      expert_count, expert_kept,
                                       expert_offset, rank_rows, stats, (char *)workspace, wl,
                                       static_cast<hipStream_t>(stream)));
 }
 
-MOE_EXPORT int moe_expert_ffn(const moe_shape *shape, const uint16_t *send_buf,
-                              const int32_t *expert_offset, const int32_t *expert_kept,
+MOE_EXPORT int moe_expert_ffn(const moe_shape *shape, const void *send_buf,
+                              const float *send_scale, const int32_t *expert_offset,
+                              const int32_t *expert_kept,
                               const uint16_t *w1, const uint16_t *w3, const uint16_t *w2,
                               uint16_t *expert_out, void *workspace, size_t workspace_bytes,
                               void *stream)
@@ -193,33 +205,35 @@ MOE_EXPORT int moe_expert_ffn(const moe_shape *shape, const uint16_t *send_buf,
     if (rc != MOE_OK)
         return rc;
     if (bad_ptr(send_buf, dm.send_rows) || bad_ptr(expert_offset) || bad_ptr(expert_kept) ||
-        bad_ptr(w1) || bad_ptr(w3) || bad_ptr(w2) || bad_ptr(expert_out, dm.send_rows))
+        bad_ptr(w1) || bad_ptr(w3) || bad_ptr(w2) || bad_ptr(expert_out, dm.send_rows) ||
+        bad_scale(dm, send_scale))
         return MOE_EINVAL;
     Workspace wl;
     if ((rc = check_ws(dm, workspace, workspace_bytes, &wl)) != MOE_OK)
         return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
     uint16_t *h = reinterpret_cast<uint16_t *>((char *)workspace + wl.h);
-    hipError_t e = launch_gate_up(dm, send_buf, expert_offset, expert_kept, w1, w3, h, st);
+    hipError_t e =
+        launch_gate_up(dm, send_buf, send_scale, expert_offset, expert_kept, w1, w3, h, st);
     if (e == hipSuccess)
         e = launch_down(dm, h, expert_offset, expert_kept, w2, expert_out, st);
     return hip_status(e);
 }
 
-MOE_EXPORT int moe_expert_gate_up(const moe_shape *shape, const uint16_t *send_buf,
-                                  const int32_t *expert_offset, const int32_t *expert_kept,
-                                  const uint16_t *w1, const uint16_t *w3, uint16_t *h,
-                                  void *stream)
+MOE_EXPORT int moe_expert_gate_up(const moe_shape *shape, const void *send_buf,
+                                  const float *send_scale, const int32_t *expert_offset,
+                                  const int32_t *expert_kept, const uint16_t *w1,
+                                  const uint16_t *w3, uint16_t *h, void *stream)
 {
     Dims dm;
     const int rc = make_dims(shape, &dm);
     if (rc != MOE_OK)
         return rc;
     if (bad_ptr(send_buf, dm.send_rows) || bad_ptr(expert_offset) || bad_ptr(expert_kept) ||
-        bad_ptr(w1) || bad_ptr(w3) || bad_ptr(h, dm.send_rows))
+        bad_ptr(w1) || bad_ptr(w3) || bad_ptr(h, dm.send_rows) || bad_scale(dm, send_scale))
         return MOE_EINVAL;
-    return hip_status(launch_gate_up(dm, send_buf, expert_offset, expert_kept, w1, w3, h,
-                                     static_cast<hipStream_t>(stream)));
+    return hip_status(launch_gate_up(dm, send_buf, send_scale, expert_offset, expert_kept, w1,
+                                     w3, h, static_cast<hipStream_t>(stream)));
 }
 
 MOE_EXPORT int moe_expert_down(const moe_shape *shape, const uint16_t *h,
@@ -254,8 +268,8 @@ MOE_EXPORT int moe_combine(const moe_shape *shape, const uint16_t *expert_out,
 MOE_EXPORT int moe_layer_fwd(const moe_shape *shape, const uint16_t *x, const uint16_t *w_gate,
                              const float *logit_bias, const uint16_t *w1, const uint16_t *w3,
                              const uint16_t *w2, uint16_t *y, float *logits_out,
-                             int32_t *topk_idx, float *topk_w, uint16_t *send_buf, int32_t *slot,
-                             int32_t *expert_count, int32_t *expert_kept, int32_t *expert_offset,
+                             int32_t *topk_idx, float *topk_w, void *send_buf,
+                             float *send_scale, int32_t *slot, int32_t *expert_count, int32_t *expert_kept, int32_t *expert_offset,
                              int32_t *rank_rows, moe_stats *stats, uint16_t *expert_out,
                              void *workspace, size_t workspace_bytes, void *stream)
 {
@@ -268,7 +282,7 @@ MOE_EXPORT int moe_layer_fwd(const moe_shape *shape, const uint16_t *x, const ui
         bad_ptr(send_buf, dm.send_rows) || bad_ptr(slot, dm.T) || bad_ptr(expert_count) ||
         bad_ptr(expert_kept) || bad_ptr(expert_offset) || bad_ptr(rank_rows) ||
         bad_ptr(stats) || bad_ptr(expert_out, dm.send_rows) || bad_opt_ptr(logit_bias) ||
-        bad_opt_ptr(logits_out))
+        bad_opt_ptr(logits_out) || bad_scale(dm, send_scale))
         return MOE_EINVAL;
     Workspace wl;
     if ((rc = check_ws(dm, workspace, workspace_bytes, &wl)) != MOE_OK)
@@ -278,10 +292,10 @@ MOE_EXPORT int moe_layer_fwd(const moe_shape *shape, const uint16_t *x, const ui
     hipError_t e =
         launch_route(dm, x, w_gate, logit_bias, logits_out, topk_idx, topk_w, ws, wl, st);
     if (e == hipSuccess)
-        e = launch_dispatch(dm, x, topk_idx, topk_w, send_buf, slot, expert_count,
+        e = launch_dispatch(dm, x, topk_idx, topk_w, send_buf, send_scale, slot, expert_count,
                             expert_kept, expert_offset, rank_rows, stats, ws, wl, st);
     if (e == hipSuccess)
-        e = launch_gate_up(dm, send_buf, expert_offset, expert_kept, w1, w3,
+        e = launch_gate_up(dm, send_buf, send_scale, expert_offset, expert_kept, w1, w3,
                            reinterpret_cast<uint16_t *>(ws + wl.h), st);
     if (e == hipSuccess)
         e = launch_down(dm, reinterpret_cast<const uint16_t *>(ws + wl.h), expert_offset,
@@ -289,6 +303,17 @@ MOE_EXPORT int moe_layer_fwd(const moe_shape *shape, const uint16_t *x, const ui
     if (e == hipSuccess)
         e = launch_combine(dm, expert_out, slot, topk_w, y, st);
     return hip_status(e);
+}
+
+MOE_EXPORT int moe_fp8_rows_to_bf16(const void *codes, const float *scales, int64_t rows,
+                                    int32_t d, uint16_t *out, void *stream)
+{
+    if (rows < 0 || d <= 0 || d % 16 != 0 || rows * (int64_t)(d / 4) > (int64_t)INT32_MAX * 256)
+        return MOE_EINVAL;
+    if (bad_ptr(codes, rows) || bad_ptr(scales, rows) || bad_ptr(out, rows))
+        return MOE_EINVAL;
+    return hip_status(launch_fp8_rows_to_bf16(static_cast<const uint8_t *>(codes), scales, rows,
+                                              d, out, static_cast<hipStream_t>(stream)));
 }
 
 MOE_EXPORT const char *moe_status_str(int status)

@@ -110,7 +110,7 @@ __global__ __launch_bounds__(kChunk) void count_kernel(const int32_t *__restrict
 
 // Single workgroup of 1024 threads: thread e owns expert e.
 __global__ __launch_bounds__(kMaxExperts) void scan_kernel(
-    int T, int k, int E, int D, int my_rank, int d, long long C, int nchunks,
+    int T, int k, int E, int D, int my_rank, int d, int fp8, long long C, int nchunks,
     const int32_t *__restrict__ chunk_counts, int32_t *__restrict__ chunk_base,
     const int32_t *__restrict__ chunk_invalid, int32_t *__restrict__ expert_count,
     int32_t *__restrict__ expert_kept, int32_t *__restrict__ expert_offset,
@@ -189,9 +189,11 @@ __global__ __launch_bounds__(kMaxExperts) void scan_kernel(
         st.padded = (C < 0) ? 0 : (long long)E * C - kt;
         st.capacity = C;
         st.send_rows = send_rows;
-        st.dispatch_bytes = kt * d * 2;
-        st.dispatch_wire_bytes = (C < 0) ? kt * d * 2 : send_rows * d * 2;
-        st.dispatch_remote_bytes = (long long)s_remote * d * 2;
+        // a dispatched row: d bf16, or d E4M3 codes plus its fp32 scale
+        const long long row_bytes = fp8 ? (long long)d + 4 : (long long)d * 2;
+        st.dispatch_bytes = kt * row_bytes;
+        st.dispatch_wire_bytes = (C < 0) ? kt * row_bytes : send_rows * row_bytes;
+        st.dispatch_remote_bytes = (long long)s_remote * row_bytes;
         st.combine_bytes = kt * d * 2;
         st.max_expert_count = s_max;
         st.invalid_index = s_invalid;
@@ -348,15 +350,56 @@ __global__ __launch_bounds__(1024) void gate_select_kernel(
 
 constexpr int kSlotGroup = 8; // slots resolved per pass over a token row
 
+// One token row of d bf16 as E4M3 codes with one fp32 scale (dispatch
+// payload of FP8 mode): s = amax/448 (1 for an all-zero row), code of
+// x/s (IEEE fp32 quotient).  The wave reads the row twice (the second time
+// from L2): once for amax, once to encode.
+__device__ __forceinline__ float row_scale_e4m3(const uint4 *src, int nvec, int lane)
+{
+    float amax = 0.f;
+    for (int c = lane; c < nvec; c += 64) {
+        const uint4 v = src[c];
+        const uint32_t p[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            amax = fmaxf(amax, fmaxf(fabsf(bf16_to_f32(p[q] & 0xffffu)),
+                                     fabsf(bf16_to_f32(p[q] >> 16))));
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1)
+        amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+    return amax > 0.f ? amax / 448.f : 1.f;
+}
+
+__device__ __forceinline__ uint2 encode8_e4m3(uint4 v, float sc)
+{
+    const uint32_t p[4] = {v.x, v.y, v.z, v.w};
+    uint32_t w[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const uint32_t a = p[2 * h], b = p[2 * h + 1];
+        w[h] = e4m3_from_f32(bf16_to_f32(a & 0xffffu) / sc) |
+               (e4m3_from_f32(bf16_to_f32(a >> 16) / sc) << 8) |
+               (e4m3_from_f32(bf16_to_f32(b & 0xffffu) / sc) << 16) |
+               (e4m3_from_f32(bf16_to_f32(b >> 16) / sc) << 24);
+    }
+    return make_uint2(w[0], w[1]);
+}
+
+// send_buf rows are d bf16 (FP8 = false) or d E4M3 codes with their scale in
+// send_scale (FP8 = true).
+template <bool FP8>
 __global__ __launch_bounds__(256) void permute_kernel(
     const uint16_t *__restrict__ x, const int32_t *__restrict__ topk_idx,
     int32_t *__restrict__ slot, const int32_t *__restrict__ chunk_base,
     const int32_t *__restrict__ expert_offset, const int32_t *__restrict__ expert_kept,
-    uint16_t *__restrict__ send_buf, int T, int d, int k, int E, long long C, int tok_blocks,
-    int pad_parts, int pos_final)
+    void *__restrict__ send_buf_v, float *__restrict__ send_scale, int T, int d, int k, int E,
+    long long C, int tok_blocks, int pad_parts, int pos_final)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int nvec = d / 8; // 16-byte vectors per row
+    const int nvec = d / 8;                    // 16-byte pieces of an x row
+    const size_t row_bytes = (size_t)d * (FP8 ? 1 : 2);
+    char *send_buf = reinterpret_cast<char *>(send_buf_v);
     if ((int)blockIdx.x < tok_blocks) {
         const int t = blockIdx.x * 4 + wave;
         if (t >= T)
@@ -364,6 +407,9 @@ __global__ __launch_bounds__(256) void permute_kernel(
         const int32_t *row = topk_idx + (size_t)t * k;
         const int32_t *base = chunk_base + (size_t)(t / kChunk) * E;
         const uint4 *src = reinterpret_cast<const uint4 *>(x + (size_t)t * d);
+        float sc = 1.f;
+        if constexpr (FP8)
+            sc = row_scale_e4m3(src, nvec, lane);
         for (int s0 = 0; s0 < k; s0 += kSlotGroup) {
             // the slots are wave-uniform: resolve them in scalar registers
             int dst[kSlotGroup];
@@ -393,6 +439,9 @@ __global__ __launch_bounds__(256) void permute_kernel(
                 for (int q = 1; q < kSlotGroup; ++q)
                     v = (lane == q) ? dst[q] : v;
                 slot[(size_t)t * k + s0 + lane] = v;
+                if constexpr (FP8)
+                    if (v >= 0)
+                        send_scale[v] = sc;
             }
             // four row pieces in flight per lane before their stores
             for (int c0 = lane; c0 < nvec; c0 += 256) {
@@ -400,50 +449,96 @@ __global__ __launch_bounds__(256) void permute_kernel(
 #pragma unroll
                 for (int u = 0; u < 4; ++u)
                     v[u] = (c0 + 64 * u < nvec) ? src[c0 + 64 * u] : make_uint4(0, 0, 0, 0);
-#pragma unroll
-                for (int q = 0; q < kSlotGroup; ++q) {
-                    if (dst[q] < 0)
-                        continue;
-                    uint4 *out = reinterpret_cast<uint4 *>(send_buf + (size_t)dst[q] * d);
+                if constexpr (FP8) {
+                    uint2 q8[4];
 #pragma unroll
                     for (int u = 0; u < 4; ++u)
-                        if (c0 + 64 * u < nvec)
-                            out[c0 + 64 * u] = v[u];
+                        q8[u] = encode8_e4m3(v[u], sc);
+#pragma unroll
+                    for (int q = 0; q < kSlotGroup; ++q) {
+                        if (dst[q] < 0)
+                            continue;
+                        uint2 *out = reinterpret_cast<uint2 *>(send_buf + (size_t)dst[q] * row_bytes);
+#pragma unroll
+                        for (int u = 0; u < 4; ++u)
+                            if (c0 + 64 * u < nvec)
+                                out[c0 + 64 * u] = q8[u];
+                    }
+                } else {
+#pragma unroll
+                    for (int q = 0; q < kSlotGroup; ++q) {
+                        if (dst[q] < 0)
+                            continue;
+                        uint4 *out = reinterpret_cast<uint4 *>(send_buf + (size_t)dst[q] * row_bytes);
+#pragma unroll
+                        for (int u = 0; u < 4; ++u)
+                            if (c0 + 64 * u < nvec)
+                                out[c0 + 64 * u] = v[u];
+                    }
                 }
             }
         }
-    } else if (C < 0) {
+        return;
+    }
+    // pad rows (capacity mode) and the dropless tail: zero bytes (E4M3 code
+    // 0 is +0), scale 0
+    const int nz = (int)(row_bytes / 16);
+    const uint4 z = make_uint4(0, 0, 0, 0);
+    long long r_lo, r_hi, r_step;
+    int r_off;
+    const int b = blockIdx.x - tok_blocks;
+    if (C < 0) {
         // dropless: rows [offset[E], T*k) hold no token (they exist only when
         // entries were invalid); zero them so the whole buffer is defined
-        const long long lo = expert_offset[E], hi = (long long)T * k;
-        const int b = blockIdx.x - tok_blocks;
-        const uint4 z = make_uint4(0, 0, 0, 0);
-        for (long long r = lo + b * 4 + wave; r < hi; r += (long long)pad_parts * 4) {
-            uint4 *dstp = reinterpret_cast<uint4 *>(send_buf + (size_t)r * d);
-            for (int c = lane; c < nvec; c += 64)
-                dstp[c] = z;
-        }
+        r_lo = expert_offset[E];
+        r_hi = (long long)T * k;
+        r_off = b * 4 + wave;
+        r_step = (long long)pad_parts * 4;
     } else {
-        // zero the pad rows [e*C + kept_e, (e+1)*C) of capacity mode
-        const int b = blockIdx.x - tok_blocks;
+        // the pad rows [e*C + kept_e, (e+1)*C) of capacity mode
         const int e = b / pad_parts, part = b % pad_parts;
         const long long per = (C + pad_parts - 1) / pad_parts;
         const long long lo_pad = (long long)e * C + expert_kept[e];
-        const long long r_lo = max((long long)e * C + part * per, lo_pad);
-        const long long r_hi = min((long long)e * C + (part + 1) * per, (long long)(e + 1) * C);
-        const uint4 z = make_uint4(0, 0, 0, 0);
-        for (long long r = r_lo + wave; r < r_hi; r += 4) {
-            uint4 *dstp = reinterpret_cast<uint4 *>(send_buf + (size_t)r * d);
-            for (int c = lane; c < nvec; c += 64)
-                dstp[c] = z;
-        }
+        r_lo = max((long long)e * C + part * per, lo_pad);
+        r_hi = min((long long)e * C + (part + 1) * per, (long long)(e + 1) * C);
+        r_off = wave;
+        r_step = 4;
     }
+    for (long long r = r_lo + r_off; r < r_hi; r += r_step) {
+        uint4 *dstp = reinterpret_cast<uint4 *>(send_buf + (size_t)r * row_bytes);
+        for (int c = lane; c < nz; c += 64)
+            dstp[c] = z;
+        if constexpr (FP8)
+            if (lane == 0)
+                send_scale[r] = 0.f;
+    }
+}
+
+// Diagnostic: out[r, i] = bf16(E4M3 value of codes[r, i] * scales[r]), the
+// decode the expert GEMM uses; exact when the scale is a power of two.
+__global__ __launch_bounds__(256) void fp8_rows_to_bf16_kernel(const uint8_t *__restrict__ codes,
+                                                               const float *__restrict__ scales,
+                                                               long long rows, int d,
+                                                               uint16_t *__restrict__ out)
+{
+    const long long q = (long long)blockIdx.x * 256 + threadIdx.x; // 4 codes each
+    if (q >= rows * (d / 4))
+        return;
+    const long long r = q / (d / 4);
+    const uint32_t w = reinterpret_cast<const uint32_t *>(codes)[q];
+    const uint2 b = e4m3x4_to_bf16x4(w);
+    const float sc = scales[r];
+    const uint32_t v[4] = {b.x & 0xffffu, b.x >> 16, b.y & 0xffffu, b.y >> 16};
+    uint16_t *o = out + q * 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        o[i] = (uint16_t)f32_to_bf16_rne(bf16_to_f32(v[i]) * sc);
 }
 
 } // namespace
 
 hipError_t launch_dispatch(const Dims &dm, const uint16_t *x, const int32_t *topk_idx,
-                           const float *topk_w, uint16_t *send_buf, int32_t *slot,
+                           const float *topk_w, void *send_buf, float *send_scale, int32_t *slot,
                            int32_t *expert_count, int32_t *expert_kept, int32_t *expert_offset,
                            int32_t *rank_rows, moe_stats *stats, char *ws, const Workspace &wl,
                            hipStream_t st)
@@ -459,7 +554,7 @@ hipError_t launch_dispatch(const Dims &dm, const uint16_t *x, const int32_t *top
         count_kernel<<<dm.nchunks, kChunk, lds, st>>>(topk_idx, dm.T, dm.k, dm.E, slot,
                                                        chunk_counts, chunk_invalid);
     }
-    scan_kernel<<<1, kMaxExperts, 0, st>>>(dm.T, dm.k, dm.E, dm.D, dm.my_rank, dm.d,
+    scan_kernel<<<1, kMaxExperts, 0, st>>>(dm.T, dm.k, dm.E, dm.D, dm.my_rank, dm.d, dm.fp8,
                                            (long long)dm.capacity, dm.nchunks, chunk_counts,
                                            chunk_base, chunk_invalid, expert_count, expert_kept,
                                            expert_offset, rank_rows, stats, all_offset);
@@ -483,10 +578,29 @@ hipError_t launch_dispatch(const Dims &dm, const uint16_t *x, const int32_t *top
         pad_blocks = pad_parts;
     }
     const long long blocks = (long long)tok_blocks + pad_blocks;
-    if (blocks > 0)
-        permute_kernel<<<(unsigned)blocks, 256, 0, st>>>(
-            x, topk_idx, slot, chunk_base, expert_offset, expert_kept, send_buf, dm.T, dm.d,
-            dm.k, dm.E, (long long)dm.capacity, tok_blocks, pad_parts, by_gate ? 1 : 0);
+    if (blocks > 0) {
+        if (dm.fp8)
+            permute_kernel<true><<<(unsigned)blocks, 256, 0, st>>>(
+                x, topk_idx, slot, chunk_base, expert_offset, expert_kept, send_buf, send_scale,
+                dm.T, dm.d, dm.k, dm.E, (long long)dm.capacity, tok_blocks, pad_parts,
+                by_gate ? 1 : 0);
+        else
+            permute_kernel<false><<<(unsigned)blocks, 256, 0, st>>>(
+                x, topk_idx, slot, chunk_base, expert_offset, expert_kept, send_buf, nullptr,
+                dm.T, dm.d, dm.k, dm.E, (long long)dm.capacity, tok_blocks, pad_parts,
+                by_gate ? 1 : 0);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_fp8_rows_to_bf16(const uint8_t *codes, const float *scales, long long rows,
+                                   int d, uint16_t *out, hipStream_t st)
+{
+    const long long quads = rows * (d / 4);
+    if (quads == 0)
+        return hipSuccess;
+    fp8_rows_to_bf16_kernel<<<(unsigned)((quads + 255) / 256), 256, 0, st>>>(codes, scales,
+                                                                             rows, d, out);
     return hipGetLastError();
 }
 

@@ -42,7 +42,8 @@ namespace {
 #endif
 
 struct GemmArgs {
-    const uint16_t *A;          // [rows, K]
+    const void *A;              // [rows, K] bf16, or E4M3 codes (A8)
+    const float *a_scale;       // [rows] fp32 row scales (A8 only)
     const int32_t *row_offset;  // [E + 1] first row of each expert
     const int32_t *row_count;   // [E] rows of each expert
     const uint16_t *B0;         // [E, N, K]
@@ -95,21 +96,28 @@ __device__ __forceinline__ void decode_work(const int32_t *__restrict__ rows, in
     }
 }
 
-template <int BM, int BN, int BK, int RING, int WM, int WN, bool DUAL>
+// A8: the A operand is E4M3 codes with one fp32 scale per row (FP8
+// dispatch); its fragments are widened to bf16 (exact) before the MFMA and
+// the row scale multiplies the fp32 sums in the epilogue.
+template <int BM, int BN, int BK, int RING, int WM, int WN, bool DUAL, bool A8>
 __global__ __launch_bounds__(256, MOE_GEMM_MIN_BLOCKS) void grouped_gemm_kernel(GemmArgs g)
 {
     static_assert(WM * WN == 4, "4 waves");
-    constexpr int RC = BK / 8;                        // 16-byte pieces per row and step
-    constexpr int RPI = 64 / RC;                      // rows filled by one wave-wide load
+    static_assert(!A8 || BK == 64, "the E4M3 A path reads both 32-deep halves of a 64-deep step");
+    constexpr int RC = BK / 8;                        // 16-byte B pieces per row and step
+    constexpr int RPI = 64 / RC;                      // B rows filled by one wave-wide load
+    constexpr int A_EB = A8 ? 1 : 2;                  // bytes per A element
+    constexpr int RC_A = BK * A_EB / 16;              // 16-byte A pieces per row and step
+    constexpr int RPI_A = 64 / RC_A;                  // A rows filled by one wave-wide load
     constexpr int NB = DUAL ? 2 * BN : BN;            // B rows per stage
-    constexpr int A_PW = BM / RPI / 4, B_PW = NB / RPI / 4; // loads per wave per stage
-    static_assert(A_PW * RPI * 4 == BM && B_PW * RPI * 4 == NB, "whole loads per wave");
+    constexpr int A_PW = BM / RPI_A / 4, B_PW = NB / RPI / 4; // loads per wave per stage
+    static_assert(A_PW * RPI_A * 4 == BM && B_PW * RPI * 4 == NB, "whole loads per wave");
     constexpr int B_BYTES = NB * BK * 2;
     constexpr int WTN = BN / WN;                      // wave tile columns
     constexpr int RT = BM / 16 / WM, CT = WTN / 16;   // 16x16 MFMA tiles per wave
     constexpr int LDC = BN + 8;                       // epilogue row (elements)
     static_assert(BM * LDC * 2 <= RING, "epilogue tile fits in the ring");
-    static_assert(2 * (BM * BK * 2 + B_BYTES) <= RING, "two full stages fit in the ring");
+    static_assert(2 * (BM * BK * A_EB + B_BYTES) <= RING, "two full stages fit in the ring");
     // Wave (wm, wn) owns the 16-row slices wm, wm+WM, wm+2*WM, ... of the tile
     // (interleaved, so a partly filled tile keeps every wave busy) and the
     // columns [wn*WTN, (wn+1)*WTN).
@@ -149,17 +157,17 @@ __global__ __launch_bounds__(256, MOE_GEMM_MIN_BLOCKS) void grouped_gemm_kernel(
     // expert's end are skipped (wave-uniform); a row past the end inside a
     // partly valid load reads row 0 of the tile instead (never multiplied
     // into a stored result).
-    const uint16_t *asrc[A_PW];
+    const char *asrc[A_PW];
     const uint16_t *bsrc[B_PW];
     int a_loads = 0; // loads this wave issues per stage for A
 #pragma unroll
     for (int j = 0; j < A_PW; ++j) {
         const int grp = 4 * j + wave;
-        const int r = grp * RPI + lane / RC;
-        const int piece = (lane % RC) ^ swz<RC>(r);
+        const int r = grp * RPI_A + lane / RC_A;
+        const int piece = (lane % RC_A) ^ swz<RC_A>(r);
         const int rr = r < rows_valid ? r : 0;
-        asrc[j] = g.A + (row0 + rr) * K + piece * 8;
-        a_loads += (grp * RPI < rows_valid) ? 1 : 0;
+        asrc[j] = reinterpret_cast<const char *>(g.A) + ((row0 + rr) * K) * A_EB + piece * 16;
+        a_loads += (grp * RPI_A < rows_valid) ? 1 : 0;
     }
 #pragma unroll
     for (int j = 0; j < B_PW; ++j) {
@@ -173,10 +181,13 @@ __global__ __launch_bounds__(256, MOE_GEMM_MIN_BLOCKS) void grouped_gemm_kernel(
     const int loads_per_stage = a_loads + B_PW;
     // A stage holds only the A rows that carry data (whole 1 KB loads), then
     // the B rows; the ring takes as many stages as fit (2 .. 8), so a tile
-    // with fewer rows keeps more K steps in flight.
-    const int a_bytes = ((rows_valid + RPI - 1) / RPI) * 1024;
+    // with fewer rows keeps more K steps in flight.  A tile of more than 192
+    // rows keeps two: its MFMA work per step already covers the load of the
+    // next, and a third stage in flight measured slower (E4M3 rows, whose
+    // full tiles would fit three: Mixtral gate/up 2.01 -> 1.85 ms).
+    const int a_bytes = ((rows_valid + RPI_A - 1) / RPI_A) * 1024;
     const int stage = a_bytes + B_BYTES;
-    const int S = min(8, RING / stage);
+    const int S = min(rows_valid > 192 ? 2 : 8, RING / stage);
 
     const uint32_t lds_base = (uint32_t)(uintptr_t)(LDS_AS char *)smem;
     auto issue = [&](int step, int slot) {
@@ -184,8 +195,8 @@ __global__ __launch_bounds__(256, MOE_GEMM_MIN_BLOCKS) void grouped_gemm_kernel(
         const int k0 = step * BK;
 #pragma unroll
         for (int j = 0; j < A_PW; ++j)
-            if ((4 * j + wave) * RPI < rows_valid)
-                dma16(asrc[j] + k0, st + (4 * j + wave) * 1024);
+            if ((4 * j + wave) * RPI_A < rows_valid)
+                dma16(asrc[j] + k0 * A_EB, st + (4 * j + wave) * 1024);
 #pragma unroll
         for (int j = 0; j < B_PW; ++j)
             dma16(bsrc[j] + k0, st + a_bytes + (4 * j + wave) * 1024);
@@ -245,6 +256,100 @@ __global__ __launch_bounds__(256, MOE_GEMM_MIN_BLOCKS) void grouped_gemm_kernel(
                     return *reinterpret_cast<const bf16x8 *>(As + r * (BK * 2) +
                                                              ((piece ^ swz<RC>(r)) << 4));
                 };
+                if constexpr (A8) {
+                    // E4M3 A: per slice, lane group q = lane/16 reads the 8
+                    // codes of each 32-deep MFMA step it needs (k = 8q.. and
+                    // 32+8q..) once; the first feed step 0, the second wait
+                    // in registers for step 1.  B is read as in the bf16 path.
+                    auto read_b8 = [&](int kc, int j) {
+                        const int piece = 4 * kc + (lane >> 4);
+                        const int n = (j < CT ? 0 : BN - CT * 16) + wn * WTN + j * 16 + (lane & 15);
+                        return *reinterpret_cast<const bf16x8 *>(
+                            Bs + n * (BK * 2) + ((piece ^ swz<RC>(n)) << 4));
+                    };
+                    auto read_a8 = [&](int i) {
+                        // codes k = 8q .. 8q+7 (step 0) and 32+8q .. 32+8q+7
+                        // (step 1): two 8-byte halves of 16-byte pieces
+                        const int r = (wm + WM * i) * 16 + (lane & 15);
+                        const int q = lane >> 4;
+                        const char *row = As + r * (BK * A_EB) + 8 * (q & 1);
+                        const uint2 a = *reinterpret_cast<const uint2 *>(
+                            row + (((q >> 1) ^ swz<RC_A>(r)) << 4));
+                        const uint2 b = *reinterpret_cast<const uint2 *>(
+                            row + (((2 + (q >> 1)) ^ swz<RC_A>(r)) << 4));
+                        return make_uint4(a.x, a.y, b.x, b.y);
+                    };
+                    auto widen = [&](uint32_t a, uint32_t b) {
+                        const uint2 x = e4m3x4_to_bf16x4(a), y = e4m3x4_to_bf16x4(b);
+                        return __builtin_bit_cast(bf16x8, make_uint4(x.x, x.y, y.x, y.y));
+                    };
+                    bf16x8 b0[NBF], b1[NBF], hi[NA];
+#pragma unroll
+                    for (int j = 0; j < NBF; ++j)
+                        b0[j] = read_b8(0, j);
+                    // A pieces are read two slices ahead and widened one
+                    // slice ahead, so neither the LDS latency nor the
+                    // conversion sits in front of a slice's MFMAs
+                    uint4 raw = read_a8(0), raw_next = raw;
+                    if (NA > 1)
+                        raw_next = read_a8(1);
+                    bf16x8 lo = widen(raw.x, raw.y);
+                    hi[0] = widen(raw.z, raw.w);
+                    // step 0: per slice, the next reads, the next slice's
+                    // widening, then 8 MFMAs on the current low half; the
+                    // high halves wait in registers for step 1
+#pragma unroll
+                    for (int i = 0; i < NA; ++i) {
+                        uint4 raw2 = raw_next;
+                        if (i + 2 < NA)
+                            raw2 = read_a8(i + 2);
+#pragma unroll
+                        for (int j = i * NBF / NA; j < (i + 1) * NBF / NA; ++j)
+                            b1[j] = read_b8(1, j);
+                        bf16x8 lo_next = lo;
+                        if (i + 1 < NA) {
+                            lo_next = widen(raw_next.x, raw_next.y);
+                            hi[i + 1] = widen(raw_next.z, raw_next.w);
+                        }
+#pragma unroll
+                        for (int j = 0; j < CT; ++j) {
+                            acc0[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                lo, b0[j], acc0[i][j], 0, 0, 0);
+                            if constexpr (DUAL)
+                                acc1[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                    lo, b0[CT + j], acc1[i][j], 0, 0, 0);
+                        }
+                        lo = lo_next;
+                        raw_next = raw2;
+                    }
+                    // step 1: no LDS reads
+#pragma unroll
+                    for (int i = 0; i < NA; ++i)
+#pragma unroll
+                        for (int j = 0; j < CT; ++j) {
+                            acc0[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                hi[i], b1[j], acc0[i][j], 0, 0, 0);
+                            if constexpr (DUAL)
+                                acc1[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                    hi[i], b1[CT + j], acc1[i][j], 0, 0, 0);
+                        }
+                    __builtin_amdgcn_sched_group_barrier(0x100, NBF + (NA > 1 ? 4 : 2), 0);
+#pragma unroll
+                    for (int i = 0; i < NA; ++i) {
+                        constexpr int lo_n = NBF / (NA > 0 ? NA : 1);
+                        const int cnt = (i + 2 < NA ? 2 : 0) + (i + 1) * NBF / NA - i * NBF / NA;
+                        if (lo_n > 0 && cnt == lo_n)
+                            __builtin_amdgcn_sched_group_barrier(0x100, lo_n, 0);
+                        else if (cnt == lo_n + 1)
+                            __builtin_amdgcn_sched_group_barrier(0x100, lo_n + 1, 0);
+                        else if (cnt == lo_n + 2)
+                            __builtin_amdgcn_sched_group_barrier(0x100, lo_n + 2, 0);
+                        else if (cnt == lo_n + 3)
+                            __builtin_amdgcn_sched_group_barrier(0x100, lo_n + 3, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x008, NBF, 0);
+                    }
+                    __builtin_amdgcn_sched_group_barrier(0x008, NA * NBF, 0);
+                } else {
                 bf16x8 bf[2][NBF], af[2];
                 read_b(0, bf[0]);
                 af[0] = read_a(0, 0);
@@ -284,6 +389,7 @@ __global__ __launch_bounds__(256, MOE_GEMM_MIN_BLOCKS) void grouped_gemm_kernel(
                             __builtin_amdgcn_sched_group_barrier(0x100, NBF + 1, 0);
                         __builtin_amdgcn_sched_group_barrier(0x008, NBF, 0);
                     }
+                }
             }
         }
 
@@ -301,8 +407,14 @@ __global__ __launch_bounds__(256, MOE_GEMM_MIN_BLOCKS) void grouped_gemm_kernel(
                     const int m = (wm + WM * i) * 16 + 4 * (lane >> 4) + q;
                     const int n = wn * WTN + j * 16 + (lane & 15);
                     float v = acc0[i][j][q];
+                    float up = DUAL ? acc1[i][j][q] : 0.f;
+                    if constexpr (A8) { // the row's dequantization scale
+                        const float sr = m < rows_valid ? g.a_scale[row0 + m] : 0.f;
+                        v *= sr;
+                        up *= sr;
+                    }
                     if constexpr (DUAL) {
-                        const float gt = v, up = acc1[i][j][q];
+                        const float gt = v;
                         v = gt / (1.f + expf(-gt)) * up; // SiLU(g) * u
                     }
                     Cs[m * LDC + n] = (uint16_t)f32_to_bf16_rne(v);
@@ -354,20 +466,30 @@ constexpr int kRing = MOE_GEMM_RING; // LDS ring bytes (one workgroup per CU)
 
 } // namespace
 
-hipError_t launch_gate_up(const Dims &dm, const uint16_t *send_buf, const int32_t *expert_offset,
-                          const int32_t *expert_kept, const uint16_t *w1, const uint16_t *w3,
-                          uint16_t *h, hipStream_t st)
+template <bool A8>
+static void launch_gate_up_t(const Dims &dm, const GemmArgs &a, long long mtiles_max,
+                             hipStream_t st)
+{
+    if (dm.H % kBN1 == 0) // H is a multiple of 64; the wide tile needs a multiple of kBN1
+        grouped_gemm_kernel<kBM, kBN1, kBK, kRing, 2, 2, true, A8>
+            <<<xcd_grid((int)(mtiles_max * (dm.H / kBN1))), 256, 0, st>>>(a);
+    else
+        grouped_gemm_kernel<kBM, 64, kBK, kRing, 2, 2, true, A8>
+            <<<xcd_grid((int)(mtiles_max * (dm.H / 64))), 256, 0, st>>>(a);
+}
+
+hipError_t launch_gate_up(const Dims &dm, const void *send_buf, const float *send_scale,
+                          const int32_t *expert_offset, const int32_t *expert_kept,
+                          const uint16_t *w1, const uint16_t *w3, uint16_t *h, hipStream_t st)
 {
     if (dm.send_rows == 0)
         return hipSuccess;
     const long long mtiles_max = (dm.send_rows + kBM - 1) / kBM + dm.E;
-    GemmArgs a{send_buf, expert_offset, expert_kept, w1, w3, h, dm.E, dm.H, dm.d};
-    if (dm.H % kBN1 == 0) // H is a multiple of 64; the wide tile needs a multiple of kBN1
-        grouped_gemm_kernel<kBM, kBN1, kBK, kRing, 2, 2, true>
-            <<<xcd_grid((int)(mtiles_max * (dm.H / kBN1))), 256, 0, st>>>(a);
+    GemmArgs a{send_buf, send_scale, expert_offset, expert_kept, w1, w3, h, dm.E, dm.H, dm.d};
+    if (dm.fp8)
+        launch_gate_up_t<true>(dm, a, mtiles_max, st);
     else
-        grouped_gemm_kernel<kBM, 64, kBK, kRing, 2, 2, true>
-            <<<xcd_grid((int)(mtiles_max * (dm.H / 64))), 256, 0, st>>>(a);
+        launch_gate_up_t<false>(dm, a, mtiles_max, st);
     return hipGetLastError();
 }
 
@@ -378,12 +500,12 @@ hipError_t launch_down(const Dims &dm, const uint16_t *h, const int32_t *expert_
     if (dm.send_rows == 0)
         return hipSuccess;
     const long long mtiles_max = (dm.send_rows + kBM - 1) / kBM + dm.E;
-    GemmArgs a{h, expert_offset, expert_kept, w2, nullptr, expert_out, dm.E, dm.d, dm.H};
+    GemmArgs a{h, nullptr, expert_offset, expert_kept, w2, nullptr, expert_out, dm.E, dm.d, dm.H};
     if (dm.d % kBN2 == 0)
-        grouped_gemm_kernel<kBM, kBN2, kBK, kRing, 2, 2, false>
+        grouped_gemm_kernel<kBM, kBN2, kBK, kRing, 2, 2, false, false>
             <<<xcd_grid((int)(mtiles_max * (dm.d / kBN2))), 256, 0, st>>>(a);
     else
-        grouped_gemm_kernel<kBM, 64, kBK, kRing, 2, 2, false>
+        grouped_gemm_kernel<kBM, 64, kBK, kRing, 2, 2, false, false>
             <<<xcd_grid((int)(mtiles_max * (dm.d / 64))), 256, 0, st>>>(a);
     return hipGetLastError();
 }

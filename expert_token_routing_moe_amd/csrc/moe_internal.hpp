@@ -38,6 +38,44 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 }
 
 // ---------------------------------------------------------------------------
+// FP8 E4M3 (OCP: sign, 4 exponent bits with bias 7, 3 mantissa bits; largest
+// finite 448, no infinities) for the dispatch payload.
+// ---------------------------------------------------------------------------
+// Nearest E4M3 code to v, ties to even, |v| >= 448 saturating to 448, the
+// sign bit kept (so -0 and tiny negatives give 0x80).
+__device__ __forceinline__ uint32_t e4m3_from_f32(float v)
+{
+    const uint32_t sgn = (__float_as_uint(v) >> 24) & 0x80u;
+    const float a = fabsf(v);
+    uint32_t c;
+    if (!(a < 448.f)) {
+        c = 0x7Eu;
+    } else if (a < 0.015625f) { // below 2^-6: multiples of 2^-9, rounded to even
+        c = (uint32_t)__builtin_rintf(a * 512.f);
+    } else { // keep 3 mantissa bits, round to nearest even (carry may bump the exponent)
+        uint32_t u = __float_as_uint(a);
+        u += 0x7FFFFu + ((u >> 20) & 1u);
+        c = (u - (120u << 23)) >> 20; // exponent bias 127 -> 7
+    }
+    return c | sgn;
+}
+
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Four E4M3 codes (one per byte of w, lowest first) as four bf16 (two
+// packed pairs).  The gfx950 packed fp8 -> fp32 conversion decodes two codes
+// at a time; every E4M3 value has at most 4 significant bits, so its fp32
+// image's upper half is the exact bf16, and one byte permute packs two.
+__device__ __forceinline__ uint2 e4m3x4_to_bf16x4(uint32_t w)
+{
+    const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8(w, false); // codes 0, 1
+    const f32x2_t b = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);  // codes 2, 3
+    return make_uint2(
+        __builtin_amdgcn_perm(__float_as_uint(a.y), __float_as_uint(a.x), 0x07060302u),
+        __builtin_amdgcn_perm(__float_as_uint(b.y), __float_as_uint(b.x), 0x07060302u));
+}
+
+// ---------------------------------------------------------------------------
 // Sizes shared by host and kernels
 // ---------------------------------------------------------------------------
 constexpr int kChunk = 256;      // tokens per histogram chunk (one per thread)
@@ -47,6 +85,7 @@ constexpr int kMaxExperts = 1024; // E limit of the LDS bitmaps and scans
 struct Dims {
     int T, d, E, k, H, D, my_rank;
     int drop_policy;   // 0: token order, 1: by gate value (capacity mode only)
+    int fp8;           // dispatch payload: 0 bf16 rows, 1 E4M3 rows + fp32 row scales
     int64_t capacity;  // C, or -1 when dropless
     int64_t send_rows; // E*C or T*k
     int nchunks;       // ceil(T / kChunk)
@@ -78,10 +117,11 @@ hipError_t launch_route(const Dims &dm, const uint16_t *x, const uint16_t *w_gat
 hipError_t launch_topk_softmax(const Dims &dm, const float *logits, int32_t *topk_idx,
                                float *topk_w, hipStream_t st);
 hipError_t launch_dispatch(const Dims &dm, const uint16_t *x, const int32_t *topk_idx,
-                           const float *topk_w, uint16_t *send_buf, int32_t *slot, int32_t *expert_count,
+                           const float *topk_w, void *send_buf, float *send_scale, int32_t *slot, int32_t *expert_count,
                            int32_t *expert_kept, int32_t *expert_offset, int32_t *rank_rows,
                            moe_stats *stats, char *ws, const Workspace &wl, hipStream_t st);
-hipError_t launch_gate_up(const Dims &dm, const uint16_t *send_buf, const int32_t *expert_offset,
+hipError_t launch_gate_up(const Dims &dm, const void *send_buf, const float *send_scale,
+                          const int32_t *expert_offset,
                           const int32_t *expert_kept, const uint16_t *w1, const uint16_t *w3,
                           uint16_t *h, hipStream_t st);
 hipError_t launch_down(const Dims &dm, const uint16_t *h, const int32_t *expert_offset,
@@ -89,6 +129,8 @@ hipError_t launch_down(const Dims &dm, const uint16_t *h, const int32_t *expert_
                        hipStream_t st);
 hipError_t launch_combine(const Dims &dm, const uint16_t *expert_out, const int32_t *slot,
                           const float *topk_w, uint16_t *y, hipStream_t st);
+hipError_t launch_fp8_rows_to_bf16(const uint8_t *codes, const float *scales, long long rows,
+                                   int d, uint16_t *out, hipStream_t st);
 
 // XCD-aware block remap: the chip dispatches consecutive workgroups to its 8
 // XCDs round robin; this turns block b into a logical work index so that each

@@ -42,6 +42,7 @@ class MoEConfig:
     seed: int = BASE_SEED
     drop_policy: int = 0   # 0: overflow dropped in token order; 1: by gate value
     min_capacity: int = 0  # lower bound on the capacity C (capacity mode)
+    dispatch_fp8: int = 0  # 1: dispatch payload as E4M3 rows with fp32 row scales
 
     def with_(self, **kw) -> "MoEConfig":
         return replace(self, **kw)

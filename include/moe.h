@@ -28,6 +28,9 @@
  *        beyond an expert's capacity are dropped by selected probability.
  *   [MC] same page, the DeepSpeed paragraph: a minimum capacity per expert
  *        regardless of the capacity factor.
+ *   [F8] same page, "What the bounds omit": FP8 dispatch sends token rows in
+ *        FP8 instead of BF16 (half the dispatch row, plus scale tensors),
+ *        while the combine path may stay wider.
  *
  * Conventions for every call
  *   - Tensor pointers are DEVICE pointers (HIP global memory) unless marked
@@ -66,7 +69,7 @@ extern "C" {
 #define MOE_EWORKSPACE (-3)   /* workspace NULL or smaller than moe_query says  */
 #define MOE_EHIP (-4)         /* a HIP launch reported an error                 */
 
-/* Shape of one layer on one device, in the pages' notation [N][CF][PL][DP][MC].
+/* Shape of one layer on one device, in the pages' notation [N][CF][PL][DP][MC][F8].
  *   T        tokens on this device (T >= 0; T = 0 enqueues nothing)
  *   d        hidden size (d > 0, d % 64 == 0)
  *   E        routed experts (1 <= E <= 1024, E % D == 0)
@@ -84,6 +87,13 @@ extern "C" {
  *            per-rank rows) are the same.  Other values -> MOE_EINVAL.
  *   min_capacity  >= 0: in capacity mode C = max(ceil(f*T*k/E), min_capacity)
  *            [MC]; 0 leaves C as computed.  Ignored when dropless.
+ *   dispatch_fp8  0: the send buffer holds bf16 rows (d * 2 bytes each).
+ *            1 [F8]: it holds OCP FP8 E4M3 rows (d bytes each) and a
+ *            separate fp32 scale per row: s = amax/448 computed in fp32 (1 for
+ *            an all-zero row), code = E4M3(x/s) with the quotient in fp32,
+ *            rounded to nearest (ties to even), saturating at 448, sign kept.
+ *            The expert sees code value * s; expert_out, h and the combine
+ *            stay bf16.  Other values -> MOE_EINVAL.
  *   capacity_factor  f > 0: capacity C = ceil(f*T*k/E), evaluated left to
  *            right in IEEE double [CF]; +INFINITY: dropless (no capacity).
  *            NaN, zero, negative -> MOE_EINVAL.
@@ -92,6 +102,7 @@ typedef struct moe_shape {
     int32_t T, d, E, k, H, D, my_rank;
     int32_t drop_policy;
     int32_t min_capacity;
+    int32_t dispatch_fp8;
     double capacity_factor;
 } moe_shape;
 
@@ -102,11 +113,16 @@ typedef struct moe_shape {
  *   padded                E*C - kept in capacity mode, 0 when dropless  [CF]
  *   capacity              C, or -1 when dropless
  *   send_rows             rows of the send buffer: E*C, or T*k when dropless
- *   dispatch_bytes        kept*d*2: bf16 token vectors that travel  [DA]
- *   dispatch_wire_bytes   send_rows*d*2 in capacity mode (pads included,
- *                         the static [E, C, d] buffer), kept*d*2 dropless
- *   dispatch_remote_bytes kept rows bound for ranks other than my_rank, *d*2
- *   combine_bytes         = dispatch_bytes (combine reverses dispatch) [CA]
+ *   dispatch_bytes        kept * row bytes: the token vectors that travel
+ *                         [DA]; a row is d*2 bytes (bf16), or d + 4 under
+ *                         FP8 dispatch (codes plus the row's scale) [F8]
+ *   dispatch_wire_bytes   send_rows * row bytes in capacity mode (pads
+ *                         included, the static [E, C, d] buffer), as
+ *                         dispatch_bytes when dropless
+ *   dispatch_remote_bytes kept rows bound for ranks other than my_rank,
+ *                         times the row bytes
+ *   combine_bytes         kept*d*2: the bf16 expert outputs that travel back
+ *                         (combine reverses dispatch) [CA]
  *   max_expert_count      max over experts of the routed count n_e
  *   invalid_index         topk_idx entries outside [0, E), or repeating an
  *                         expert listed earlier for the same token; each is
@@ -149,7 +165,7 @@ int moe_route(const moe_shape *shape, const uint16_t *x, const uint16_t *w_gate,
 int moe_topk_from_logits(const moe_shape *shape, const float *logits, int32_t *topk_idx,
                          float *topk_w, void *stream);
 
-/* Dispatch [N][CF][TD][PL][M][DP]: histogram n_e, capacity, positions,
+/* Dispatch [N][CF][TD][PL][M][DP][F8]: histogram n_e, capacity, positions,
  * slots and the send buffer.
  *   x             [T, d] bf16
  *   topk_idx      [T, k] int32 (entries outside [0, E), and repeats of an
@@ -157,7 +173,9 @@ int moe_topk_from_logits(const moe_shape *shape, const float *logits, int32_t *t
  *                 stats->invalid_index and dropped)
  *   topk_w        [T, k] fp32 gates (as moe_route writes them): read only by
  *                 drop policy 1 in capacity mode, may be NULL otherwise
- *   send_buf      [send_rows, d] bf16 out.  Expert e's kept rows are
+ *   send_buf      [send_rows, d] out: bf16, or E4M3 codes under FP8 dispatch
+ *                 (the row of a kept assignment is its token's row, quantized
+ *                 with that row's scale).  Expert e's kept rows are
  *                 [expert_offset[e], expert_offset[e] + expert_kept[e]), in
  *                 ascending token order; capacity mode gives expert e the
  *                 rows [e*C, (e+1)*C) and zero-fills the pad rows; when
@@ -166,6 +184,8 @@ int moe_topk_from_logits(const moe_shape *shape, const float *logits, int32_t *t
  *                 are in ascending order, so rank r's chunk -- what the
  *                 dispatch all-to-all sends to rank r -- is rows
  *                 [expert_offset[r*E/D], expert_offset[(r+1)*E/D]).
+ *   send_scale    [send_rows] fp32 out under FP8 dispatch (pad rows: 0), may
+ *                 be NULL otherwise
  *   slot          [T, k] int32 out: send_buf row of assignment (t, s), or -1
  *                 if dropped
  *   expert_count  [E] int32 out: n_e, assignments routed to expert e
@@ -175,20 +195,23 @@ int moe_topk_from_logits(const moe_shape *shape, const float *logits, int32_t *t
  *   stats         one moe_stats, device memory, out
  *   workspace     device, >= moe_query's size */
 int moe_dispatch(const moe_shape *shape, const uint16_t *x, const int32_t *topk_idx,
-                 const float *topk_w, uint16_t *send_buf, int32_t *slot, int32_t *expert_count, int32_t *expert_kept,
+                 const float *topk_w, void *send_buf, float *send_scale, int32_t *slot, int32_t *expert_count, int32_t *expert_kept,
                  int32_t *expert_offset, int32_t *rank_rows, moe_stats *stats, void *workspace,
                  size_t workspace_bytes, void *stream);
 
 /* Expert FFN [M]: for every expert e, on its kept rows X_e of send_buf,
  *   h = bf16(SiLU(X_e W1_e^T) * (X_e W3_e^T)),  out = bf16(h W2_e^T),
  * SiLU(z) = z / (1 + exp(-z)), fp32 accumulation on bf16 matrix cores.
- *   send_buf       [send_rows, d] bf16
+ *   send_buf       [send_rows, d] bf16, or E4M3 codes under FP8 dispatch
+ *   send_scale     [send_rows] fp32 row scales under FP8 dispatch, may be
+ *                  NULL otherwise; the expert's input row is code * scale
  *   expert_offset  [E+1] int32, expert_kept [E] int32 (as moe_dispatch
  *                  writes them; kept rows must lie inside send_buf)
  *   w1, w3         [E, H, d] bf16;  w2 [E, d, H] bf16
  *   expert_out     [send_rows, d] bf16 out; only kept rows are written
  *   workspace      device, >= moe_query's size (holds h) */
-int moe_expert_ffn(const moe_shape *shape, const uint16_t *send_buf, const int32_t *expert_offset,
+int moe_expert_ffn(const moe_shape *shape, const void *send_buf, const float *send_scale,
+                   const int32_t *expert_offset,
                    const int32_t *expert_kept, const uint16_t *w1, const uint16_t *w3,
                    const uint16_t *w2, uint16_t *expert_out, void *workspace,
                    size_t workspace_bytes, void *stream);
@@ -199,7 +222,7 @@ int moe_expert_ffn(const moe_shape *shape, const uint16_t *send_buf, const int32
  *   of send_buf; only kept rows are written.
  * moe_expert_down:     expert_out = bf16(h W2_e^T) on the same rows.
  * Arguments as in moe_expert_ffn; neither needs a workspace. */
-int moe_expert_gate_up(const moe_shape *shape, const uint16_t *send_buf,
+int moe_expert_gate_up(const moe_shape *shape, const void *send_buf, const float *send_scale,
                        const int32_t *expert_offset, const int32_t *expert_kept,
                        const uint16_t *w1, const uint16_t *w3, uint16_t *h, void *stream);
 int moe_expert_down(const moe_shape *shape, const uint16_t *h, const int32_t *expert_offset,
@@ -220,10 +243,20 @@ int moe_combine(const moe_shape *shape, const uint16_t *expert_out, const int32_
 int moe_layer_fwd(const moe_shape *shape, const uint16_t *x, const uint16_t *w_gate,
                   const float *logit_bias, const uint16_t *w1, const uint16_t *w3,
                   const uint16_t *w2, uint16_t *y, float *logits_out, int32_t *topk_idx,
-                  float *topk_w, uint16_t *send_buf, int32_t *slot, int32_t *expert_count,
+                  float *topk_w, void *send_buf, float *send_scale, int32_t *slot,
+                  int32_t *expert_count,
                   int32_t *expert_kept, int32_t *expert_offset, int32_t *rank_rows,
                   moe_stats *stats, uint16_t *expert_out, void *workspace,
                   size_t workspace_bytes, void *stream);
+
+/* Diagnostic decode of FP8 dispatch rows [F8]: out[r, i] = bf16(value of
+ * E4M3 code codes[r*d + i] * scales[r]), with the product rounded to fp32
+ * then to bf16 (nearest even); exact when every scale is a power of two.
+ * It uses the same decode as the expert GEMM.
+ *   codes   [rows, d] E4M3 (device); scales [rows] fp32 (device)
+ *   rows >= 0; d > 0, d % 16 == 0;  out [rows, d] bf16 (device) */
+int moe_fp8_rows_to_bf16(const void *codes, const float *scales, int64_t rows, int32_t d,
+                         uint16_t *out, void *stream);
 
 /* Static string naming a status code (never NULL). */
 const char *moe_status_str(int status);

@@ -87,6 +87,7 @@ def test_query_workspace_grows_only_for_gate_order_drops():
     (dict(drop_policy=2), api.MOE_EINVAL),
     (dict(drop_policy=-1), api.MOE_EINVAL),
     (dict(min_capacity=-1), api.MOE_EINVAL),
+    (dict(dispatch_fp8=2), api.MOE_EINVAL),
     (dict(capacity_factor=1e12), api.MOE_EUNSUPPORTED),  # E*C does not fit int32 rows
 ])
 def test_query_rejects_bad_shapes(kw, status):
@@ -113,25 +114,35 @@ def test_entry_points_reject_null_and_misaligned_pointers():
     assert _raw("moe_route", S, mis, good, nul, nul, good, good, good, 1 << 30, nul) == api.MOE_EINVAL
     assert _raw("moe_route", S, good, good, mis, nul, good, good, good, 1 << 30, nul) == api.MOE_EINVAL
     assert _raw("moe_topk_from_logits", S, good, nul, good, nul) == api.MOE_EINVAL
-    args = [good] * 10   # x, topk_idx, topk_w, send_buf, slot, ..., stats
-    args[4] = nul        # slot is required
+    args = [good] * 11   # x, topk_idx, topk_w, send_buf, send_scale, slot, ..., stats
+    args[5] = nul        # slot is required
     assert _raw("moe_dispatch", S, *args, good, 1 << 30, nul) == api.MOE_EINVAL
-    args = [good] * 10
+    args = [good] * 11
     args[2] = mis        # topk_w is optional under drop policy 0, but must be aligned
     assert _raw("moe_dispatch", S, *args, good, 1 << 30, nul) == api.MOE_EINVAL
     s1 = api.Shape(T=256, d=512, E=8, k=2, H=1024, D=2, capacity_factor=1.25,
                    drop_policy=1).c()
-    args = [good] * 10
+    args = [good] * 11
     args[2] = nul        # drop policy 1 needs the gates
     assert _raw("moe_dispatch", ctypes.byref(s1), *args, good, 1 << 30, nul) == api.MOE_EINVAL
-    assert _raw("moe_expert_ffn", S, good, good, good, good, good, mis, good, good, 1 << 30,
+    s8 = api.Shape(T=256, d=512, E=8, k=2, H=1024, D=2, capacity_factor=1.25,
+                   dispatch_fp8=1).c()
+    args = [good] * 11
+    args[4] = nul        # FP8 dispatch needs the row scales
+    assert _raw("moe_dispatch", ctypes.byref(s8), *args, good, 1 << 30, nul) == api.MOE_EINVAL
+    assert _raw("moe_expert_gate_up", ctypes.byref(s8), good, nul, good, good, good, good, good,
                 nul) == api.MOE_EINVAL
+    assert _raw("moe_fp8_rows_to_bf16", good, good, 4, 24, good, nul) == api.MOE_EINVAL  # d % 16
+    assert _raw("moe_fp8_rows_to_bf16", good, good, -1, 32, good, nul) == api.MOE_EINVAL
+    assert _raw("moe_expert_ffn", S, good, nul, good, good, good, good, mis, good, good,
+                1 << 30, nul) == api.MOE_EINVAL
     assert _raw("moe_combine", S, good, good, good, nul, nul) == api.MOE_EINVAL
-    lay = [good] * 19
+    lay = [good] * 20
     lay[2] = nul   # optional bias
     lay[7] = nul   # optional logits_out
+    lay[11] = nul  # optional send_scale (bf16 dispatch)
     lay[10] = nul  # send_buf is required
-    assert _raw("moe_layer_fwd", S, *lay[:18], good, 1 << 30, nul) == api.MOE_EINVAL
+    assert _raw("moe_layer_fwd", S, *lay[:19], good, 1 << 30, nul) == api.MOE_EINVAL
 
 
 def test_entry_points_reject_small_or_missing_workspace():
@@ -145,8 +156,8 @@ def test_entry_points_reject_small_or_missing_workspace():
     assert _raw("moe_route", S, good, good, None, None, good, good, None, ws, None) == api.MOE_EWORKSPACE
     assert _raw("moe_route", S, good, good, None, None, good, good, P((1 << 20) + 16), ws,
                 None) == api.MOE_EWORKSPACE   # workspace must be 256-byte aligned
-    assert _raw("moe_dispatch", S, *([good] * 10), good, ws - 256, None) == api.MOE_EWORKSPACE
-    assert _raw("moe_expert_ffn", S, *([good] * 7), good, 0, None) == api.MOE_EWORKSPACE
+    assert _raw("moe_dispatch", S, *([good] * 11), good, ws - 256, None) == api.MOE_EWORKSPACE
+    assert _raw("moe_expert_ffn", S, *([good] * 8), good, 0, None) == api.MOE_EWORKSPACE
 
 
 def test_status_strings():

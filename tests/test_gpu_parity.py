@@ -115,7 +115,8 @@ def test_topk_on_identical_logits_with_ties(E, k):
 
 
 def _run_dispatch(shape, x, topk_idx, buf, topk_w=None):
-    api.moe_dispatch(shape, x, topk_idx, topk_w, buf.send_buf, buf.slot, buf.expert_count,
+    api.moe_dispatch(shape, x, topk_idx, topk_w, buf.send_buf, buf.send_scale, buf.slot,
+                     buf.expert_count,
                      buf.expert_kept, buf.expert_offset, buf.rank_rows, buf.stats, buf.workspace)
     torch.cuda.synchronize()
 
@@ -164,7 +165,7 @@ def test_expert_ffn_stage(case):
     off = _i32(ref["expert_offset"])
     kept = _i32(ref["expert_kept"])
     out = torch.zeros_like(send)
-    api.moe_expert_ffn(shape, send, off, kept, inp["w1"], inp["w3"], inp["w2"], out,
+    api.moe_expert_ffn(shape, send, None, off, kept, inp["w1"], inp["w3"], inp["w2"], out,
                        buf.workspace)
     torch.cuda.synchronize()
     got = bf16_bits(out)
@@ -314,6 +315,88 @@ def test_layer_fwd_by_gate_end_to_end(name):
     assert_bf16_close(t2f(buf.y), bits_to_f64(yref), "y")
 
 
+# ---------------------------------------------------------------------------
+# FP8 dispatch payload: E4M3 rows with fp32 row scales; combine stays bf16.
+# ---------------------------------------------------------------------------
+
+def test_fp8_decode_every_code():
+    """The expert GEMM's E4M3 -> bf16 decode, through the diagnostic entry
+    point: all 256 codes at unit and power-of-two scales, bit-exact."""
+    codes = np.arange(256, dtype=np.uint8).reshape(16, 16)
+    codes = np.concatenate([codes] * 4)                      # 64 rows
+    scales = (2.0 ** np.repeat([0, -3, 4, 0], 16)).astype(np.float32)
+    out = torch.empty(64, 16, dtype=torch.bfloat16, device=DEV)
+    api.moe_fp8_rows_to_bf16(torch.from_numpy(codes).to(DEV), _f32(scales), out)
+    torch.cuda.synchronize()
+    got = t2f(out)
+    want = oracle.fp8_values(codes) * scales[:, None].astype(np.float64)
+    nan = np.isnan(want)
+    assert np.all(np.isnan(got[nan]))
+    np.testing.assert_array_equal(got[~nan], want[~nan])
+    np.testing.assert_array_equal(np.signbit(got[~nan]), np.signbit(want[~nan]))
+
+
+def _fp8_shape(shape):
+    return dataclasses.replace(shape, dispatch_fp8=1)
+
+
+def test_dispatch_fp8_bit_exact(case):
+    cfg, inp, h, bias, ref, shape, buf = case
+    sh8 = _fp8_shape(shape)
+    b8 = api.LayerBuffers.allocate(sh8, DEV)
+    _run_dispatch(sh8, inp["x"], _i32(ref["topk_idx"]), b8)
+    r = oracle.dispatch(h["x"], ref["topk_idx"], T=cfg.T, d=cfg.d, E=cfg.E, D=cfg.D,
+                        my_rank=cfg.my_rank, cf=cfg.cf, fp8=True)
+    n = r["stats"]["send_rows"]
+    for key in ("expert_count", "expert_kept", "expert_offset", "rank_rows", "slot"):
+        np.testing.assert_array_equal(getattr(b8, key).cpu().numpy(), r[key], err_msg=key)
+    assert api.stats_dict(b8.stats) == r["stats"]
+    np.testing.assert_array_equal(b8.send_buf[:n].cpu().numpy(), r["send_buf"])
+    np.testing.assert_array_equal(b8.send_scale[:n].cpu().numpy(), r["send_scale"])
+
+
+def test_expert_ffn_fp8_stage(case):
+    cfg, inp, h, bias, ref, shape, buf = case
+    sh8 = _fp8_shape(shape)
+    r = oracle.dispatch(h["x"], ref["topk_idx"], T=cfg.T, d=cfg.d, E=cfg.E, D=cfg.D,
+                        my_rank=cfg.my_rank, cf=cfg.cf, fp8=True)
+    send = torch.from_numpy(r["send_buf"]).to(DEV)
+    scale = _f32(r["send_scale"])
+    out = torch.zeros(send.shape, dtype=torch.bfloat16, device=DEV)
+    ws = api.LayerBuffers.allocate(sh8, DEV).workspace
+    api.moe_expert_ffn(sh8, send, scale, _i32(r["expert_offset"]), _i32(r["expert_kept"]),
+                       inp["w1"], inp["w3"], inp["w2"], out, ws)
+    torch.cuda.synchronize()
+    got = bf16_bits(out)
+    want = oracle.expert_ffn_all(r["send_buf"], r["expert_offset"], r["expert_kept"], h["w1"],
+                                 h["w3"], h["w2"], send_scale=r["send_scale"])
+    for e in range(cfg.E):
+        lo, n = int(r["expert_offset"][e]), int(r["expert_kept"][e])
+        if n:
+            assert_bf16_close(bits_to_f64(got[lo:lo + n]), bits_to_f64(want[lo:lo + n]),
+                              f"fp8 expert {e}")
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_layer_fwd_fp8_end_to_end(name):
+    cfg = SMALL[name].with_(dispatch_fp8=1)
+    inp = make_inputs(cfg, DEV)
+    h = _host(inp)
+    shape = api.Shape.from_config(cfg)
+    buf = api.LayerBuffers.allocate(shape, DEV)
+    api.moe_layer_fwd(shape, inp["x"], inp["w_gate"], inp["bias"], inp["w1"], inp["w3"],
+                      inp["w2"], buf)
+    torch.cuda.synchronize()
+    idx, w = buf.topk_idx.cpu().numpy(), buf.topk_w.cpu().numpy()
+    r = oracle.dispatch(h["x"], idx, T=cfg.T, d=cfg.d, E=cfg.E, D=cfg.D, cf=cfg.cf, fp8=True)
+    n = r["stats"]["send_rows"]
+    np.testing.assert_array_equal(buf.send_buf[:n].cpu().numpy(), r["send_buf"])
+    eo = oracle.expert_ffn_all(r["send_buf"], r["expert_offset"], r["expert_kept"], h["w1"],
+                               h["w3"], h["w2"], send_scale=r["send_scale"])
+    yref = oracle.combine(eo, r["slot"], w)
+    assert_bf16_close(t2f(buf.y), bits_to_f64(yref), "y (fp8 dispatch)")
+
+
 @pytest.mark.parametrize("k", [2, 8])
 def test_identity_experts_round_trip_on_gpu(k):
     """Dispatch then combine with identity experts and nothing dropped gives x
@@ -359,11 +442,18 @@ def _expert_weights(inp, e):
     return (bf16_bits(inp["w1"][e]), bf16_bits(inp["w3"][e]), bf16_bits(inp["w2"][e]))
 
 
+FULL_VARIANTS = {
+    "skewed_by_gate": CONFIGS["skewed"].with_(drop_policy=1),
+    "dsv3_prefill_fp8": CONFIGS["dsv3_prefill"].with_(dispatch_fp8=1),
+    "mixtral_fp8": CONFIGS["mixtral"].with_(dispatch_fp8=1),
+}
+
+
 @pytest.mark.parametrize("name", ["mixtral", "dsv3_prefill", "dsv3_decode", "skewed",
-                                  "skewed_by_gate"])
+                                  "skewed_by_gate", "dsv3_prefill_fp8", "mixtral_fp8"])
 def test_full_size_config(name):
-    cfg = (CONFIGS["skewed"].with_(drop_policy=1) if name == "skewed_by_gate"
-           else CONFIGS[name])
+    cfg = FULL_VARIANTS.get(name) or CONFIGS[name]
+    fp8 = bool(cfg.dispatch_fp8)
     print(f"\n[full {name}] T={cfg.T} d={cfg.d} E={cfg.E} k={cfg.k} H={cfg.H}", flush=True)
     inp = make_inputs(cfg, DEV)
     shape = api.Shape.from_config(cfg)
@@ -392,7 +482,8 @@ def test_full_size_config(name):
     assert not bad.any()
     # accounting and layout: bit-exact on the GPU's routing (send buffer sampled)
     r = oracle.dispatch(x, idx, T=cfg.T, d=cfg.d, E=cfg.E, D=cfg.D, my_rank=cfg.my_rank,
-                        cf=cfg.cf, with_send_buf=False, drop_policy=cfg.drop_policy, topk_w=w)
+                        cf=cfg.cf, with_send_buf=False, drop_policy=cfg.drop_policy, topk_w=w,
+                        fp8=fp8)
     for key in ("expert_count", "expert_kept", "expert_offset", "rank_rows", "slot"):
         np.testing.assert_array_equal(getattr(buf, key).cpu().numpy(), r[key], err_msg=key)
     st = api.stats_dict(buf.stats)
@@ -401,8 +492,15 @@ def test_full_size_config(name):
     rng = np.random.default_rng(0)
     slot = r["slot"]
     for t in rng.choice(cfg.T, min(cfg.T, 64), replace=False):
+        if fp8:
+            q, sc = oracle.fp8_quantize_rows(x[t:t + 1])
         for s in range(cfg.k):
-            if slot[t, s] >= 0:
+            if slot[t, s] < 0:
+                continue
+            if fp8:
+                np.testing.assert_array_equal(buf.send_buf[slot[t, s]].cpu().numpy(), q[0])
+                assert buf.send_scale[slot[t, s]].item() == sc[0]
+            else:
                 assert torch.equal(buf.send_buf[slot[t, s]].view(torch.int16),
                                    inp["x"][t].view(torch.int16))
     if r["stats"]["capacity"] > 0:
@@ -410,10 +508,11 @@ def test_full_size_config(name):
         C = r["stats"]["capacity"]
         for e in rng.choice(cfg.E, min(cfg.E, 8), replace=False):
             pads = buf.send_buf[e * C + kept[e]:(e + 1) * C]
-            assert torch.count_nonzero(pads.view(torch.int16)) == 0
+            assert torch.count_nonzero(pads) == 0
     # expert FFN: sampled experts (busiest, quietest non-empty, one more), sampled rows
     eo = bf16_bits(buf.expert_out)
-    sb = bf16_bits(buf.send_buf)
+    sb = buf.send_buf.cpu().numpy() if fp8 else bf16_bits(buf.send_buf)
+    ss = buf.send_scale.cpu().numpy() if fp8 else None
     kept = r["expert_kept"]
     nz = np.nonzero(kept)[0]
     experts = sorted({int(nz[np.argmax(kept[nz])]), int(nz[np.argmin(kept[nz])]),
@@ -422,7 +521,8 @@ def test_full_size_config(name):
     for e in experts:
         lo, n = int(r["expert_offset"][e]), int(kept[e])
         rows = np.sort(rng.choice(n, min(n, max_rows), replace=False)) + lo
-        got = oracle.expert_ffn(sb[rows], *_expert_weights(inp, e))
+        got = (oracle.expert_ffn_fp8(sb[rows], ss[rows], *_expert_weights(inp, e)) if fp8
+               else oracle.expert_ffn(sb[rows], *_expert_weights(inp, e)))
         assert_bf16_close(bits_to_f64(eo[rows]), bits_to_f64(got), f"{name} expert {e}")
     # combine: sampled tokens on the GPU's expert outputs (stage parity)
     toks = np.sort(rng.choice(cfg.T, min(cfg.T, 256), replace=False))
@@ -436,7 +536,12 @@ def test_full_size_config(name):
             if slot[t, s] < 0:
                 continue
             e = int(idx[t, s])
-            acc.append((float(w[t, s]), oracle.expert_ffn(x[t:t + 1], *_expert_weights(inp, e))))
+            if fp8:
+                q, sc = oracle.fp8_quantize_rows(x[t:t + 1])
+                o = oracle.expert_ffn_fp8(q, sc, *_expert_weights(inp, e))
+            else:
+                o = oracle.expert_ffn(x[t:t + 1], *_expert_weights(inp, e))
+            acc.append((float(w[t, s]), o))
         yt = np.zeros(cfg.d)
         for g, o in acc:
             yt += g * bits_to_f64(o[0])
@@ -471,7 +576,7 @@ def test_rank_local_expert_share():
     loc = api.Shape(cfg.T, cfg.d, el, cfg.k, cfg.H, 1, 0, INF)
     h = torch.empty(buf.send_buf.shape[0], cfg.H, dtype=torch.bfloat16, device=DEV)
     out = torch.full(buf.send_buf.shape, 0x1234, dtype=torch.int16, device=DEV)
-    api.moe_expert_gate_up(loc, buf.send_buf, buf.expert_offset, buf.expert_kept, w["w1"],
+    api.moe_expert_gate_up(loc, buf.send_buf, None, buf.expert_offset, buf.expert_kept, w["w1"],
                            w["w3"], h)
     api.moe_expert_down(loc, h, buf.expert_offset, buf.expert_kept, w["w2"],
                         out.view(torch.bfloat16))
