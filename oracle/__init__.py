@@ -77,6 +77,8 @@ def _load():
     lib.oracle_logits.restype = None
     lib.oracle_topk.argtypes = [i32, i32, i32, P, P, P, P]
     lib.oracle_topk.restype = None
+    lib.oracle_topk_grouped.argtypes = [i32, i32, i32, i32, i32, P, P, P, P]
+    lib.oracle_topk_grouped.restype = None
     lib.oracle_capacity.argtypes = [i32, i32, i32, ctypes.c_double, i32]
     lib.oracle_capacity.restype = ctypes.c_int64
     lib.oracle_dispatch.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.c_double, i32, i32,
@@ -92,7 +94,7 @@ def _load():
     lib.oracle_dispatch.restype = ctypes.c_int
     lib.oracle_expert_ffn.argtypes = [i32, i32, i32, P, P, P, P, P]
     lib.oracle_expert_ffn.restype = None
-    lib.oracle_combine.argtypes = [i32, i32, i32, P, P, P, P]
+    lib.oracle_combine.argtypes = [i32, i32, i32, P, P, P, P, P]
     lib.oracle_combine.restype = None
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
@@ -133,15 +135,21 @@ def logits(x: np.ndarray, w_gate: np.ndarray, bias: np.ndarray | None = None) ->
     return out
 
 
-def topk(lg: np.ndarray, k: int):
-    """KeepTopK + softmax on fp32 logits [T, E] -> (idx int32 [T,k], w fp32 [T,k], gap f64 [T])."""
+def topk(lg: np.ndarray, k: int, groups: int = 1, group_limit: int = 1):
+    """KeepTopK + softmax on fp32 logits [T, E] -> (idx int32 [T,k], w fp32 [T,k], gap f64 [T]).
+
+    groups > 1 and group_limit < groups: only the experts of the group_limit
+    groups with the largest best logit may be chosen (group-limited routing)."""
     lg = _c(lg, np.float32)
     T, E = lg.shape
-    assert 1 <= k <= E
+    assert 1 <= k <= E and E <= 4096 and groups <= 1024
+    if groups > 1 and group_limit < groups:
+        assert E % groups == 0 and k <= group_limit * (E // groups)
     idx = np.empty((T, k), np.int32)
     w = np.empty((T, k), np.float32)
     gap = np.empty((T,), np.float64)
-    _load().oracle_topk(T, E, k, _ptr(lg), _ptr(idx), _ptr(w), _ptr(gap))
+    _load().oracle_topk_grouped(T, E, k, groups, group_limit, _ptr(lg), _ptr(idx), _ptr(w),
+                                _ptr(gap))
     return idx, w, gap
 
 
@@ -255,8 +263,10 @@ def expert_ffn_fp8(codes: np.ndarray, scales: np.ndarray, w1: np.ndarray, w3: np
     return out
 
 
-def combine(expert_out: np.ndarray, slot: np.ndarray, topk_w: np.ndarray) -> np.ndarray:
-    """y[t] = bf16(sum_s G[t,s] * expert_out[slot[t,s]]) over kept s; dropped -> 0."""
+def combine(expert_out: np.ndarray, slot: np.ndarray, topk_w: np.ndarray,
+            shared_out: np.ndarray | None = None) -> np.ndarray:
+    """y[t] = bf16(sum_s G[t,s] * expert_out[slot[t,s]] + shared_out[t]) over kept s;
+    dropped -> 0; shared_out (the shared expert's [T, d] output) is optional."""
     expert_out = _c(expert_out, np.uint16)
     slot = _c(slot, np.int32)
     topk_w = _c(topk_w, np.float32)
@@ -264,8 +274,12 @@ def combine(expert_out: np.ndarray, slot: np.ndarray, topk_w: np.ndarray) -> np.
     d = expert_out.shape[1]
     assert topk_w.shape == (T, k)
     assert slot.max(initial=-1) < expert_out.shape[0]
+    if shared_out is not None:
+        shared_out = _c(shared_out, np.uint16)
+        assert shared_out.shape == (T, d)
     y = np.empty((T, d), np.uint16)
-    _load().oracle_combine(T, d, k, _ptr(expert_out), _ptr(slot), _ptr(topk_w), _ptr(y))
+    _load().oracle_combine(T, d, k, _ptr(expert_out), _ptr(slot), _ptr(topk_w),
+                           _ptr(shared_out), _ptr(y))
     return y
 
 
@@ -289,15 +303,19 @@ def expert_ffn_all(send_buf: np.ndarray, expert_offset: np.ndarray, expert_kept:
 
 
 def layer_fwd(x, w_gate, w1, w3, w2, *, k: int, D: int, cf: float, my_rank: int = 0,
-              bias=None, drop_policy: int = 0, min_capacity: int = 0, fp8: bool = False) -> dict:
-    """The whole forward pass, stage by stage, returning every intermediate."""
+              bias=None, drop_policy: int = 0, min_capacity: int = 0, fp8: bool = False,
+              groups: int = 1, group_limit: int = 1, shared=None) -> dict:
+    """The whole forward pass, stage by stage, returning every intermediate.
+    shared: (w1s, w3s, w2s) of the shared expert, applied to every token."""
     T, d = x.shape
     E = w_gate.shape[1]
     lg = logits(x, w_gate, bias)
-    idx, w, gap = topk(lg, k)
+    idx, w, gap = topk(lg, k, groups, group_limit)
     disp = dispatch(x, idx, T=T, d=d, E=E, D=D, my_rank=my_rank, cf=cf,
                     drop_policy=drop_policy, topk_w=w, min_capacity=min_capacity, fp8=fp8)
     eo = expert_ffn_all(disp["send_buf"], disp["expert_offset"], disp["expert_kept"], w1, w3, w2,
                         send_scale=disp["send_scale"])
-    y = combine(eo, disp["slot"], w)
-    return dict(logits=lg, topk_idx=idx, topk_w=w, gap=gap, expert_out=eo, y=y, **disp)
+    so = expert_ffn(x, *shared) if shared is not None else None
+    y = combine(eo, disp["slot"], w, so)
+    return dict(logits=lg, topk_idx=idx, topk_w=w, gap=gap, expert_out=eo, y=y, shared_out=so,
+                **disp)

@@ -47,6 +47,13 @@
  *        rows in FP8 instead of BF16, halving the dispatch row, while the
  *        combine path may stay wider; quantization scale tensors travel
  *        with it.
+ *   [GL] same page, the traffic bounds: DeepSeek-V3 dispatches each token
+ *        to at most 4 nodes, which Megatron exposes as group-limited
+ *        routing.
+ *   [SE] same page, the token-assignment worksheet: the shared expert is
+ *        replicated on every EP rank (compute and memory, no dispatch
+ *        traffic) in Megatron, or routed as a ninth expert in DeepSeek's
+ *        decode deployment.
  *
  * Readings taken where the pages are silent (each also listed in the design
  * notes): eps = 0 at inference; an optional per-expert logit bias b is added
@@ -64,7 +71,12 @@
  * element encoded as E4M3(x/s) with x/s computed in fp32, rounded to the
  * nearest E4M3 value (ties to even), saturated at +-448, sign kept (so -0
  * and tiny negatives give 0x80); the expert sees code value * s, and the
- * combine stays bf16; gates are not
+ * combine stays bf16; group-limited routing [GL] splits the E experts into
+ * G equal contiguous groups, scores each group by its largest logit for
+ * the token, keeps the M best groups (ties to the lower group index) and
+ * runs KeepTopK over their experts only; the shared expert [SE] follows
+ * the replicated convention: a SwiGLU of every token, bf16 output, added
+ * with weight 1 in the combine; gates are not
  * renormalised after a drop; a routing entry outside [0, E) or repeating
  * an expert already listed for its token is invalid (counted, dropped),
  * since KeepTopK yields k distinct experts; the expert is SwiGLU, W2 (SiLU(W1 x) * (W3 x))
@@ -138,27 +150,65 @@ void oracle_logits(int T, int d, int E, const uint16_t *x, const uint16_t *w_gat
 }
 
 /* ------------------------------------------------------------------ */
-/* Step 2: G = Softmax(KeepTopK(H, k)).                      [G]       */
-/* KeepTopK by rank: rank(e) = #{e' : h_e' > h_e, or h_e' == h_e and   */
-/* e' < e}.  Expert e is kept iff rank(e) < k; it is written to output */
-/* position rank(e).  The softmax over the kept logits equals the      */
-/* softmax over the KeepTopK vector, whose other entries are -inf and  */
-/* contribute exp(-inf) = 0.  gap[t] = h_(k) - h_(k+1), the distance   */
-/* between the last kept and the first rejected order statistic        */
-/* (+inf when k == E).                                                 */
+/* Step 2: G = Softmax(KeepTopK(H, k)).                  [G][GL]       */
+/* Group limit (G groups of E/G contiguous experts, at most M groups   */
+/* per token; G <= 1 or M >= G means no limit): group g's score is the */
+/* largest logit of its experts; group rank(g) = #{g' : s_g' > s_g, or */
+/* s_g' == s_g and g' < g}; the experts of groups with rank < M are    */
+/* allowed, the others act as -inf.                                     */
+/* KeepTopK by rank among allowed experts: rank(e) = #{allowed e' :    */
+/* h_e' > h_e, or h_e' == h_e and e' < e}.  Expert e is kept iff       */
+/* rank(e) < k; it is written to output position rank(e).  The softmax */
+/* over the kept logits equals the softmax over the KeepTopK vector,   */
+/* whose other entries are -inf and contribute exp(-inf) = 0.          */
+/* gap[t] = h_(k) - h_(k+1) among the allowed experts (+inf when all   */
+/* are kept), and under a group limit also at most s_(M) - s_(M+1):    */
+/* the distance to the nearest change of the selection.                */
 /* ------------------------------------------------------------------ */
-void oracle_topk(int T, int E, int k, const float *logits, int32_t *topk_idx,
-                 float *topk_w, double *gap)
+void oracle_topk_grouped(int T, int E, int k, int G, int M, const float *logits,
+                         int32_t *topk_idx, float *topk_w, double *gap)
 {
+    const int limited = G > 1 && M < G;
+    const int per = limited ? E / G : E;
 #pragma omp parallel for schedule(static)
     for (int t = 0; t < T; ++t) {
         const float *h = logits + (size_t)t * E;
         double first_rejected = -INFINITY;
         int have_rejected = 0;
+        double group_gap = INFINITY;
+        /* allowed[e]: expert e's group is among the M best */
+        char allowed[4096];
+        for (int e = 0; e < E; ++e)
+            allowed[e] = 1;
+        if (limited) {
+            float score[1024];
+            for (int g = 0; g < G; ++g) {
+                score[g] = h[g * per];
+                for (int e = g * per + 1; e < (g + 1) * per; ++e)
+                    if (h[e] > score[g])
+                        score[g] = h[e];
+            }
+            double last_group = INFINITY, first_out = -INFINITY;
+            for (int g = 0; g < G; ++g) {
+                int grank = 0;
+                for (int g2 = 0; g2 < G; ++g2)
+                    if (score[g2] > score[g] || (score[g2] == score[g] && g2 < g))
+                        ++grank;
+                for (int e = g * per; e < (g + 1) * per; ++e)
+                    allowed[e] = grank < M;
+                if (grank == M - 1)
+                    last_group = score[g];
+                if (grank == M)
+                    first_out = score[g];
+            }
+            group_gap = last_group - first_out;
+        }
         for (int e = 0; e < E; ++e) {
+            if (!allowed[e])
+                continue;
             int rank = 0;
             for (int e2 = 0; e2 < E; ++e2)
-                if (h[e2] > h[e] || (h[e2] == h[e] && e2 < e))
+                if (allowed[e2] && (h[e2] > h[e] || (h[e2] == h[e] && e2 < e)))
                     ++rank;
             if (rank < k) {
                 topk_idx[(size_t)t * k + rank] = e;
@@ -178,9 +228,16 @@ void oracle_topk(int T, int E, int k, const float *logits, int32_t *topk_idx,
                 (float)(exp((double)h[topk_idx[(size_t)t * k + s]] - hmax) / denom);
         if (gap) {
             double last_kept = (double)h[topk_idx[(size_t)t * k + k - 1]];
-            gap[t] = have_rejected ? last_kept - first_rejected : INFINITY;
+            double g_e = have_rejected ? last_kept - first_rejected : INFINITY;
+            gap[t] = g_e < group_gap ? g_e : group_gap;
         }
     }
+}
+
+void oracle_topk(int T, int E, int k, const float *logits, int32_t *topk_idx,
+                 float *topk_w, double *gap)
+{
+    oracle_topk_grouped(T, E, k, 1, 1, logits, topk_idx, topk_w, gap);
 }
 
 /* ------------------------------------------------------------------ */
@@ -532,13 +589,15 @@ void oracle_expert_ffn_fp8(int n, int d, int H, const uint8_t *codes, const floa
 }
 
 /* ------------------------------------------------------------------ */
-/* Step 6: combine.                                     [G][CA][TD]    */
-/* y[t] = bf16( sum over kept s, in rank order, of G[t,s] * O[slot] ). */
+/* Step 6: combine.                                 [G][CA][TD][SE]    */
+/* y[t] = bf16( sum over kept s, in rank order, of G[t,s] * O[slot]    */
+/*              + S[t] ), S the shared expert's output (or nothing).   */
 /* A dropped assignment (slot < 0) adds nothing; the residual is the   */
-/* caller's.  expert_out [*, d] bf16, slot/topk_w [T, k], y [T, d].    */
+/* caller's.  expert_out [*, d] bf16, slot/topk_w [T, k], shared_out   */
+/* [T, d] bf16 or NULL, y [T, d].                                      */
 /* ------------------------------------------------------------------ */
 void oracle_combine(int T, int d, int k, const uint16_t *expert_out, const int32_t *slot,
-                    const float *topk_w, uint16_t *y)
+                    const float *topk_w, const uint16_t *shared_out, uint16_t *y)
 {
 #pragma omp parallel for schedule(static)
     for (int t = 0; t < T; ++t) {
@@ -551,6 +610,8 @@ void oracle_combine(int T, int d, int k, const uint16_t *expert_out, const int32
                 acc += (double)topk_w[(size_t)t * k + s] *
                        bf16_value(expert_out[(size_t)sl * d + m]);
             }
+            if (shared_out)
+                acc += bf16_value(shared_out[(size_t)t * d + m]);
             y[(size_t)t * d + m] = oracle_bf16_from_double(acc);
         }
     }

@@ -664,3 +664,101 @@ def test_fp8_decode_example_page_bytes(sizing):
     assert st["kept"] == p["vectors"]
     assert abs(st["dispatch_bytes"] / 1e6 - p["printed_MB"]) <= p["printed_precision_MB"]
     assert abs(st["combine_bytes"] / 1e6 - sizing["decode_combine"]["printed_MB"]) <= 0.05
+
+
+# ---------------------------------------------------------------------------
+# Group-limited routing ("MoE Expert Parallelism Sizing: Traffic, Capacity,
+# Fabric", traffic bounds: at most 4 nodes per token, Megatron's group-limited
+# routing) and the replicated shared expert (same page, token-assignment
+# worksheet).  Group score: the group's largest logit.
+# ---------------------------------------------------------------------------
+
+def _small_int_logits(T, E, seed):
+    rng = np.random.default_rng(seed)
+    return rng.integers(-4, 5, (T, E)).astype(np.float32)   # many exact ties
+
+
+@pytest.mark.parametrize("E,k,G,M", [(16, 4, 4, 4), (16, 4, 1, 1), (12, 3, 3, 5)])
+def test_group_limit_that_does_not_bind_is_plain_topk(E, k, G, M):
+    lg = _small_int_logits(200, E, E + k)
+    a = oracle.topk(lg, k)
+    b = oracle.topk(lg, k, G, M)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+
+
+@pytest.mark.parametrize("E,k", [(8, 2), (16, 5)])
+def test_one_expert_per_group_with_k_groups_is_plain_topk(E, k):
+    lg = _small_int_logits(300, E, 3 * E + k)
+    a_idx, a_w, _ = oracle.topk(lg, k)
+    b_idx, b_w, _ = oracle.topk(lg, k, E, k)
+    np.testing.assert_array_equal(a_idx, b_idx)
+    np.testing.assert_array_equal(a_w, b_w)
+
+
+@pytest.mark.parametrize("E,k,G,M,seed", [(16, 4, 4, 2, 1), (32, 8, 8, 4, 2), (12, 3, 6, 2, 3),
+                                          (64, 6, 8, 3, 4)])
+def test_group_limited_selection_brute_force(E, k, G, M, seed):
+    T = 400
+    lg = _small_int_logits(T, E, seed)
+    if seed % 2 == 0:
+        lg = lg + np.random.default_rng(seed).standard_normal((T, E)).astype(np.float32) * 0.3
+    idx, w, gap = oracle.topk(lg, k, G, M)
+    per = E // G
+    for t in range(T):
+        score = lg[t].reshape(G, per).max(axis=1)
+        groups = sorted(range(G), key=lambda g: (-score[g], g))[:M]
+        allowed = [e for e in range(E) if e // per in groups]
+        want = sorted(allowed, key=lambda e: (-lg[t, e], e))[:k]
+        assert list(idx[t]) == want, (t, list(idx[t]), want)
+        assert len({e // per for e in idx[t]}) <= M
+        z = np.exp(lg[t, want].astype(np.float64) - lg[t, want].max())
+        np.testing.assert_allclose(w[t], z / z.sum(), rtol=1e-6)
+
+
+def test_group_limited_gap_sees_group_near_ties():
+    # groups {0,1} and {2,3}: their best logits differ by 1e-6, far below the
+    # experts' own spacing, so the reported gap is the groups' distance
+    lg = np.array([[1.0, -3.0, 1.0 - 1e-6, -5.0]], np.float32)
+    _, _, gap = oracle.topk(lg, 1, 2, 1)
+    assert 0 < gap[0] <= 2e-6
+    _, _, gap_plain = oracle.topk(lg, 1)
+    assert gap_plain[0] == gap[0]          # without a limit it is the same boundary here
+    lg = np.array([[1.0, 0.9, 1.0 - 1e-6, -5.0]], np.float32)
+    idx, _, gap = oracle.topk(lg, 2, 2, 1)
+    assert list(idx[0]) == [0, 1] and gap[0] <= 2e-6   # expert 2 would win without the limit
+
+
+def test_combine_with_shared_expert_closed_forms():
+    rng = np.random.default_rng(21)
+    T, d, k = 40, 32, 2
+    x = bf16_bits(torch.randn(T, d).to(torch.bfloat16))
+    slot = np.arange(T * k, dtype=np.int32).reshape(T, k)
+    eo = np.repeat(x, k, axis=0)               # identity experts: every row is its token's x
+    w = rng.random((T, k)).astype(np.float32)
+    w /= w.sum(axis=1, keepdims=True).astype(np.float32)
+    # all dropped: y is the shared expert's output, bit for bit
+    y = oracle.combine(eo, np.full((T, k), -1, np.int32), w, shared_out=x)
+    np.testing.assert_array_equal(y, x)
+    # weights (1, 0) and the shared expert equal to x: y = bf16(2x), exact
+    w1 = np.zeros((T, k), np.float32)
+    w1[:, 0] = 1.0
+    y = oracle.combine(eo, slot, w1, shared_out=x)
+    two_x = bf16_bits((torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).float() * 2)
+                      .to(torch.bfloat16))
+    np.testing.assert_array_equal(y, two_x)
+    # no shared expert given: unchanged routed sum
+    np.testing.assert_array_equal(oracle.combine(eo, slot, w), oracle.combine(eo, slot, w, None))
+
+
+def test_layer_fwd_with_shared_expert_adds_dense_swiglu():
+    cfg = CONFIGS["tiny"].with_(T=24)
+    inp = make_inputs(cfg, "cpu")
+    h = {n: bf16_bits(v) for n, v in inp.items() if v is not None}
+    ws = [bf16_bits((torch.randn(*s) * 0.05).to(torch.bfloat16))
+          for s in ((96, cfg.d), (96, cfg.d), (cfg.d, 96))]
+    r = oracle.layer_fwd(h["x"], h["w_gate"], h["w1"], h["w3"], h["w2"], k=cfg.k, D=cfg.D,
+                         cf=cfg.cf, shared=ws)
+    np.testing.assert_array_equal(r["shared_out"], oracle.expert_ffn(h["x"], *ws))
+    np.testing.assert_array_equal(r["y"], oracle.combine(r["expert_out"], r["slot"], r["topk_w"],
+                                                         r["shared_out"]))
