@@ -49,7 +49,10 @@ def stage_traffic(cfg, st, touched):
                         flops=4 * kept * d * H),
         "down": dict(bytes=touched * d * H * 2 + kept * H * 2 + kept * d * 2,
                      flops=2 * kept * d * H),
-        "combine": dict(bytes=kept * d * 2 + T * d * 2 + T * k * 8, flops=0),
+        "combine": dict(bytes=kept * d * 2 + T * d * 2 + T * k * 8
+                        + (T * d * 2 if cfg.shared_H else 0), flops=0),
+        "shared": dict(bytes=3 * cfg.shared_H * d * 2 + T * d * 2 * 2 + T * cfg.shared_H * 2 * 2,
+                       flops=6 * T * d * cfg.shared_H),
     }
 
 
@@ -86,6 +89,8 @@ def cpu_baseline(cfg, inp, budget_s):
     wg = bf16_bits(inp["w_gate"])
     bias = None if inp["bias"] is None else inp["bias"].cpu().numpy()
     experts = {}
+    shared = (tuple(bf16_bits(inp[n]) for n in ("w1s", "w3s", "w2s")) if cfg.shared_H
+              else None)
     batch = 16
     done, spent = 0, 0.0
     while done < cfg.T and spent < budget_s:
@@ -93,7 +98,7 @@ def cpu_baseline(cfg, inp, budget_s):
         tb = xb.shape[0]
         t0 = time.perf_counter()
         lg = oracle.logits(xb, wg, bias)
-        idx, w, _ = oracle.topk(lg, cfg.k)
+        idx, w, _ = oracle.topk(lg, cfg.k, cfg.n_groups, cfg.group_limit)
         r = oracle.dispatch(xb, idx, T=tb, d=cfg.d, E=cfg.E, D=cfg.D, cf=cfg.cf,
                             drop_policy=cfg.drop_policy, topk_w=w, min_capacity=cfg.min_capacity,
                             fp8=bool(cfg.dispatch_fp8))
@@ -106,7 +111,8 @@ def cpu_baseline(cfg, inp, budget_s):
         w1, w3, w2 = ({e: v[i] for e, v in experts.items()} for i in range(3))
         eo = oracle.expert_ffn_all(r["send_buf"], r["expert_offset"], r["expert_kept"],
                                    w1, w3, w2, send_scale=r["send_scale"])
-        oracle.combine(eo, r["slot"], w)
+        so = oracle.expert_ffn(xb, *shared) if shared else None
+        oracle.combine(eo, r["slot"], w, so)
         spent += time.perf_counter() - t0
         done += tb
         log(f"  cpu oracle: {done} tokens in {spent:.1f} s")
@@ -204,6 +210,12 @@ def main():
                     help="lower bound on the expert capacity (default: the workload's)")
     ap.add_argument("--dispatch-fp8", action="store_true",
                     help="dispatch payload as E4M3 rows with fp32 row scales (combine stays bf16)")
+    ap.add_argument("--groups", type=int, default=None, metavar="G",
+                    help="group-limited routing: G expert groups (with --group-limit)")
+    ap.add_argument("--group-limit", type=int, default=None, metavar="M",
+                    help="group-limited routing: at most M groups per token")
+    ap.add_argument("--shared-expert", type=int, default=None, metavar="H",
+                    help="add a replicated shared expert of SwiGLU hidden size H")
     ap.add_argument("--no-rank-local", action="store_true",
                     help="skip the expert-parallel rank-local GEMM measurement")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -226,6 +238,10 @@ def main():
         cfg = cfg.with_(min_capacity=args.min_capacity)
     if args.dispatch_fp8:
         cfg = cfg.with_(dispatch_fp8=1)
+    if args.groups is not None:
+        cfg = cfg.with_(n_groups=args.groups, group_limit=args.group_limit or 1)
+    if args.shared_expert is not None:
+        cfg = cfg.with_(shared_H=args.shared_expert)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     log(f"bench: {cfg.name} T={cfg.T} d={cfg.d} E={cfg.E} k={cfg.k} H={cfg.H} cf={cfg.cf}")
@@ -234,32 +250,42 @@ def main():
     buf = api.LayerBuffers.allocate(shape, dev, keep_logits=False)
     h = torch.empty(max(buf.send_buf.shape[0], 0), cfg.H, dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream()
-    stages = ["route", "dispatch", "gate_up", "down", "combine"]
+    stages = ["route", "dispatch", "gate_up", "down"]
+    if cfg.shared_H:
+        stages.append("shared")
+    stages.append("combine")
 
     def step(ev=None):
-        rec = (lambda i: ev[i].record(stream)) if ev else (lambda i: None)
-        rec(0)
+        marks = iter(range(len(stages) + 1))
+        rec = (lambda: ev[next(marks)].record(stream)) if ev else (lambda: None)
+        rec()
         api.moe_route(shape, inp["x"], inp["w_gate"], inp["bias"], None, buf.topk_idx,
                       buf.topk_w, buf.workspace, stream)
-        rec(1)
+        rec()
         api.moe_dispatch(shape, inp["x"], buf.topk_idx, buf.topk_w, buf.send_buf,
                          buf.send_scale, buf.slot, buf.expert_count, buf.expert_kept, buf.expert_offset, buf.rank_rows,
                          buf.stats, buf.workspace, stream)
-        rec(2)
+        rec()
         api.moe_expert_gate_up(shape, buf.send_buf, buf.send_scale, buf.expert_offset,
                                buf.expert_kept, inp["w1"], inp["w3"], h, stream)
-        rec(3)
+        rec()
         api.moe_expert_down(shape, h, buf.expert_offset, buf.expert_kept, inp["w2"],
                             buf.expert_out, stream)
-        rec(4)
-        api.moe_combine(shape, buf.expert_out, buf.slot, buf.topk_w, buf.y, stream)
-        rec(5)
+        rec()
+        if cfg.shared_H:
+            api.moe_shared_expert(shape, inp["x"], inp["w1s"], inp["w3s"], inp["w2s"],
+                                  buf.shared_out, buf.workspace, stream)
+            rec()
+        api.moe_combine(shape, buf.expert_out, buf.slot, buf.topk_w, buf.shared_out, buf.y,
+                        stream)
+        rec()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     log(f"bench: warmup {args.warmup} done")
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+              for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -318,6 +344,8 @@ def main():
         "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "E": cfg.E, "k": cfg.k,
                    "H": cfg.H, "capacity_factor": None if cfg.cf == float("inf") else cfg.cf,
                    "drop_policy": cfg.drop_policy, "min_capacity": cfg.min_capacity,
+                   "dispatch_fp8": cfg.dispatch_fp8, "n_groups": cfg.n_groups,
+                   "group_limit": cfg.group_limit, "shared_H": cfg.shared_H,
                    "D": cfg.D, "parallelism": "single GPU share (EP rank-local layout)"},
         "grouped_gemm": {"tflops": round(gemm_flops / gemm_s / 1e12, 1),
                          "mfma_util": round(gemm_flops / gemm_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),

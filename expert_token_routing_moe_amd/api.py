@@ -42,7 +42,8 @@ class moe_shape(ctypes.Structure):
         ("k", ctypes.c_int32), ("H", ctypes.c_int32), ("D", ctypes.c_int32),
         ("my_rank", ctypes.c_int32), ("drop_policy", ctypes.c_int32),
         ("min_capacity", ctypes.c_int32), ("dispatch_fp8", ctypes.c_int32),
-        ("capacity_factor", ctypes.c_double),
+        ("n_groups", ctypes.c_int32), ("group_limit", ctypes.c_int32),
+        ("shared_H", ctypes.c_int32), ("capacity_factor", ctypes.c_double),
     ]
 
 
@@ -68,8 +69,9 @@ def lib():
         "moe_expert_ffn": [S, P, P, P, P, P, P, P, P, P, SZ, P],
         "moe_expert_gate_up": [S, P, P, P, P, P, P, P, P],
         "moe_expert_down": [S, P, P, P, P, P, P],
-        "moe_combine": [S, P, P, P, P, P],
-        "moe_layer_fwd": [S] + [P] * 20 + [SZ, P],
+        "moe_combine": [S, P, P, P, P, P, P],
+        "moe_shared_expert": [S, P, P, P, P, P, P, SZ, P],
+        "moe_layer_fwd": [S] + [P] * 24 + [SZ, P],
         "moe_fp8_rows_to_bf16": [P, P, ctypes.c_int64, ctypes.c_int32, P, P],
     }
     for name, argtypes in sig.items():
@@ -102,16 +104,21 @@ class Shape:
     drop_policy: int = 0
     min_capacity: int = 0
     dispatch_fp8: int = 0
+    n_groups: int = 0
+    group_limit: int = 0
+    shared_H: int = 0
 
     def c(self) -> moe_shape:
         return moe_shape(self.T, self.d, self.E, self.k, self.H, self.D, self.my_rank,
                          self.drop_policy, self.min_capacity, self.dispatch_fp8,
+                         self.n_groups, self.group_limit, self.shared_H,
                          float(self.capacity_factor))
 
     @classmethod
     def from_config(cls, cfg) -> "Shape":
         return cls(cfg.T, cfg.d, cfg.E, cfg.k, cfg.H, cfg.D, cfg.my_rank, cfg.cf,
-                   cfg.drop_policy, cfg.min_capacity, cfg.dispatch_fp8)
+                   cfg.drop_policy, cfg.min_capacity, cfg.dispatch_fp8, cfg.n_groups,
+                   cfg.group_limit, cfg.shared_H)
 
 
 def _p(t: torch.Tensor | None, dtype=None):
@@ -203,23 +210,36 @@ def moe_expert_down(shape, h, expert_offset, expert_kept, w2, expert_out, stream
         _p(w2, BF16), _p(expert_out, BF16), _stream(stream)))
 
 
-def moe_combine(shape, expert_out, slot, topk_w, y, stream=None):
+def moe_combine(shape, expert_out, slot, topk_w, shared_out, y, stream=None):
+    """shared_out: the shared expert's [T, d] output, added with weight 1, or None."""
     s = shape.c()
     _check("moe_combine", lib().moe_combine(
-        ctypes.byref(s), _p(expert_out, BF16), _p(slot, I32), _p(topk_w, F32), _p(y, BF16),
+        ctypes.byref(s), _p(expert_out, BF16), _p(slot, I32), _p(topk_w, F32),
+        _p(shared_out, BF16), _p(y, BF16), _stream(stream)))
+
+
+def moe_shared_expert(shape, x, w1s, w3s, w2s, shared_out, workspace, stream=None):
+    s = shape.c()
+    _check("moe_shared_expert", lib().moe_shared_expert(
+        ctypes.byref(s), _p(x, BF16), _p(w1s, BF16), _p(w3s, BF16), _p(w2s, BF16),
+        _p(shared_out, BF16), _p(workspace), workspace.numel() * workspace.element_size(),
         _stream(stream)))
 
 
-def moe_layer_fwd(shape, x, w_gate, logit_bias, w1, w3, w2, buf: "LayerBuffers", stream=None):
+def moe_layer_fwd(shape, x, w_gate, logit_bias, w1, w3, w2, buf: "LayerBuffers", stream=None,
+                  shared=None):
+    """shared: (w1s, w3s, w2s) of the shared expert when shape.shared_H > 0."""
     s = shape.c()
+    w1s, w3s, w2s = shared if shared is not None else (None, None, None)
     _check("moe_layer_fwd", lib().moe_layer_fwd(
         ctypes.byref(s), _p(x, BF16), _p(w_gate, BF16), _p(logit_bias, F32), _p(w1, BF16),
-        _p(w3, BF16), _p(w2, BF16), _p(buf.y, BF16), _p(buf.logits, F32),
+        _p(w3, BF16), _p(w2, BF16), _p(w1s, BF16), _p(w3s, BF16), _p(w2s, BF16),
+        _p(buf.y, BF16), _p(buf.logits, F32),
         _p(buf.topk_idx, I32), _p(buf.topk_w, F32), _send(shape, buf.send_buf),
         _p(buf.send_scale, F32), _p(buf.slot, I32),
         _p(buf.expert_count, I32), _p(buf.expert_kept, I32), _p(buf.expert_offset, I32),
         _p(buf.rank_rows, I32), _p(buf.stats, torch.int64), _p(buf.expert_out, BF16),
-        _p(buf.workspace), buf.workspace.numel(), _stream(stream)))
+        _p(buf.shared_out, BF16), _p(buf.workspace), buf.workspace.numel(), _stream(stream)))
 
 
 def moe_fp8_rows_to_bf16(codes, scales, out, stream=None):
@@ -246,6 +266,7 @@ class LayerBuffers:
     rank_rows: torch.Tensor
     stats: torch.Tensor
     expert_out: torch.Tensor
+    shared_out: torch.Tensor | None
     workspace: torch.Tensor
 
     @classmethod
@@ -265,6 +286,7 @@ class LayerBuffers:
             expert_offset=z(E + 1, dt=I32), rank_rows=z(D, dt=I32),
             stats=z(len(STAT_NAMES), dt=torch.int64),
             expert_out=z(send_rows, d, dt=BF16),
+            shared_out=z(T, d, dt=BF16) if shape.shared_H > 0 else None,
             workspace=z(ws, dt=torch.uint8),
         )
 

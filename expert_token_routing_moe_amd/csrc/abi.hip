@@ -31,6 +31,8 @@ Workspace workspace_layout(const Dims &dm)
     w.all_offset = take(by_gate ? (size_t)dm.E * sizeof(int32_t) : 0);
     w.by_expert = take(by_gate ? (size_t)dm.T * dm.k * sizeof(int32_t) : 0);
     w.h = take((size_t)dm.send_rows * dm.H * sizeof(uint16_t));
+    w.shared_rows = take(dm.shared_H > 0 ? 4 * sizeof(int32_t) : 0);
+    w.shared_h = take((size_t)(dm.shared_H > 0 ? dm.T : 0) * dm.shared_H * sizeof(uint16_t));
     w.total = std::max<size_t>(off, 256);
     return w;
 }
@@ -55,6 +57,17 @@ static int make_dims(const moe_shape *s, Dims *dm)
         return MOE_EINVAL;
     if (s->dispatch_fp8 != 0 && s->dispatch_fp8 != 1)
         return MOE_EINVAL;
+    // group-limited routing: G equal groups, at most M per token, k of them
+    // must be reachable
+    if (s->n_groups < 0 || s->shared_H < 0)
+        return MOE_EINVAL;
+    const bool grouped = s->n_groups > 1 && s->group_limit < s->n_groups;
+    if (s->n_groups > 1 && (s->E % s->n_groups != 0 || s->group_limit < 1))
+        return MOE_EINVAL;
+    if (grouped && (long long)s->group_limit * (s->E / s->n_groups) < s->k)
+        return MOE_EINVAL;
+    if (s->shared_H % 64 != 0)
+        return MOE_EUNSUPPORTED;
     if (s->d % 64 != 0 || s->H % 64 != 0 || s->E > kMaxExperts)
         return MOE_EUNSUPPORTED;
     const long long assignments = (long long)s->T * s->k;
@@ -85,6 +98,9 @@ static int make_dims(const moe_shape *s, Dims *dm)
     dm->my_rank = s->my_rank;
     dm->drop_policy = s->drop_policy;
     dm->fp8 = s->dispatch_fp8;
+    dm->n_groups = grouped ? s->n_groups : 1;
+    dm->group_limit = grouped ? s->group_limit : 1;
+    dm->shared_H = s->shared_H;
     dm->capacity = C;
     dm->send_rows = send_rows;
     dm->nchunks = (s->T + kChunk - 1) / kChunk;
@@ -252,26 +268,49 @@ MOE_EXPORT int moe_expert_down(const moe_shape *shape, const uint16_t *h,
 }
 
 MOE_EXPORT int moe_combine(const moe_shape *shape, const uint16_t *expert_out,
-                           const int32_t *slot, const float *topk_w, uint16_t *y, void *stream)
+                           const int32_t *slot, const float *topk_w, const uint16_t *shared_out,
+                           uint16_t *y, void *stream)
 {
     Dims dm;
     const int rc = make_dims(shape, &dm);
     if (rc != MOE_OK)
         return rc;
     if (bad_ptr(expert_out, dm.send_rows) || bad_ptr(slot, dm.T) || bad_ptr(topk_w, dm.T) ||
-        bad_ptr(y, dm.T))
+        bad_ptr(y, dm.T) || bad_opt_ptr(shared_out))
         return MOE_EINVAL;
-    return hip_status(
-        launch_combine(dm, expert_out, slot, topk_w, y, static_cast<hipStream_t>(stream)));
+    return hip_status(launch_combine(dm, expert_out, slot, topk_w, shared_out, y,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+MOE_EXPORT int moe_shared_expert(const moe_shape *shape, const uint16_t *x, const uint16_t *w1s,
+                                 const uint16_t *w3s, const uint16_t *w2s, uint16_t *shared_out,
+                                 void *workspace, size_t workspace_bytes, void *stream)
+{
+    Dims dm;
+    int rc = make_dims(shape, &dm);
+    if (rc != MOE_OK)
+        return rc;
+    if (dm.shared_H == 0)
+        return MOE_EINVAL;
+    if (bad_ptr(x, dm.T) || bad_ptr(w1s) || bad_ptr(w3s) || bad_ptr(w2s) ||
+        bad_ptr(shared_out, dm.T))
+        return MOE_EINVAL;
+    Workspace wl;
+    if ((rc = check_ws(dm, workspace, workspace_bytes, &wl)) != MOE_OK)
+        return rc;
+    return hip_status(launch_shared_expert(dm, x, w1s, w3s, w2s, shared_out, (char *)workspace,
+                                           wl, static_cast<hipStream_t>(stream)));
 }
 
 MOE_EXPORT int moe_layer_fwd(const moe_shape *shape, const uint16_t *x, const uint16_t *w_gate,
                              const float *logit_bias, const uint16_t *w1, const uint16_t *w3,
-                             const uint16_t *w2, uint16_t *y, float *logits_out,
+                             const uint16_t *w2, const uint16_t *w1s, const uint16_t *w3s,
+                             const uint16_t *w2s, uint16_t *y, float *logits_out,
                              int32_t *topk_idx, float *topk_w, void *send_buf,
                              float *send_scale, int32_t *slot, int32_t *expert_count, int32_t *expert_kept, int32_t *expert_offset,
                              int32_t *rank_rows, moe_stats *stats, uint16_t *expert_out,
-                             void *workspace, size_t workspace_bytes, void *stream)
+                             uint16_t *shared_out, void *workspace, size_t workspace_bytes,
+                             void *stream)
 {
     Dims dm;
     int rc = make_dims(shape, &dm);
@@ -283,6 +322,10 @@ MOE_EXPORT int moe_layer_fwd(const moe_shape *shape, const uint16_t *x, const ui
         bad_ptr(expert_kept) || bad_ptr(expert_offset) || bad_ptr(rank_rows) ||
         bad_ptr(stats) || bad_ptr(expert_out, dm.send_rows) || bad_opt_ptr(logit_bias) ||
         bad_opt_ptr(logits_out) || bad_scale(dm, send_scale))
+        return MOE_EINVAL;
+    if (dm.shared_H > 0 ? (bad_ptr(w1s) || bad_ptr(w3s) || bad_ptr(w2s) || bad_ptr(shared_out, dm.T))
+                        : (bad_opt_ptr(w1s) || bad_opt_ptr(w3s) || bad_opt_ptr(w2s) ||
+                           bad_opt_ptr(shared_out)))
         return MOE_EINVAL;
     Workspace wl;
     if ((rc = check_ws(dm, workspace, workspace_bytes, &wl)) != MOE_OK)
@@ -300,8 +343,11 @@ MOE_EXPORT int moe_layer_fwd(const moe_shape *shape, const uint16_t *x, const ui
     if (e == hipSuccess)
         e = launch_down(dm, reinterpret_cast<const uint16_t *>(ws + wl.h), expert_offset,
                         expert_kept, w2, expert_out, st);
+    const bool shared = dm.shared_H > 0;
+    if (e == hipSuccess && shared)
+        e = launch_shared_expert(dm, x, w1s, w3s, w2s, shared_out, ws, wl, st);
     if (e == hipSuccess)
-        e = launch_combine(dm, expert_out, slot, topk_w, y, st);
+        e = launch_combine(dm, expert_out, slot, topk_w, shared ? shared_out : nullptr, y, st);
     return hip_status(e);
 }
 

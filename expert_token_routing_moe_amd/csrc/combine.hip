@@ -2,7 +2,9 @@
 // at the token's home device ("Mixture-of-Experts (MoE) Architecture and
 // Expert Parallelism", section 2; "EP Math -- Expert Parallelism (MoE)",
 // "The combine all-to-all").  A dropped assignment (slot -1) adds nothing
-// ("Token drop").
+// ("Token drop").  With a shared expert (replicated on every rank, "MoE
+// Expert Parallelism Sizing: Traffic, Capacity, Fabric", token-assignment
+// worksheet) its bf16 output row is added last, with weight 1.
 //
 // A wavefront per token.  Its slots and gates are read once into scalar
 // registers; for every 16-byte piece of the row, the lane issues all k
@@ -13,10 +15,22 @@
 namespace moe {
 namespace {
 
+// acc[0..7] += the 8 bf16 values of one 16-byte row piece
+__device__ __forceinline__ void add_row_piece(float *acc, uint4 v)
+{
+    const uint32_t p[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        acc[2 * q] += bf16_to_f32(p[q] & 0xffffu);
+        acc[2 * q + 1] += bf16_to_f32(p[q] >> 16);
+    }
+}
+
 template <int KM> // upper bound on k (compile time), so the gathers unroll
 __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict__ expert_out,
                                                       const int32_t *__restrict__ slot,
                                                       const float *__restrict__ topk_w,
+                                                      const uint16_t *__restrict__ shared_out,
                                                       uint16_t *__restrict__ y, int T, int d,
                                                       int k)
 {
@@ -54,6 +68,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict
                 acc[2 * q + 1] = fmaf(g[s], bf16_to_f32(p[q] >> 16), acc[2 * q + 1]);
             }
         }
+        if (shared_out)
+            add_row_piece(acc, reinterpret_cast<const uint4 *>(shared_out + (size_t)t * d)[c]);
         dst[c] = make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
                             pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
     }
@@ -62,7 +78,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict
 // Any k: the slots are walked in rank order, one gather at a time.
 __global__ __launch_bounds__(256) void combine_kernel_any_k(
     const uint16_t *__restrict__ expert_out, const int32_t *__restrict__ slot,
-    const float *__restrict__ topk_w, uint16_t *__restrict__ y, int T, int d, int k)
+    const float *__restrict__ topk_w, const uint16_t *__restrict__ shared_out,
+    uint16_t *__restrict__ y, int T, int d, int k)
 {
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -87,6 +104,8 @@ __global__ __launch_bounds__(256) void combine_kernel_any_k(
                 acc[2 * q + 1] = fmaf(g, bf16_to_f32(p[q] >> 16), acc[2 * q + 1]);
             }
         }
+        if (shared_out)
+            add_row_piece(acc, reinterpret_cast<const uint4 *>(shared_out + (size_t)t * d)[c]);
         dst[c] = make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
                             pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
     }
@@ -95,20 +114,24 @@ __global__ __launch_bounds__(256) void combine_kernel_any_k(
 } // namespace
 
 hipError_t launch_combine(const Dims &dm, const uint16_t *expert_out, const int32_t *slot,
-                          const float *topk_w, uint16_t *y, hipStream_t st)
+                          const float *topk_w, const uint16_t *shared_out, uint16_t *y,
+                          hipStream_t st)
 {
     if (dm.T == 0)
         return hipSuccess;
     const int blocks = (dm.T + 3) / 4;
     if (dm.k <= 2)
-        combine_kernel<2><<<blocks, 256, 0, st>>>(expert_out, slot, topk_w, y, dm.T, dm.d, dm.k);
+        combine_kernel<2><<<blocks, 256, 0, st>>>(expert_out, slot, topk_w, shared_out, y, dm.T,
+                                                             dm.d, dm.k);
     else if (dm.k <= 4)
-        combine_kernel<4><<<blocks, 256, 0, st>>>(expert_out, slot, topk_w, y, dm.T, dm.d, dm.k);
+        combine_kernel<4><<<blocks, 256, 0, st>>>(expert_out, slot, topk_w, shared_out, y, dm.T,
+                                                             dm.d, dm.k);
     else if (dm.k <= 8)
-        combine_kernel<8><<<blocks, 256, 0, st>>>(expert_out, slot, topk_w, y, dm.T, dm.d, dm.k);
+        combine_kernel<8><<<blocks, 256, 0, st>>>(expert_out, slot, topk_w, shared_out, y, dm.T,
+                                                             dm.d, dm.k);
     else
-        combine_kernel_any_k<<<blocks, 256, 0, st>>>(expert_out, slot, topk_w, y, dm.T, dm.d,
-                                                     dm.k);
+        combine_kernel_any_k<<<blocks, 256, 0, st>>>(expert_out, slot, topk_w, shared_out, y,
+                                                     dm.T, dm.d, dm.k);
     return hipGetLastError();
 }
 

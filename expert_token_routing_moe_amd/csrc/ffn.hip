@@ -510,4 +510,36 @@ hipError_t launch_down(const Dims &dm, const uint16_t *h, const int32_t *expert_
     return hipGetLastError();
 }
 
+// The shared expert (replicated on every rank, "MoE Expert Parallelism
+// Sizing: Traffic, Capacity, Fabric", token-assignment worksheet): the same
+// two grouped GEMMs with one group of all T tokens, A = x.
+__global__ void shared_rows_kernel(int32_t *rows, int T)
+{
+    if (threadIdx.x == 0) {
+        rows[0] = 0; // row_offset[0]
+        rows[1] = T; // row_offset[1]
+        rows[2] = T; // row_count[0]
+    }
+}
+
+hipError_t launch_shared_expert(const Dims &dm, const uint16_t *x, const uint16_t *w1s,
+                                const uint16_t *w3s, const uint16_t *w2s, uint16_t *shared_out,
+                                char *ws, const Workspace &wl, hipStream_t st)
+{
+    if (dm.T == 0 || dm.shared_H == 0)
+        return hipSuccess;
+    int32_t *rows = reinterpret_cast<int32_t *>(ws + wl.shared_rows);
+    uint16_t *hs = reinterpret_cast<uint16_t *>(ws + wl.shared_h);
+    shared_rows_kernel<<<1, 64, 0, st>>>(rows, dm.T);
+    Dims ds = dm;
+    ds.E = 1;
+    ds.H = dm.shared_H;
+    ds.send_rows = dm.T;
+    ds.fp8 = 0;
+    hipError_t e = launch_gate_up(ds, x, nullptr, rows, rows + 2, w1s, w3s, hs, st);
+    if (e == hipSuccess)
+        e = launch_down(ds, hs, rows, rows + 2, w2s, shared_out, st);
+    return e;
+}
+
 } // namespace moe

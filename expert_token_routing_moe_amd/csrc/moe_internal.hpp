@@ -86,6 +86,9 @@ struct Dims {
     int T, d, E, k, H, D, my_rank;
     int drop_policy;   // 0: token order, 1: by gate value (capacity mode only)
     int fp8;           // dispatch payload: 0 bf16 rows, 1 E4M3 rows + fp32 row scales
+    int n_groups;      // expert groups for group-limited routing (<= 1: none)
+    int group_limit;   // groups a token may use (routing is limited iff < n_groups)
+    int shared_H;      // shared expert's SwiGLU hidden size (0: none)
     int64_t capacity;  // C, or -1 when dropless
     int64_t send_rows; // E*C or T*k
     int nchunks;       // ceil(T / kChunk)
@@ -101,6 +104,8 @@ struct Workspace {
     size_t all_offset;    // int32 [E]          exclusive scan of n_e (drop policy 1)
     size_t by_expert;     // int32 [T*k]        assignments grouped by expert (drop policy 1)
     size_t h;             // bf16 [send_rows, H] SwiGLU hidden activations
+    size_t shared_rows;   // int32 [4]          row offsets/count of the shared expert's one group
+    size_t shared_h;      // bf16 [T, shared_H] the shared expert's hidden activations
     size_t total;
 };
 
@@ -128,7 +133,11 @@ hipError_t launch_down(const Dims &dm, const uint16_t *h, const int32_t *expert_
                        const int32_t *expert_kept, const uint16_t *w2, uint16_t *expert_out,
                        hipStream_t st);
 hipError_t launch_combine(const Dims &dm, const uint16_t *expert_out, const int32_t *slot,
-                          const float *topk_w, uint16_t *y, hipStream_t st);
+                          const float *topk_w, const uint16_t *shared_out, uint16_t *y,
+                          hipStream_t st);
+hipError_t launch_shared_expert(const Dims &dm, const uint16_t *x, const uint16_t *w1s,
+                                const uint16_t *w3s, const uint16_t *w2s, uint16_t *shared_out,
+                                char *ws, const Workspace &wl, hipStream_t st);
 hipError_t launch_fp8_rows_to_bf16(const uint8_t *codes, const float *scales, long long rows,
                                    int d, uint16_t *out, hipStream_t st);
 

@@ -211,17 +211,34 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v)
     return v;
 }
 
+// The wave's own LDS operations have completed (lgkmcnt(0)); the compiler
+// keeps memory accesses on their side.
+__device__ __forceinline__ void lds_wait()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    asm volatile("" ::: "memory");
+}
+
 // One wavefront per token; lane l holds logits l, l+64, ... (V per lane).
 // The logit of (t, e) is the sum, in slice order, of the sk_count partials
 // plus the bias; it is written to logits_out when that is non-null.
+// Group limit ("MoE Expert Parallelism Sizing: Traffic, Capacity, Fabric":
+// at most M nodes per token, Megatron's group-limited routing), when
+// G > 1 and M < G: the E experts form G contiguous groups; each group's
+// score is its best logit (LDS atomic max of the order-preserving key), the
+// M best groups are picked by M wave arg-max rounds (ties to the lower
+// group), and the other groups' experts are retired before KeepTopK.
 template <int V>
 __global__ __launch_bounds__(256) void topk_softmax_kernel(
     const float *__restrict__ partial, int sk_count, const float *__restrict__ bias,
     float *__restrict__ logits_out, int32_t *__restrict__ topk_idx, float *__restrict__ topk_w,
-    int T, int E, int k)
+    int T, int E, int k, int G, int M)
 {
-    const int lane = threadIdx.x & 63;
-    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    __shared__ uint32_t s_gscore[4][kMaxExperts];
+    __shared__ uint8_t s_allow[4][kMaxExperts];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int t = blockIdx.x * 4 + wave;
     if (t >= T)
         return;
     uint64_t key[V];
@@ -238,6 +255,42 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(
             if (logits_out)
                 logits_out[(size_t)t * E + e] = h;
             key[j] = topk_key(h, e, E);
+        }
+    }
+    if (G > 1 && M < G) {
+        uint32_t *gs = s_gscore[wave];
+        uint8_t *allow = s_allow[wave];
+        const int per = E / G;
+        for (int g = lane; g < G; g += 64) {
+            gs[g] = 0u; // below every real score
+            allow[g] = 0;
+        }
+        lds_wait();
+#pragma unroll
+        for (int j = 0; j < V; ++j) {
+            const int e = lane + 64 * j;
+            if (e < E)
+                atomicMax(&gs[e / per], (uint32_t)(key[j] >> 32));
+        }
+        lds_wait();
+        for (int r = 0; r < M; ++r) {
+            uint64_t best = 0;
+            for (int g = lane; g < G; g += 64) {
+                const uint64_t gk = ((uint64_t)gs[g] << 32) | (uint32_t)(G - 1 - g);
+                best = (gs[g] != 0u && gk > best) ? gk : best;
+            }
+            const int gw = G - 1 - (int)(uint32_t)(wave_max_u64(best) & 0xffffffffu);
+            if (lane == 0) {
+                gs[gw] = 0u; // retired
+                allow[gw] = 1;
+            }
+            lds_wait();
+        }
+#pragma unroll
+        for (int j = 0; j < V; ++j) {
+            const int e = lane + 64 * j;
+            if (e < E && !allow[e / per])
+                key[j] = 0;
         }
     }
     float hmax = 0.f, denom = 0.f;
@@ -280,7 +333,8 @@ hipError_t launch_topk(const Dims &dm, const float *partial, int sk, const float
     const int V = (dm.E + 63) / 64;
 #define MOE_TOPK(VV)                                                                       \
     topk_softmax_kernel<VV><<<blocks, 256, 0, st>>>(partial, sk, bias, logits_out, topk_idx,  \
-                                                   topk_w, dm.T, dm.E, dm.k)
+                                                   topk_w, dm.T, dm.E, dm.k, dm.n_groups,    \
+                                                   dm.group_limit)
     if (V <= 1)
         MOE_TOPK(1);
     else if (V <= 2)

@@ -43,6 +43,9 @@ class MoEConfig:
     drop_policy: int = 0   # 0: overflow dropped in token order; 1: by gate value
     min_capacity: int = 0  # lower bound on the capacity C (capacity mode)
     dispatch_fp8: int = 0  # 1: dispatch payload as E4M3 rows with fp32 row scales
+    n_groups: int = 0      # expert groups for group-limited routing (<= 1: none)
+    group_limit: int = 0   # groups a token may use
+    shared_H: int = 0      # hidden size of a shared (replicated) expert; 0: none
 
     def with_(self, **kw) -> "MoEConfig":
         return replace(self, **kw)
@@ -73,7 +76,7 @@ CONFIGS = {
     )
 }
 
-_X, _WG, _W1, _W3, _W2 = range(5)
+_X, _WG, _W1, _W3, _W2, _W1S, _W3S, _W2S = range(8)
 
 
 def _gen(seed: int, tid: int, device) -> torch.Generator:
@@ -95,7 +98,8 @@ def _normal_bf16_stacked(n, shape, std, g, device) -> torch.Tensor:
 
 
 def make_inputs(cfg: MoEConfig, device="cpu", *, experts: bool = True) -> dict:
-    """Draw x [T,d], w_gate [d,E], bias [E] fp32 (or None), w1/w3 [E,H,d], w2 [E,d,H].
+    """Draw x [T,d], w_gate [d,E], bias [E] fp32 (or None), w1/w3 [E,H,d], w2 [E,d,H],
+    and with a shared expert w1s/w3s [shared_H,d], w2s [d,shared_H].
 
     ``experts=False`` skips the expert weights (routing-only tests).
     """
@@ -117,6 +121,13 @@ def make_inputs(cfg: MoEConfig, device="cpu", *, experts: bool = True) -> dict:
                                          _gen(cfg.seed, _W3, dev), dev)
         out["w2"] = _normal_bf16_stacked(cfg.E, (cfg.d, cfg.H), cfg.w_std,
                                          _gen(cfg.seed, _W2, dev), dev)
+        if cfg.shared_H > 0:
+            out["w1s"] = _normal_bf16((cfg.shared_H, cfg.d), cfg.w_std,
+                                      _gen(cfg.seed, _W1S, dev), dev)
+            out["w3s"] = _normal_bf16((cfg.shared_H, cfg.d), cfg.w_std,
+                                      _gen(cfg.seed, _W3S, dev), dev)
+            out["w2s"] = _normal_bf16((cfg.d, cfg.shared_H), cfg.w_std,
+                                      _gen(cfg.seed, _W2S, dev), dev)
     return out
 
 

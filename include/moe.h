@@ -31,6 +31,10 @@
  *   [F8] same page, "What the bounds omit": FP8 dispatch sends token rows in
  *        FP8 instead of BF16 (half the dispatch row, plus scale tensors),
  *        while the combine path may stay wider.
+ *   [GL] same page, the traffic bounds: at most 4 nodes per token
+ *        (DeepSeek-V3), exposed by Megatron as group-limited routing.
+ *   [SE] same page, the token-assignment worksheet: the shared expert is
+ *        replicated on every rank (compute and memory, no dispatch traffic).
  *
  * Conventions for every call
  *   - Tensor pointers are DEVICE pointers (HIP global memory) unless marked
@@ -69,7 +73,7 @@ extern "C" {
 #define MOE_EWORKSPACE (-3)   /* workspace NULL or smaller than moe_query says  */
 #define MOE_EHIP (-4)         /* a HIP launch reported an error                 */
 
-/* Shape of one layer on one device, in the pages' notation [N][CF][PL][DP][MC][F8].
+/* Shape of one layer on one device, in the pages' notation [N][CF][PL][DP][MC][F8][GL][SE].
  *   T        tokens on this device (T >= 0; T = 0 enqueues nothing)
  *   d        hidden size (d > 0, d % 64 == 0)
  *   E        routed experts (1 <= E <= 1024, E % D == 0)
@@ -94,6 +98,15 @@ extern "C" {
  *            rounded to nearest (ties to even), saturating at 448, sign kept.
  *            The expert sees code value * s; expert_out, h and the combine
  *            stay bf16.  Other values -> MOE_EINVAL.
+ *   n_groups, group_limit  [GL]: with n_groups = G > 1 and group_limit =
+ *            M < G, the experts form G contiguous groups of E/G; a group's
+ *            score for a token is its largest logit, the M best groups are
+ *            kept (ties to the lower group index) and KeepTopK picks among
+ *            their experts only.  G must divide E and M*E/G >= k (else
+ *            MOE_EINVAL); n_groups <= 1 or group_limit >= n_groups: no limit.
+ *   shared_H  [SE]: SwiGLU hidden size of a shared expert applied to every
+ *            token and added, with weight 1, to the combine; 0 = none;
+ *            shared_H % 64 == 0 (else MOE_EUNSUPPORTED).
  *   capacity_factor  f > 0: capacity C = ceil(f*T*k/E), evaluated left to
  *            right in IEEE double [CF]; +INFINITY: dropless (no capacity).
  *            NaN, zero, negative -> MOE_EINVAL.
@@ -103,6 +116,8 @@ typedef struct moe_shape {
     int32_t drop_policy;
     int32_t min_capacity;
     int32_t dispatch_fp8;
+    int32_t n_groups, group_limit;
+    int32_t shared_H;
     double capacity_factor;
 } moe_shape;
 
@@ -144,8 +159,9 @@ typedef struct moe_stats {
 int moe_query(const moe_shape *shape, int64_t *send_rows, int64_t *capacity,
               size_t *workspace_bytes);
 
-/* Router [G]: logits H = x W_g (+ bias), fp32 accumulation of exact bf16
- * products; then KeepTopK + softmax over the kept logits.
+/* Router [G][GL]: logits H = x W_g (+ bias), fp32 accumulation of exact
+ * bf16 products; then KeepTopK (within the token's best groups under a
+ * group limit) + softmax over the kept logits.
  *   x           [T, d] bf16
  *   w_gate      [d, E] bf16 (d_model x E, as W_g is written on the page)
  *   logit_bias  [E] fp32 or NULL; added to H, so it enters selection and
@@ -229,25 +245,41 @@ int moe_expert_down(const moe_shape *shape, const uint16_t *h, const int32_t *ex
                     const int32_t *expert_kept, const uint16_t *w2, uint16_t *expert_out,
                     void *stream);
 
-/* Combine [G][CA][TD]: y[t] = bf16(sum over s with slot[t,s] >= 0, in s
- * order, of topk_w[t,s] * expert_out[slot[t,s]]) with fp32 accumulation.
- * Dropped assignments add nothing; the residual is the caller's to add.
- *   expert_out  [send_rows, d] bf16;  slot, topk_w [T, k];  y [T, d] bf16 out */
+/* Combine [G][CA][TD][SE]: y[t] = bf16(sum over s with slot[t,s] >= 0, in s
+ * order, of topk_w[t,s] * expert_out[slot[t,s]], then + shared_out[t]) with
+ * fp32 accumulation.  Dropped assignments add nothing; the residual is the
+ * caller's to add.
+ *   expert_out  [send_rows, d] bf16;  slot, topk_w [T, k];
+ *   shared_out  [T, d] bf16 (the shared expert's output) or NULL;
+ *   y [T, d] bf16 out */
 int moe_combine(const moe_shape *shape, const uint16_t *expert_out, const int32_t *slot,
-                const float *topk_w, uint16_t *y, void *stream);
+                const float *topk_w, const uint16_t *shared_out, uint16_t *y, void *stream);
 
-/* The whole forward pass: moe_route, moe_dispatch, moe_expert_ffn and
- * moe_combine enqueued back to back on `stream`, with no host
- * synchronisation; every intermediate lands in the caller's buffers with the
- * meaning given above.  logit_bias and logits_out may be NULL. */
+/* Shared expert [SE][M]: shared_out = bf16(SiLU(x W1s^T) * (x W3s^T)) W2s^T
+ * for every token (h rounded to bf16, fp32 accumulation), the same SwiGLU as
+ * the routed experts, on x directly: it is replicated, so nothing is
+ * dispatched for it.  Requires shape->shared_H > 0 (else MOE_EINVAL).
+ *   x [T, d] bf16;  w1s, w3s [shared_H, d] bf16;  w2s [d, shared_H] bf16
+ *   shared_out [T, d] bf16 out;  workspace >= moe_query's size */
+int moe_shared_expert(const moe_shape *shape, const uint16_t *x, const uint16_t *w1s,
+                      const uint16_t *w3s, const uint16_t *w2s, uint16_t *shared_out,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
+/* The whole forward pass: moe_route, moe_dispatch, moe_expert_ffn,
+ * moe_shared_expert (when shared_H > 0) and moe_combine enqueued back to
+ * back on `stream`, with no host synchronisation; every intermediate lands
+ * in the caller's buffers with the meaning given above.  logit_bias and
+ * logits_out may be NULL; w1s, w3s, w2s and shared_out are required when
+ * shared_H > 0 and may be NULL otherwise. */
 int moe_layer_fwd(const moe_shape *shape, const uint16_t *x, const uint16_t *w_gate,
                   const float *logit_bias, const uint16_t *w1, const uint16_t *w3,
-                  const uint16_t *w2, uint16_t *y, float *logits_out, int32_t *topk_idx,
+                  const uint16_t *w2, const uint16_t *w1s, const uint16_t *w3s,
+                  const uint16_t *w2s, uint16_t *y, float *logits_out, int32_t *topk_idx,
                   float *topk_w, void *send_buf, float *send_scale, int32_t *slot,
                   int32_t *expert_count,
                   int32_t *expert_kept, int32_t *expert_offset, int32_t *rank_rows,
-                  moe_stats *stats, uint16_t *expert_out, void *workspace,
-                  size_t workspace_bytes, void *stream);
+                  moe_stats *stats, uint16_t *expert_out, uint16_t *shared_out,
+                  void *workspace, size_t workspace_bytes, void *stream);
 
 /* Diagnostic decode of FP8 dispatch rows [F8]: out[r, i] = bf16(value of
  * E4M3 code codes[r*d + i] * scales[r]), with the product rounded to fp32

@@ -88,6 +88,12 @@ def test_query_workspace_grows_only_for_gate_order_drops():
     (dict(drop_policy=-1), api.MOE_EINVAL),
     (dict(min_capacity=-1), api.MOE_EINVAL),
     (dict(dispatch_fp8=2), api.MOE_EINVAL),
+    (dict(n_groups=3, group_limit=1), api.MOE_EINVAL),    # 8 experts in 3 groups
+    (dict(n_groups=4, group_limit=0), api.MOE_EINVAL),
+    (dict(n_groups=8, group_limit=1, k=2), api.MOE_EINVAL),  # 1 group of 1 expert < k
+    (dict(n_groups=-1), api.MOE_EINVAL),
+    (dict(shared_H=-64), api.MOE_EINVAL),
+    (dict(shared_H=100), api.MOE_EUNSUPPORTED),
     (dict(capacity_factor=1e12), api.MOE_EUNSUPPORTED),  # E*C does not fit int32 rows
 ])
 def test_query_rejects_bad_shapes(kw, status):
@@ -136,13 +142,28 @@ def test_entry_points_reject_null_and_misaligned_pointers():
     assert _raw("moe_fp8_rows_to_bf16", good, good, -1, 32, good, nul) == api.MOE_EINVAL
     assert _raw("moe_expert_ffn", S, good, nul, good, good, good, good, mis, good, good,
                 1 << 30, nul) == api.MOE_EINVAL
-    assert _raw("moe_combine", S, good, good, good, nul, nul) == api.MOE_EINVAL
-    lay = [good] * 20
-    lay[2] = nul   # optional bias
-    lay[7] = nul   # optional logits_out
-    lay[11] = nul  # optional send_scale (bf16 dispatch)
-    lay[10] = nul  # send_buf is required
-    assert _raw("moe_layer_fwd", S, *lay[:19], good, 1 << 30, nul) == api.MOE_EINVAL
+    assert _raw("moe_combine", S, good, good, good, nul, nul, nul) == api.MOE_EINVAL
+    assert _raw("moe_combine", S, good, good, good, mis, good, nul) == api.MOE_EINVAL
+    assert _raw("moe_shared_expert", S, good, good, good, good, good, good, 1 << 30,
+                nul) == api.MOE_EINVAL            # no shared expert in this shape
+    ss = api.Shape(T=256, d=512, E=8, k=2, H=1024, D=2, capacity_factor=1.25,
+                   shared_H=128).c()
+    assert _raw("moe_shared_expert", ctypes.byref(ss), good, good, nul, good, good, good,
+                1 << 30, nul) == api.MOE_EINVAL   # w3s missing
+    # x, w_gate, bias, w1, w3, w2, w1s, w3s, w2s, y, logits_out, topk_idx,
+    # topk_w, send_buf, send_scale, slot, count, kept, offset, rank_rows,
+    # stats, expert_out, shared_out
+    lay = [good] * 23
+    for i in (2, 6, 7, 8, 10, 14, 22):   # optional in this shape
+        lay[i] = nul
+    lay[13] = nul                        # send_buf is required
+    assert _raw("moe_layer_fwd", S, *lay, good, 1 << 30, nul) == api.MOE_EINVAL
+    lay[13] = good
+    lay[22] = mis                        # an optional pointer must still be aligned
+    assert _raw("moe_layer_fwd", S, *lay, good, 1 << 30, nul) == api.MOE_EINVAL
+    lay[22] = nul
+    assert _raw("moe_layer_fwd", ctypes.byref(ss), *lay, good, 1 << 30,
+                nul) == api.MOE_EINVAL       # shared_H > 0 needs its weights
 
 
 def test_entry_points_reject_small_or_missing_workspace():
@@ -173,4 +194,4 @@ def test_binding_refuses_cpu_tensors():
     x = torch.zeros(4, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         api.moe_combine(shape, x, torch.zeros(4, 1, dtype=torch.int32),
-                        torch.zeros(4, 1), x)
+                        torch.zeros(4, 1), None, x)

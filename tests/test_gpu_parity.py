@@ -180,7 +180,7 @@ def test_combine_stage(case):
     cfg, inp, h, bias, ref, shape, buf = case
     eo = torch.from_numpy(ref["expert_out"].view(np.int16)).view(torch.bfloat16).to(DEV)
     y = torch.empty(cfg.T, cfg.d, dtype=torch.bfloat16, device=DEV)
-    api.moe_combine(shape, eo, _i32(ref["slot"]), _f32(ref["topk_w"]), y)
+    api.moe_combine(shape, eo, _i32(ref["slot"]), _f32(ref["topk_w"]), None, y)
     torch.cuda.synchronize()
     got, want = t2f(y), bits_to_f64(ref["y"])
     res = assert_bf16_close(got, want, "combine")
@@ -397,6 +397,107 @@ def test_layer_fwd_fp8_end_to_end(name):
     assert_bf16_close(t2f(buf.y), bits_to_f64(yref), "y (fp8 dispatch)")
 
 
+# ---------------------------------------------------------------------------
+# Group-limited routing and the replicated shared expert.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("E,k,G,M,ties", [(256, 8, 8, 4, False), (256, 8, 8, 4, True),
+                                          (64, 6, 8, 3, True), (16, 4, 4, 2, True),
+                                          (12, 3, 6, 2, False), (1024, 8, 64, 5, False)])
+def test_topk_group_limited_on_identical_logits(E, k, G, M, ties):
+    T = 777
+    rng = np.random.default_rng(E + G + M)
+    if ties:
+        lg = rng.integers(-3, 4, (T, E)).astype(np.float32)
+    else:
+        lg = rng.standard_normal((T, E)).astype(np.float32)
+    shape = api.Shape(T=T, d=64, E=E, k=k, H=64, n_groups=G, group_limit=M)
+    idx = torch.empty(T, k, dtype=torch.int32, device=DEV)
+    w = torch.empty(T, k, dtype=torch.float32, device=DEV)
+    api.moe_topk_from_logits(shape, _f32(lg), idx, w)
+    torch.cuda.synchronize()
+    o_idx, o_w, _ = oracle.topk(lg, k, G, M)
+    np.testing.assert_array_equal(idx.cpu().numpy(), o_idx)
+    np.testing.assert_allclose(w.cpu().numpy(), o_w, rtol=4e-6, atol=1e-7)
+
+
+GROUPED = {
+    "tiny_g4m2_shared": CONFIGS["tiny"].with_(n_groups=4, group_limit=2, shared_H=256),
+    "e256_k8_g8m4_shared": SMALL["e256_k8"].with_(n_groups=8, group_limit=4, shared_H=128),
+    "dropless_e16_g8m3": SMALL["dropless_e16"].with_(n_groups=8, group_limit=3),
+    "ragged_shared": SMALL["ragged_e6"].with_(shared_H=192),
+}
+
+
+@pytest.mark.parametrize("name", list(GROUPED))
+def test_layer_fwd_grouped_and_shared_end_to_end(name):
+    cfg = GROUPED[name]
+    print(f"\n[grouped {name}] G={cfg.n_groups} M={cfg.group_limit} shared_H={cfg.shared_H}",
+          flush=True)
+    inp = make_inputs(cfg, DEV)
+    h = _host(inp)
+    bias = None if inp["bias"] is None else inp["bias"].cpu().numpy()
+    shape = api.Shape.from_config(cfg)
+    buf = api.LayerBuffers.allocate(shape, DEV)
+    shared = (inp["w1s"], inp["w3s"], inp["w2s"]) if cfg.shared_H else None
+    api.moe_layer_fwd(shape, inp["x"], inp["w_gate"], inp["bias"], inp["w1"], inp["w3"],
+                      inp["w2"], buf, shared=shared)
+    torch.cuda.synchronize()
+    # routing against the oracle's logits (the gap covers group near-ties too)
+    lg_ref = oracle.logits(h["x"], h["w_gate"], bias)
+    r_idx, _, gap = oracle.topk(lg_ref, cfg.k, cfg.n_groups, cfg.group_limit)
+    idx, w = buf.topk_idx.cpu().numpy(), buf.topk_w.cpu().numpy()
+    assert not routing_mismatch(idx, r_idx, lg_ref, gap).any()
+    # on identical logits the selection is bit-exact
+    o_idx, o_w, _ = oracle.topk(buf.logits.cpu().numpy(), cfg.k, cfg.n_groups, cfg.group_limit)
+    np.testing.assert_array_equal(idx, o_idx)
+    # downstream on the GPU's own routing
+    r = oracle.dispatch(h["x"], idx, T=cfg.T, d=cfg.d, E=cfg.E, D=cfg.D, cf=cfg.cf)
+    _assert_dispatch_equal(buf, r, r["stats"]["send_rows"])
+    eo = oracle.expert_ffn_all(r["send_buf"], r["expert_offset"], r["expert_kept"], h["w1"],
+                               h["w3"], h["w2"])
+    so = None
+    if cfg.shared_H:
+        so = oracle.expert_ffn(h["x"], h["w1s"], h["w3s"], h["w2s"])
+        assert_bf16_close(t2f(buf.shared_out), bits_to_f64(so), "shared expert")
+    yref = oracle.combine(eo, r["slot"], w, so)
+    assert_bf16_close(t2f(buf.y), bits_to_f64(yref), "y")
+
+
+def test_shared_expert_and_combine_stages():
+    cfg = CONFIGS["tiny"].with_(shared_H=320, T=300)
+    inp = make_inputs(cfg, DEV)
+    h = _host(inp)
+    shape = api.Shape.from_config(cfg)
+    buf = api.LayerBuffers.allocate(shape, DEV)
+    api.moe_shared_expert(shape, inp["x"], inp["w1s"], inp["w3s"], inp["w2s"], buf.shared_out,
+                          buf.workspace)
+    torch.cuda.synchronize()
+    so = oracle.expert_ffn(h["x"], h["w1s"], h["w3s"], h["w2s"])
+    assert_bf16_close(t2f(buf.shared_out), bits_to_f64(so), "shared expert")
+    # combine on identical inputs: within one bf16 ulp of the oracle
+    ref = oracle.layer_fwd(h["x"], h["w_gate"], h["w1"], h["w3"], h["w2"], k=cfg.k, D=cfg.D,
+                           cf=cfg.cf)
+    eo = torch.from_numpy(ref["expert_out"].view(np.int16)).view(torch.bfloat16).to(DEV)
+    sot = torch.from_numpy(so.view(np.int16)).view(torch.bfloat16).to(DEV)
+    y = torch.empty(cfg.T, cfg.d, dtype=torch.bfloat16, device=DEV)
+    api.moe_combine(shape, eo, _i32(ref["slot"]), _f32(ref["topk_w"]), sot, y)
+    torch.cuda.synchronize()
+    want = bits_to_f64(oracle.combine(ref["expert_out"], ref["slot"], ref["topk_w"], so))
+    got = t2f(y)
+    # one bf16 ulp of the result, plus the fp32 rounding of k + 1 terms: the
+    # shared term can nearly cancel the routed sum
+    mag = np.abs(bits_to_f64(so))
+    for s_ in range(cfg.k):
+        sl = ref["slot"][:, s_]
+        rows = np.where(sl[:, None] >= 0, np.abs(bits_to_f64(ref["expert_out"][np.maximum(sl, 0)])), 0)
+        mag += ref["topk_w"][:, s_:s_ + 1].astype(np.float64) * rows
+    ulp = np.ldexp(1.0, np.frexp(np.abs(want))[1] - 8)
+    bound = np.maximum(ulp, 2.0 ** -133) + (cfg.k + 1) * 2.0 ** -24 * mag
+    assert np.all(np.abs(got - want) <= bound)
+    assert np.mean(got == want) > 0.95
+
+
 @pytest.mark.parametrize("k", [2, 8])
 def test_identity_experts_round_trip_on_gpu(k):
     """Dispatch then combine with identity experts and nothing dropped gives x
@@ -408,7 +509,7 @@ def test_identity_experts_round_trip_on_gpu(k):
     api.moe_route(shape, inp["x"], inp["w_gate"], None, buf.logits, buf.topk_idx, buf.topk_w,
                   buf.workspace)
     _run_dispatch(shape, inp["x"], buf.topk_idx, buf)
-    api.moe_combine(shape, buf.send_buf, buf.slot, buf.topk_w, buf.y)
+    api.moe_combine(shape, buf.send_buf, buf.slot, buf.topk_w, None, buf.y)
     torch.cuda.synchronize()
     assert torch.equal(buf.y.view(torch.int16), inp["x"].view(torch.int16))
 
@@ -443,6 +544,8 @@ def _expert_weights(inp, e):
 
 
 FULL_VARIANTS = {
+    "dsv3_prefill_g8m4_shared": CONFIGS["dsv3_prefill"].with_(n_groups=8, group_limit=4,
+                                                              shared_H=2048),
     "skewed_by_gate": CONFIGS["skewed"].with_(drop_policy=1),
     "dsv3_prefill_fp8": CONFIGS["dsv3_prefill"].with_(dispatch_fp8=1),
     "mixtral_fp8": CONFIGS["mixtral"].with_(dispatch_fp8=1),
@@ -450,7 +553,8 @@ FULL_VARIANTS = {
 
 
 @pytest.mark.parametrize("name", ["mixtral", "dsv3_prefill", "dsv3_decode", "skewed",
-                                  "skewed_by_gate", "dsv3_prefill_fp8", "mixtral_fp8"])
+                                  "skewed_by_gate", "dsv3_prefill_fp8", "mixtral_fp8",
+                                  "dsv3_prefill_g8m4_shared"])
 def test_full_size_config(name):
     cfg = FULL_VARIANTS.get(name) or CONFIGS[name]
     fp8 = bool(cfg.dispatch_fp8)
@@ -458,11 +562,13 @@ def test_full_size_config(name):
     inp = make_inputs(cfg, DEV)
     shape = api.Shape.from_config(cfg)
     buf = api.LayerBuffers.allocate(shape, DEV)
+    shared = (inp["w1s"], inp["w3s"], inp["w2s"]) if cfg.shared_H else None
     api.moe_layer_fwd(shape, inp["x"], inp["w_gate"], inp["bias"], inp["w1"], inp["w3"],
-                      inp["w2"], buf)
+                      inp["w2"], buf, shared=shared)
     torch.cuda.synchronize()
     x = bf16_bits(inp["x"])
     wg = bf16_bits(inp["w_gate"])
+    G, M = cfg.n_groups, cfg.group_limit
     bias = None if inp["bias"] is None else inp["bias"].cpu().numpy()
     # routing: every token
     lg_ref = oracle.logits(x, wg, bias)
@@ -471,10 +577,10 @@ def test_full_size_config(name):
         bits_to_f64(x), bits_to_f64(wg)))
     idx = buf.topk_idx.cpu().numpy()
     w = buf.topk_w.cpu().numpy()
-    o_idx, o_w, _ = oracle.topk(lg, cfg.k)
+    o_idx, o_w, _ = oracle.topk(lg, cfg.k, G, M)
     np.testing.assert_array_equal(idx, o_idx)
     np.testing.assert_allclose(w, o_w, rtol=4e-6, atol=1e-7)
-    r_idx, _, gap = oracle.topk(lg_ref, cfg.k)
+    r_idx, _, gap = oracle.topk(lg_ref, cfg.k, G, M)
     flips = np.any(idx != r_idx, axis=1)
     bad = routing_mismatch(idx, r_idx, lg_ref, gap)
     print(f"  tokens routed differently from the oracle's logits: {int(flips.sum())} "
@@ -524,9 +630,17 @@ def test_full_size_config(name):
         got = (oracle.expert_ffn_fp8(sb[rows], ss[rows], *_expert_weights(inp, e)) if fp8
                else oracle.expert_ffn(sb[rows], *_expert_weights(inp, e)))
         assert_bf16_close(bits_to_f64(eo[rows]), bits_to_f64(got), f"{name} expert {e}")
-    # combine: sampled tokens on the GPU's expert outputs (stage parity)
+    # shared expert: sampled tokens
     toks = np.sort(rng.choice(cfg.T, min(cfg.T, 256), replace=False))
-    yref = oracle.combine(eo, slot[toks], w[toks])
+    so = None
+    if cfg.shared_H:
+        ws_ = tuple(bf16_bits(inp[n]) for n in ("w1s", "w3s", "w2s"))
+        so_gpu = bf16_bits(buf.shared_out)
+        so_ref = oracle.expert_ffn(x[toks[:48]], *ws_)
+        assert_bf16_close(bits_to_f64(so_gpu[toks[:48]]), bits_to_f64(so_ref), "shared expert")
+        so = so_gpu[toks]
+    # combine: sampled tokens on the GPU's expert outputs (stage parity)
+    yref = oracle.combine(eo, slot[toks], w[toks], so)
     y = bf16_bits(buf.y)
     assert_bf16_close(bits_to_f64(y[toks]), bits_to_f64(yref), f"{name} combine")
     # end to end for a few tokens, every step by the oracle from x
@@ -545,6 +659,8 @@ def test_full_size_config(name):
         yt = np.zeros(cfg.d)
         for g, o in acc:
             yt += g * bits_to_f64(o[0])
+        if cfg.shared_H:
+            yt += bits_to_f64(oracle.expert_ffn(x[t:t + 1], *ws_)[0])
         ref_row = np.array([oracle.bf16_from_double(v) for v in yt], np.uint16)
         assert_bf16_close(bits_to_f64(y[t]), bits_to_f64(ref_row), f"{name} token {t}")
     del inp, buf
