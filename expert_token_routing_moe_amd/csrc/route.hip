@@ -24,24 +24,63 @@
 
 namespace moe {
 
-// Split of K for the logit GEMM: enough workgroups to cover the chip (~512),
-// at least four K steps per slice.  Shared by the workspace layout.
+int router_epad(int E) { return (E + 63) / 64 * 64; }
+
+// Experts per logit tile: all 256 of a multiple of 256 (one workgroup per
+// CU, so x is read once per expert group of 256), else 128 or 64 (two
+// workgroups per CU).
+static int router_be(int E)
+{
+    const int epad = router_epad(E);
+    return epad % 256 == 0 ? 256 : epad % 128 == 0 ? 128 : 64;
+}
+
+// Split of K for the logit GEMM: enough workgroups to cover the chip (one
+// or two per CU), at least four K steps per slice.  Shared by the workspace
+// layout.
 int router_ksplit(int T, int E, int d)
 {
-    const int tiles = ((T + 63) / 64) * ((E + 127) / 128);
+    const int be = router_be(E);
+    const int tiles = ((T + 63) / 64) * (router_epad(E) / be);
     const int steps = d / 64;
     if (tiles == 0)
         return 1; // T = 0: nothing to split
-    int sk = (512 + tiles - 1) / tiles;
+    const int target = be == 256 ? 256 : 512;
+    int sk = (target + tiles - 1) / tiles;
     sk = std::min(sk, std::max(1, steps / 4));
     return std::max(1, sk);
 }
 
-int router_epad(int E) { return (E + 63) / 64 * 64; }
-
 namespace {
 
-// W_g [d, E] -> W_g^T [E_pad, d], 64 x 64 tiles through LDS.
+// W_g [d, E] -> W_g^T [E_pad, d], 64 x 64 tiles through LDS.  E % 8 == 0:
+// 16-byte loads of 8 experts and 16-byte stores of 8 K values.
+__global__ __launch_bounds__(256) void transpose_wg_vec_kernel(const uint16_t *__restrict__ wg,
+                                                               uint16_t *__restrict__ wgt,
+                                                               int d, int E)
+{
+    __shared__ __attribute__((aligned(16))) uint16_t tile[64][72]; // [k][e], 144-byte rows
+    const int k0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
+    for (int c = threadIdx.x; c < 512; c += 256) {
+        const int kr = c >> 3, ec = (c & 7) * 8;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (e0 + ec < E) // E % 8 == 0: all 8 experts are in range or none
+            v = *reinterpret_cast<const uint4 *>(wg + (size_t)(k0 + kr) * E + e0 + ec);
+        *reinterpret_cast<uint4 *>(&tile[kr][ec]) = v;
+    }
+    __syncthreads();
+    for (int c = threadIdx.x; c < 512; c += 256) {
+        const int er = c & 63, kc = (c >> 6) * 8; // neighbouring lanes read neighbouring columns
+        uint32_t w[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            w[j] = (uint32_t)tile[kc + 2 * j][er] | ((uint32_t)tile[kc + 2 * j + 1][er] << 16);
+        *reinterpret_cast<uint4 *>(wgt + (size_t)(e0 + er) * d + k0 + kc) =
+            make_uint4(w[0], w[1], w[2], w[3]);
+    }
+}
+
+// Any E: element by element.
 __global__ __launch_bounds__(256) void transpose_wg_kernel(const uint16_t *__restrict__ wg,
                                                            uint16_t *__restrict__ wgt, int d,
                                                            int E)
@@ -62,10 +101,9 @@ __global__ __launch_bounds__(256) void transpose_wg_kernel(const uint16_t *__res
 
 constexpr int RBT = 64;   // tokens per tile
 constexpr int RBK = 64;   // K step
-constexpr int RRING = 78 * 1024;
 
-template <int BE>
-__global__ __launch_bounds__(256, 2) void router_logits_kernel(
+template <int BE, int RRING, int MINB>
+__global__ __launch_bounds__(256, MINB) void router_logits_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ wgt,
     float *__restrict__ partial, int T, int d, int E, int n_et, int sk_count, int total)
 {
@@ -82,11 +120,13 @@ __global__ __launch_bounds__(256, 2) void router_logits_kernel(
     const int w = xcd_remap(blockIdx.x, total);
     if (w < 0)
         return;
-    // work order: token tile, then K slice, then expert tile (the expert tiles
-    // of one token tile and slice read the same x rows)
+    // work order: K slice, then token tile, then expert tile.  The XCD remap
+    // gives each XCD a contiguous range, so the workgroups of one XCD share
+    // one slice of W_g^T in their L2 while each streams its own x rows.
+    const int n_tt = total / (n_et * sk_count);
     const int et = w % n_et;
-    const int sk = (w / n_et) % sk_count;
-    const int tt = w / (n_et * sk_count);
+    const int tt = (w / n_et) % n_tt;
+    const int sk = w / (n_et * n_tt);
     const int t0 = tt * RBT, e0 = et * BE;
     const int steps = d / RBK;
     const int s_lo = steps * sk / sk_count, s_hi = steps * (sk + 1) / sk_count;
@@ -199,16 +239,32 @@ __device__ __forceinline__ float key_value(uint64_t key)
     return __uint_as_float(u);
 }
 
+// v = max(v, v of the lane that DPP control CTRL selects), for the rows in
+// ROW_MASK; a lane without a source keeps its own value.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint64_t max_dpp(uint64_t v)
+{
+    const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+    const uint32_t olo = (uint32_t)__builtin_amdgcn_update_dpp((int)lo, (int)lo, CTRL, ROW_MASK, 0xF, false);
+    const uint32_t ohi = (uint32_t)__builtin_amdgcn_update_dpp((int)hi, (int)hi, CTRL, ROW_MASK, 0xF, false);
+    const uint64_t o = ((uint64_t)ohi << 32) | olo;
+    return o > v ? o : v;
+}
+
+// Maximum over the wavefront, returned in every lane: within each 16-lane row
+// by quad permutes and the half-row / row mirrors, across rows by the row
+// broadcasts of lanes 15 and 31 (lane 63 then holds the total).
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v)
 {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        const uint32_t lo = __shfl_xor((unsigned)(v & 0xffffffffu), off, 64);
-        const uint32_t hi = __shfl_xor((unsigned)(v >> 32), off, 64);
-        const uint64_t o = ((uint64_t)hi << 32) | lo;
-        v = o > v ? o : v;
-    }
-    return v;
+    v = max_dpp<0xB1, 0xF>(v);  // quad_perm [1, 0, 3, 2]
+    v = max_dpp<0x4E, 0xF>(v);  // quad_perm [2, 3, 0, 1]
+    v = max_dpp<0x141, 0xF>(v); // row_half_mirror
+    v = max_dpp<0x140, 0xF>(v); // row_mirror
+    v = max_dpp<0x142, 0xA>(v); // row_bcast:15 into rows 1 and 3
+    v = max_dpp<0x143, 0xC>(v); // row_bcast:31 into rows 2 and 3
+    const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+    const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
+    return ((uint64_t)hi << 32) | lo;
 }
 
 // The wave's own LDS operations have completed (lgkmcnt(0)); the compiler
@@ -361,18 +417,22 @@ hipError_t launch_route(const Dims &dm, const uint16_t *x, const uint16_t *w_gat
     const int epad = router_epad(E);
     uint16_t *wgt = reinterpret_cast<uint16_t *>(ws + wl.wg_t);
     float *partial = reinterpret_cast<float *>(ws + wl.logits);
-    transpose_wg_kernel<<<dim3(d / 64, epad / 64), 256, 0, st>>>(w_gate, wgt, d, E);
+    if (E % 8 == 0)
+        transpose_wg_vec_kernel<<<dim3(d / 64, epad / 64), 256, 0, st>>>(w_gate, wgt, d, E);
+    else
+        transpose_wg_kernel<<<dim3(d / 64, epad / 64), 256, 0, st>>>(w_gate, wgt, d, E);
     const int sk = router_ksplit(T, E, d);
     const int n_tt = (T + RBT - 1) / RBT;
-    if (epad % 128 == 0) {
-        const int n_et = epad / 128, total = n_tt * n_et * sk;
-        router_logits_kernel<128><<<xcd_grid(total), 256, 0, st>>>(x, wgt, partial, T, d, E,
-                                                                   n_et, sk, total);
-    } else {
-        const int n_et = epad / 64, total = n_tt * n_et * sk;
-        router_logits_kernel<64><<<xcd_grid(total), 256, 0, st>>>(x, wgt, partial, T, d, E,
-                                                                  n_et, sk, total);
-    }
+    const int be = router_be(E), n_et = epad / be, total = n_tt * n_et * sk;
+    if (be == 256)
+        router_logits_kernel<256, 156 * 1024, 1><<<xcd_grid(total), 256, 0, st>>>(
+            x, wgt, partial, T, d, E, n_et, sk, total);
+    else if (be == 128)
+        router_logits_kernel<128, 78 * 1024, 2><<<xcd_grid(total), 256, 0, st>>>(
+            x, wgt, partial, T, d, E, n_et, sk, total);
+    else
+        router_logits_kernel<64, 78 * 1024, 2><<<xcd_grid(total), 256, 0, st>>>(
+            x, wgt, partial, T, d, E, n_et, sk, total);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
