@@ -29,6 +29,11 @@
 // on the host.  The work order is expert-major, then N tile, then M tile, and
 // the XCD remap gives each XCD a contiguous range of it: the N tiles of one
 // expert run side by side and share that expert's rows in one L2.
+//
+// Epilogue.  Results go from the accumulators straight to global memory: a
+// 4x4 transpose inside each lane quad (DPP) turns the MFMA layout into
+// 8-byte row pieces, converted to bf16 by v_cvt_pk_bf16_f32.  No LDS is used,
+// so the whole ring serves the K loop.
 #include <type_traits>
 
 #include "moe_internal.hpp"
@@ -37,9 +42,6 @@
 namespace moe {
 namespace {
 
-#ifndef MOE_GEMM_MIN_BLOCKS
-#define MOE_GEMM_MIN_BLOCKS 1 // workgroups per CU the register budget must allow
-#endif
 
 struct GemmArgs {
     const void *A;              // [rows, K] bf16, or E4M3 codes (A8)
@@ -50,6 +52,7 @@ struct GemmArgs {
     const uint16_t *B1;         // [E, N, K] (gate/up GEMM: W3) or null
     uint16_t *out;              // [rows, N]
     int E, N, K;
+    int rot;                    // 1: each N tile starts its K walk at its own offset
 };
 
 // Tile work of expert e is ceil(rows_e / BM) * (N / BN) tiles.  Wave 0 of the
@@ -96,11 +99,44 @@ __device__ __forceinline__ void decode_work(const int32_t *__restrict__ rows, in
     }
 }
 
+// Exchange with the lane of the quad that CTRL (a quad_perm) names.
+template <int CTRL>
+__device__ __forceinline__ float quad_dpp(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// 4x4 transpose inside a lane quad.  On entry lane c (= lane % 4) holds
+// v[q] = M[q][c]; returns row c of M, columns 0..3, as four bf16 (RNE),
+// lowest column first.  Every lane of the wave must take part.
+__device__ __forceinline__ uint2 quad_transpose_bf16(const float v[4], int c)
+{
+    // with lane c^2: keep rows rb, rb+1 (rb = 2 for c >= 2, else 0)
+    const bool hi = c & 2;
+    const float r0 = quad_dpp<0x4E>(hi ? v[0] : v[2]); // M[rb][c^2]
+    const float r1 = quad_dpp<0x4E>(hi ? v[1] : v[3]); // M[rb+1][c^2]
+    const float x0 = hi ? v[2] : v[0], x1 = hi ? v[3] : v[1]; // M[rb][c], M[rb+1][c]
+    // with lane c^1: keep row R = rb + (c & 1)
+    const bool odd = c & 1;
+    const float u0 = quad_dpp<0xB1>(odd ? x0 : x1); // M[R][c^1]
+    const float u1 = quad_dpp<0xB1>(odd ? r0 : r1); // M[R][c^3]
+    const float k0 = odd ? x1 : x0, k1 = odd ? r1 : r0; // M[R][c], M[R][c^2]
+    float o[4];
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+        const int dlt = cc ^ c;
+        o[cc] = dlt == 0 ? k0 : dlt == 1 ? u0 : dlt == 2 ? k1 : u1;
+    }
+    return make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+}
+
 // A8: the A operand is E4M3 codes with one fp32 scale per row (FP8
 // dispatch); its fragments are widened to bf16 (exact) before the MFMA and
 // the row scale multiplies the fp32 sums in the epilogue.
-template <int BM, int BN, int BK, int RING, int WM, int WN, bool DUAL, bool A8>
-__global__ __launch_bounds__(256, MOE_GEMM_MIN_BLOCKS) void grouped_gemm_kernel(GemmArgs g)
+// MINB: workgroups per CU the register budget must allow (RING * MINB fits
+// the CU's 160 KB of LDS).
+template <int BM, int BN, int BK, int RING, int MINB, int WM, int WN, bool DUAL, bool A8>
+__global__ __launch_bounds__(256, MINB) void grouped_gemm_kernel(GemmArgs g)
 {
     static_assert(WM * WN == 4, "4 waves");
     static_assert(!A8 || BK == 64, "the E4M3 A path reads both 32-deep halves of a 64-deep step");
@@ -115,8 +151,6 @@ __global__ __launch_bounds__(256, MOE_GEMM_MIN_BLOCKS) void grouped_gemm_kernel(
     constexpr int B_BYTES = NB * BK * 2;
     constexpr int WTN = BN / WN;                      // wave tile columns
     constexpr int RT = BM / 16 / WM, CT = WTN / 16;   // 16x16 MFMA tiles per wave
-    constexpr int LDC = BN + 8;                       // epilogue row (elements)
-    static_assert(BM * LDC * 2 <= RING, "epilogue tile fits in the ring");
     static_assert(2 * (BM * BK * A_EB + B_BYTES) <= RING, "two full stages fit in the ring");
     // Wave (wm, wn) owns the 16-row slices wm, wm+WM, wm+2*WM, ... of the tile
     // (interleaved, so a partly filled tile keeps every wave busy) and the
@@ -189,10 +223,19 @@ __global__ __launch_bounds__(256, MOE_GEMM_MIN_BLOCKS) void grouped_gemm_kernel(
     const int stage = a_bytes + B_BYTES;
     const int S = min(rows_valid > 192 ? 2 : 8, RING / stage);
 
+    // K walk.  When the B rows lie a multiple of 4 KB apart, workgroups that
+    // read the same 128-byte column of every row at the same time load a
+    // few HBM channels only; starting each N tile's walk at its own step
+    // spreads them.  The M tiles of one N tile keep one start, so they stay
+    // in step and share the weight tile in L2.  The sum over K is then
+    // taken in the rotated (but fixed) order.
+    const int nsteps = K / BK;
+    const int krot = g.rot ? (n_tile * 5) % nsteps : 0;
     const uint32_t lds_base = (uint32_t)(uintptr_t)(LDS_AS char *)smem;
     auto issue = [&](int step, int slot) {
         const uint32_t st = lds_base + slot * stage;
-        const int k0 = step * BK;
+        const int ks = step + krot;
+        const int k0 = (ks < nsteps ? ks : ks - nsteps) * BK;
 #pragma unroll
         for (int j = 0; j < A_PW; ++j)
             if ((4 * j + wave) * RPI_A < rows_valid)
@@ -202,7 +245,6 @@ __global__ __launch_bounds__(256, MOE_GEMM_MIN_BLOCKS) void grouped_gemm_kernel(
             dma16(bsrc[j] + k0, st + a_bytes + (4 * j + wave) * 1024);
     };
 
-    const int nsteps = K / BK;
     for (int u = 0; u < S - 1 && u < nsteps; ++u)
         issue(u, u);
 
@@ -393,39 +435,39 @@ __global__ __launch_bounds__(256, MOE_GEMM_MIN_BLOCKS) void grouped_gemm_kernel(
             }
         }
 
-        // Epilogue through LDS so that global stores are whole 16-byte row
-        // pieces.  D layout of a 16x16 MFMA tile: lane holds rows
-        // 4*(lane/16)+q, column lane%16.
-        __syncthreads();
-        uint16_t *Cs = reinterpret_cast<uint16_t *>(smem);
+        // Epilogue straight from registers.  D layout of a 16x16 MFMA tile:
+        // lane holds rows 4*(lane/16)+q (q = 0..3) of column lane%16.  A 4x4
+        // transpose inside each lane quad (two DPP exchanges) gives lane c
+        // of a quad row 4*(lane/16)+c of the quad's four columns, so each
+        // lane stores 8 bytes and one wave store covers 16 rows x 32 bytes.
+        const int c4 = lane & 3;
 #pragma unroll
-        for (int i = 0; i < NA; ++i)
+        for (int i = 0; i < NA; ++i) {
+            const int mq = (wm + WM * i) * 16 + 4 * (lane >> 4); // row of q = 0
+            float sr[4] = {1.f, 1.f, 1.f, 1.f};
+            if constexpr (A8) { // the rows' dequantization scales
 #pragma unroll
-            for (int j = 0; j < CT; ++j)
+                for (int q = 0; q < 4; ++q)
+                    sr[q] = mq + q < rows_valid ? g.a_scale[row0 + mq + q] : 0.f;
+            }
+            const int m = mq + c4;
+#pragma unroll
+            for (int j = 0; j < CT; ++j) {
+                float v[4];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const int m = (wm + WM * i) * 16 + 4 * (lane >> 4) + q;
-                    const int n = wn * WTN + j * 16 + (lane & 15);
-                    float v = acc0[i][j][q];
-                    float up = DUAL ? acc1[i][j][q] : 0.f;
-                    if constexpr (A8) { // the row's dequantization scale
-                        const float sr = m < rows_valid ? g.a_scale[row0 + m] : 0.f;
-                        v *= sr;
-                        up *= sr;
-                    }
+                    float gt = acc0[i][j][q] * sr[q];
                     if constexpr (DUAL) {
-                        const float gt = v;
-                        v = gt / (1.f + expf(-gt)) * up; // SiLU(g) * u
+                        const float up = acc1[i][j][q] * sr[q];
+                        gt = gt / (1.f + expf(-gt)) * up; // SiLU(g) * u
                     }
-                    Cs[m * LDC + n] = (uint16_t)f32_to_bf16_rne(v);
+                    v[q] = gt;
                 }
-        __syncthreads();
-        constexpr int CPR = BN / 8; // 16-byte pieces per output row
-        for (int c = tid; c < BM * CPR; c += 256) {
-            const int r = c / CPR, cc = c % CPR;
-            if (r < rows_valid)
-                *reinterpret_cast<uint4 *>(g.out + (row0 + r) * N + n0 + cc * 8) =
-                    *reinterpret_cast<const uint4 *>(Cs + r * LDC + cc * 8);
+                const uint2 o = quad_transpose_bf16(v, c4);
+                const int n = wn * WTN + j * 16 + 4 * ((lane & 15) >> 2);
+                if (m < rows_valid)
+                    *reinterpret_cast<uint2 *>(g.out + (row0 + m) * N + n0 + n) = o;
+            }
         }
     };
 
@@ -449,8 +491,17 @@ __global__ __launch_bounds__(256, MOE_GEMM_MIN_BLOCKS) void grouped_gemm_kernel(
 #ifndef MOE_GEMM_BK
 #define MOE_GEMM_BK 64
 #endif
-#ifndef MOE_GEMM_RING
-#define MOE_GEMM_RING (156 * 1024)
+#ifndef MOE_GU_RING
+#define MOE_GU_RING (156 * 1024)
+#endif
+#ifndef MOE_GU_MINB
+#define MOE_GU_MINB 1
+#endif
+#ifndef MOE_DN_RING
+#define MOE_DN_RING (156 * 1024)
+#endif
+#ifndef MOE_DN_MINB
+#define MOE_DN_MINB 1
 #endif
 #ifndef MOE_GEMM_BN1
 #define MOE_GEMM_BN1 128
@@ -458,11 +509,38 @@ __global__ __launch_bounds__(256, MOE_GEMM_MIN_BLOCKS) void grouped_gemm_kernel(
 #ifndef MOE_GEMM_BN2
 #define MOE_GEMM_BN2 256
 #endif
-constexpr int kBM = 256;             // M tile of both GEMMs
-constexpr int kBN1 = MOE_GEMM_BN1;   // h columns per gate/up tile (x2 for W1 and W3)
-constexpr int kBN2 = MOE_GEMM_BN2;   // output columns per down tile
-constexpr int kBK = MOE_GEMM_BK;     // K step
-constexpr int kRing = MOE_GEMM_RING; // LDS ring bytes (one workgroup per CU)
+#ifndef MOE_GEMM_ROT_GU
+#define MOE_GEMM_ROT_GU 0
+#endif
+#ifndef MOE_GEMM_ROT_DN
+#define MOE_GEMM_ROT_DN 1
+#endif
+#ifndef MOE_GU_BM
+#define MOE_GU_BM 256
+#endif
+#ifndef MOE_DN_BM
+#define MOE_DN_BM 256
+#endif
+constexpr int kBM1 = MOE_GU_BM;       // M tile of the gate/up GEMM
+constexpr int kBM2 = MOE_DN_BM;       // and of the down GEMM
+constexpr int kBN1 = MOE_GEMM_BN1;    // h columns per gate/up tile (x2 for W1 and W3)
+constexpr int kBN2 = MOE_GEMM_BN2;    // output columns per down tile
+constexpr int kBK = MOE_GEMM_BK;      // K step
+constexpr int kRing1 = MOE_GU_RING;   // LDS ring bytes of a gate/up workgroup
+constexpr int kMinB1 = MOE_GU_MINB;   // gate/up workgroups per CU
+constexpr int kRing2 = MOE_DN_RING;   // and of the down GEMM
+constexpr int kMinB2 = MOE_DN_MINB;
+
+// Rotated K walks for B rows of K bf16 values whose pitch is a power of two
+// of at least 4 KB (measured: DeepSeek-V3 down GEMM, K = 2048, 1.64 -> 1.61
+// ms).  The gate/up GEMM keeps the plain walk: there the N tiles of an expert
+// share its rows in L2 only while they walk K together (Mixtral gate/up,
+// K = 4096: 1.81 -> 1.92 ms rotated).
+int rotate_k(int K)
+{
+    const int pitch = K * 2;
+    return pitch >= 4096 && (pitch & (pitch - 1)) == 0 ? 1 : 0;
+}
 
 } // namespace
 
@@ -471,10 +549,10 @@ static void launch_gate_up_t(const Dims &dm, const GemmArgs &a, long long mtiles
                              hipStream_t st)
 {
     if (dm.H % kBN1 == 0) // H is a multiple of 64; the wide tile needs a multiple of kBN1
-        grouped_gemm_kernel<kBM, kBN1, kBK, kRing, 2, 2, true, A8>
+        grouped_gemm_kernel<kBM1, kBN1, kBK, kRing1, kMinB1, 2, 2, true, A8>
             <<<xcd_grid((int)(mtiles_max * (dm.H / kBN1))), 256, 0, st>>>(a);
     else
-        grouped_gemm_kernel<kBM, 64, kBK, kRing, 2, 2, true, A8>
+        grouped_gemm_kernel<kBM1, 64, kBK, kRing1, kMinB1, 2, 2, true, A8>
             <<<xcd_grid((int)(mtiles_max * (dm.H / 64))), 256, 0, st>>>(a);
 }
 
@@ -484,8 +562,9 @@ hipError_t launch_gate_up(const Dims &dm, const void *send_buf, const float *sen
 {
     if (dm.send_rows == 0)
         return hipSuccess;
-    const long long mtiles_max = (dm.send_rows + kBM - 1) / kBM + dm.E;
-    GemmArgs a{send_buf, send_scale, expert_offset, expert_kept, w1, w3, h, dm.E, dm.H, dm.d};
+    const long long mtiles_max = (dm.send_rows + kBM1 - 1) / kBM1 + dm.E;
+    GemmArgs a{send_buf, send_scale, expert_offset, expert_kept, w1, w3, h, dm.E, dm.H, dm.d,
+               MOE_GEMM_ROT_GU ? rotate_k(dm.d) : 0};
     if (dm.fp8)
         launch_gate_up_t<true>(dm, a, mtiles_max, st);
     else
@@ -499,13 +578,14 @@ hipError_t launch_down(const Dims &dm, const uint16_t *h, const int32_t *expert_
 {
     if (dm.send_rows == 0)
         return hipSuccess;
-    const long long mtiles_max = (dm.send_rows + kBM - 1) / kBM + dm.E;
-    GemmArgs a{h, nullptr, expert_offset, expert_kept, w2, nullptr, expert_out, dm.E, dm.d, dm.H};
+    const long long mtiles_max = (dm.send_rows + kBM2 - 1) / kBM2 + dm.E;
+    GemmArgs a{h, nullptr, expert_offset, expert_kept, w2, nullptr, expert_out, dm.E, dm.d, dm.H,
+               MOE_GEMM_ROT_DN ? rotate_k(dm.H) : 0};
     if (dm.d % kBN2 == 0)
-        grouped_gemm_kernel<kBM, kBN2, kBK, kRing, 2, 2, false, false>
+        grouped_gemm_kernel<kBM2, kBN2, kBK, kRing2, kMinB2, 2, 2, false, false>
             <<<xcd_grid((int)(mtiles_max * (dm.d / kBN2))), 256, 0, st>>>(a);
     else
-        grouped_gemm_kernel<kBM, 64, kBK, kRing, 2, 2, false, false>
+        grouped_gemm_kernel<kBM2, 64, kBK, kRing2, kMinB2, 2, 2, false, false>
             <<<xcd_grid((int)(mtiles_max * (dm.d / 64))), 256, 0, st>>>(a);
     return hipGetLastError();
 }
