@@ -30,10 +30,9 @@
 // the XCD remap gives each XCD a contiguous range of it: the N tiles of one
 // expert run side by side and share that expert's rows in one L2.
 //
-// Epilogue.  Results go from the accumulators straight to global memory: a
-// 4x4 transpose inside each lane quad (DPP) turns the MFMA layout into
-// 8-byte row pieces, converted to bf16 by v_cvt_pk_bf16_f32.  No LDS is used,
-// so the whole ring serves the K loop.
+// Epilogue.  A 4x4 transpose inside each lane quad (DPP) turns the MFMA
+// layout into 8-byte row pieces, converted to bf16 by v_cvt_pk_bf16_f32; they
+// are gathered in LDS (the ring is free by then) and leave as 16-byte pieces.
 #include <type_traits>
 
 #include "moe_internal.hpp"
@@ -435,11 +434,19 @@ __global__ __launch_bounds__(256, MINB) void grouped_gemm_kernel(GemmArgs g)
             }
         }
 
-        // Epilogue straight from registers.  D layout of a 16x16 MFMA tile:
-        // lane holds rows 4*(lane/16)+q (q = 0..3) of column lane%16.  A 4x4
-        // transpose inside each lane quad (two DPP exchanges) gives lane c
-        // of a quad row 4*(lane/16)+c of the quad's four columns, so each
-        // lane stores 8 bytes and one wave store covers 16 rows x 32 bytes.
+        // Epilogue through LDS.  D layout of a 16x16 MFMA tile: lane holds
+        // rows 4*(lane/16)+q (q = 0..3) of column lane%16.  A 4x4 transpose
+        // inside each lane quad (two DPP exchanges) gives lane c of a quad row
+        // 4*(lane/16)+c of the quad's four columns, packed to bf16 and written
+        // to LDS as one 8-byte piece.  LDS rows are LDC elements apart, 32
+        // bytes past a multiple of 256, so the 8 rows one write covers per
+        // pass fall in distinct banks.  The tile then leaves in 16-byte
+        // pieces, each wave store covering whole rows (a third of the time of
+        // 32-byte row pieces straight from the quads).
+        constexpr int LDC = BN + 16;
+        static_assert(BM * LDC * 2 <= RING, "epilogue tile fits in the ring");
+        __syncthreads(); // every wave is done with the ring
+        uint16_t *Cs = reinterpret_cast<uint16_t *>(smem);
         const int c4 = lane & 3;
 #pragma unroll
         for (int i = 0; i < NA; ++i) {
@@ -465,9 +472,15 @@ __global__ __launch_bounds__(256, MINB) void grouped_gemm_kernel(GemmArgs g)
                 }
                 const uint2 o = quad_transpose_bf16(v, c4);
                 const int n = wn * WTN + j * 16 + 4 * ((lane & 15) >> 2);
-                if (m < rows_valid)
-                    *reinterpret_cast<uint2 *>(g.out + (row0 + m) * N + n0 + n) = o;
+                *reinterpret_cast<uint2 *>(Cs + m * LDC + n) = o;
             }
+        }
+        __syncthreads();
+        constexpr int CPR = BN / 8; // 16-byte pieces per output row
+        for (int c = tid; c < rows_valid * CPR; c += 256) {
+            const int r = c / CPR, cc = c % CPR;
+            *reinterpret_cast<uint4 *>(g.out + (row0 + r) * N + n0 + cc * 8) =
+                *reinterpret_cast<const uint4 *>(Cs + r * LDC + cc * 8);
         }
     };
 
