@@ -297,20 +297,44 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(
     const int t = blockIdx.x * 4 + wave;
     if (t >= T)
         return;
+    // The lane's partial sums are loaded in batches of SKB slices, all
+    // loads of a batch issued before any is added (one memory round trip per
+    // batch instead of one per slice), then summed in slice order.
+    constexpr int SKB = 8;
+    float h[V], bv[V];
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+        const int e = lane + 64 * j;
+        h[j] = 0.f;
+        bv[j] = (bias && e < E) ? bias[e] : 0.f;
+    }
+    for (int s0 = 0; s0 < sk_count; s0 += SKB) {
+        float pv[V][SKB];
+#pragma unroll
+        for (int j = 0; j < V; ++j)
+#pragma unroll
+            for (int u = 0; u < SKB; ++u) {
+                const int e = lane + 64 * j, s = s0 + u;
+                pv[j][u] = (e < E && s < sk_count) ? partial[((size_t)s * T + t) * E + e] : 0.f;
+            }
+#pragma unroll
+        for (int j = 0; j < V; ++j)
+#pragma unroll
+            for (int u = 0; u < SKB; ++u)
+                if (s0 + u < sk_count)
+                    h[j] = s0 + u == 0 ? pv[j][u] : h[j] + pv[j][u];
+    }
     uint64_t key[V];
 #pragma unroll
     for (int j = 0; j < V; ++j) {
         const int e = lane + 64 * j;
         key[j] = 0ull; // sorts below every real key
         if (e < E) {
-            float h = partial[(size_t)t * E + e];
-            for (int s = 1; s < sk_count; ++s)
-                h += partial[((size_t)s * T + t) * E + e];
             if (bias)
-                h += bias[e];
+                h[j] += bv[j];
             if (logits_out)
-                logits_out[(size_t)t * E + e] = h;
-            key[j] = topk_key(h, e, E);
+                logits_out[(size_t)t * E + e] = h[j];
+            key[j] = topk_key(h[j], e, E);
         }
     }
     if (G > 1 && M < G) {
@@ -350,8 +374,11 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(
         }
     }
     float hmax = 0.f, denom = 0.f;
-    // k rounds of a wave-wide arg-max; the winner's key is retired.  Lane
-    // (s % 64) stores rank s's index and its unnormalised weight.
+    // k rounds of a wave-wide arg-max; the winner's key is retired.  Lane s
+    // keeps rank s's index and unnormalised weight (ranks past 64: lane
+    // s % 64 stores them and rereads them to normalise).
+    int my_e = 0;
+    float my_p = 0.f;
     for (int s = 0; s < k; ++s) {
         uint64_t best = 0;
 #pragma unroll
@@ -369,12 +396,20 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(
         const float p = expf(v - hmax);
         denom += p; // same order in every lane
         if (lane == (s & 63)) {
-            topk_idx[(size_t)t * k + s] = e;
-            topk_w[(size_t)t * k + s] = p;
+            if (s < 64) {
+                my_e = e;
+                my_p = p;
+            } else {
+                topk_idx[(size_t)t * k + s] = e;
+                topk_w[(size_t)t * k + s] = p;
+            }
         }
     }
-    // normalise; each lane rereads only what it wrote itself
-    for (int s = lane; s < k; s += 64) {
+    if (lane < k) {
+        topk_idx[(size_t)t * k + lane] = my_e;
+        topk_w[(size_t)t * k + lane] = my_p / denom;
+    }
+    for (int s = lane + 64; s < k; s += 64) {
         const size_t o = (size_t)t * k + s;
         topk_w[o] = topk_w[o] / denom;
     }
