@@ -55,6 +55,10 @@ __device__ __forceinline__ bool entry_valid(const int32_t *row, int s, int E)
     return true;
 }
 
+// KM > 0: k <= KM, and a token's k expert ids are loaded once into registers
+// (all loads in flight together), so the validity checks and the bitmap
+// updates run on registers; KM == 0: any k, read from memory as needed.
+template <int KM>
 __global__ __launch_bounds__(kChunk) void count_kernel(const int32_t *__restrict__ topk_idx,
                                                        int T, int k, int E,
                                                        int32_t *__restrict__ pos_in_chunk,
@@ -66,32 +70,67 @@ __global__ __launch_bounds__(kChunk) void count_kernel(const int32_t *__restrict
     const int i = threadIdx.x;
     const int chunk = blockIdx.x;
     const int t = chunk * kChunk + i;
+    const int32_t *row = topk_idx + (size_t)t * k;
+    int32_t ids[KM > 0 ? KM : 1];
+    bool ok[KM > 0 ? KM : 1];
+    if constexpr (KM > 0) {
+#pragma unroll
+        for (int s = 0; s < KM; ++s)
+            ids[s] = (t < T && s < k) ? row[s] : -1;
+#pragma unroll
+        for (int s = 0; s < KM; ++s) {
+            ok[s] = s < k && ids[s] >= 0 && ids[s] < E;
+#pragma unroll
+            for (int s2 = 0; s2 < s; ++s2)
+                ok[s] = ok[s] && ids[s2] != ids[s];
+        }
+    }
     for (int w = i; w < E * kWords; w += kChunk)
         bm[w] = 0u;
     if (i == 0)
         s_invalid = 0;
     __syncthreads();
-    const int32_t *row = topk_idx + (size_t)t * k;
     const uint32_t bit = 1u << (i & 31);
     if (t < T) {
-        for (int s = 0; s < k; ++s)
-            if (entry_valid(row, s, E))
-                atomicOr(&bm[row[s] * kWords + (i >> 5)], bit);
+        if constexpr (KM > 0) {
+#pragma unroll
+            for (int s = 0; s < KM; ++s)
+                if (ok[s])
+                    atomicOr(&bm[ids[s] * kWords + (i >> 5)], bit);
+        } else {
+            for (int s = 0; s < k; ++s)
+                if (entry_valid(row, s, E))
+                    atomicOr(&bm[row[s] * kWords + (i >> 5)], bit);
+        }
     }
     __syncthreads();
     if (t < T) {
         int invalid = 0;
-        for (int s = 0; s < k; ++s) {
-            int32_t p = -1;
-            if (entry_valid(row, s, E)) {
-                const uint32_t *m = bm + row[s] * kWords;
-                p = __popc(m[i >> 5] & (bit - 1u));
-                for (int w = 0; w < (i >> 5); ++w)
-                    p += __popc(m[w]);
-            } else {
-                ++invalid;
+        auto position = [&](int e) { // earlier tokens of the chunk routed to e
+            const uint32_t *m = bm + e * kWords;
+            int p = __popc(m[i >> 5] & (bit - 1u));
+            for (int w = 0; w < (i >> 5); ++w)
+                p += __popc(m[w]);
+            return p;
+        };
+        if constexpr (KM > 0) {
+#pragma unroll
+            for (int s = 0; s < KM; ++s) {
+                if (s >= k)
+                    break;
+                const int32_t p = ok[s] ? position(ids[s]) : -1;
+                invalid += ok[s] ? 0 : 1;
+                pos_in_chunk[(size_t)t * k + s] = p;
             }
-            pos_in_chunk[(size_t)t * k + s] = p;
+        } else {
+            for (int s = 0; s < k; ++s) {
+                int32_t p = -1;
+                if (entry_valid(row, s, E))
+                    p = position(row[s]);
+                else
+                    ++invalid;
+                pos_in_chunk[(size_t)t * k + s] = p;
+            }
         }
         if (invalid)
             atomicAdd(&s_invalid, invalid);
@@ -130,9 +169,18 @@ __global__ __launch_bounds__(kMaxExperts) void scan_kernel(
     }
     int n = 0, kept = 0;
     if (e < E) {
-        for (int c = 0; c < nchunks; ++c) {
-            chunk_base[(size_t)c * E + e] = n;
-            n += chunk_counts[(size_t)c * E + e];
+        // the chunk counts are loaded 16 at a time, all in flight together
+        for (int c0 = 0; c0 < nchunks; c0 += 16) {
+            int cv[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u)
+                cv[u] = c0 + u < nchunks ? chunk_counts[(size_t)(c0 + u) * E + e] : 0;
+#pragma unroll
+            for (int u = 0; u < 16; ++u)
+                if (c0 + u < nchunks) {
+                    chunk_base[(size_t)(c0 + u) * E + e] = n;
+                    n += cv[u];
+                }
         }
         kept = (C < 0 || n < C) ? n : (int)C;
         expert_count[e] = n;
@@ -551,8 +599,20 @@ hipError_t launch_dispatch(const Dims &dm, const uint16_t *x, const int32_t *top
     int32_t *by_expert = reinterpret_cast<int32_t *>(ws + wl.by_expert);
     if (dm.nchunks > 0) {
         const size_t lds = (size_t)dm.E * kWords * sizeof(uint32_t);
-        count_kernel<<<dm.nchunks, kChunk, lds, st>>>(topk_idx, dm.T, dm.k, dm.E, slot,
-                                                       chunk_counts, chunk_invalid);
+#define MOE_COUNT(KM)                                                                        \
+    count_kernel<KM><<<dm.nchunks, kChunk, lds, st>>>(topk_idx, dm.T, dm.k, dm.E, slot,      \
+                                                      chunk_counts, chunk_invalid)
+        if (dm.k <= 2)
+            MOE_COUNT(2);
+        else if (dm.k <= 4)
+            MOE_COUNT(4);
+        else if (dm.k <= 8)
+            MOE_COUNT(8);
+        else if (dm.k <= 16)
+            MOE_COUNT(16);
+        else
+            MOE_COUNT(0);
+#undef MOE_COUNT
     }
     scan_kernel<<<1, kMaxExperts, 0, st>>>(dm.T, dm.k, dm.E, dm.D, dm.my_rank, dm.d, dm.fp8,
                                            (long long)dm.capacity, dm.nchunks, chunk_counts,
