@@ -459,25 +459,26 @@ __global__ __launch_bounds__(256) void permute_kernel(
         if constexpr (FP8)
             sc = row_scale_e4m3(src, nvec, lane);
         for (int s0 = 0; s0 < k; s0 += kSlotGroup) {
-            // the slots are wave-uniform: resolve them in scalar registers
-            int dst[kSlotGroup];
+            // The slots are wave-uniform: resolve them in scalar registers,
+            // in two rounds of loads (positions and experts, then the chunk
+            // bases and expert offsets) with every load of a round in flight
+            // together; an entry with no position reads expert 0's values
+            // and ignores them.
+            int pq[kSlotGroup], eq[kSlotGroup], dst[kSlotGroup];
 #pragma unroll
             for (int q = 0; q < kSlotGroup; ++q) {
                 const int s = s0 + q;
-                int sl = -1;
-                if (s < k) {
-                    // in-chunk position (in-expert position if pos_final), or -1
-                    const int p = __builtin_amdgcn_readfirstlane(slot[(size_t)t * k + s]);
-                    if (p >= 0) {
-                        const int e = __builtin_amdgcn_readfirstlane(row[s]);
-                        const long long pos =
-                            pos_final ? p
-                                      : (long long)__builtin_amdgcn_readfirstlane(base[e]) + p;
-                        if (C < 0 || pos < C)
-                            sl = __builtin_amdgcn_readfirstlane(expert_offset[e]) + (int)pos;
-                    }
-                }
-                dst[q] = sl;
+                // in-chunk position (in-expert position if pos_final), or -1
+                pq[q] = s < k ? __builtin_amdgcn_readfirstlane(slot[(size_t)t * k + s]) : -1;
+                eq[q] = s < k ? __builtin_amdgcn_readfirstlane(row[s]) : 0;
+            }
+#pragma unroll
+            for (int q = 0; q < kSlotGroup; ++q) {
+                const int e = pq[q] >= 0 ? eq[q] : 0; // a valid entry's expert is in [0, E)
+                const long long pos =
+                    pos_final ? pq[q] : (long long)__builtin_amdgcn_readfirstlane(base[e]) + pq[q];
+                const int off = __builtin_amdgcn_readfirstlane(expert_offset[e]);
+                dst[q] = (pq[q] >= 0 && (C < 0 || pos < C)) ? off + (int)pos : -1;
             }
             // every lane has read the positions before lane 0 overwrites them
             __builtin_amdgcn_wave_barrier();
