@@ -156,7 +156,7 @@ __global__ __launch_bounds__(kMaxExperts) void scan_kernel(
     int32_t *__restrict__ rank_rows, moe_stats *__restrict__ stats,
     int32_t *__restrict__ all_offset)
 {
-    __shared__ int32_t s_n[kMaxExperts], s_kept[kMaxExperts];
+    __shared__ int32_t s_rank[kMaxExperts];
     __shared__ int32_t s_wave_sum[kMaxExperts / 64];
     __shared__ int s_kept_total, s_max, s_remote, s_invalid;
     const int e = threadIdx.x;
@@ -186,8 +186,6 @@ __global__ __launch_bounds__(kMaxExperts) void scan_kernel(
         expert_count[e] = n;
         expert_kept[e] = kept;
     }
-    s_n[e] = n;
-    s_kept[e] = kept;
     // exclusive scan of n over experts (dropless offsets): wave scan + wave totals
     int incl = n;
 #pragma unroll
@@ -200,8 +198,9 @@ __global__ __launch_bounds__(kMaxExperts) void scan_kernel(
         s_wave_sum[wave] = incl;
     __syncthreads();
     int wave_base = 0;
-    for (int w = 0; w < wave; ++w)
-        wave_base += s_wave_sum[w];
+#pragma unroll
+    for (int w = 0; w < kMaxExperts / 64; ++w) // all reads in flight together
+        wave_base += w < wave ? s_wave_sum[w] : 0;
     const int excl = wave_base + incl - n;
     if (e < E)
         expert_offset[e] = (C < 0) ? excl : (int)((long long)e * C);
@@ -209,18 +208,31 @@ __global__ __launch_bounds__(kMaxExperts) void scan_kernel(
         all_offset[e] = excl; // where expert e's assignments start in the by-expert list
     if (e == E - 1)
         expert_offset[E] = (C < 0) ? excl + n : (int)((long long)E * C);
-    // reductions
-    if (e < E) {
-        atomicAdd(&s_kept_total, kept);
-        atomicMax(&s_max, n);
-    }
+    // reductions: within each wave first (one LDS atomic per wave)
+    int inv = 0;
     for (int c = e; c < nchunks; c += kMaxExperts)
-        atomicAdd(&s_invalid, chunk_invalid[c]);
+        inv += chunk_invalid[c];
+    int kt = kept, mx = n;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        kt += __shfl_xor(kt, off, 64);
+        mx = max(mx, __shfl_xor(mx, off, 64));
+        inv += __shfl_xor(inv, off, 64);
+    }
+    if (lane == 0) {
+        atomicAdd(&s_kept_total, kt);
+        atomicMax(&s_max, mx);
+        atomicAdd(&s_invalid, inv);
+    }
     const int epr = E / D;
+    if (e < D)
+        s_rank[e] = 0;
+    __syncthreads();
+    if (e < E && kept)
+        atomicAdd(&s_rank[e / epr], kept);
+    __syncthreads();
     for (int r = e; r < D; r += kMaxExperts) {
-        int rows = 0;
-        for (int q = r * epr; q < (r + 1) * epr; ++q)
-            rows += s_kept[q];
+        const int rows = s_rank[r];
         rank_rows[r] = rows;
         if (r != my_rank)
             atomicAdd(&s_remote, rows);
