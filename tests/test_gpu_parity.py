@@ -96,7 +96,8 @@ def test_router_logits_and_selection(case):
     assert not bad.any(), f"routing differs beyond near-ties for tokens {np.nonzero(bad)[0][:8]}"
 
 
-@pytest.mark.parametrize("E,k", [(8, 2), (6, 3), (64, 2), (256, 8), (5, 5), (300, 7)])
+@pytest.mark.parametrize("E,k", [(8, 2), (6, 3), (64, 2), (256, 8), (5, 5), (300, 7),
+                                 (200, 70), (1024, 16)])
 def test_topk_on_identical_logits_with_ties(E, k):
     rng = np.random.default_rng(E * 7 + k)
     T = 333
@@ -156,6 +157,47 @@ def test_dispatch_invalid_and_repeated_entries(case):
                         cf=cfg.cf)
     assert r["stats"]["invalid_index"] > 0
     _assert_dispatch_equal(buf, r, r["stats"]["send_rows"])
+
+
+@pytest.mark.parametrize("k,cf", [(12, INF), (12, 1.0), (20, INF), (20, 0.75)])
+def test_dispatch_and_combine_large_k(k, cf):
+    """k above 8 (the count kernel's 16-slot and generic paths, the combine's
+    any-k path), with repeated and out-of-range expert ids mixed in:
+    dispatch bit-exact, combine within one bf16 ulp of the oracle's."""
+    T, d, E = 600, 128, 32
+    rng = np.random.default_rng(k * 10 + int(cf == INF))
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    bad = rng.integers(0, T, 40)
+    idx[bad, rng.integers(0, k, 40)] = rng.choice([-1, E, E + 5], 40)
+    idx[bad[:10], 1] = idx[bad[:10], 0]          # repeated experts within a token
+    w = rng.random((T, k)).astype(np.float32)
+    x = torch.randn(T, d, device=DEV).to(torch.bfloat16)
+    shape = api.Shape(T=T, d=d, E=E, k=k, H=64, D=4, capacity_factor=cf)
+    buf = api.LayerBuffers.allocate(shape, DEV)
+    _run_dispatch(shape, x, _i32(idx), buf)
+    torch.cuda.synchronize()
+    r = oracle.dispatch(bf16_bits(x), idx, T=T, d=d, E=E, D=4, my_rank=0, cf=cf)
+    assert r["stats"]["invalid_index"] > 0
+    _assert_dispatch_equal(buf, r, r["stats"]["send_rows"])
+    n = r["stats"]["send_rows"]
+    eo_bits = bf16_bits(torch.randn(max(n, 1), d).to(torch.bfloat16))[:n]
+    eo = torch.from_numpy(eo_bits.view(np.int16)).view(torch.bfloat16).to(DEV)
+    y = torch.empty(T, d, dtype=torch.bfloat16, device=DEV)
+    api.moe_combine(shape, eo, _i32(r["slot"]), _f32(w), None, y)
+    torch.cuda.synchronize()
+    want = bits_to_f64(oracle.combine(eo_bits, r["slot"], w))
+    got = t2f(y)
+    # fp32 accumulation of k terms, then one rounding to bf16: at most one bf16
+    # ulp of the result plus k+1 fp32 roundings of the sum of |terms|
+    # (cancellation can make the result far smaller than its terms)
+    rows = bits_to_f64(eo_bits)
+    mag = np.zeros((T, d))
+    for s in range(k):
+        sl = r["slot"][:, s]
+        m = sl >= 0
+        mag[m] += np.abs(w[m, s, None].astype(np.float64) * rows[sl[m]])
+    ulp = np.ldexp(1.0, np.frexp(np.abs(want))[1] - 8)
+    assert np.all(np.abs(got - want) <= np.maximum(ulp, 2.0 ** -133) + (k + 1) * 2.0 ** -24 * mag)
 
 
 def test_expert_ffn_stage(case):
