@@ -46,6 +46,9 @@ SMALL = {
                         x_std=1.0, wg_std=0.125, w_std=0.05, seed=15),
     "one_token": MoEConfig("one_token", T=1, d=128, E=8, k=2, H=128, cf=1.0, D=2,
                            x_std=1.0, wg_std=0.1, w_std=0.05, seed=16),
+    # H = 2048: W2 rows 4 KB apart, so the down GEMM takes its rotated K walk
+    "h2048": MoEConfig("h2048", T=200, d=128, E=4, k=2, H=2048, cf=INF, D=2,
+                       x_std=1.0, wg_std=0.1, w_std=0.03, seed=17),
 }
 
 DEV = "cuda"
