@@ -220,6 +220,10 @@ def main():
                     help="skip the expert-parallel rank-local GEMM measurement")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (scale reference for HBM counters)")
+    ap.add_argument("--flush-mall", action="store_true",
+                    help="read a 512 MiB buffer before every timed step, so the 256 MB "
+                         "last-level cache holds nothing of the previous step; the step time "
+                         "is then the sum of the stages' event times, without the read")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs the single-GPU share of the MoE layer only: every box here has "
@@ -287,12 +291,19 @@ def main():
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
               for _ in range(args.steps)]
     torch.cuda.synchronize()
+    scratch = (torch.ones(128 << 20, dtype=torch.float32, device=dev) if args.flush_mall
+               else None)
     t0 = time.perf_counter()
     for i in range(args.steps):
+        if scratch is not None:
+            scratch.sum()  # reads 512 MiB: clean lines, nothing left to write back
         step(events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
+    if scratch is not None:  # the stages' own time, without the reads between steps
+        ms_step = sum(e[j].elapsed_time(e[j + 1]) for e in events
+                      for j in range(len(stages))) / args.steps
     samples = {s: [events[i][j].elapsed_time(events[i][j + 1]) for i in range(args.steps)]
                for j, s in enumerate(stages)}
     stage_ms = {s: sum(v) / len(v) for s, v in samples.items()}
@@ -346,7 +357,8 @@ def main():
                    "drop_policy": cfg.drop_policy, "min_capacity": cfg.min_capacity,
                    "dispatch_fp8": cfg.dispatch_fp8, "n_groups": cfg.n_groups,
                    "group_limit": cfg.group_limit, "shared_H": cfg.shared_H,
-                   "D": cfg.D, "parallelism": "single GPU share (EP rank-local layout)"},
+                   "D": cfg.D, "parallelism": "single GPU share (EP rank-local layout)",
+                   "mall_flush": bool(args.flush_mall)},
         "grouped_gemm": {"tflops": round(gemm_flops / gemm_s / 1e12, 1),
                          "mfma_util": round(gemm_flops / gemm_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
                          "touched_experts": touched},
