@@ -135,9 +135,10 @@ __device__ __forceinline__ uint2 quad_transpose_bf16(const float v[4], int c)
 // MINB: workgroups per CU the register budget must allow (RING * MINB fits
 // the CU's 160 KB of LDS).
 template <int BM, int BN, int BK, int RING, int MINB, int WM, int WN, bool DUAL, bool A8>
-__global__ __launch_bounds__(256, MINB) void grouped_gemm_kernel(GemmArgs g)
+__global__ __launch_bounds__(WM * WN * 64, MINB) void grouped_gemm_kernel(GemmArgs g)
 {
-    static_assert(WM * WN == 4, "4 waves");
+    constexpr int NW = WM * WN; // waves per workgroup
+    static_assert(NW == 4 || NW == 8, "4 or 8 waves");
     static_assert(!A8 || BK == 64, "the E4M3 A path reads both 32-deep halves of a 64-deep step");
     constexpr int RC = BK / 8;                        // 16-byte B pieces per row and step
     constexpr int RPI = 64 / RC;                      // B rows filled by one wave-wide load
@@ -145,8 +146,8 @@ __global__ __launch_bounds__(256, MINB) void grouped_gemm_kernel(GemmArgs g)
     constexpr int RC_A = BK * A_EB / 16;              // 16-byte A pieces per row and step
     constexpr int RPI_A = 64 / RC_A;                  // A rows filled by one wave-wide load
     constexpr int NB = DUAL ? 2 * BN : BN;            // B rows per stage
-    constexpr int A_PW = BM / RPI_A / 4, B_PW = NB / RPI / 4; // loads per wave per stage
-    static_assert(A_PW * RPI_A * 4 == BM && B_PW * RPI * 4 == NB, "whole loads per wave");
+    constexpr int A_PW = BM / RPI_A / NW, B_PW = NB / RPI / NW; // loads per wave per stage
+    static_assert(A_PW * RPI_A * NW == BM && B_PW * RPI * NW == NB, "whole loads per wave");
     constexpr int B_BYTES = NB * BK * 2;
     constexpr int WTN = BN / WN;                      // wave tile columns
     constexpr int RT = BM / 16 / WM, CT = WTN / 16;   // 16x16 MFMA tiles per wave
@@ -184,7 +185,7 @@ __global__ __launch_bounds__(256, MINB) void grouped_gemm_kernel(GemmArgs g)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WN, wn = wave % WN;
 
-    // Load descriptors.  Load j of wave w fills rows [(4j + w) * RPI, +RPI) of
+    // Load descriptors.  Load j of wave w fills rows [(NW*j + w) * RPI, +RPI) of
     // its region; lane l writes piece l % RC of row l / RC, i.e. it fetches
     // source piece (l % RC) ^ swz(row).  A loads whose rows all lie past the
     // expert's end are skipped (wave-uniform); a row past the end inside a
@@ -195,7 +196,7 @@ __global__ __launch_bounds__(256, MINB) void grouped_gemm_kernel(GemmArgs g)
     int a_loads = 0; // loads this wave issues per stage for A
 #pragma unroll
     for (int j = 0; j < A_PW; ++j) {
-        const int grp = 4 * j + wave;
+        const int grp = NW * j + wave;
         const int r = grp * RPI_A + lane / RC_A;
         const int piece = (lane % RC_A) ^ swz<RC_A>(r);
         const int rr = r < rows_valid ? r : 0;
@@ -204,7 +205,7 @@ __global__ __launch_bounds__(256, MINB) void grouped_gemm_kernel(GemmArgs g)
     }
 #pragma unroll
     for (int j = 0; j < B_PW; ++j) {
-        const int grp = 4 * j + wave;
+        const int grp = NW * j + wave;
         const int r = grp * RPI + lane / RC;
         const int piece = (lane % RC) ^ swz<RC>(r);
         const uint16_t *base = (DUAL && r >= BN) ? g.B1 : g.B0;
@@ -237,11 +238,11 @@ __global__ __launch_bounds__(256, MINB) void grouped_gemm_kernel(GemmArgs g)
         const int k0 = (ks < nsteps ? ks : ks - nsteps) * BK;
 #pragma unroll
         for (int j = 0; j < A_PW; ++j)
-            if ((4 * j + wave) * RPI_A < rows_valid)
-                dma16(asrc[j] + k0 * A_EB, st + (4 * j + wave) * 1024);
+            if ((NW * j + wave) * RPI_A < rows_valid)
+                dma16(asrc[j] + k0 * A_EB, st + (NW * j + wave) * 1024);
 #pragma unroll
         for (int j = 0; j < B_PW; ++j)
-            dma16(bsrc[j] + k0, st + a_bytes + (4 * j + wave) * 1024);
+            dma16(bsrc[j] + k0, st + a_bytes + (NW * j + wave) * 1024);
     };
 
     for (int u = 0; u < S - 1 && u < nsteps; ++u)
@@ -483,7 +484,7 @@ __global__ __launch_bounds__(256, MINB) void grouped_gemm_kernel(GemmArgs g)
         }
         __syncthreads();
         constexpr int CPR = BN / 8; // 16-byte pieces per output row
-        for (int c = tid; c < rows_valid * CPR; c += 256) {
+        for (int c = tid; c < rows_valid * CPR; c += NW * 64) {
             const int r = c / CPR, cc = c % CPR;
             *reinterpret_cast<uint4 *>(g.out + (row0 + r) * N + n0 + cc * 8) =
                 *reinterpret_cast<const uint4 *>(Cs + r * LDC + cc * 8);
@@ -549,6 +550,26 @@ constexpr int kRing1 = MOE_GU_RING;   // LDS ring bytes of a gate/up workgroup
 constexpr int kMinB1 = MOE_GU_MINB;   // gate/up workgroups per CU
 constexpr int kRing2 = MOE_DN_RING;   // and of the down GEMM
 constexpr int kMinB2 = MOE_DN_MINB;
+// Eight waves per workgroup, 2 x 4: every wave then needs at most ~220
+// registers, so two share a SIMD and one's MFMAs run while the other waits
+// on LDS or on its loads (four waves of twice the tile: one per SIMD, 512
+// registers each).  Measured against 2 x 2: DeepSeek-V3 gate/up 2.84 -> 2.74
+// ms, Mixtral gate/up 1.68 -> 1.62 ms and down 0.88 -> 0.79 ms; 4 x 2 lands
+// in between (its waves read more B fragments from LDS).
+#ifndef MOE_GU_WM
+#define MOE_GU_WM 2
+#endif
+#ifndef MOE_GU_WN
+#define MOE_GU_WN 4
+#endif
+#ifndef MOE_DN_WM
+#define MOE_DN_WM 2
+#endif
+#ifndef MOE_DN_WN
+#define MOE_DN_WN 4
+#endif
+constexpr int kWM1 = MOE_GU_WM, kWN1 = MOE_GU_WN; // wave grid of a gate/up workgroup
+constexpr int kWM2 = MOE_DN_WM, kWN2 = MOE_DN_WN; // and of a down workgroup
 
 // Rotated K walks for B rows of K bf16 values whose pitch is a power of two
 // of at least 4 KB (measured: DeepSeek-V3 down GEMM, K = 2048, 1.64 -> 1.61
@@ -567,12 +588,13 @@ template <bool A8>
 static void launch_gate_up_t(const Dims &dm, const GemmArgs &a, long long mtiles_max,
                              hipStream_t st)
 {
+    constexpr int threads = kWM1 * kWN1 * 64;
     if (dm.H % kBN1 == 0) // H is a multiple of 64; the wide tile needs a multiple of kBN1
-        grouped_gemm_kernel<kBM1, kBN1, kBK, kRing1, kMinB1, 2, 2, true, A8>
-            <<<xcd_grid((int)(mtiles_max * (dm.H / kBN1))), 256, 0, st>>>(a);
+        grouped_gemm_kernel<kBM1, kBN1, kBK, kRing1, kMinB1, kWM1, kWN1, true, A8>
+            <<<xcd_grid((int)(mtiles_max * (dm.H / kBN1))), threads, 0, st>>>(a);
     else
-        grouped_gemm_kernel<kBM1, 64, kBK, kRing1, kMinB1, 2, 2, true, A8>
-            <<<xcd_grid((int)(mtiles_max * (dm.H / 64))), 256, 0, st>>>(a);
+        grouped_gemm_kernel<kBM1, 64, kBK, kRing1, kMinB1, kWM1, kWN1, true, A8>
+            <<<xcd_grid((int)(mtiles_max * (dm.H / 64))), threads, 0, st>>>(a);
 }
 
 hipError_t launch_gate_up(const Dims &dm, const void *send_buf, const float *send_scale,
@@ -600,12 +622,13 @@ hipError_t launch_down(const Dims &dm, const uint16_t *h, const int32_t *expert_
     const long long mtiles_max = (dm.send_rows + kBM2 - 1) / kBM2 + dm.E;
     GemmArgs a{h, nullptr, expert_offset, expert_kept, w2, nullptr, expert_out, dm.E, dm.d, dm.H,
                MOE_GEMM_ROT_DN ? rotate_k(dm.H) : 0};
+    constexpr int threads = kWM2 * kWN2 * 64;
     if (dm.d % kBN2 == 0)
-        grouped_gemm_kernel<kBM2, kBN2, kBK, kRing2, kMinB2, 2, 2, false, false>
-            <<<xcd_grid((int)(mtiles_max * (dm.d / kBN2))), 256, 0, st>>>(a);
+        grouped_gemm_kernel<kBM2, kBN2, kBK, kRing2, kMinB2, kWM2, kWN2, false, false>
+            <<<xcd_grid((int)(mtiles_max * (dm.d / kBN2))), threads, 0, st>>>(a);
     else
-        grouped_gemm_kernel<kBM2, 64, kBK, kRing2, kMinB2, 2, 2, false, false>
-            <<<xcd_grid((int)(mtiles_max * (dm.d / 64))), 256, 0, st>>>(a);
+        grouped_gemm_kernel<kBM2, 64, kBK, kRing2, kMinB2, kWM2, kWN2, false, false>
+            <<<xcd_grid((int)(mtiles_max * (dm.d / 64))), threads, 0, st>>>(a);
     return hipGetLastError();
 }
 
