@@ -99,21 +99,26 @@ __global__ __launch_bounds__(256) void transpose_wg_kernel(const uint16_t *__res
     }
 }
 
+#ifndef MOE_ROUTER_WN
+#define MOE_ROUTER_WN 4 // wave columns of a 256-expert logit tile (2 x WN waves)
+#endif
 constexpr int RBT = 64;   // tokens per tile
 constexpr int RBK = 64;   // K step
 
-template <int BE, int RRING, int MINB>
-__global__ __launch_bounds__(256, MINB) void router_logits_kernel(
+template <int BE, int RRING, int MINB, int WM, int WN>
+__global__ __launch_bounds__(WM * WN * 64, MINB) void router_logits_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ wgt,
     float *__restrict__ partial, int T, int d, int E, int n_et, int sk_count, int total)
 {
+    constexpr int NW = WM * WN;                    // waves per workgroup
     constexpr int RC = RBK / 8, RPI = 64 / RC;     // 8 pieces per row, 8 rows per load
-    constexpr int A_PW = RBT / RPI / 4;            // x loads per wave per stage
-    constexpr int B_PW = BE / RPI / 4;             // W_g^T loads per wave per stage
+    constexpr int A_PW = RBT / RPI / NW;           // x loads per wave per stage
+    constexpr int B_PW = BE / RPI / NW;            // W_g^T loads per wave per stage
+    static_assert(A_PW * RPI * NW == RBT && B_PW * RPI * NW == BE, "whole loads per wave");
     constexpr int A_BYTES = RBT * RBK * 2, STAGE = (RBT + BE) * RBK * 2;
     constexpr int S = RRING / STAGE < 8 ? RRING / STAGE : 8;
     static_assert(S >= 2, "two stages fit");
-    constexpr int WTT = RBT / 2, WTE = BE / 2;     // 2 x 2 waves
+    constexpr int WTT = RBT / WM, WTE = BE / WN;   // WM x WN waves
     constexpr int RT = WTT / 16, CT = WTE / 16;
     __shared__ __attribute__((aligned(1024))) char smem[S * STAGE];
 
@@ -134,20 +139,20 @@ __global__ __launch_bounds__(256, MINB) void router_logits_kernel(
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wt = wave >> 1, we = wave & 1;
+    const int wt = wave / WN, we = wave % WN;
 
     const uint16_t *asrc[A_PW];
     const uint16_t *bsrc[B_PW];
 #pragma unroll
     for (int j = 0; j < A_PW; ++j) {
-        const int r = (4 * j + wave) * RPI + lane / RC;
+        const int r = (NW * j + wave) * RPI + lane / RC;
         const int piece = (lane % RC) ^ swz<RC>(r);
         const int t = (t0 + r < T) ? t0 + r : t0; // rows past T read row t0 (never stored)
         asrc[j] = x + (size_t)t * d + (size_t)s_lo * RBK + piece * 8;
     }
 #pragma unroll
     for (int j = 0; j < B_PW; ++j) {
-        const int r = (4 * j + wave) * RPI + lane / RC;
+        const int r = (NW * j + wave) * RPI + lane / RC;
         const int piece = (lane % RC) ^ swz<RC>(r);
         bsrc[j] = wgt + (size_t)(e0 + r) * d + (size_t)s_lo * RBK + piece * 8;
     }
@@ -157,10 +162,10 @@ __global__ __launch_bounds__(256, MINB) void router_logits_kernel(
         const int k0 = step * RBK;
 #pragma unroll
         for (int j = 0; j < A_PW; ++j)
-            dma16(asrc[j] + k0, st + (4 * j + wave) * 1024);
+            dma16(asrc[j] + k0, st + (NW * j + wave) * 1024);
 #pragma unroll
         for (int j = 0; j < B_PW; ++j)
-            dma16(bsrc[j] + k0, st + A_BYTES + (4 * j + wave) * 1024);
+            dma16(bsrc[j] + k0, st + A_BYTES + (NW * j + wave) * 1024);
     };
 
     floatx4 acc[RT][CT];
@@ -460,13 +465,14 @@ hipError_t launch_route(const Dims &dm, const uint16_t *x, const uint16_t *w_gat
     const int n_tt = (T + RBT - 1) / RBT;
     const int be = router_be(E), n_et = epad / be, total = n_tt * n_et * sk;
     if (be == 256)
-        router_logits_kernel<256, 156 * 1024, 1><<<xcd_grid(total), 256, 0, st>>>(
+        router_logits_kernel<256, 156 * 1024, 1, 2, MOE_ROUTER_WN>
+            <<<xcd_grid(total), 2 * MOE_ROUTER_WN * 64, 0, st>>>(
             x, wgt, partial, T, d, E, n_et, sk, total);
     else if (be == 128)
-        router_logits_kernel<128, 78 * 1024, 2><<<xcd_grid(total), 256, 0, st>>>(
+        router_logits_kernel<128, 78 * 1024, 2, 2, 2><<<xcd_grid(total), 256, 0, st>>>(
             x, wgt, partial, T, d, E, n_et, sk, total);
     else
-        router_logits_kernel<64, 78 * 1024, 2><<<xcd_grid(total), 256, 0, st>>>(
+        router_logits_kernel<64, 78 * 1024, 2, 2, 2><<<xcd_grid(total), 256, 0, st>>>(
             x, wgt, partial, T, d, E, n_et, sk, total);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess)
