@@ -9,7 +9,8 @@
 // A wavefront per token.  Its slots and gates are read once into scalar
 // registers; for every 16-byte piece of the row, the lane issues all k
 // gathers before using any of them, accumulates G * row in fp32 in rank
-// order, and stores the bf16 result (round to nearest even).
+// order, and stores the bf16 result (round to nearest even).  The gathers are
+// non-temporal loads: every expert_out row is read once.
 #include "moe_internal.hpp"
 
 namespace moe {
@@ -54,7 +55,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict
 #pragma unroll
         for (int s = 0; s < KM; ++s)
             v[s] = rows[s] >= 0
-                       ? reinterpret_cast<const uint4 *>(expert_out + (size_t)rows[s] * d)[c]
+                       ? load_nt(reinterpret_cast<const uint4 *>(expert_out + (size_t)rows[s] * d) + c)
                        : make_uint4(0, 0, 0, 0);
         float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -96,7 +97,7 @@ __global__ __launch_bounds__(256) void combine_kernel_any_k(
             if (r < 0)
                 continue;
             const float g = gw[s];
-            const uint4 v = reinterpret_cast<const uint4 *>(expert_out + (size_t)r * d)[c];
+            const uint4 v = load_nt(reinterpret_cast<const uint4 *>(expert_out + (size_t)r * d) + c);
             const uint32_t p[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
             for (int q = 0; q < 4; ++q) {

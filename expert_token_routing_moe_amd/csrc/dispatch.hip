@@ -504,7 +504,8 @@ __global__ __launch_bounds__(256) void permute_kernel(
                     if (v >= 0)
                         send_scale[v] = sc;
             }
-            // four row pieces in flight per lane before their stores
+            // four row pieces in flight per lane before their stores; the
+            // stores are non-temporal (the rows are read by the GEMM only)
             for (int c0 = lane; c0 < nvec; c0 += 256) {
                 uint4 v[4];
 #pragma unroll
@@ -523,7 +524,7 @@ __global__ __launch_bounds__(256) void permute_kernel(
 #pragma unroll
                         for (int u = 0; u < 4; ++u)
                             if (c0 + 64 * u < nvec)
-                                out[c0 + 64 * u] = q8[u];
+                                store_nt(out + c0 + 64 * u, q8[u]);
                     }
                 } else {
 #pragma unroll
@@ -534,7 +535,7 @@ __global__ __launch_bounds__(256) void permute_kernel(
 #pragma unroll
                         for (int u = 0; u < 4; ++u)
                             if (c0 + 64 * u < nvec)
-                                out[c0 + 64 * u] = v[u];
+                                store_nt(out + c0 + 64 * u, v[u]);
                     }
                 }
             }

@@ -231,6 +231,12 @@ __global__ __launch_bounds__(WM * WN * 64, MINB) void grouped_gemm_kernel(GemmAr
     // taken in the rotated (but fixed) order.
     const int nsteps = K / BK;
     const int krot = g.rot ? (n_tile * 5) % nsteps : 0;
+    // The down projection's weights are loaded non-temporal: all N tiles of
+    // an expert re-read the same h rows (A), and weight lines that no other
+    // workgroup will ask for again would otherwise push those out of L2.
+    // (gate/up reads its A rows in step across the N tiles and gains
+    // nothing from it; at Mixtral's size it loses.)
+    constexpr bool B_NT = !DUAL;
     const uint32_t lds_base = (uint32_t)(uintptr_t)(LDS_AS char *)smem;
     auto issue = [&](int step, int slot) {
         const uint32_t st = lds_base + slot * stage;
@@ -242,7 +248,7 @@ __global__ __launch_bounds__(WM * WN * 64, MINB) void grouped_gemm_kernel(GemmAr
                 dma16(asrc[j] + k0 * A_EB, st + (NW * j + wave) * 1024);
 #pragma unroll
         for (int j = 0; j < B_PW; ++j)
-            dma16(bsrc[j] + k0, st + a_bytes + (NW * j + wave) * 1024);
+            dma16<B_NT>(bsrc[j] + k0, st + a_bytes + (NW * j + wave) * 1024);
     };
 
     for (int u = 0; u < S - 1 && u < nsteps; ++u)
@@ -449,7 +455,8 @@ __global__ __launch_bounds__(WM * WN * 64, MINB) void grouped_gemm_kernel(GemmAr
         // bytes past a multiple of 256, so the 8 rows one write covers per
         // pass fall in distinct banks.  The tile then leaves in 16-byte
         // pieces, each wave store covering whole rows (a third of the time of
-        // 32-byte row pieces straight from the quads).
+        // 32-byte row pieces straight from the quads).  The stores are
+        // non-temporal: h and expert_out are read by the next kernel only.
         constexpr int LDC = BN + 16;
         static_assert(BM * LDC * 2 <= RING, "epilogue tile fits in the ring");
         __syncthreads(); // every wave is done with the ring
@@ -486,8 +493,8 @@ __global__ __launch_bounds__(WM * WN * 64, MINB) void grouped_gemm_kernel(GemmAr
         constexpr int CPR = BN / 8; // 16-byte pieces per output row
         for (int c = tid; c < rows_valid * CPR; c += NW * 64) {
             const int r = c / CPR, cc = c % CPR;
-            *reinterpret_cast<uint4 *>(g.out + (row0 + r) * N + n0 + cc * 8) =
-                *reinterpret_cast<const uint4 *>(Cs + r * LDC + cc * 8);
+            store_nt(reinterpret_cast<uint4 *>(g.out + (row0 + r) * N + n0 + cc * 8),
+                     *reinterpret_cast<const uint4 *>(Cs + r * LDC + cc * 8));
         }
     };
 

@@ -37,6 +37,26 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 // fp32 -> bf16 bits, rounded as pack_bf16x2 does.
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) { return pack_bf16x2(f, 0.f) & 0xffffu; }
 
+// Non-temporal 16- and 8-byte accesses, for data that one kernel touches once:
+// rows a gather reads once, and rows a kernel writes for the next kernel
+// (hundreds of MB, far beyond the L2).  They keep such lines from pushing
+// out of L2 the lines that a kernel does re-read (the GEMMs' A rows).
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint4 load_nt(const uint4 *p)
+{
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void store_nt(uint4 *p, uint4 v)
+{
+    __builtin_nontemporal_store(u32x4_t{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4_t *>(p));
+}
+__device__ __forceinline__ void store_nt(uint2 *p, uint2 v)
+{
+    __builtin_nontemporal_store(u32x2_t{v.x, v.y}, reinterpret_cast<u32x2_t *>(p));
+}
+
 // ---------------------------------------------------------------------------
 // FP8 E4M3 (OCP: sign, 4 exponent bits with bias 7, 3 mantissa bits; largest
 // finite 448, no infinities) for the dispatch payload.

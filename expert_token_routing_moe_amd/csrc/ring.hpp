@@ -53,17 +53,29 @@ __device__ __forceinline__ void ring_barrier()
 // address lds_addr (wave-uniform, passed in M0).  Written as inline asm so
 // that the compiler, which cannot tell the ring's slots apart, does not drain
 // the whole load counter before every LDS read; the ring's waits are the
-// explicit wait_vmcnt calls.  M0 is restored afterwards.
+// explicit wait_vmcnt calls.  M0 is restored afterwards.  NT marks the load
+// non-temporal, so the L2 keeps the line only briefly (for data that the
+// launch reads once and that would otherwise push out data it re-reads).
+template <bool NT = false>
 __device__ __forceinline__ void dma16(const void *gptr, uint32_t lds_addr)
 {
     uint32_t saved;
-    asm volatile("s_mov_b32 %0, m0\n\t"
-                 "s_mov_b32 m0, %2\n\t"
-                 "global_load_lds_dwordx4 %1, off\n\t"
-                 "s_mov_b32 m0, %0"
-                 : "=&s"(saved)
-                 : "v"(gptr), "s"(lds_addr)
-                 : "memory");
+    if constexpr (NT)
+        asm volatile("s_mov_b32 %0, m0\n\t"
+                     "s_mov_b32 m0, %2\n\t"
+                     "global_load_lds_dwordx4 %1, off nt\n\t"
+                     "s_mov_b32 m0, %0"
+                     : "=&s"(saved)
+                     : "v"(gptr), "s"(lds_addr)
+                     : "memory");
+    else
+        asm volatile("s_mov_b32 %0, m0\n\t"
+                     "s_mov_b32 m0, %2\n\t"
+                     "global_load_lds_dwordx4 %1, off\n\t"
+                     "s_mov_b32 m0, %0"
+                     : "=&s"(saved)
+                     : "v"(gptr), "s"(lds_addr)
+                     : "memory");
 }
 
 // 16-byte piece p of row r is stored at piece p ^ swz(r) of that row.
