@@ -422,6 +422,46 @@ def test_expert_ffn_fp8_stage(case):
                               f"fp8 expert {e}")
 
 
+# Expert row counts that reach every per-wave slice count (0..8) of a 256-row
+# tile at each ring depth the GEMM picks (4, 3 and 2 stages; 2 also through its
+# compile-time two-stage path, 161..256 rows), experts cut into 2 and 3 equal
+# M tiles (257, 384, 400, 513 rows), and empty experts.
+TILE_ROWS = [1, 16, 17, 40, 56, 57, 96, 97, 128, 160, 161, 170, 176, 177, 192, 193, 224, 256,
+             257, 384, 400, 513, 0, 3]
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_expert_ffn_every_tile_shape(fp8):
+    counts = np.array(TILE_ROWS, np.int32)
+    E, n = len(counts), int(counts.sum())
+    cfg = MoEConfig("tile_rows", T=n, d=256, E=E, k=1, H=256, cf=INF, D=1, x_std=1.0,
+                    wg_std=0.1, w_std=0.05, seed=18, dispatch_fp8=int(fp8))
+    print(f"\n[tile rows] fp8={fp8} E={E} rows={n}", flush=True)
+    inp = make_inputs(cfg, DEV)
+    shape = api.Shape.from_config(cfg)
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    x = bf16_bits(inp["x"])  # expert e's rows are x[off[e]:off[e + 1]]
+    w1, w3, w2 = (bf16_bits(inp[k]) for k in ("w1", "w3", "w2"))
+    if fp8:
+        q, sc = oracle.fp8_quantize_rows(x)
+        send, scale = torch.from_numpy(q).to(DEV), _f32(sc)
+        want = oracle.expert_ffn_all(q, off, counts, w1, w3, w2, send_scale=sc)
+    else:
+        send, scale = inp["x"], None
+        want = oracle.expert_ffn_all(x, off, counts, w1, w3, w2)
+    out = torch.zeros(n, cfg.d, dtype=torch.bfloat16, device=DEV)
+    ws = api.LayerBuffers.allocate(shape, DEV).workspace
+    api.moe_expert_ffn(shape, send, scale, _i32(off), _i32(counts), inp["w1"], inp["w3"],
+                       inp["w2"], out, ws)
+    torch.cuda.synchronize()
+    got = bf16_bits(out)
+    for e in range(E):
+        lo, m = int(off[e]), int(counts[e])
+        if m:
+            assert_bf16_close(bits_to_f64(got[lo:lo + m]), bits_to_f64(want[lo:lo + m]),
+                              f"expert {e} ({m} rows)")
+
+
 @pytest.mark.parametrize("name", list(SMALL))
 def test_layer_fwd_fp8_end_to_end(name):
     cfg = SMALL[name].with_(dispatch_fp8=1)
