@@ -58,7 +58,7 @@ def stage_traffic(cfg, st, touched):
 
 def kernel_source_digest():
     h = hashlib.sha256()
-    for name in ("ffn.hip", "moe_internal.hpp"):
+    for name in ("ffn.hip", "moe_internal.hpp", "ring.hpp"):
         with open(os.path.join(ROOT, "expert_token_routing_moe_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]

@@ -17,7 +17,8 @@
 // load counter (s_waitcnt vmcnt) for exactly the stages it needs, then one
 // workgroup barrier per step publishes the stage.  Rows are stored unpadded
 // with an XOR swizzle of their 16-byte pieces, so the MFMA fragment reads are
-// free of bank conflicts.
+// free of bank conflicts.  Weight loads are non-temporal (each weight byte is
+// read once per M tile), A loads are not (every N tile re-reads them).
 //
 // Tiles.  An M tile holds up to 256 rows (an expert's rows are split into
 // equal tiles), so every expert with at most 256 rows streams each weight
@@ -32,7 +33,8 @@
 //
 // Epilogue.  A 4x4 transpose inside each lane quad (DPP) turns the MFMA
 // layout into 8-byte row pieces, converted to bf16 by v_cvt_pk_bf16_f32; they
-// are gathered in LDS (the ring is free by then) and leave as 16-byte pieces.
+// are gathered in LDS (the ring is free by then) and leave as 16-byte
+// non-temporal stores (the next kernel is the only reader).
 #include <type_traits>
 
 #include "moe_internal.hpp"
