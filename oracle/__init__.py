@@ -157,6 +157,16 @@ def capacity(T: int, k: int, E: int, cf: float, min_capacity: int = 0) -> int:
     return int(_load().oracle_capacity(T, k, E, float(cf), int(min_capacity)))
 
 
+def imbalance(loads) -> float:
+    """Load imbalance ratio (max - mean) / mean over per-rank (or per-expert)
+    loads, as "MoE Expert Parallelism Sizing: Traffic, Capacity, Fabric"
+    defines it in "Rank-level skew and the straggler effect"; 0 when every
+    load equals the mean."""
+    a = np.asarray(loads, np.float64)
+    m = a.mean()
+    return float((a.max() - m) / m) if m > 0 else 0.0
+
+
 def fp8_value(code: int) -> float:
     """Value of an E4M3 code (OCP: bias 7, max 448, 0x7F/0xFF NaN)."""
     return float(_load().oracle_fp8_value(int(code)))

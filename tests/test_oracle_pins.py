@@ -223,6 +223,30 @@ def test_page_expert_params(sizing):
     assert abs(3 * d * H / 1e6 - p["printed_millions"]) <= p["printed_precision_millions"]
 
 
+def test_page_rank_imbalance(sizing):
+    """Four ranks (one expert each, k = 1) loaded 256, 48, 48, 48 rows: the
+    page's ratio of 1.56, the hottest rank at 2.56 times the mean, and the
+    page's straggler figure from the EP64 balanced bound."""
+    p = sizing["rank_imbalance"]
+    loads = [256, 48, 48, 48]
+    idx = np.repeat(np.arange(4, dtype=np.int32), loads)[:, None]
+    r = oracle.dispatch(None, idx, T=len(idx), d=64, E=4, D=4, cf=INF, with_send_buf=False)
+    np.testing.assert_array_equal(r["rank_rows"], loads)
+    ratio = oracle.imbalance(r["rank_rows"])
+    assert ratio == pytest.approx(p["ratio"], abs=1e-12)
+    assert max(loads) / np.mean(loads) == pytest.approx(p["max_over_mean"], abs=1e-12)
+    # balanced routing: ratio 0 at rank and expert level
+    g = sizing["assignments_dsv3"]["shape"]
+    T, k, E, d = g["T"], g["k"], g["E"], g["d"]
+    rb = oracle.dispatch(None, _balanced_routing(T, k, E), T=T, d=d, E=E, D=64, cf=INF,
+                         with_send_buf=False)
+    assert oracle.imbalance(rb["rank_rows"]) == 0.0
+    assert oracle.imbalance(rb["expert_count"]) == 0.0
+    bound = rb["stats"]["dispatch_remote_bytes"]
+    straggler = bound * (1 + ratio)
+    assert abs(straggler / 1e9 - p["straggler_printed_GB"]) <= p["straggler_printed_precision_GB"]
+
+
 # A worked example by hand: T=6, E=3, k=2, T*k/E = 4.
 HAND_IDX = np.array([[0, 1], [1, 0], [0, 2], [2, 1], [0, 1], [1, 2]], np.int32)
 
