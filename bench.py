@@ -339,6 +339,16 @@ def main():
     roof["kernel"] = f"grouped_gemm {dom}"
     gemm_flops = traffic["gate_up"]["flops"] + traffic["down"]["flops"]
     gemm_s = (stage_ms["gate_up"] + stage_ms["down"]) / 1e3
+    # load imbalance (max - mean) / mean, over experts (routed counts) and over
+    # destination ranks (kept rows), from the device counters and rank rows
+    counts = {k: st[k] for k in ("kept", "dropped", "padded", "max_expert_count")}
+    rank_rows = buf.rank_rows.cpu().tolist()
+    mean_e = st["assignments"] / cfg.E
+    mean_r = sum(rank_rows) / len(rank_rows)
+    counts["imbalance"] = {
+        "expert": round((st["max_expert_count"] - mean_e) / mean_e, 4) if mean_e else 0.0,
+        "rank": round((max(rank_rows) - mean_r) / mean_r, 4) if mean_r else 0.0,
+    }
     out = {
         "metric": METRIC,
         "value": round(cfg.T / (ms_step / 1e3), 1),
@@ -363,7 +373,7 @@ def main():
                          "mfma_util": round(gemm_flops / gemm_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
                          "touched_experts": touched},
         "stages": per_stage,
-        "counts": {k: st[k] for k in ("kept", "dropped", "padded", "max_expert_count")},
+        "counts": counts,
         "roofline": roof,
     }
     if cfg.D > 1 and cfg.cf == float("inf") and not args.no_rank_local:
