@@ -6,7 +6,9 @@ KeepTopK/softmax), dispatch (histogram, capacity, permute), the SwiGLU
 grouped GEMMs (gate/up, then down) and the combine, each through its C-ABI
 entry point on one stream.  HIP events recorded on that stream around every
 stage give per-stage durations over the timed region; the dominant kernel's
-roofline is computed from its algorithmic bytes and flops.
+roofline is computed from its algorithmic bytes and flops.  Each stage's
+byte rate is also given as a fraction of this device's own streaming-read
+rate, measured after the timed steps with moe_stream_read.
 
 For a dropless workload spread over D > 1 ranks, the expert GEMMs are also
 timed on one rank's share under D-way expert parallelism (E/D experts, the
@@ -196,6 +198,31 @@ def rank_local_gemm(cfg, inp, dev, steps, warmup):
     return res
 
 
+def device_read_rate(dev, stream):
+    """Streaming-read rate of this device, GB/s: the best of five reads of a
+    2 GiB buffer through moe_stream_read (the expert GEMMs' non-temporal
+    16-byte loads), timed with events on the given stream."""
+    import torch
+
+    from expert_token_routing_moe_amd import api
+
+    n = 1 << 31
+    src = torch.ones(n // 4, dtype=torch.int32, device=dev)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    api.moe_stream_read(src, sink, stream)  # warm-up
+    best = float("inf")
+    for _ in range(5):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        api.moe_stream_read(src, sink, stream)
+        e1.record(stream)
+        e1.synchronize()
+        best = min(best, e0.elapsed_time(e1))
+    del src
+    return n / (best / 1e3) / 1e9
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -313,6 +340,8 @@ def main():
     st = api.stats_dict(buf.stats)
     touched = int((buf.expert_kept > 0).sum().item())
     traffic = stage_traffic(cfg, st, touched)
+    read_gbs = device_read_rate(dev, stream)
+    log(f"bench: streaming read on this device {read_gbs:.0f} GB/s")
     per_stage = {}
     for s in stages:
         t = stage_ms[s] / 1e3
@@ -322,6 +351,7 @@ def main():
                             p90=round(pct(samples[s], 0.9), 5),
                             gbs=round(traffic[s]["bytes"] / t / 1e9, 1),
                             hbm_frac=round(traffic[s]["bytes"] / t / 1e9 / HBM_PEAK_GBS, 4),
+                            read_frac=round(traffic[s]["bytes"] / t / 1e9 / read_gbs, 4),
                             tflops=round(traffic[s]["flops"] / t / 1e12, 2))
     dom = max(("gate_up", "down"), key=lambda s: stage_ms[s])
     t_dom = stage_ms[dom] / 1e3
@@ -335,6 +365,9 @@ def main():
         roof = dict(bound="mfma", achieved=round(achieved, 1), peak=MFMA_BF16_PEAK_TFLOPS,
                     unit="TFLOP/s")
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    if roof["bound"] == "hbm":  # against what this device's reads reach
+        roof["device_read_gbs"] = round(read_gbs, 1)
+        roof["frac_of_device_read"] = round(roof["achieved"] / read_gbs, 4)
     roof["traffic"] = measured_traffic(dom, cfg.name)
     roof["kernel"] = f"grouped_gemm {dom}"
     gemm_flops = traffic["gate_up"]["flops"] + traffic["down"]["flops"]

@@ -73,6 +73,7 @@ def lib():
         "moe_shared_expert": [S, P, P, P, P, P, P, SZ, P],
         "moe_layer_fwd": [S] + [P] * 24 + [SZ, P],
         "moe_fp8_rows_to_bf16": [P, P, ctypes.c_int64, ctypes.c_int32, P, P],
+        "moe_stream_read": [P, SZ, P, P],
     }
     for name, argtypes in sig.items():
         f = getattr(L, name)
@@ -247,6 +248,17 @@ def moe_fp8_rows_to_bf16(codes, scales, out, stream=None):
     rows, d = codes.shape
     _check("moe_fp8_rows_to_bf16", lib().moe_fp8_rows_to_bf16(
         _p(codes, torch.uint8), _p(scales, F32), rows, d, _p(out, BF16), _stream(stream)))
+
+
+STREAM_READ_MARK = 0x9E3779B9
+
+
+def moe_stream_read(src, sink, stream=None):
+    """Read src once with the expert GEMMs' non-temporal loads (a probe of the
+    device's streaming-read rate).  sink[0] is set to STREAM_READ_MARK only
+    by a reading lane whose XOR of the words it read equals the mark."""
+    _check("moe_stream_read", lib().moe_stream_read(
+        _p(src), src.numel() * src.element_size(), _p(sink, I32), _stream(stream)))
 
 
 @dataclass

@@ -362,6 +362,13 @@ MOE_EXPORT int moe_fp8_rows_to_bf16(const void *codes, const float *scales, int6
                                               d, out, static_cast<hipStream_t>(stream)));
 }
 
+MOE_EXPORT int moe_stream_read(const void *src, size_t bytes, uint32_t *sink, void *stream)
+{
+    if (bytes % 16 != 0 || bad_ptr(src, (long long)(bytes / 16)) || bad_ptr(sink))
+        return MOE_EINVAL;
+    return hip_status(launch_stream_read(src, bytes, sink, static_cast<hipStream_t>(stream)));
+}
+
 MOE_EXPORT const char *moe_status_str(int status)
 {
     switch (status) {

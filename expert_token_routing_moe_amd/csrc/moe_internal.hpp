@@ -155,6 +155,7 @@ hipError_t launch_down(const Dims &dm, const uint16_t *h, const int32_t *expert_
 hipError_t launch_combine(const Dims &dm, const uint16_t *expert_out, const int32_t *slot,
                           const float *topk_w, const uint16_t *shared_out, uint16_t *y,
                           hipStream_t st);
+hipError_t launch_stream_read(const void *src, size_t bytes, uint32_t *sink, hipStream_t st);
 hipError_t launch_shared_expert(const Dims &dm, const uint16_t *x, const uint16_t *w1s,
                                 const uint16_t *w3s, const uint16_t *w2s, uint16_t *shared_out,
                                 char *ws, const Workspace &wl, hipStream_t st);

@@ -290,6 +290,19 @@ int moe_layer_fwd(const moe_shape *shape, const uint16_t *x, const uint16_t *w_g
 int moe_fp8_rows_to_bf16(const void *codes, const float *scales, int64_t rows, int32_t d,
                          uint16_t *out, void *stream);
 
+/* Diagnostic, not a step of the layer: reads bytes of device memory at
+ * src once, with the non-temporal 16-byte loads that the expert GEMMs use
+ * for their weights, so that a caller can time this device's streaming-read
+ * rate beside the layer's kernels.  Each reading lane XORs the 32-bit words
+ * it reads; a lane whose XOR equals MOE_STREAM_READ_MARK stores it to *sink,
+ * and nothing else is written (so a buffer of zeros holding the mark in one
+ * word sets *sink to the mark exactly when that word is read).
+ *   src   device, 16-byte aligned; bytes % 16 == 0 (bytes == 0: no launch)
+ *   sink  device uint32, 16-byte aligned
+ * Returns MOE_EINVAL for a bad pointer or size, MOE_EHIP on a launch error. */
+#define MOE_STREAM_READ_MARK 0x9E3779B9u
+int moe_stream_read(const void *src, size_t bytes, uint32_t *sink, void *stream);
+
 /* Static string naming a status code (never NULL). */
 const char *moe_status_str(int status);
 

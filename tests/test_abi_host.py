@@ -181,6 +181,20 @@ def test_entry_points_reject_small_or_missing_workspace():
     assert _raw("moe_expert_ffn", S, *([good] * 8), good, 0, None) == api.MOE_EWORKSPACE
 
 
+def test_stream_read_rejects_bad_arguments():
+    P = ctypes.c_void_p
+    good = P(1 << 20)
+    assert _raw("moe_stream_read", None, ctypes.c_size_t(16), good, None) == api.MOE_EINVAL
+    assert _raw("moe_stream_read", good, ctypes.c_size_t(24), good, None) == api.MOE_EINVAL
+    assert _raw("moe_stream_read", P((1 << 20) + 8), ctypes.c_size_t(16), good,
+                None) == api.MOE_EINVAL
+    assert _raw("moe_stream_read", good, ctypes.c_size_t(16), None, None) == api.MOE_EINVAL
+    assert _raw("moe_stream_read", good, ctypes.c_size_t(16), P((1 << 20) + 4),
+                None) == api.MOE_EINVAL
+    # nothing to read: accepted, nothing enqueued
+    assert _raw("moe_stream_read", None, ctypes.c_size_t(0), good, None) == api.MOE_OK
+
+
 def test_status_strings():
     L = api.lib()
     for st in (0, -1, -2, -3, -4, 7):

@@ -364,6 +364,34 @@ def test_layer_fwd_by_gate_end_to_end(name):
 # FP8 dispatch payload: E4M3 rows with fp32 row scales; combine stays bf16.
 # ---------------------------------------------------------------------------
 
+@pytest.mark.parametrize("nbytes", [16, 4099 * 16, 3 << 20, 64 << 20])
+def test_stream_read_reads_every_word(nbytes):
+    """The read-rate probe reads every word once (ragged tails, one to 2048
+    workgroups): a zero buffer holding the mark in one word, at the first,
+    last, a middle and a tail position, sets the sink; with the mark in two
+    words read by one lane the lane's XOR is zero and nothing is stored."""
+    mark = np.uint32(api.STREAM_READ_MARK).view(np.int32)
+    n = nbytes // 4
+    src = torch.zeros(n, dtype=torch.int32, device=DEV)
+    sink = torch.zeros(4, dtype=torch.int32, device=DEV)
+    for p in sorted({0, n - 1, n // 2, max(0, n - 5), 3}):
+        if p >= n:
+            continue
+        src.zero_()
+        sink.zero_()
+        src[p] = int(mark)
+        api.moe_stream_read(src, sink)
+        torch.cuda.synchronize()
+        assert int(sink[0].item()) == int(mark), f"word {p} of {n} not read"
+    src.zero_()
+    sink.zero_()
+    src[0] = int(mark)
+    src[1] = int(mark)  # same 16-byte piece, same lane: XOR 0
+    api.moe_stream_read(src, sink)
+    torch.cuda.synchronize()
+    assert int(sink[0].item()) == 0
+
+
 def test_fp8_decode_every_code():
     """The expert GEMM's E4M3 -> bf16 decode, through the diagnostic entry
     point: all 256 codes at unit and power-of-two scales, bit-exact."""
