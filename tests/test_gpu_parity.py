@@ -611,6 +611,55 @@ def test_shared_expert_and_combine_stages():
     assert np.mean(got == want) > 0.95
 
 
+# every output the layer writes in full (expert_out: only its kept rows)
+GRAPH_OUTPUTS = ("y", "logits", "topk_idx", "topk_w", "send_buf", "send_scale", "slot",
+                 "expert_count", "expert_kept", "expert_offset", "rank_rows", "stats",
+                 "shared_out")
+
+
+@pytest.mark.parametrize("name,fp8", [("tiny", False), ("e64_skew", False), ("ragged_e6", True)])
+def test_layer_fwd_in_hip_graph(name, fp8):
+    """The whole layer call is captured in a HIP graph (no allocation, no
+    memset, no host synchronisation inside) and every replay reproduces the
+    eager outputs bit for bit, also after eager kernels overwrite every
+    output between replays."""
+    cfg = SMALL[name].with_(dispatch_fp8=int(fp8))
+    print(f"\n[graph {name} fp8={fp8}]", flush=True)
+    inp = make_inputs(cfg, DEV)
+    shape = api.Shape.from_config(cfg)
+    buf = api.LayerBuffers.allocate(shape, DEV)
+    call = lambda: api.moe_layer_fwd(shape, inp["x"], inp["w_gate"], inp["bias"], inp["w1"],
+                                     inp["w3"], inp["w2"], buf)
+    call()
+    torch.cuda.synchronize()
+    outs = {n: getattr(buf, n) for n in GRAPH_OUTPUTS if getattr(buf, n) is not None}
+    ref = {n: t.clone() for n, t in outs.items()}
+    off, kept = buf.expert_offset.cpu().numpy(), buf.expert_kept.cpu().numpy()
+    rows = torch.from_numpy(np.concatenate(
+        [np.arange(off[e], off[e] + kept[e]) for e in range(cfg.E)]).astype(np.int64)).to(DEV)
+    ref_eo = buf.expert_out[rows].clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for t in list(outs.values()) + [buf.expert_out]:  # eager work between replays
+            t.view(torch.uint8).fill_(0xA5 if rep % 2 else 0x5A)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for n, t in outs.items():
+            assert torch.equal(t.view(torch.uint8), ref[n].view(torch.uint8)), (rep, n)
+        assert torch.equal(buf.expert_out[rows].view(torch.int16), ref_eo.view(torch.int16)), rep
+    del g
+
+
 @pytest.mark.parametrize("k", [2, 8])
 def test_identity_experts_round_trip_on_gpu(k):
     """Dispatch then combine with identity experts and nothing dropped gives x
