@@ -35,6 +35,8 @@
  *        (DeepSeek-V3), exposed by Megatron as group-limited routing.
  *   [SE] same page, the token-assignment worksheet: the shared expert is
  *        replicated on every rank (compute and memory, no dispatch traffic).
+ *   [RS] same page, "Rank-level skew and the straggler effect": the load
+ *        imbalance ratio (max - mean) / mean.
  *
  * Conventions for every call
  *   - Tensor pointers are DEVICE pointers (HIP global memory) unless marked
@@ -138,7 +140,10 @@ typedef struct moe_shape {
  *                         times the row bytes
  *   combine_bytes         kept*d*2: the bf16 expert outputs that travel back
  *                         (combine reverses dispatch) [CA]
- *   max_expert_count      max over experts of the routed count n_e
+ *   max_expert_count      max over experts of the routed count n_e; with
+ *                         the mean T*k/E it gives the load imbalance
+ *                         (max - mean) / mean over experts [RS] (rank_rows
+ *                         gives it over destination ranks)
  *   invalid_index         topk_idx entries outside [0, E), or repeating an
  *                         expert listed earlier for the same token; each is
  *                         treated as dropped (slot -1), never as an error
