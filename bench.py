@@ -253,8 +253,9 @@ def main():
                          "is then the sum of the stages' event times, without the read")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py runs the single-GPU share of the MoE layer only: every box here has "
-              "one GPU and this build has no multi-GPU path; use --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU's share of the MoE layer; the library has no "
+              "multi-GPU path (the expert-parallel exchange is not implemented); use --gpus 1.",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
