@@ -244,7 +244,7 @@ def test_layer_fwd_end_to_end(case):
     flips = np.any(idx != ref["topk_idx"], axis=1)
     assert not routing_mismatch(idx, ref["topk_idx"], ref["logits"], ref["gap"]).any()
     if flips.any():
-        # a legitimate near-tie flip: judge the rest on the GPU's own routing
+        # a legitimate near-tie flip: check the rest on the GPU's own routing
         w = buf.topk_w.cpu().numpy()
         r = oracle.dispatch(h["x"], idx, T=cfg.T, d=cfg.d, E=cfg.E, D=cfg.D,
                             my_rank=cfg.my_rank, cf=cfg.cf)
@@ -349,7 +349,7 @@ def test_layer_fwd_by_gate_end_to_end(name):
     api.moe_layer_fwd(shape, inp["x"], inp["w_gate"], inp["bias"], inp["w1"], inp["w3"],
                       inp["w2"], buf)
     torch.cuda.synchronize()
-    # judged on the GPU's own routing (checked against the oracle elsewhere)
+    # checked on the GPU's own routing (itself checked against the oracle elsewhere)
     idx, w = buf.topk_idx.cpu().numpy(), buf.topk_w.cpu().numpy()
     r = oracle.dispatch(h["x"], idx, T=cfg.T, d=cfg.d, E=cfg.E, D=cfg.D, cf=cfg.cf,
                         drop_policy=1, topk_w=w)
