@@ -6,7 +6,8 @@ and it imports nothing from the product package: the two share no code.
 
 The arithmetic lives in ``moe_oracle.c`` (plain C loops, IEEE double
 accumulation, OpenMP over tokens or rows); this module only marshals numpy
-arrays.  bf16 tensors are passed as ``numpy.uint16`` arrays of raw bits.
+arrays, apart from ``imbalance``, a one-line ratio over loads the C code
+returns.  bf16 tensors are passed as ``numpy.uint16`` arrays of raw bits.
 
 Sources, cited by page title and section:
   * "Mixture-of-Experts (MoE) Architecture and Expert Parallelism",
@@ -15,7 +16,9 @@ Sources, cited by page title and section:
   * "EP Math -- Expert Parallelism (MoE)" -- notation (T, d, k, D), dispatch
     and combine volumes, capacity factor, token drop, expert placement.
   * "MoE Expert Parallelism Sizing: Traffic, Capacity, Fabric" -- the
-    gated three-matrix expert, drop-before-exchange, per-destination chunks.
+    gated three-matrix expert, drop-before-exchange, per-destination chunks,
+    and ("Rank-level skew and the straggler effect") the load imbalance
+    ratio.
 
 Every function is pinned by tests in ``tests/test_oracle_pins.py`` against
 values the pages print, closed forms, invariants and brute force.
