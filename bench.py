@@ -165,7 +165,7 @@ def rank_local_gemm(cfg, inp, dev, steps, warmup):
         if ev:
             ev[0].record(stream)
         api.moe_expert_gate_up(loc, buf.send_buf, buf.send_scale, buf.expert_offset,
-                               buf.expert_kept, w1, w3, h, stream)
+                               buf.expert_kept, w1, w3, h, stream, workspace=buf.workspace)
         if ev:
             ev[1].record(stream)
         api.moe_expert_down(loc, h, buf.expert_offset, buf.expert_kept, w2, buf.expert_out,
@@ -299,7 +299,8 @@ def main():
                          buf.stats, buf.workspace, stream)
         rec()
         api.moe_expert_gate_up(shape, buf.send_buf, buf.send_scale, buf.expert_offset,
-                               buf.expert_kept, inp["w1"], inp["w3"], h, stream)
+                               buf.expert_kept, inp["w1"], inp["w3"], h, stream,
+                               workspace=buf.workspace)
         rec()
         api.moe_expert_down(shape, h, buf.expert_offset, buf.expert_kept, inp["w2"],
                             buf.expert_out, stream)

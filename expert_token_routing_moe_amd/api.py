@@ -67,7 +67,7 @@ def lib():
         "moe_topk_from_logits": [S, P, P, P, P],
         "moe_dispatch": [S, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
         "moe_expert_ffn": [S, P, P, P, P, P, P, P, P, P, SZ, P],
-        "moe_expert_gate_up": [S, P, P, P, P, P, P, P, P],
+        "moe_expert_gate_up": [S, P, P, P, P, P, P, P, P, SZ, P],
         "moe_expert_down": [S, P, P, P, P, P, P],
         "moe_combine": [S, P, P, P, P, P, P],
         "moe_shared_expert": [S, P, P, P, P, P, P, SZ, P],
@@ -196,12 +196,16 @@ def moe_expert_ffn(shape, send_buf, send_scale, expert_offset, expert_kept, w1, 
 
 
 def moe_expert_gate_up(shape, send_buf, send_scale, expert_offset, expert_kept, w1, w3, h,
-                       stream=None):
+                       stream=None, workspace=None):
+    """workspace (optional, uint8 of moe_query's size): lets E4M3 rows be
+    widened to bf16 in one pass before the GEMM on MFMA-bound shapes."""
     s = shape.c()
     _check("moe_expert_gate_up", lib().moe_expert_gate_up(
         ctypes.byref(s), _send(shape, send_buf), _p(send_scale, F32), _p(expert_offset, I32),
         _p(expert_kept, I32),
-        _p(w1, BF16), _p(w3, BF16), _p(h, BF16), _stream(stream)))
+        _p(w1, BF16), _p(w3, BF16), _p(h, BF16), _p(workspace),
+        0 if workspace is None else workspace.numel() * workspace.element_size(),
+        _stream(stream)))
 
 
 def moe_expert_down(shape, h, expert_offset, expert_kept, w2, expert_out, stream=None):

@@ -31,6 +31,7 @@ Workspace workspace_layout(const Dims &dm)
     w.all_offset = take(by_gate ? (size_t)dm.E * sizeof(int32_t) : 0);
     w.by_expert = take(by_gate ? (size_t)dm.T * dm.k * sizeof(int32_t) : 0);
     w.h = take((size_t)dm.send_rows * dm.H * sizeof(uint16_t));
+    w.a_wide = take(dm.fp8_widen ? (size_t)dm.send_rows * dm.d * sizeof(uint16_t) : 0);
     w.shared_rows = take(dm.shared_H > 0 ? 4 * sizeof(int32_t) : 0);
     w.shared_h = take((size_t)(dm.shared_H > 0 ? dm.T : 0) * dm.shared_H * sizeof(uint16_t));
     w.total = std::max<size_t>(off, 256);
@@ -103,6 +104,10 @@ static int make_dims(const moe_shape *s, Dims *dm)
     dm->shared_H = s->shared_H;
     dm->capacity = C;
     dm->send_rows = send_rows;
+    // rows an expert is expected to hold: C, or the mean T*k/E when dropless
+    const int64_t per_expert =
+        C >= 0 ? C : ((int64_t)s->T * s->k + s->E - 1) / s->E;
+    dm->fp8_widen = s->dispatch_fp8 == 1 && per_expert >= kFp8WidenRows;
     dm->nchunks = (s->T + kChunk - 1) / kChunk;
     return MOE_OK;
 }
@@ -229,8 +234,9 @@ MOE_EXPORT int moe_expert_ffn(const moe_shape *shape, const void *send_buf,
         return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
     uint16_t *h = reinterpret_cast<uint16_t *>((char *)workspace + wl.h);
-    hipError_t e =
-        launch_gate_up(dm, send_buf, send_scale, expert_offset, expert_kept, w1, w3, h, st);
+    uint16_t *a_wide = reinterpret_cast<uint16_t *>((char *)workspace + wl.a_wide);
+    hipError_t e = launch_gate_up(dm, send_buf, send_scale, expert_offset, expert_kept, w1, w3,
+                                  h, a_wide, st);
     if (e == hipSuccess)
         e = launch_down(dm, h, expert_offset, expert_kept, w2, expert_out, st);
     return hip_status(e);
@@ -239,17 +245,25 @@ MOE_EXPORT int moe_expert_ffn(const moe_shape *shape, const void *send_buf,
 MOE_EXPORT int moe_expert_gate_up(const moe_shape *shape, const void *send_buf,
                                   const float *send_scale, const int32_t *expert_offset,
                                   const int32_t *expert_kept, const uint16_t *w1,
-                                  const uint16_t *w3, uint16_t *h, void *stream)
+                                  const uint16_t *w3, uint16_t *h, void *workspace,
+                                  size_t workspace_bytes, void *stream)
 {
     Dims dm;
-    const int rc = make_dims(shape, &dm);
+    int rc = make_dims(shape, &dm);
     if (rc != MOE_OK)
         return rc;
     if (bad_ptr(send_buf, dm.send_rows) || bad_ptr(expert_offset) || bad_ptr(expert_kept) ||
         bad_ptr(w1) || bad_ptr(w3) || bad_ptr(h, dm.send_rows) || bad_scale(dm, send_scale))
         return MOE_EINVAL;
+    uint16_t *a_wide = nullptr; // the workspace is optional here
+    if (workspace) {
+        Workspace wl;
+        if ((rc = check_ws(dm, workspace, workspace_bytes, &wl)) != MOE_OK)
+            return rc;
+        a_wide = reinterpret_cast<uint16_t *>((char *)workspace + wl.a_wide);
+    }
     return hip_status(launch_gate_up(dm, send_buf, send_scale, expert_offset, expert_kept, w1,
-                                     w3, h, static_cast<hipStream_t>(stream)));
+                                     w3, h, a_wide, static_cast<hipStream_t>(stream)));
 }
 
 MOE_EXPORT int moe_expert_down(const moe_shape *shape, const uint16_t *h,
@@ -339,7 +353,8 @@ MOE_EXPORT int moe_layer_fwd(const moe_shape *shape, const uint16_t *x, const ui
                             expert_kept, expert_offset, rank_rows, stats, ws, wl, st);
     if (e == hipSuccess)
         e = launch_gate_up(dm, send_buf, send_scale, expert_offset, expert_kept, w1, w3,
-                           reinterpret_cast<uint16_t *>(ws + wl.h), st);
+                           reinterpret_cast<uint16_t *>(ws + wl.h),
+                           reinterpret_cast<uint16_t *>(ws + wl.a_wide), st);
     if (e == hipSuccess)
         e = launch_down(dm, reinterpret_cast<const uint16_t *>(ws + wl.h), expert_offset,
                         expert_kept, w2, expert_out, st);

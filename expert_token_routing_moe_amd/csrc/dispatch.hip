@@ -589,7 +589,7 @@ __global__ __launch_bounds__(256) void fp8_rows_to_bf16_kernel(const uint8_t *__
     const long long r = q / (d / 4);
     const uint32_t w = reinterpret_cast<const uint32_t *>(codes)[q];
     const uint2 b = e4m3x4_to_bf16x4(w);
-    const float sc = scales[r];
+    const float sc = scales ? scales[r] : 1.f;
     const uint32_t v[4] = {b.x & 0xffffu, b.x >> 16, b.y & 0xffffu, b.y >> 16};
     uint16_t *o = out + q * 4;
 #pragma unroll

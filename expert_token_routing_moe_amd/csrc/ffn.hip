@@ -46,7 +46,7 @@ namespace {
 
 struct GemmArgs {
     const void *A;              // [rows, K] bf16, or E4M3 codes (A8)
-    const float *a_scale;       // [rows] fp32 row scales (A8 only)
+    const float *a_scale;       // [rows] fp32 row scales (E4M3 rows; else null)
     const int32_t *row_offset;  // [E + 1] first row of each expert
     const int32_t *row_count;   // [E] rows of each expert
     const uint16_t *B0;         // [E, N, K]
@@ -480,7 +480,8 @@ __global__ __launch_bounds__(WM * WN * 64, MINB) void grouped_gemm_kernel(GemmAr
         for (int i = 0; i < NA; ++i) {
             const int mq = (wm + WM * i) * 16 + 4 * (lane >> 4); // row of q = 0
             float sr[4] = {1.f, 1.f, 1.f, 1.f};
-            if constexpr (A8) { // the rows' dequantization scales
+            if (A8 || g.a_scale) { // the rows' dequantization scales (E4M3 rows,
+                                   // in registers or widened beforehand)
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
                     sr[q] = mq + q < rows_valid ? g.a_scale[row0 + mq + q] : 0.f;
@@ -624,17 +625,29 @@ static void launch_gate_up_t(const Dims &dm, const GemmArgs &a, long long mtiles
 
 hipError_t launch_gate_up(const Dims &dm, const void *send_buf, const float *send_scale,
                           const int32_t *expert_offset, const int32_t *expert_kept,
-                          const uint16_t *w1, const uint16_t *w3, uint16_t *h, hipStream_t st)
+                          const uint16_t *w1, const uint16_t *w3, uint16_t *h, uint16_t *a_wide,
+                          hipStream_t st)
 {
     if (dm.send_rows == 0)
         return hipSuccess;
     const long long mtiles_max = (dm.send_rows + kBM1 - 1) / kBM1 + dm.E;
-    GemmArgs a{send_buf, send_scale, expert_offset, expert_kept, w1, w3, h, dm.E, dm.H, dm.d,
-               MOE_GEMM_ROT_GU ? rotate_k(dm.d) : 0};
-    if (dm.fp8)
-        launch_gate_up_t<true>(dm, a, mtiles_max, st);
-    else
+    GemmArgs a{send_buf, dm.fp8 ? send_scale : nullptr, expert_offset, expert_kept, w1, w3, h,
+               dm.E, dm.H, dm.d, MOE_GEMM_ROT_GU ? rotate_k(dm.d) : 0};
+    if (dm.fp8 && dm.fp8_widen && a_wide) {
+        // E4M3 values widened to bf16 (exact), row scales applied in the
+        // epilogue as in the E4M3 loop: the same products in the same
+        // order, so the same output bits
+        const hipError_t e = launch_fp8_rows_to_bf16(static_cast<const uint8_t *>(send_buf),
+                                                     nullptr, dm.send_rows, dm.d, a_wide, st);
+        if (e != hipSuccess)
+            return e;
+        a.A = a_wide;
         launch_gate_up_t<false>(dm, a, mtiles_max, st);
+    } else if (dm.fp8) {
+        launch_gate_up_t<true>(dm, a, mtiles_max, st);
+    } else {
+        launch_gate_up_t<false>(dm, a, mtiles_max, st);
+    }
     return hipGetLastError();
 }
 
@@ -683,7 +696,8 @@ hipError_t launch_shared_expert(const Dims &dm, const uint16_t *x, const uint16_
     ds.H = dm.shared_H;
     ds.send_rows = dm.T;
     ds.fp8 = 0;
-    hipError_t e = launch_gate_up(ds, x, nullptr, rows, rows + 2, w1s, w3s, hs, st);
+    ds.fp8_widen = false;
+    hipError_t e = launch_gate_up(ds, x, nullptr, rows, rows + 2, w1s, w3s, hs, nullptr, st);
     if (e == hipSuccess)
         e = launch_down(ds, hs, rows, rows + 2, w2s, shared_out, st);
     return e;

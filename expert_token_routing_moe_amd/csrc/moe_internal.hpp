@@ -112,7 +112,13 @@ struct Dims {
     int64_t capacity;  // C, or -1 when dropless
     int64_t send_rows; // E*C or T*k
     int nchunks;       // ceil(T / kChunk)
+    // E4M3 rows are widened to bf16 in a separate pass before the gate/up
+    // GEMM (given a workspace) when an expert is expected to hold at least
+    // kFp8WidenRows rows: there the GEMM is bound by the matrix cores, and
+    // the bf16 loop runs faster than the loop that widens in registers.
+    bool fp8_widen;
 };
+constexpr int64_t kFp8WidenRows = 512;
 
 // Byte offsets of each region inside the caller's workspace.
 struct Workspace {
@@ -124,6 +130,7 @@ struct Workspace {
     size_t all_offset;    // int32 [E]          exclusive scan of n_e (drop policy 1)
     size_t by_expert;     // int32 [T*k]        assignments grouped by expert (drop policy 1)
     size_t h;             // bf16 [send_rows, H] SwiGLU hidden activations
+    size_t a_wide;        // bf16 [send_rows, d] E4M3 send rows widened (fp8_widen only)
     size_t shared_rows;   // int32 [4]          row offsets/count of the shared expert's one group
     size_t shared_h;      // bf16 [T, shared_H] the shared expert's hidden activations
     size_t total;
@@ -145,10 +152,11 @@ hipError_t launch_dispatch(const Dims &dm, const uint16_t *x, const int32_t *top
                            const float *topk_w, void *send_buf, float *send_scale, int32_t *slot, int32_t *expert_count,
                            int32_t *expert_kept, int32_t *expert_offset, int32_t *rank_rows,
                            moe_stats *stats, char *ws, const Workspace &wl, hipStream_t st);
+// a_wide: NULL, or (with dm.fp8_widen) room for the widened E4M3 rows
 hipError_t launch_gate_up(const Dims &dm, const void *send_buf, const float *send_scale,
                           const int32_t *expert_offset,
                           const int32_t *expert_kept, const uint16_t *w1, const uint16_t *w3,
-                          uint16_t *h, hipStream_t st);
+                          uint16_t *h, uint16_t *a_wide, hipStream_t st);
 hipError_t launch_down(const Dims &dm, const uint16_t *h, const int32_t *expert_offset,
                        const int32_t *expert_kept, const uint16_t *w2, uint16_t *expert_out,
                        hipStream_t st);
@@ -159,6 +167,7 @@ hipError_t launch_stream_read(const void *src, size_t bytes, uint32_t *sink, hip
 hipError_t launch_shared_expert(const Dims &dm, const uint16_t *x, const uint16_t *w1s,
                                 const uint16_t *w3s, const uint16_t *w2s, uint16_t *shared_out,
                                 char *ws, const Workspace &wl, hipStream_t st);
+// scales NULL: every row's scale is 1 (the E4M3 values themselves, exact in bf16)
 hipError_t launch_fp8_rows_to_bf16(const uint8_t *codes, const float *scales, long long rows,
                                    int d, uint16_t *out, hipStream_t st);
 

@@ -242,10 +242,17 @@ int moe_expert_ffn(const moe_shape *shape, const void *send_buf, const float *se
  *   expert's kept rows; h is [send_rows, H] bf16, row r of h belongs to row r
  *   of send_buf; only kept rows are written.
  * moe_expert_down:     expert_out = bf16(h W2_e^T) on the same rows.
- * Arguments as in moe_expert_ffn; neither needs a workspace. */
+ * Arguments as in moe_expert_ffn.  moe_expert_down needs no workspace; for
+ * moe_expert_gate_up it is optional (NULL, 0 allowed; otherwise at least
+ * moe_query's size, and h must not lie inside it).  With dispatch_fp8 set
+ * and an expected load of at least 512 rows per expert (C, or T*k/E when
+ * dropless), a workspace lets the E4M3 rows be widened to bf16 in one pass
+ * before the GEMM (moe_expert_ffn and moe_layer_fwd always do); without one
+ * the GEMM widens them in registers.  Both give the same output bits. */
 int moe_expert_gate_up(const moe_shape *shape, const void *send_buf, const float *send_scale,
                        const int32_t *expert_offset, const int32_t *expert_kept,
-                       const uint16_t *w1, const uint16_t *w3, uint16_t *h, void *stream);
+                       const uint16_t *w1, const uint16_t *w3, uint16_t *h, void *workspace,
+                       size_t workspace_bytes, void *stream);
 int moe_expert_down(const moe_shape *shape, const uint16_t *h, const int32_t *expert_offset,
                     const int32_t *expert_kept, const uint16_t *w2, uint16_t *expert_out,
                     void *stream);

@@ -62,6 +62,21 @@ def test_query_minimum_capacity_matches_oracle(T, cf, mc):
         assert sr == (T * 2 if cap < 0 else 8 * cap)
 
 
+def test_query_workspace_holds_widened_fp8_rows_only_when_mfma_bound():
+    """E4M3 send rows get a bf16 copy in the workspace only where an expert is
+    expected to hold >= 512 rows (C here; T*k/E when dropless)."""
+    base = dict(T=4096, d=4096, E=8, k=2, H=1024, D=8, capacity_factor=1.0)
+    _, _, ws_bf = api.moe_query(api.Shape(**base))
+    sr, cap, ws_f8 = api.moe_query(api.Shape(**base, dispatch_fp8=1))
+    assert cap == 1024
+    assert sr * 4096 * 2 <= ws_f8 - ws_bf < sr * 4096 * 2 + 4096
+    for kw in (dict(base, T=1024), dict(base, T=1024, capacity_factor=math.inf),
+               dict(base, T=2044, capacity_factor=math.inf)):   # C 256; 256; 511 per expert
+        assert api.moe_query(api.Shape(**kw))[2] == api.moe_query(api.Shape(**kw, dispatch_fp8=1))[2]
+    dl = dict(base, T=2048, capacity_factor=math.inf)            # 512 per expert
+    assert api.moe_query(api.Shape(**dl, dispatch_fp8=1))[2] > api.moe_query(api.Shape(**dl))[2]
+
+
 def test_query_workspace_grows_only_for_gate_order_drops():
     base = dict(T=256, d=128, E=8, k=2, H=128, D=2, capacity_factor=1.25)
     _, _, ws0 = api.moe_query(api.Shape(**base))
@@ -137,7 +152,10 @@ def test_entry_points_reject_null_and_misaligned_pointers():
     args[4] = nul        # FP8 dispatch needs the row scales
     assert _raw("moe_dispatch", ctypes.byref(s8), *args, good, 1 << 30, nul) == api.MOE_EINVAL
     assert _raw("moe_expert_gate_up", ctypes.byref(s8), good, nul, good, good, good, good, good,
-                nul) == api.MOE_EINVAL
+                nul, 0, nul) == api.MOE_EINVAL
+    # the workspace is optional for moe_expert_gate_up, but checked when given
+    assert _raw("moe_expert_gate_up", ctypes.byref(s8), good, good, good, good, good, good, good,
+                good, 16, nul) == api.MOE_EWORKSPACE
     assert _raw("moe_fp8_rows_to_bf16", good, good, 4, 24, good, nul) == api.MOE_EINVAL  # d % 16
     assert _raw("moe_fp8_rows_to_bf16", good, good, -1, 32, good, nul) == api.MOE_EINVAL
     assert _raw("moe_expert_ffn", S, good, nul, good, good, good, good, mis, good, good,

@@ -490,6 +490,44 @@ def test_expert_ffn_every_tile_shape(fp8):
                               f"expert {e} ({m} rows)")
 
 
+def test_fp8_widened_gate_up_matches_register_path():
+    """At >= 512 rows per expert (MFMA-bound) the gate/up GEMM, given a
+    workspace, widens the E4M3 rows to bf16 in one pass before the bf16 loop;
+    without one it widens them in registers.  The two give the same bits on
+    every kept row, and the layer (which takes the widened path) matches the
+    oracle."""
+    cfg = MoEConfig("fp8_widen", T=1536, d=256, E=4, k=2, H=256, cf=INF, D=2, x_std=1.0,
+                    wg_std=0.1, w_std=0.05, seed=19, dispatch_fp8=1)  # 768 rows per expert
+    print(f"\n[fp8 widen] T={cfg.T} E={cfg.E} k={cfg.k}", flush=True)
+    inp = make_inputs(cfg, DEV)
+    shape = api.Shape.from_config(cfg)
+    buf = api.LayerBuffers.allocate(shape, DEV)
+    api.moe_layer_fwd(shape, inp["x"], inp["w_gate"], inp["bias"], inp["w1"], inp["w3"],
+                      inp["w2"], buf)
+    torch.cuda.synchronize()
+    n = buf.send_buf.shape[0]
+    hw = torch.zeros(n, cfg.H, dtype=torch.bfloat16, device=DEV)
+    hr = torch.zeros(n, cfg.H, dtype=torch.bfloat16, device=DEV)
+    args = (shape, buf.send_buf, buf.send_scale, buf.expert_offset, buf.expert_kept,
+            inp["w1"], inp["w3"])
+    api.moe_expert_gate_up(*args, hw, workspace=buf.workspace)
+    api.moe_expert_gate_up(*args, hr)
+    torch.cuda.synchronize()
+    off, kept = buf.expert_offset.cpu().numpy(), buf.expert_kept.cpu().numpy()
+    assert kept.min() >= 512
+    for e in range(cfg.E):
+        lo, m = int(off[e]), int(kept[e])
+        assert torch.equal(hw[lo:lo + m].view(torch.int16), hr[lo:lo + m].view(torch.int16)), e
+    w1, w3, w2 = (bf16_bits(inp[k]) for k in ("w1", "w3", "w2"))
+    want = oracle.expert_ffn_all(buf.send_buf.cpu().numpy(), off, kept, w1, w3, w2,
+                                 send_scale=buf.send_scale.cpu().numpy())
+    got = bf16_bits(buf.expert_out)
+    for e in range(cfg.E):
+        lo, m = int(off[e]), int(kept[e])
+        assert_bf16_close(bits_to_f64(got[lo:lo + m]), bits_to_f64(want[lo:lo + m]),
+                          f"fp8 widened expert {e}")
+
+
 @pytest.mark.parametrize("name", list(SMALL))
 def test_layer_fwd_fp8_end_to_end(name):
     cfg = SMALL[name].with_(dispatch_fp8=1)
