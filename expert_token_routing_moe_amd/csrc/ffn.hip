@@ -610,6 +610,27 @@ int rotate_k(int K)
 
 } // namespace
 
+// E4M3 send rows -> bf16 code values (exact; the row scales stay apart),
+// for the rows [0, min(*row_end, rows_max)) that the experts' groups cover.
+// Each lane widens 16 codes per pass (one 16-byte load, two 16-byte
+// stores), grid-stride.
+__global__ __launch_bounds__(256) void widen_e4m3_kernel(const uint4 *__restrict__ codes,
+                                                         const int32_t *__restrict__ row_end,
+                                                         long long rows_max, int d,
+                                                         uint4 *__restrict__ out)
+{
+    const long long rows = min((long long)*row_end, rows_max);
+    const long long n = rows * (d / 16); // 16-code pieces
+    for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n;
+         i += (long long)gridDim.x * 256) {
+        const uint4 c = load_nt(codes + i);
+        const uint2 a = e4m3x4_to_bf16x4(c.x), b = e4m3x4_to_bf16x4(c.y);
+        const uint2 e = e4m3x4_to_bf16x4(c.z), f = e4m3x4_to_bf16x4(c.w);
+        out[2 * i] = make_uint4(a.x, a.y, b.x, b.y);
+        out[2 * i + 1] = make_uint4(e.x, e.y, f.x, f.y);
+    }
+}
+
 template <bool A8>
 static void launch_gate_up_t(const Dims &dm, const GemmArgs &a, long long mtiles_max,
                              hipStream_t st)
@@ -637,8 +658,10 @@ hipError_t launch_gate_up(const Dims &dm, const void *send_buf, const float *sen
         // E4M3 values widened to bf16 (exact), row scales applied in the
         // epilogue as in the E4M3 loop: the same products in the same
         // order, so the same output bits
-        const hipError_t e = launch_fp8_rows_to_bf16(static_cast<const uint8_t *>(send_buf),
-                                                     nullptr, dm.send_rows, dm.d, a_wide, st);
+        widen_e4m3_kernel<<<2048, 256, 0, st>>>(static_cast<const uint4 *>(send_buf),
+                                                 expert_offset + dm.E, dm.send_rows, dm.d,
+                                                 reinterpret_cast<uint4 *>(a_wide));
+        const hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
         a.A = a_wide;
