@@ -22,8 +22,11 @@ Workspace workspace_layout(const Dims &dm)
         off = align_up(off + bytes);
         return at;
     };
-    w.logits = take((size_t)router_ksplit(dm.T, dm.E, dm.d) * dm.T * dm.E * sizeof(float));
-    w.wg_t = take((size_t)router_epad(dm.E) * dm.d * sizeof(uint16_t));
+    w.logits = take(router_partials(dm.T, dm.E, dm.d) ? (size_t)router_ksplit(dm.T, dm.E, dm.d) *
+                                                            dm.T * router_epad(dm.E) * sizeof(float)
+                                                      : 0);
+    w.wg_pad = take(router_ldw(dm.E) != dm.E ? (size_t)dm.d * router_ldw(dm.E) * sizeof(uint16_t)
+                                             : 0);
     w.chunk_counts = take((size_t)dm.nchunks * dm.E * sizeof(int32_t));
     w.chunk_base = take((size_t)dm.nchunks * dm.E * sizeof(int32_t));
     w.chunk_invalid = take((size_t)dm.nchunks * sizeof(int32_t));

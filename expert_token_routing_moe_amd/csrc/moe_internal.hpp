@@ -122,8 +122,8 @@ constexpr int64_t kFp8WidenRows = 512;
 
 // Byte offsets of each region inside the caller's workspace.
 struct Workspace {
-    size_t logits;        // fp32 [SK, T, E]    router partial logits (SK = router_ksplit)
-    size_t wg_t;          // bf16 [E_pad, d]    W_g transposed for the logit GEMM
+    size_t logits;        // fp32 [SK, T, E_pad] router partial logits (SK = router_ksplit)
+    size_t wg_pad;        // bf16 [d, E8]       W_g with rows padded to 8 experts (E % 8 != 0)
     size_t chunk_counts;  // int32 [nchunks, E] per-chunk expert counts
     size_t chunk_base;    // int32 [nchunks, E] exclusive scan of the counts over chunks
     size_t chunk_invalid; // int32 [nchunks]    invalid entries per chunk
@@ -142,7 +142,9 @@ Workspace workspace_layout(const Dims &dm);
 // Launchers (return hipGetLastError() of their launches)
 // ---------------------------------------------------------------------------
 int router_ksplit(int T, int E, int d); // K slices of the logit GEMM
+bool router_partials(int T, int E, int d); // the logit GEMM stores partial sums (S * n_et > 1)
 int router_epad(int E);                 // E rounded up to 64
+int router_ldw(int E);                  // W_g row length the router reads (E rounded up to 8)
 hipError_t launch_route(const Dims &dm, const uint16_t *x, const uint16_t *w_gate,
                         const float *bias, float *logits_out, int32_t *topk_idx, float *topk_w,
                         char *ws, const Workspace &wl, hipStream_t st);

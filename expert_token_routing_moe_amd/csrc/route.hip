@@ -3,20 +3,27 @@
 // Expert Parallelism", section 2 "The Gating Network Formulation"; the noise
 // term is zero at inference).
 //
-// Three launches:
-//  1. W_g [d, E] is transposed into the workspace as W_g^T [E_pad, d]
-//     (E_pad = E rounded up to 64, zero rows past E), so both operands of the
-//     logit GEMM are K-contiguous.
-//  2. The logit GEMM (M = T tokens, N = E_pad, K = d) on
-//     v_mfma_f32_16x16x32_bf16: bf16 products are exact in fp32 and
-//     accumulate in fp32.  A workgroup owns a 64-token x BE-expert tile and
-//     one of SK slices of K, fed through an LDS ring by direct-to-LDS loads;
-//     it writes fp32 partial logits [SK][T][E].  Splitting K fills the chip
-//     when T*E is small.
-//  3. KeepTopK + softmax, one wavefront per token: the SK partials are summed
-//     in slice order and the bias added (the logits), then k rounds of a
-//     wave-wide arg-max on order-preserving 64-bit keys (value bits, then
-//     E-1-e, so a tie goes to the lower expert index).
+// Logits.  A workgroup owns a BT-token x BE-expert tile of the logits over
+// one of S slices of K.  x rows and W_g rows stream through one LDS ring by
+// direct-to-LDS loads; W_g is read in the page's own [d, E] layout (each K
+// step's rows are one contiguous block of memory), and the matrix-core B
+// fragments, which need 8 consecutive K values of one expert, come out of
+// the ring by the gfx950 transposing LDS read (ds_read_b64_tr_b16).  bf16
+// products are exact in fp32 and accumulate in fp32
+// (v_mfma_f32_16x16x32_bf16).
+//
+// Selection, one wavefront per token: k rounds of a wave-wide arg-max on
+// order-preserving 64-bit keys (value bits, then E-1-e, so a tie goes to the
+// lower expert index), a softmax over the kept logits, optionally within the
+// token's best expert groups.
+//
+// One launch when a token tile's logits fit one workgroup (one slice, one
+// expert tile): it selects from its own tile.  Otherwise every slice stores
+// its fp32 partial tile and a second launch, one wavefront per token, sums
+// the partials in slice order (a fixed order: deterministic), adds the bias
+// and selects.  The kernel boundary is the device-wide barrier: on this
+// eight-XCD part a release inside the kernel means an L2 write-back per
+// workgroup, which measured slower than the second launch.
 #include <type_traits>
 
 #include "moe_internal.hpp"
@@ -27,205 +34,68 @@ namespace moe {
 int router_epad(int E) { return (E + 63) / 64 * 64; }
 
 // Experts per logit tile: all 256 of a multiple of 256 (one workgroup per
-// CU, so x is read once per expert group of 256), else 128 or 64 (two
-// workgroups per CU).
+// CU, eight waves), else 128 or 64 (two workgroups per CU, four waves).
 static int router_be(int E)
 {
     const int epad = router_epad(E);
     return epad % 256 == 0 ? 256 : epad % 128 == 0 ? 128 : 64;
 }
 
-// Split of K for the logit GEMM: enough workgroups to cover the chip (one
-// or two per CU), at least four K steps per slice.  Shared by the workspace
-// layout.
+// W_g row length as the router reads it: E when E % 8 == 0 (the caller's
+// tensor), else E rounded up to 8 (a zero-padded copy in the workspace).
+int router_ldw(int E) { return (E + 7) / 8 * 8; }
+
+// Launch shape of the logit GEMM: 64-token tiles, and K cut into S slices
+// when the token tiles alone leave the chip short of workgroups (one or two
+// per CU): enough slices to fill it, at least four K steps each, at most 32.
+// (128-token tiles with twice the slices measured the same time at the
+// DeepSeek-V3 prefill shape for twice the partial-sum bytes.)  T = 0:
+// nothing to split.
+void router_plan(int T, int E, int d, int *bt, int *sk)
+{
+    const int be = router_be(E), n_et = router_epad(E) / be;
+    const int target = be == 256 ? 256 : 512;
+    const int steps = d / 64;
+    *bt = 64;
+    *sk = 1;
+    const int tiles = ((T + 63) / 64) * n_et;
+    if (T == 0 || tiles >= target)
+        return;
+    int s = (target + tiles - 1) / tiles;
+    s = std::min(s, std::max(1, steps / 4));
+    *sk = std::max(1, std::min(s, 32));
+}
+
 int router_ksplit(int T, int E, int d)
 {
-    const int be = router_be(E);
-    const int tiles = ((T + 63) / 64) * (router_epad(E) / be);
-    const int steps = d / 64;
-    if (tiles == 0)
-        return 1; // T = 0: nothing to split
-    const int target = be == 256 ? 256 : 512;
-    int sk = (target + tiles - 1) / tiles;
-    sk = std::min(sk, std::max(1, steps / 4));
-    return std::max(1, sk);
+    int bt, sk;
+    router_plan(T, E, d, &bt, &sk);
+    return sk;
+}
+
+bool router_partials(int T, int E, int d)
+{
+    return T > 0 && router_ksplit(T, E, d) * (router_epad(E) / router_be(E)) > 1;
 }
 
 namespace {
 
-// W_g [d, E] -> W_g^T [E_pad, d], 64 x 64 tiles through LDS.  E % 8 == 0:
-// 16-byte loads of 8 experts and 16-byte stores of 8 K values.
-__global__ __launch_bounds__(256) void transpose_wg_vec_kernel(const uint16_t *__restrict__ wg,
-                                                               uint16_t *__restrict__ wgt,
-                                                               int d, int E)
+
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+// Ring slot of W_g piece p (16 bytes, 8 experts) of K row r inside the tile
+// row of BPR pieces: p ^ swzb(r).  The four rows one transposing read
+// touches per 16-lane group land in four distinct 32-byte slots of one
+// 128-byte block, and the groups of a wave in different blocks.
+template <int BPR>
+__device__ __forceinline__ int swzb(int r)
 {
-    __shared__ __attribute__((aligned(16))) uint16_t tile[64][72]; // [k][e], 144-byte rows
-    const int k0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
-    for (int c = threadIdx.x; c < 512; c += 256) {
-        const int kr = c >> 3, ec = (c & 7) * 8;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (e0 + ec < E) // E % 8 == 0: all 8 experts are in range or none
-            v = *reinterpret_cast<const uint4 *>(wg + (size_t)(k0 + kr) * E + e0 + ec);
-        *reinterpret_cast<uint4 *>(&tile[kr][ec]) = v;
-    }
-    __syncthreads();
-    for (int c = threadIdx.x; c < 512; c += 256) {
-        const int er = c & 63, kc = (c >> 6) * 8; // neighbouring lanes read neighbouring columns
-        uint32_t w[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            w[j] = (uint32_t)tile[kc + 2 * j][er] | ((uint32_t)tile[kc + 2 * j + 1][er] << 16);
-        *reinterpret_cast<uint4 *>(wgt + (size_t)(e0 + er) * d + k0 + kc) =
-            make_uint4(w[0], w[1], w[2], w[3]);
-    }
-}
-
-// Any E: element by element.
-__global__ __launch_bounds__(256) void transpose_wg_kernel(const uint16_t *__restrict__ wg,
-                                                           uint16_t *__restrict__ wgt, int d,
-                                                           int E)
-{
-    __shared__ uint16_t tile[64][65];
-    const int k0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
-    for (int i = threadIdx.x; i < 64 * 64; i += 256) {
-        const int kr = i / 64, ec = i % 64;
-        const int e = e0 + ec;
-        tile[kr][ec] = (e < E) ? wg[(size_t)(k0 + kr) * E + e] : (uint16_t)0;
-    }
-    __syncthreads();
-    for (int i = threadIdx.x; i < 64 * 64; i += 256) {
-        const int er = i / 64, kc = i % 64;
-        wgt[(size_t)(e0 + er) * d + k0 + kc] = tile[kc][er];
-    }
-}
-
-#ifndef MOE_ROUTER_WN
-#define MOE_ROUTER_WN 4 // wave columns of a 256-expert logit tile (2 x WN waves)
-#endif
-constexpr int RBT = 64;   // tokens per tile
-constexpr int RBK = 64;   // K step
-
-template <int BE, int RRING, int MINB, int WM, int WN>
-__global__ __launch_bounds__(WM * WN * 64, MINB) void router_logits_kernel(
-    const uint16_t *__restrict__ x, const uint16_t *__restrict__ wgt,
-    float *__restrict__ partial, int T, int d, int E, int n_et, int sk_count, int total)
-{
-    constexpr int NW = WM * WN;                    // waves per workgroup
-    constexpr int RC = RBK / 8, RPI = 64 / RC;     // 8 pieces per row, 8 rows per load
-    constexpr int A_PW = RBT / RPI / NW;           // x loads per wave per stage
-    constexpr int B_PW = BE / RPI / NW;            // W_g^T loads per wave per stage
-    static_assert(A_PW * RPI * NW == RBT && B_PW * RPI * NW == BE, "whole loads per wave");
-    constexpr int A_BYTES = RBT * RBK * 2, STAGE = (RBT + BE) * RBK * 2;
-    constexpr int S = RRING / STAGE < 8 ? RRING / STAGE : 8;
-    static_assert(S >= 2, "two stages fit");
-    constexpr int WTT = RBT / WM, WTE = BE / WN;   // WM x WN waves
-    constexpr int RT = WTT / 16, CT = WTE / 16;
-    __shared__ __attribute__((aligned(1024))) char smem[S * STAGE];
-
-    const int w = xcd_remap(blockIdx.x, total);
-    if (w < 0)
-        return;
-    // work order: K slice, then token tile, then expert tile.  The XCD remap
-    // gives each XCD a contiguous range, so the workgroups of one XCD share
-    // one slice of W_g^T in their L2 while each streams its own x rows.
-    const int n_tt = total / (n_et * sk_count);
-    const int et = w % n_et;
-    const int tt = (w / n_et) % n_tt;
-    const int sk = w / (n_et * n_tt);
-    const int t0 = tt * RBT, e0 = et * BE;
-    const int steps = d / RBK;
-    const int s_lo = steps * sk / sk_count, s_hi = steps * (sk + 1) / sk_count;
-    const int nsteps = s_hi - s_lo;
-
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wt = wave / WN, we = wave % WN;
-
-    const uint16_t *asrc[A_PW];
-    const uint16_t *bsrc[B_PW];
-#pragma unroll
-    for (int j = 0; j < A_PW; ++j) {
-        const int r = (NW * j + wave) * RPI + lane / RC;
-        const int piece = (lane % RC) ^ swz<RC>(r);
-        const int t = (t0 + r < T) ? t0 + r : t0; // rows past T read row t0 (never stored)
-        asrc[j] = x + (size_t)t * d + (size_t)s_lo * RBK + piece * 8;
-    }
-#pragma unroll
-    for (int j = 0; j < B_PW; ++j) {
-        const int r = (NW * j + wave) * RPI + lane / RC;
-        const int piece = (lane % RC) ^ swz<RC>(r);
-        bsrc[j] = wgt + (size_t)(e0 + r) * d + (size_t)s_lo * RBK + piece * 8;
-    }
-    const uint32_t lds_base = (uint32_t)(uintptr_t)(LDS_AS char *)smem;
-    auto issue = [&](int step, int slot) {
-        const uint32_t st = lds_base + slot * STAGE;
-        const int k0 = step * RBK;
-#pragma unroll
-        for (int j = 0; j < A_PW; ++j)
-            dma16(asrc[j] + k0, st + (NW * j + wave) * 1024);
-#pragma unroll
-        for (int j = 0; j < B_PW; ++j)
-            dma16(bsrc[j] + k0, st + A_BYTES + (NW * j + wave) * 1024);
-    };
-
-    floatx4 acc[RT][CT];
-#pragma unroll
-    for (int i = 0; i < RT; ++i)
-#pragma unroll
-        for (int j = 0; j < CT; ++j)
-            acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-    for (int u = 0; u < S - 1 && u < nsteps; ++u)
-        issue(u, u);
-    for (int st = 0; st < nsteps; ++st) {
-        const int ahead = min(S - 2, nsteps - 1 - st);
-        wait_vmcnt(ahead * (A_PW + B_PW));
-        ring_barrier();
-        if (st + S - 1 < nsteps)
-            issue(st + S - 1, (st + S - 1) % S);
-        const char *As = smem + (st % S) * STAGE;
-        const char *Bs = As + A_BYTES;
-#pragma unroll
-        for (int kc = 0; kc < RC; kc += 4) {
-            const int piece = kc + (lane >> 4);
-            bf16x8 a[RT], b[CT];
-#pragma unroll
-            for (int i = 0; i < RT; ++i) {
-                const int r = wt * WTT + i * 16 + (lane & 15);
-                a[i] = *reinterpret_cast<const bf16x8 *>(As + r * (RBK * 2) +
-                                                         ((piece ^ swz<RC>(r)) << 4));
-            }
-#pragma unroll
-            for (int j = 0; j < CT; ++j) {
-                const int n = we * WTE + j * 16 + (lane & 15);
-                b[j] = *reinterpret_cast<const bf16x8 *>(Bs + n * (RBK * 2) +
-                                                         ((piece ^ swz<RC>(n)) << 4));
-            }
-#pragma unroll
-            for (int i = 0; i < RT; ++i)
-#pragma unroll
-                for (int j = 0; j < CT; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j],
-                                                                         0, 0, 0);
-        }
-    }
-
-    // D layout of a 16x16 MFMA tile: lane holds rows 4*(lane/16)+q, column lane%16.
-    float *out = partial + (size_t)sk * T * E;
-#pragma unroll
-    for (int j = 0; j < CT; ++j) {
-        const int e = e0 + we * WTE + j * 16 + (lane & 15);
-        if (e >= E)
-            continue;
-#pragma unroll
-        for (int i = 0; i < RT; ++i)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int t = t0 + wt * WTT + i * 16 + 4 * (lane >> 4) + q;
-                if (t < T)
-                    out[(size_t)t * E + e] = acc[i][j][q];
-            }
-    }
+    int s = (r & 3) << 1;
+    if constexpr (BPR >= 16)
+        s |= ((r >> 3) & 1) << 3;
+    if constexpr (BPR >= 32)
+        s |= ((r >> 4) & 1) << 4;
+    return s;
 }
 
 // Order-preserving key of a finite fp32 logit and its expert index: larger
@@ -247,19 +117,16 @@ __device__ __forceinline__ float key_value(uint64_t key)
 // v = max(v, v of the lane that DPP control CTRL selects), for the rows in
 // ROW_MASK; a lane without a source keeps its own value.
 template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ uint64_t max_dpp(uint64_t v)
+__device__ __forceinline__ uint32_t max_dpp(uint32_t v)
 {
-    const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
-    const uint32_t olo = (uint32_t)__builtin_amdgcn_update_dpp((int)lo, (int)lo, CTRL, ROW_MASK, 0xF, false);
-    const uint32_t ohi = (uint32_t)__builtin_amdgcn_update_dpp((int)hi, (int)hi, CTRL, ROW_MASK, 0xF, false);
-    const uint64_t o = ((uint64_t)ohi << 32) | olo;
+    const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, ROW_MASK, 0xF, false);
     return o > v ? o : v;
 }
 
 // Maximum over the wavefront, returned in every lane: within each 16-lane row
 // by quad permutes and the half-row / row mirrors, across rows by the row
 // broadcasts of lanes 15 and 31 (lane 63 then holds the total).
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v)
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
 {
     v = max_dpp<0xB1, 0xF>(v);  // quad_perm [1, 0, 3, 2]
     v = max_dpp<0x4E, 0xF>(v);  // quad_perm [2, 3, 0, 1]
@@ -267,8 +134,15 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v)
     v = max_dpp<0x140, 0xF>(v); // row_mirror
     v = max_dpp<0x142, 0xA>(v); // row_bcast:15 into rows 1 and 3
     v = max_dpp<0x143, 0xC>(v); // row_bcast:31 into rows 2 and 3
-    const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, 63);
-    const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Maximum of a 64-bit key over the wavefront: the largest upper half, then
+// the largest lower half among the lanes that hold it.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v)
+{
+    const uint32_t hi = wave_max_u32((uint32_t)(v >> 32));
+    const uint32_t lo = wave_max_u32((uint32_t)(v >> 32) == hi ? (uint32_t)v : 0u);
     return ((uint64_t)hi << 32) | lo;
 }
 
@@ -281,70 +155,29 @@ __device__ __forceinline__ void lds_wait()
     asm volatile("" ::: "memory");
 }
 
-// One wavefront per token; lane l holds logits l, l+64, ... (V per lane).
-// The logit of (t, e) is the sum, in slice order, of the sk_count partials
-// plus the bias; it is written to logits_out when that is non-null.
-// Group limit ("MoE Expert Parallelism Sizing: Traffic, Capacity, Fabric":
-// at most M nodes per token, Megatron's group-limited routing), when
-// G > 1 and M < G: the E experts form G contiguous groups; each group's
-// score is its best logit (LDS atomic max of the order-preserving key), the
-// M best groups are picked by M wave arg-max rounds (ties to the lower
-// group), and the other groups' experts are retired before KeepTopK.
+// KeepTopK + softmax of one token by one wavefront.  Lane l holds the
+// logits (bias included) of experts l, l+64, ... in h[0..V); experts >= E
+// are ignored.  Group limit ("MoE Expert Parallelism Sizing: Traffic,
+// Capacity, Fabric": at most M nodes per token, Megatron's group-limited
+// routing), when G > 1 and M < G: the E experts form G contiguous groups;
+// each group's score is its best logit (LDS atomic max of the
+// order-preserving key), the M best groups are picked by M wave arg-max
+// rounds (ties to the lower group), and the other groups' experts are
+// retired before KeepTopK.  gs/allow: this wave's LDS scratch (G entries).
 template <int V>
-__global__ __launch_bounds__(256) void topk_softmax_kernel(
-    const float *__restrict__ partial, int sk_count, const float *__restrict__ bias,
-    float *__restrict__ logits_out, int32_t *__restrict__ topk_idx, float *__restrict__ topk_w,
-    int T, int E, int k, int G, int M)
+__device__ __forceinline__ void topk_softmax_token(const float (&h)[V], int E, int k, int G,
+                                                   int M, uint32_t *gs, uint8_t *allow,
+                                                   int32_t *__restrict__ idx_row,
+                                                   float *__restrict__ w_row)
 {
-    __shared__ uint32_t s_gscore[4][kMaxExperts];
-    __shared__ uint8_t s_allow[4][kMaxExperts];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int t = blockIdx.x * 4 + wave;
-    if (t >= T)
-        return;
-    // The lane's partial sums are loaded in batches of SKB slices, all
-    // loads of a batch issued before any is added (one memory round trip per
-    // batch instead of one per slice), then summed in slice order.
-    constexpr int SKB = 8;
-    float h[V], bv[V];
-#pragma unroll
-    for (int j = 0; j < V; ++j) {
-        const int e = lane + 64 * j;
-        h[j] = 0.f;
-        bv[j] = (bias && e < E) ? bias[e] : 0.f;
-    }
-    for (int s0 = 0; s0 < sk_count; s0 += SKB) {
-        float pv[V][SKB];
-#pragma unroll
-        for (int j = 0; j < V; ++j)
-#pragma unroll
-            for (int u = 0; u < SKB; ++u) {
-                const int e = lane + 64 * j, s = s0 + u;
-                pv[j][u] = (e < E && s < sk_count) ? partial[((size_t)s * T + t) * E + e] : 0.f;
-            }
-#pragma unroll
-        for (int j = 0; j < V; ++j)
-#pragma unroll
-            for (int u = 0; u < SKB; ++u)
-                if (s0 + u < sk_count)
-                    h[j] = s0 + u == 0 ? pv[j][u] : h[j] + pv[j][u];
-    }
+    const int lane = threadIdx.x & 63;
     uint64_t key[V];
 #pragma unroll
     for (int j = 0; j < V; ++j) {
         const int e = lane + 64 * j;
-        key[j] = 0ull; // sorts below every real key
-        if (e < E) {
-            if (bias)
-                h[j] += bv[j];
-            if (logits_out)
-                logits_out[(size_t)t * E + e] = h[j];
-            key[j] = topk_key(h[j], e, E);
-        }
+        key[j] = e < E ? topk_key(h[j], e, E) : 0ull; // 0 sorts below every real key
     }
     if (G > 1 && M < G) {
-        uint32_t *gs = s_gscore[wave];
-        uint8_t *allow = s_allow[wave];
         const int per = E / G;
         for (int g = lane; g < G; g += 64) {
             gs[g] = 0u; // below every real score
@@ -405,32 +238,354 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(
                 my_e = e;
                 my_p = p;
             } else {
-                topk_idx[(size_t)t * k + s] = e;
-                topk_w[(size_t)t * k + s] = p;
+                idx_row[s] = e;
+                w_row[s] = p;
             }
         }
     }
     if (lane < k) {
-        topk_idx[(size_t)t * k + lane] = my_e;
-        topk_w[(size_t)t * k + lane] = my_p / denom;
+        idx_row[lane] = my_e;
+        w_row[lane] = my_p / denom;
     }
-    for (int s = lane + 64; s < k; s += 64) {
-        const size_t o = (size_t)t * k + s;
-        topk_w[o] = topk_w[o] / denom;
+    for (int s = lane + 64; s < k; s += 64)
+        w_row[s] = w_row[s] / denom;
+}
+
+// Selection on caller-given logits: one wavefront per token.
+template <int V>
+__global__ __launch_bounds__(256) void topk_softmax_kernel(const float *__restrict__ logits,
+                                                           int32_t *__restrict__ topk_idx,
+                                                           float *__restrict__ topk_w, int T,
+                                                           int E, int k, int G, int M)
+{
+    __shared__ uint32_t s_gscore[4][kMaxExperts];
+    __shared__ uint8_t s_allow[4][kMaxExperts];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int t = blockIdx.x * 4 + wave;
+    if (t >= T)
+        return;
+    float h[V];
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+        const int e = lane + 64 * j;
+        h[j] = e < E ? logits[(size_t)t * E + e] : 0.f;
+    }
+    topk_softmax_token<V>(h, E, k, G, M, s_gscore[wave], s_allow[wave], topk_idx + (size_t)t * k,
+                          topk_w + (size_t)t * k);
+}
+
+struct RouteArgs {
+    const uint16_t *x;        // [T, d] bf16
+    const uint16_t *wg;       // [d, ldw] bf16 (ldw % 8 == 0, ldw >= E)
+    const float *bias;        // [E] or null
+    float *logits_out;        // [T, E] or null
+    int32_t *topk_idx;        // [T, k]
+    float *topk_w;            // [T, k]
+    float *partial;           // [S, T, E_pad] fp32 partial logits (S * n_et > 1)
+    int T, d, E, ldw, epad, k, G, M;
+    int n_tt, n_et, S, total;
+};
+
+// Logits of tokens [t0, t0 + TC) and all E_pad experts sit in LDS (row pitch
+// ldl floats, bias included); each wavefront selects for tokens wave,
+// wave + NW, ...
+template <int V, int NW>
+__device__ __forceinline__ void select_rows(const RouteArgs &a, const float *L, int ldl, int t0,
+                                            int TC, char *gscratch)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint32_t *gs = reinterpret_cast<uint32_t *>(gscratch) + wave * kMaxExperts;
+    uint8_t *allow = reinterpret_cast<uint8_t *>(gscratch + NW * kMaxExperts * 4) +
+                     wave * kMaxExperts;
+    for (int tl = wave; tl < TC; tl += NW) {
+        const int t = t0 + tl;
+        if (t >= a.T)
+            break;
+        float h[V];
+#pragma unroll
+        for (int j = 0; j < V; ++j) {
+            const int e = lane + 64 * j;
+            h[j] = e < a.E ? L[tl * ldl + e] : 0.f;
+        }
+        topk_softmax_token<V>(h, a.E, a.k, a.G, a.M, gs, allow, a.topk_idx + (size_t)t * a.k,
+                              a.topk_w + (size_t)t * a.k);
     }
 }
 
-hipError_t launch_topk(const Dims &dm, const float *partial, int sk, const float *bias,
-                       float *logits_out, int32_t *topk_idx, float *topk_w, hipStream_t st)
+template <int NW>
+__device__ __forceinline__ void select_dispatch(const RouteArgs &a, const float *L, int ldl,
+                                                int t0, int TC, char *gscratch)
+{
+    const int V = a.epad / 64;
+    if (V <= 1)
+        select_rows<1, NW>(a, L, ldl, t0, TC, gscratch);
+    else if (V <= 2)
+        select_rows<2, NW>(a, L, ldl, t0, TC, gscratch);
+    else if (V <= 4)
+        select_rows<4, NW>(a, L, ldl, t0, TC, gscratch);
+    else if (V <= 8)
+        select_rows<8, NW>(a, L, ldl, t0, TC, gscratch);
+    else
+        select_rows<16, NW>(a, L, ldl, t0, TC, gscratch);
+}
+
+// The logit GEMM.  BT tokens x BE experts x one K slice per workgroup; with
+// one slice and one expert tile (S * n_et == 1, so BE == E_pad) it selects
+// from its own tile, else it stores the fp32 partial tile.
+template <int BT, int RBK, int BE, int RRING, int MINB, int WM, int WN>
+__global__ __launch_bounds__(WM * WN * 64, MINB) void route_logits_kernel(RouteArgs a)
+{
+    constexpr int NW = WM * WN;                  // waves per workgroup
+    constexpr int NT = NW * 64;
+    constexpr int RC = RBK / 8, RPI = 64 / RC;   // x: pieces per row, rows per load
+    constexpr int A_PW = BT / RPI / NW;          // x loads per wave per stage
+    constexpr int BPR = BE / 8;                  // W_g: pieces per tile row
+    constexpr int BRPL = 64 / BPR;               // W_g rows per wave-wide load
+    constexpr int B_PW = RBK / BRPL / NW;        // W_g loads per wave per stage
+    static_assert(A_PW * RPI * NW == BT && B_PW * BRPL * NW == RBK, "whole loads per wave");
+    constexpr int A_BYTES = BT * RBK * 2, STAGE = A_BYTES + RBK * BE * 2;
+    constexpr int NS = RRING / STAGE < 8 ? RRING / STAGE : 8;
+    static_assert(NS >= 2, "two stages fit");
+    constexpr int WTT = BT / WM, WTE = BE / WN;  // wave tile
+    constexpr int RT = WTT / 16, CT = WTE / 16;
+    constexpr int LDC = BE + 4;                  // epilogue tile pitch (floats)
+    static_assert(BT * LDC * 4 <= RRING, "epilogue tile fits in the ring");
+    constexpr int GSCR = NW * kMaxExperts * 5;   // selection scratch (group limit)
+    __shared__ __attribute__((aligned(1024))) char smem[RRING];
+
+    const int w = xcd_remap(blockIdx.x, a.total);
+    if (w < 0)
+        return;
+    // work order: K slice, then token tile, then expert tile.  The XCD remap
+    // gives each XCD a contiguous range, so the workgroups of one XCD share
+    // one slice of W_g in their L2 while each streams its own x rows.
+    const int et = w % a.n_et;
+    const int tt = (w / a.n_et) % a.n_tt;
+    const int sk = w / (a.n_et * a.n_tt);
+    const int t0 = tt * BT, e0 = et * BE;
+    const int T = a.T, d = a.d, ldw = a.ldw;
+    // slices are cut on 64-deep boundaries, so the sum over K is taken in
+    // the same order whatever the step depth
+    const int steps = d / 64, spm = 64 / RBK;
+    const int s_lo = steps * sk / a.S * spm, s_hi = steps * (sk + 1) / a.S * spm;
+    const int nsteps = s_hi - s_lo;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wt = wave / WN, we = wave % WN;
+
+    // Load j of wave w fills ring bytes [(NW*j + w) * 1 KB, +1 KB) of its
+    // region.  x: lane l writes piece l % 8 of row l / 8 (source piece
+    // swizzled).  W_g: lane l writes slot l % BPR of K row l / BPR, i.e.
+    // source piece (l % BPR) ^ swzb(row); pieces past the row's end (the
+    // last tile when E_pad > ldw) read piece 0 instead (never selected).
+    const uint16_t *asrc[A_PW];
+    const uint16_t *bsrc[B_PW];
+#pragma unroll
+    for (int j = 0; j < A_PW; ++j) {
+        const int r = (NW * j + wave) * RPI + lane / RC;
+        const int piece = (lane % RC) ^ swz<RC>(r);
+        const int t = (t0 + r < T) ? t0 + r : t0; // rows past T read row t0 (never stored)
+        asrc[j] = a.x + (size_t)t * d + (size_t)s_lo * RBK + piece * 8;
+    }
+#pragma unroll
+    for (int j = 0; j < B_PW; ++j) {
+        const int r = (NW * j + wave) * BRPL + lane / BPR;
+        const int piece = (lane % BPR) ^ swzb<BPR>(r);
+        const int e = e0 + piece * 8 < ldw ? e0 + piece * 8 : 0;
+        bsrc[j] = a.wg + ((size_t)s_lo * RBK + r) * ldw + e;
+    }
+    const uint32_t lds_base = (uint32_t)(uintptr_t)(LDS_AS char *)smem;
+    auto issue = [&](int step, int slot) {
+        const uint32_t st = lds_base + slot * STAGE;
+#pragma unroll
+        for (int j = 0; j < A_PW; ++j)
+            dma16(asrc[j] + step * RBK, st + (NW * j + wave) * 1024);
+#pragma unroll
+        for (int j = 0; j < B_PW; ++j)
+            dma16(bsrc[j] + (size_t)step * RBK * ldw, st + A_BYTES + (NW * j + wave) * 1024);
+    };
+
+    floatx4 acc[RT][CT];
+#pragma unroll
+    for (int i = 0; i < RT; ++i)
+#pragma unroll
+        for (int j = 0; j < CT; ++j)
+            acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    for (int u = 0; u < NS - 1 && u < nsteps; ++u)
+        issue(u, u);
+    LDS_AS char *lds = (LDS_AS char *)smem;
+    for (int st = 0; st < nsteps; ++st) {
+        const int ahead = min(NS - 2, nsteps - 1 - st);
+        wait_vmcnt(ahead * (A_PW + B_PW));
+        ring_barrier();
+        if (st + NS - 1 < nsteps)
+            issue(st + NS - 1, (st + NS - 1) % NS);
+        const int As = (st % NS) * STAGE;
+        const int Bs = As + A_BYTES;
+#pragma unroll
+        for (int kc = 0; kc < RC; kc += 4) {
+            bf16x8 av[RT], bv[CT];
+            const int piece = kc + (lane >> 4);
+#pragma unroll
+            for (int i = 0; i < RT; ++i) {
+                const int r = wt * WTT + i * 16 + (lane & 15);
+                av[i] = *reinterpret_cast<const LDS_AS bf16x8 *>(
+                    lds + As + r * (RBK * 2) + ((piece ^ swz<RC>(r)) << 4));
+            }
+            // B fragment of expert column n = n0 + (lane & 15): lane group
+            // g = lane / 16 needs K rows 8g .. 8g+7 of this 32-deep half.  A
+            // transposing read takes, per 16-lane group, four K rows of 16
+            // experts (source lane jj reads row jj / 4, experts 4 (jj % 4)
+            // .. +3) and hands lane i the four K values of expert i.
+            const int grp = lane >> 4, jj = lane & 15;
+#pragma unroll
+            for (int j = 0; j < CT; ++j) {
+                const int n0 = we * WTE + j * 16;
+                const int p = (n0 >> 3) + ((jj & 3) >> 1);
+                const int half = (jj & 1) * 8;
+                bf16x4 lo, hi;
+                {
+                    const int r = kc * 8 + grp * 8 + (jj >> 2);
+                    lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(reinterpret_cast<LDS_AS bf16x4 *>(
+                        lds + Bs + r * (BE * 2) + ((p ^ swzb<BPR>(r)) << 4) + half));
+                }
+                {
+                    const int r = kc * 8 + grp * 8 + 4 + (jj >> 2);
+                    hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(reinterpret_cast<LDS_AS bf16x4 *>(
+                        lds + Bs + r * (BE * 2) + ((p ^ swzb<BPR>(r)) << 4) + half));
+                }
+                bv[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            }
+#pragma unroll
+            for (int i = 0; i < RT; ++i)
+#pragma unroll
+                for (int j = 0; j < CT; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[i], bv[j], acc[i][j],
+                                                                         0, 0, 0);
+        }
+    }
+
+    // D layout of a 16x16 MFMA tile: lane holds rows 4*(lane/16)+q, column
+    // lane%16.
+    if (a.S * a.n_et > 1) {
+        // partial tile -> [sk, t, e0 .. e0 + BE) of the [S, T, E_pad] sums,
+        // 64-byte row pieces straight from the accumulators
+        float *out = a.partial + (size_t)sk * T * a.epad;
+#pragma unroll
+        for (int i = 0; i < RT; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int t = t0 + wt * WTT + i * 16 + 4 * (lane >> 4) + q;
+                if (t < T)
+#pragma unroll
+                    for (int j = 0; j < CT; ++j)
+                        out[(size_t)t * a.epad + e0 + we * WTE + j * 16 + (lane & 15)] =
+                            acc[i][j][q];
+            }
+        return;
+    }
+    // one slice, one expert tile (64-token tiles only: the planner uses
+    // 128-token tiles with partial sums): the tile goes to LDS and straight
+    // to selection
+    if constexpr (BT * LDC * 4 + GSCR <= RRING) {
+    __syncthreads(); // every wave is done with the ring
+    float *C = reinterpret_cast<float *>(smem);
+#pragma unroll
+    for (int i = 0; i < RT; ++i)
+#pragma unroll
+        for (int j = 0; j < CT; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                C[(wt * WTT + i * 16 + 4 * (lane >> 4) + q) * LDC + we * WTE + j * 16 +
+                  (lane & 15)] = acc[i][j][q];
+    __syncthreads();
+    for (int c = tid; c < BT * BE; c += NT) {
+        const int r = c / BE, e = c % BE;
+        float v = C[r * LDC + e];
+        if (e < a.E) {
+            if (a.bias)
+                v += a.bias[e];
+            if (a.logits_out && t0 + r < T)
+                a.logits_out[(size_t)(t0 + r) * a.E + e] = v;
+        }
+        C[r * LDC + e] = v;
+    }
+    __syncthreads();
+    select_dispatch<NW>(a, C, LDC, t0, BT, smem + BT * LDC * 4);
+    }
+}
+
+// Sum of the S partial logits of a token in slice order (loads in batches
+// of 8 slices, every load of a batch in flight together), plus the bias,
+// then selection: one wavefront per token.
+template <int V>
+__global__ __launch_bounds__(256) void route_select_kernel(RouteArgs a)
+{
+    __shared__ uint32_t s_gscore[4][kMaxExperts];
+    __shared__ uint8_t s_allow[4][kMaxExperts];
+    constexpr int SB = 8;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int t = blockIdx.x * 4 + wave;
+    if (t >= a.T)
+        return;
+    const int S = a.S, E = a.E, epad = a.epad;
+    float h[V];
+    for (int s0 = 0; s0 < S; s0 += SB) {
+        float pv[SB][V];
+#pragma unroll
+        for (int u = 0; u < SB; ++u)
+#pragma unroll
+            for (int j = 0; j < V; ++j) {
+                const int e = lane + 64 * j;
+                pv[u][j] = (s0 + u < S && e < E)
+                               ? a.partial[((size_t)(s0 + u) * a.T + t) * epad + e]
+                               : 0.f;
+            }
+#pragma unroll
+        for (int u = 0; u < SB; ++u)
+#pragma unroll
+            for (int j = 0; j < V; ++j)
+                if (s0 + u < S)
+                    h[j] = s0 + u == 0 ? pv[u][j] : h[j] + pv[u][j];
+    }
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+        const int e = lane + 64 * j;
+        if (e < E) {
+            if (a.bias)
+                h[j] += a.bias[e];
+            if (a.logits_out)
+                a.logits_out[(size_t)t * E + e] = h[j];
+        }
+    }
+    topk_softmax_token<V>(h, E, a.k, a.G, a.M, s_gscore[wave], s_allow[wave],
+                          a.topk_idx + (size_t)t * a.k, a.topk_w + (size_t)t * a.k);
+}
+
+// W_g [d, E] -> [d, ldw] with zero columns E .. ldw-1 (E % 8 != 0 only).
+__global__ __launch_bounds__(256) void pad_wg_kernel(const uint16_t *__restrict__ wg,
+                                                     uint16_t *__restrict__ out, int d, int E,
+                                                     int ldw)
+{
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (long long)d * ldw)
+        return;
+    const int r = (int)(i / ldw), e = (int)(i % ldw);
+    out[i] = e < E ? wg[(size_t)r * E + e] : (uint16_t)0;
+}
+
+hipError_t launch_topk(const Dims &dm, const float *logits, int32_t *topk_idx, float *topk_w,
+                       hipStream_t st)
 {
     if (dm.T == 0)
         return hipSuccess;
     const int blocks = (dm.T + 3) / 4;
     const int V = (dm.E + 63) / 64;
 #define MOE_TOPK(VV)                                                                       \
-    topk_softmax_kernel<VV><<<blocks, 256, 0, st>>>(partial, sk, bias, logits_out, topk_idx,  \
-                                                   topk_w, dm.T, dm.E, dm.k, dm.n_groups,    \
-                                                   dm.group_limit)
+    topk_softmax_kernel<VV><<<blocks, 256, 0, st>>>(logits, topk_idx, topk_w, dm.T, dm.E, \
+                                                   dm.k, dm.n_groups, dm.group_limit)
     if (V <= 1)
         MOE_TOPK(1);
     else if (V <= 2)
@@ -454,36 +609,69 @@ hipError_t launch_route(const Dims &dm, const uint16_t *x, const uint16_t *w_gat
     if (dm.T == 0)
         return hipSuccess;
     const int T = dm.T, E = dm.E, d = dm.d;
-    const int epad = router_epad(E);
-    uint16_t *wgt = reinterpret_cast<uint16_t *>(ws + wl.wg_t);
-    float *partial = reinterpret_cast<float *>(ws + wl.logits);
-    if (E % 8 == 0)
-        transpose_wg_vec_kernel<<<dim3(d / 64, epad / 64), 256, 0, st>>>(w_gate, wgt, d, E);
-    else
-        transpose_wg_kernel<<<dim3(d / 64, epad / 64), 256, 0, st>>>(w_gate, wgt, d, E);
-    const int sk = router_ksplit(T, E, d);
-    const int n_tt = (T + RBT - 1) / RBT;
-    const int be = router_be(E), n_et = epad / be, total = n_tt * n_et * sk;
+    const int ldw = router_ldw(E);
+    const uint16_t *wg = w_gate;
+    if (ldw != E) {
+        uint16_t *pad = reinterpret_cast<uint16_t *>(ws + wl.wg_pad);
+        const long long n = (long long)d * ldw;
+        pad_wg_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(w_gate, pad, d, E, ldw);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+        wg = pad;
+    }
+    RouteArgs a{};
+    a.x = x;
+    a.wg = wg;
+    a.bias = bias;
+    a.logits_out = logits_out;
+    a.topk_idx = topk_idx;
+    a.topk_w = topk_w;
+    a.partial = reinterpret_cast<float *>(ws + wl.logits);
+    a.T = T;
+    a.d = d;
+    a.E = E;
+    a.ldw = ldw;
+    a.epad = router_epad(E);
+    a.k = dm.k;
+    a.G = dm.n_groups;
+    a.M = dm.group_limit;
+    const int be = router_be(E);
+    int bt;
+    router_plan(T, E, d, &bt, &a.S);
+    a.n_tt = (T + bt - 1) / bt;
+    a.n_et = a.epad / be;
+    a.total = a.n_tt * a.n_et * a.S;
     if (be == 256)
-        router_logits_kernel<256, 156 * 1024, 1, 2, MOE_ROUTER_WN>
-            <<<xcd_grid(total), 2 * MOE_ROUTER_WN * 64, 0, st>>>(
-            x, wgt, partial, T, d, E, n_et, sk, total);
+        route_logits_kernel<64, 64, 256, 156 * 1024, 1, 2, 4><<<xcd_grid(a.total), 512, 0, st>>>(a);
     else if (be == 128)
-        router_logits_kernel<128, 78 * 1024, 2, 2, 2><<<xcd_grid(total), 256, 0, st>>>(
-            x, wgt, partial, T, d, E, n_et, sk, total);
+        route_logits_kernel<64, 64, 128, 78 * 1024, 2, 2, 2><<<xcd_grid(a.total), 256, 0, st>>>(a);
     else
-        router_logits_kernel<64, 78 * 1024, 2, 2, 2><<<xcd_grid(total), 256, 0, st>>>(
-            x, wgt, partial, T, d, E, n_et, sk, total);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess)
+        route_logits_kernel<64, 64, 64, 78 * 1024, 2, 2, 2><<<xcd_grid(a.total), 256, 0, st>>>(a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.S * a.n_et == 1)
         return e;
-    return launch_topk(dm, partial, sk, bias, logits_out, topk_idx, topk_w, st);
+    const int blocks = (T + 3) / 4;
+    const int V = a.epad / 64;
+#define MOE_SEL(VV) route_select_kernel<VV><<<blocks, 256, 0, st>>>(a)
+    if (V <= 1)
+        MOE_SEL(1);
+    else if (V <= 2)
+        MOE_SEL(2);
+    else if (V <= 4)
+        MOE_SEL(4);
+    else if (V <= 8)
+        MOE_SEL(8);
+    else
+        MOE_SEL(16);
+#undef MOE_SEL
+    return hipGetLastError();
 }
 
 hipError_t launch_topk_softmax(const Dims &dm, const float *logits, int32_t *topk_idx,
                                float *topk_w, hipStream_t st)
 {
-    return launch_topk(dm, logits, 1, nullptr, nullptr, topk_idx, topk_w, st);
+    return launch_topk(dm, logits, topk_idx, topk_w, st);
 }
 
 } // namespace moe

@@ -99,6 +99,58 @@ def test_router_logits_and_selection(case):
     assert not bad.any(), f"routing differs beyond near-ties for tokens {np.nonzero(bad)[0][:8]}"
 
 
+# Router launch shapes: several K slices (partial sums; the last workgroup
+# of a token tile selects), several expert tiles per token tile (E > 256),
+# 256-, 128- and 64-expert tiles, a non-power-of-two slice count, W_g rows
+# that are not a multiple of 8 experts (padded copy), a group limit, a bias,
+# one token.  (T, d, E, k, G, M, bias)
+ROUTE_CASES = [
+    (200, 1024, 512, 8, 0, 0, False),   # 2 expert tiles of 256, 4 slices
+    (100, 512, 384, 6, 0, 0, True),     # 3 expert tiles of 128, 2 slices
+    (333, 2048, 256, 8, 8, 4, True),    # 8 slices, group limit
+    (70, 768, 64, 2, 0, 0, False),      # 64-expert tile, 3 slices
+    (129, 512, 12, 3, 0, 0, True),      # E % 8 != 0
+    (1, 4096, 256, 8, 0, 0, False),     # one token, 8 slices
+    (64, 7168, 1024, 16, 0, 0, False),  # 4 expert tiles of 256, 8 slices, 16-token chunks
+]
+
+
+@pytest.mark.parametrize("T,d,E,k,G,M,with_bias", ROUTE_CASES)
+def test_router_launch_shapes(T, d, E, k, G, M, with_bias):
+    print(f"\n[route T={T} d={d} E={E} k={k} G={G} M={M} bias={with_bias}]", flush=True)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(T * 131 + E)
+    x = torch.randn(T, d, generator=g, device=DEV).to(torch.bfloat16)
+    wg = (torch.randn(d, E, generator=g, device=DEV) / math.sqrt(d)).to(torch.bfloat16)
+    bias = torch.randn(E, generator=g, device=DEV) if with_bias else None
+    shape = api.Shape(T=T, d=d, E=E, k=k, H=64, D=1, n_groups=G, group_limit=M)
+    _, _, ws_bytes = api.moe_query(shape)
+    lg = torch.empty(T, E, dtype=torch.float32, device=DEV)
+    idx = torch.empty(T, k, dtype=torch.int32, device=DEV)
+    w = torch.empty(T, k, dtype=torch.float32, device=DEV)
+    # a workspace full of arbitrary bytes: the arrival counters need no clearing
+    ws = torch.randint(0, 256, (ws_bytes,), dtype=torch.uint8, generator=g, device=DEV)
+    api.moe_route(shape, x, wg, bias, lg, idx, w, ws)
+    torch.cuda.synchronize()
+    xh, wh = bf16_bits(x), bf16_bits(wg)
+    bh = None if bias is None else bias.cpu().numpy()
+    ref = oracle.logits(xh, wh, bh)
+    got = lg.cpu().numpy()
+    assert np.all(np.abs(got.astype(np.float64) - ref) <= logit_tolerance(bits_to_f64(xh),
+                                                                          bits_to_f64(wh)))
+    o_idx, o_w, _ = oracle.topk(got, k, G, M)
+    np.testing.assert_array_equal(idx.cpu().numpy(), o_idx)
+    np.testing.assert_allclose(w.cpu().numpy(), o_w, rtol=4e-6, atol=1e-7)
+    r_idx, _, gap = oracle.topk(ref, k, G, M)
+    assert not routing_mismatch(idx.cpu().numpy(), r_idx, ref, gap).any()
+    # again, without the logits output, on the workspace the first call left:
+    # bitwise the same selection
+    idx2, w2 = torch.empty_like(idx), torch.empty_like(w)
+    api.moe_route(shape, x, wg, bias, None, idx2, w2, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(idx2, idx) and torch.equal(w2.view(torch.int32), w.view(torch.int32))
+
+
 @pytest.mark.parametrize("E,k", [(8, 2), (6, 3), (64, 2), (256, 8), (5, 5), (300, 7),
                                  (200, 70), (1024, 16)])
 def test_topk_on_identical_logits_with_ties(E, k):
