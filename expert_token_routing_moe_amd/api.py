@@ -21,7 +21,8 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe_mi355x.so")
 
-MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = 0, -1, -2, -3, -4
+MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP, MOE_ESCRATCH = 0, -1, -2, -3, -4, -5
+DISPATCH_SCRATCH_BYTES = 8 << 20  # MOE_DISPATCH_SCRATCH_BYTES
 
 STAT_NAMES = (
     "assignments", "kept", "dropped", "padded", "capacity", "send_rows",
@@ -66,6 +67,7 @@ def lib():
         "moe_route": [S, P, P, P, P, P, P, P, SZ, P],
         "moe_topk_from_logits": [S, P, P, P, P],
         "moe_dispatch": [S, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
+        "moe_dispatch_noalloc": [S, P, P, P, P, P, P, P, P, P, P, P, P],
         "moe_expert_ffn": [S, P, P, P, P, P, P, P, P, P, SZ, P],
         "moe_expert_gate_up": [S, P, P, P, P, P, P, P, P, SZ, P],
         "moe_expert_down": [S, P, P, P, P, P, P],
@@ -183,6 +185,19 @@ def moe_dispatch(shape, x, topk_idx, topk_w, send_buf, send_scale, slot, expert_
         _p(expert_count, I32), _p(expert_kept, I32), _p(expert_offset, I32),
         _p(rank_rows, I32), _p(stats, torch.int64), _p(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def moe_dispatch_noalloc(shape, x, topk_idx, topk_w, send_buf, send_scale, slot, expert_count,
+                         expert_kept, expert_offset, rank_rows, stats, stream=None):
+    """moe_dispatch without a workspace: the library's static per-GPU scratch
+    holds the dispatch's intermediates (no allocation; overlapping calls on
+    one GPU race)."""
+    s = shape.c()
+    _check("moe_dispatch_noalloc", lib().moe_dispatch_noalloc(
+        ctypes.byref(s), _p(x, BF16), _p(topk_idx, I32), _p(topk_w, F32), _send(shape, send_buf),
+        _p(send_scale, F32), _p(slot, I32),
+        _p(expert_count, I32), _p(expert_kept, I32), _p(expert_offset, I32),
+        _p(rank_rows, I32), _p(stats, torch.int64), _stream(stream)))
 
 
 def moe_expert_ffn(shape, send_buf, send_scale, expert_offset, expert_kept, w1, w3, w2,

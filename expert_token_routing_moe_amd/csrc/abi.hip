@@ -4,6 +4,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "moe_internal.hpp"
 
@@ -132,6 +133,60 @@ static int check_ws(const Dims &dm, const void *ws, size_t ws_bytes, Workspace *
 
 static int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
 
+// The dispatch's own regions of a workspace, laid out from offset 0 (the
+// scratch of moe_dispatch_noalloc).
+static Workspace dispatch_layout(const Dims &dm)
+{
+    Workspace w{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off = align_up(off + bytes);
+        return at;
+    };
+    w.chunk_counts = take((size_t)dm.nchunks * dm.E * sizeof(int32_t));
+    w.chunk_base = take((size_t)dm.nchunks * dm.E * sizeof(int32_t));
+    w.chunk_invalid = take((size_t)dm.nchunks * sizeof(int32_t));
+    const bool by_gate = dm.drop_policy == 1 && dm.capacity >= 0;
+    w.all_offset = take(by_gate ? (size_t)dm.E * sizeof(int32_t) : 0);
+    w.by_expert = take(by_gate ? (size_t)dm.T * dm.k * sizeof(int32_t) : 0);
+    w.total = off;
+    return w;
+}
+
+// Scratch of moe_dispatch_noalloc: one array per GPU, for the life of the
+// process.  In host code `scratch` names a host-side stand-in, not the
+// device array: its device address comes from hipGetSymbolAddress, taken
+// once per device with that device current, and only that address is
+// passed to kernels.
+static __device__ __align__(256) char scratch[MOE_DISPATCH_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
+static char *scratch_ptr[kMaxDevices];
+static std::mutex scratch_mu;
+
+// The current device's scratch address (looked up on its first use), or null
+// with *err set.
+static char *device_scratch(hipError_t *err)
+{
+    int dev = 0;
+    *err = hipGetDevice(&dev);
+    if (*err != hipSuccess)
+        return nullptr;
+    if (dev < 0 || dev >= kMaxDevices) {
+        *err = hipErrorInvalidDevice;
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_ptr[dev]) {
+        void *p = nullptr;
+        *err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (*err != hipSuccess)
+            return nullptr;
+        scratch_ptr[dev] = static_cast<char *>(p);
+    }
+    return scratch_ptr[dev];
+}
+
 } // namespace moe
 
 using namespace moe;
@@ -215,6 +270,37 @@ MOE_EXPORT int moe_dispatch(const moe_shape *shape, const uint16_t *x, const int
                                       expert_count, expert_kept,
                                       expert_offset, rank_rows, stats, (char *)workspace, wl,
                                       static_cast<hipStream_t>(stream)));
+}
+
+MOE_EXPORT int moe_dispatch_noalloc(const moe_shape *shape, const uint16_t *x,
+                                    const int32_t *topk_idx, const float *topk_w, void *send_buf,
+                                    float *send_scale, int32_t *slot, int32_t *expert_count,
+                                    int32_t *expert_kept, int32_t *expert_offset,
+                                    int32_t *rank_rows, moe_stats *stats, void *stream)
+{
+    Dims dm;
+    const int rc = make_dims(shape, &dm);
+    if (rc != MOE_OK)
+        return rc;
+    const bool need_w = dm.drop_policy == 1 && dm.capacity >= 0;
+    if (need_w ? bad_ptr(topk_w, dm.T) : bad_opt_ptr(topk_w))
+        return MOE_EINVAL;
+    if (bad_scale(dm, send_scale))
+        return MOE_EINVAL;
+    if (bad_ptr(x, dm.T) || bad_ptr(topk_idx, dm.T) || bad_ptr(send_buf, dm.send_rows) ||
+        bad_ptr(slot, dm.T) || bad_ptr(expert_count) || bad_ptr(expert_kept) ||
+        bad_ptr(expert_offset) || bad_ptr(rank_rows) || bad_ptr(stats))
+        return MOE_EINVAL;
+    const Workspace wl = dispatch_layout(dm);
+    if (wl.total > MOE_DISPATCH_SCRATCH_BYTES)
+        return MOE_ESCRATCH;
+    hipError_t e;
+    char *ws = device_scratch(&e);
+    if (!ws)
+        return MOE_EHIP;
+    return hip_status(launch_dispatch(dm, x, topk_idx, topk_w, send_buf, send_scale, slot,
+                                      expert_count, expert_kept, expert_offset, rank_rows, stats,
+                                      ws, wl, static_cast<hipStream_t>(stream)));
 }
 
 MOE_EXPORT int moe_expert_ffn(const moe_shape *shape, const void *send_buf,
@@ -400,6 +486,8 @@ MOE_EXPORT const char *moe_status_str(int status)
         return "workspace missing or too small";
     case MOE_EHIP:
         return "HIP launch error";
+    case MOE_ESCRATCH:
+        return "shape needs more dispatch scratch than the static array holds";
     default:
         return "unknown status";
     }

@@ -74,6 +74,8 @@ extern "C" {
 #define MOE_EUNSUPPORTED (-2) /* valid shape that no kernel here handles         */
 #define MOE_EWORKSPACE (-3)   /* workspace NULL or smaller than moe_query says  */
 #define MOE_EHIP (-4)         /* a HIP launch reported an error                 */
+#define MOE_ESCRATCH (-5)     /* moe_dispatch_noalloc: the shape needs more     */
+                              /* scratch than MOE_DISPATCH_SCRATCH_BYTES        */
 
 /* Shape of one layer on one device, in the pages' notation [N][CF][PL][DP][MC][F8][GL][SE].
  *   T        tokens on this device (T >= 0; T = 0 enqueues nothing)
@@ -219,6 +221,26 @@ int moe_dispatch(const moe_shape *shape, const uint16_t *x, const int32_t *topk_
                  const float *topk_w, void *send_buf, float *send_scale, int32_t *slot, int32_t *expert_count, int32_t *expert_kept,
                  int32_t *expert_offset, int32_t *rank_rows, moe_stats *stats, void *workspace,
                  size_t workspace_bytes, void *stream);
+
+/* moe_dispatch for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * Arguments, outputs and results are those of moe_dispatch (bit for bit);
+ * there is no workspace argument.  The dispatch's scratch (per-chunk expert
+ * counts and their scan, and under drop policy 1 the by-expert assignment
+ * list) lives in a static device array of MOE_DISPATCH_SCRATCH_BYTES that
+ * each GPU the library runs on holds until the process ends; its address is
+ * looked up on the first call on a device.  Nothing is allocated, freed or
+ * cleared with a memset.  Every call on one GPU shares that GPU's array, so
+ * calls that overlap in time on one GPU (different streams, or different
+ * host threads) race and must not be issued.  Returns MOE_ESCRATCH, before
+ * anything is enqueued, for a shape whose scratch exceeds the array:
+ * 8 * ceil(T/256) * E + 4 * ceil(T/256) bytes, plus 4 * (E + T*k) under drop
+ * policy 1 in capacity mode, each region rounded up to 256 bytes. */
+#define MOE_DISPATCH_SCRATCH_BYTES ((size_t)8 << 20)
+int moe_dispatch_noalloc(const moe_shape *shape, const uint16_t *x, const int32_t *topk_idx,
+                         const float *topk_w, void *send_buf, float *send_scale, int32_t *slot,
+                         int32_t *expert_count, int32_t *expert_kept, int32_t *expert_offset,
+                         int32_t *rank_rows, moe_stats *stats, void *stream);
 
 /* Expert FFN [M]: for every expert e, on its kept rows X_e of send_buf,
  *   h = bf16(SiLU(X_e W1_e^T) * (X_e W3_e^T)),  out = bf16(h W2_e^T),

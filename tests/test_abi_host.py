@@ -199,6 +199,28 @@ def test_entry_points_reject_small_or_missing_workspace():
     assert _raw("moe_expert_ffn", S, *([good] * 8), good, 0, None) == api.MOE_EWORKSPACE
 
 
+def test_noalloc_dispatch_rejects_shapes_beyond_its_scratch():
+    """moe_dispatch_noalloc refuses, on the host and before any GPU work, a
+    shape whose dispatch scratch exceeds the static array: per-chunk counts
+    and bases of 4096 chunks x 1024 experts are 32 MiB."""
+    P = ctypes.c_void_p
+    good = P(1 << 20)
+    big = api.Shape(T=1 << 20, d=64, E=1024, k=2, H=64, D=1)
+    s = big.c()
+    assert 8 * (big.T // 256) * big.E > api.DISPATCH_SCRATCH_BYTES
+    assert _raw("moe_dispatch_noalloc", ctypes.byref(s), *([good] * 11),
+                None) == api.MOE_ESCRATCH
+    # the by-expert list of drop policy 1 counts too: 4 * T * k alone is 8 MiB here
+    pol = api.Shape(T=1 << 19, d=64, E=8, k=4, H=64, D=1, capacity_factor=1.0, drop_policy=1)
+    s = pol.c()
+    assert _raw("moe_dispatch_noalloc", ctypes.byref(s), *([good] * 11),
+                None) == api.MOE_ESCRATCH
+    # bad arguments are still reported as such
+    s = api.Shape(T=256, d=64, E=8, k=2, H=64, D=2, capacity_factor=1.25).c()
+    assert _raw("moe_dispatch_noalloc", ctypes.byref(s), None, *([good] * 10),
+                None) == api.MOE_EINVAL
+
+
 def test_stream_read_rejects_bad_arguments():
     P = ctypes.c_void_p
     good = P(1 << 20)
@@ -215,7 +237,7 @@ def test_stream_read_rejects_bad_arguments():
 
 def test_status_strings():
     L = api.lib()
-    for st in (0, -1, -2, -3, -4, 7):
+    for st in (0, -1, -2, -3, -4, -5, 7):
         assert L.moe_status_str(st)
 
 
