@@ -92,11 +92,17 @@ def _load():
     lib.oracle_fp8_from_float.restype = ctypes.c_uint8
     lib.oracle_fp8_quantize_rows.argtypes = [i32, i32, P, P, P]
     lib.oracle_fp8_quantize_rows.restype = None
-    lib.oracle_expert_ffn_fp8.argtypes = [i32, i32, i32, P, P, P, P, P, P]
+    lib.oracle_expert_ffn_fp8.argtypes = [i32, i32, i32, P, P, P, P, P, P, P]
     lib.oracle_expert_ffn_fp8.restype = None
     lib.oracle_dispatch.restype = ctypes.c_int
-    lib.oracle_expert_ffn.argtypes = [i32, i32, i32, P, P, P, P, P]
+    lib.oracle_expert_ffn.argtypes = [i32, i32, i32, P, P, P, P, P, P]
     lib.oracle_expert_ffn.restype = None
+    lib.oracle_expert_gate_up.argtypes = [i32, i32, i32, P, P, P, P, P]
+    lib.oracle_expert_gate_up.restype = None
+    lib.oracle_expert_gate_up_fp8.argtypes = [i32, i32, i32, P, P, P, P, P, P]
+    lib.oracle_expert_gate_up_fp8.restype = None
+    lib.oracle_expert_down.argtypes = [i32, i32, i32, P, P, P, P]
+    lib.oracle_expert_down.restype = None
     lib.oracle_combine.argtypes = [i32, i32, i32, P, P, P, P, P]
     lib.oracle_combine.restype = None
     lib.oracle_num_threads.argtypes = []
@@ -242,8 +248,13 @@ def dispatch(x: np.ndarray | None, topk_idx: np.ndarray, *, T: int, d: int, E: i
     return out
 
 
-def expert_ffn(rows: np.ndarray, w1: np.ndarray, w3: np.ndarray, w2: np.ndarray) -> np.ndarray:
-    """One expert's SwiGLU FFN: rows [n, d], w1/w3 [H, d], w2 [d, H] (bf16 bits) -> [n, d]."""
+def expert_ffn(rows: np.ndarray, w1: np.ndarray, w3: np.ndarray, w2: np.ndarray,
+               bound: bool = False):
+    """One expert's SwiGLU FFN: rows [n, d], w1/w3 [H, d], w2 [d, H] (bf16 bits) -> [n, d].
+
+    bound=True also returns, per output element, how far the unrounded
+    result of an fp32 evaluation of the same expert may lie from the exact
+    W2 h (float64 [n, d]; see the C source for the derivation)."""
     rows = _c(rows, np.uint16)
     w1 = _c(w1, np.uint16)
     w3 = _c(w3, np.uint16)
@@ -252,14 +263,17 @@ def expert_ffn(rows: np.ndarray, w1: np.ndarray, w3: np.ndarray, w2: np.ndarray)
     H = w1.shape[0]
     assert w1.shape == (H, d) and w3.shape == (H, d) and w2.shape == (d, H)
     out = np.empty((n, d), np.uint16)
+    bnd = np.zeros((n, d), np.float64) if bound else None
     if n:
-        _load().oracle_expert_ffn(n, d, H, _ptr(rows), _ptr(w1), _ptr(w3), _ptr(w2), _ptr(out))
-    return out
+        _load().oracle_expert_ffn(n, d, H, _ptr(rows), _ptr(w1), _ptr(w3), _ptr(w2), _ptr(out),
+                                  _ptr(bnd))
+    return (out, bnd) if bound else out
 
 
 def expert_ffn_fp8(codes: np.ndarray, scales: np.ndarray, w1: np.ndarray, w3: np.ndarray,
-                   w2: np.ndarray) -> np.ndarray:
-    """The SwiGLU FFN on E4M3 rows: codes [n, d] uint8, scales [n] fp32 -> bf16 [n, d]."""
+                   w2: np.ndarray, bound: bool = False):
+    """The SwiGLU FFN on E4M3 rows: codes [n, d] uint8, scales [n] fp32 -> bf16 [n, d]
+    (and the fp32-evaluation bound with bound=True, as expert_ffn)."""
     codes = _c(codes, np.uint8)
     scales = _c(scales, np.float32)
     w1 = _c(w1, np.uint16)
@@ -270,10 +284,59 @@ def expert_ffn_fp8(codes: np.ndarray, scales: np.ndarray, w1: np.ndarray, w3: np
     assert scales.shape == (n,)
     assert w1.shape == (H, d) and w3.shape == (H, d) and w2.shape == (d, H)
     out = np.empty((n, d), np.uint16)
+    bnd = np.zeros((n, d), np.float64) if bound else None
     if n:
         _load().oracle_expert_ffn_fp8(n, d, H, _ptr(codes), _ptr(scales), _ptr(w1), _ptr(w3),
-                                      _ptr(w2), _ptr(out))
-    return out
+                                      _ptr(w2), _ptr(out), _ptr(bnd))
+    return (out, bnd) if bound else out
+
+
+def expert_gate_up(rows: np.ndarray, w1: np.ndarray, w3: np.ndarray, *, codes=None,
+                   scales=None, bound: bool = False):
+    """The gate/up half of the expert: h = bf16(SiLU(X W1^T) * (X W3^T)) [n, H].
+
+    rows [n, d] bf16 bits, or codes [n, d] E4M3 + scales [n] (rows=None).
+    bound=True also returns, per element of h, the bound on how far an fp32
+    evaluation of SiLU(g) u lies from the exact value (float64 [n, H])."""
+    w1 = _c(w1, np.uint16)
+    w3 = _c(w3, np.uint16)
+    H, d = w1.shape
+    assert w3.shape == (H, d)
+    if codes is not None:
+        codes = _c(codes, np.uint8)
+        scales = _c(scales, np.float32)
+        n = codes.shape[0]
+        assert codes.shape == (n, d) and scales.shape == (n,)
+    else:
+        rows = _c(rows, np.uint16)
+        n = rows.shape[0]
+        assert rows.shape == (n, d)
+    h = np.empty((n, H), np.uint16)
+    bnd = np.zeros((n, H), np.float64) if bound else None
+    if n:
+        if codes is not None:
+            _load().oracle_expert_gate_up_fp8(n, d, H, _ptr(codes), _ptr(scales), _ptr(w1),
+                                              _ptr(w3), _ptr(h), _ptr(bnd))
+        else:
+            _load().oracle_expert_gate_up(n, d, H, _ptr(rows), _ptr(w1), _ptr(w3), _ptr(h),
+                                          _ptr(bnd))
+    return (h, bnd) if bound else h
+
+
+def expert_down(h: np.ndarray, w2: np.ndarray, bound: bool = False):
+    """The down half of the expert: out = bf16(h W2^T) [n, d] from h [n, H] bf16 bits.
+    bound=True also returns G(H) sum_j |h_j w2_mj| per element (the fp32
+    accumulation bound for the same h)."""
+    h = _c(h, np.uint16)
+    w2 = _c(w2, np.uint16)
+    n, H = h.shape
+    d = w2.shape[0]
+    assert w2.shape == (d, H)
+    out = np.empty((n, d), np.uint16)
+    bnd = np.zeros((n, d), np.float64) if bound else None
+    if n:
+        _load().oracle_expert_down(n, d, H, _ptr(h), _ptr(w2), _ptr(out), _ptr(bnd))
+    return (out, bnd) if bound else out
 
 
 def combine(expert_out: np.ndarray, slot: np.ndarray, topk_w: np.ndarray,
@@ -298,21 +361,27 @@ def combine(expert_out: np.ndarray, slot: np.ndarray, topk_w: np.ndarray,
 
 def expert_ffn_all(send_buf: np.ndarray, expert_offset: np.ndarray, expert_kept: np.ndarray,
                    w1: np.ndarray, w3: np.ndarray, w2: np.ndarray,
-                   send_scale: np.ndarray | None = None) -> np.ndarray:
+                   send_scale: np.ndarray | None = None, bound: bool = False):
     """Every expert's FFN on its kept rows; rows that no assignment fills stay
-    zero.  With send_scale the rows are E4M3 codes (FP8 dispatch)."""
+    zero.  With send_scale the rows are E4M3 codes (FP8 dispatch).  bound=True
+    also returns the per-element fp32-evaluation bound (0 on unfilled rows)."""
     out = np.zeros(send_buf.shape, np.uint16)
+    bnd = np.zeros(send_buf.shape, np.float64) if bound else None
     E = expert_kept.shape[0]
     for e in range(E):
         lo, n = int(expert_offset[e]), int(expert_kept[e])
         if not n:
             continue
         if send_scale is None:
-            out[lo:lo + n] = expert_ffn(send_buf[lo:lo + n], w1[e], w3[e], w2[e])
+            r = expert_ffn(send_buf[lo:lo + n], w1[e], w3[e], w2[e], bound=bound)
         else:
-            out[lo:lo + n] = expert_ffn_fp8(send_buf[lo:lo + n], send_scale[lo:lo + n],
-                                            w1[e], w3[e], w2[e])
-    return out
+            r = expert_ffn_fp8(send_buf[lo:lo + n], send_scale[lo:lo + n], w1[e], w3[e], w2[e],
+                               bound=bound)
+        if bound:
+            out[lo:lo + n], bnd[lo:lo + n] = r
+        else:
+            out[lo:lo + n] = r
+    return (out, bnd) if bound else out
 
 
 def layer_fwd(x, w_gate, w1, w3, w2, *, k: int, D: int, cf: float, my_rank: int = 0,
@@ -326,9 +395,9 @@ def layer_fwd(x, w_gate, w1, w3, w2, *, k: int, D: int, cf: float, my_rank: int 
     idx, w, gap = topk(lg, k, groups, group_limit)
     disp = dispatch(x, idx, T=T, d=d, E=E, D=D, my_rank=my_rank, cf=cf,
                     drop_policy=drop_policy, topk_w=w, min_capacity=min_capacity, fp8=fp8)
-    eo = expert_ffn_all(disp["send_buf"], disp["expert_offset"], disp["expert_kept"], w1, w3, w2,
-                        send_scale=disp["send_scale"])
-    so = expert_ffn(x, *shared) if shared is not None else None
+    eo, eo_bound = expert_ffn_all(disp["send_buf"], disp["expert_offset"], disp["expert_kept"],
+                                  w1, w3, w2, send_scale=disp["send_scale"], bound=True)
+    so, so_bound = expert_ffn(x, *shared, bound=True) if shared is not None else (None, None)
     y = combine(eo, disp["slot"], w, so)
     return dict(logits=lg, topk_idx=idx, topk_w=w, gap=gap, expert_out=eo, y=y, shared_out=so,
-                **disp)
+                expert_out_bound=eo_bound, shared_out_bound=so_bound, **disp)

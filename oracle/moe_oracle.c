@@ -537,12 +537,152 @@ int oracle_dispatch(int T, int d, int E, int k, int D, int my_rank, double cf,
 /* rows [n, d] bf16; w1, w3 [H, d] bf16; w2 [d, H] bf16; out [n, d].   */
 /* g = W1 x, u = W3 x (double), h = bf16(SiLU(g) * u) with             */
 /* SiLU(z) = z / (1 + exp(-z)), out = bf16(W2 h).                      */
+/*                                                                     */
+/* bound (optional, [n, d] double; test infrastructure): how far the   */
+/* unrounded result of an fp32 evaluation of the same expert may lie   */
+/* from the exact W2 h, given bf16 inputs equal to these, under the    */
+/* standard probabilistic model of rounding errors (independent, mean  */
+/* zero; Higham and Mary, SIAM J. Sci. Comput. 41(5), 2019): a sum of  */
+/* m products in fp32, in any order, is within                         */
+/*   G(m) * sum|terms|,  G(m) = exp(L sqrt(m) u + m u^2/(1-u)) - 1,     */
+/* of the exact sum, u = 2^-24, L = 8 (failing with probability below  */
+/* 2 m exp(-L^2/2) < 3e-10 per sum at m = 14336).  So g and u are      */
+/* within Gg = G(d+2) sum|x w1| and Gu (the +2 covers the row scale of */
+/* E4M3 rows and a final rounding); SiLU(g) * u, evaluated in fp32     */
+/* (exp, add, divide, multiply: 8 u relative allowed), within          */
+/*   e = 1.01 (|SiLU'(g) u| Gg + |SiLU(g)| Gu) + Gg Gu + 8 u |v|        */
+/* of v = SiLU(g) u, so the fp32 side's h_j is a bf16 value in         */
+/* [bf16(v - e), bf16(v + e)], at most s_j = that interval's width     */
+/* from this h_j (s_j = 0 unless v_j lies within e_j of a bf16         */
+/* rounding boundary).  Which way such an h_j goes is taken as         */
+/* independent of the others, so their effect on an output sums to at */
+/* most L sqrt(sum (s_j w2_j)^2) (Hoeffding; failing with probability  */
+/* below 2 exp(-L^2/2) = 3e-14), and                                   */
+/*   bound = L sqrt(sum (s w2)^2) + G(H) (sum|h w2| + sum s|w2|).       */
 /* ------------------------------------------------------------------ */
-/* rows given either as bf16 (codes == NULL) or [F8] as E4M3 codes with a
- * per-row scale: the row value is code value * scale (exact in double). */
+#define BOUND_L 8.0
+static double gamma_n(double m)
+{
+    const double u = ldexp(1.0, -24);
+    return exp(BOUND_L * sqrt(m) * u + m * u * u / (1.0 - u)) - 1.0;
+}
+
+/* Gate/up half of the expert on one row: h_j = bf16(SiLU(g_j) u_j) for
+ * j < H, g = W1 x, u = W3 x in double; with e non-NULL also e_j, the bound
+ * on |fp32 evaluation of SiLU(g_j) u_j - SiLU(g_j) u_j| derived above; with
+ * spread non-NULL the width s_j of [bf16(v - e), bf16(v + e)]. */
+static void gate_up_row(int d, int H, const double *xr, const uint16_t *w1, const uint16_t *w3,
+                        double *h, double *e, double *spread)
+{
+    const double u32 = ldexp(1.0, -24);
+    for (int j = 0; j < H; ++j) {
+        double g = 0.0, u = 0.0, ag = 0.0, au = 0.0;
+        for (int i = 0; i < d; ++i) {
+            const double a = xr[i] * bf16_value(w1[(size_t)j * d + i]);
+            const double b = xr[i] * bf16_value(w3[(size_t)j * d + i]);
+            g += a;
+            u += b;
+            ag += fabs(a);
+            au += fabs(b);
+        }
+        const double sg = 1.0 / (1.0 + exp(-g));
+        const double silu = g * sg;
+        const double v = silu * u;
+        h[j] = bf16_value(oracle_bf16_from_double(v));
+        if (e || spread) {
+            const double Gg = gamma_n(d + 2) * ag, Gu = gamma_n(d + 2) * au;
+            const double dsilu = sg * (1.0 + g * (1.0 - sg));
+            const double ej = 1.01 * (fabs(dsilu * u) * Gg + fabs(silu) * Gu) + Gg * Gu +
+                              8.0 * u32 * fabs(v);
+            if (e)
+                e[j] = ej;
+            if (spread)
+                spread[j] = bf16_value(oracle_bf16_from_double(v + ej)) -
+                            bf16_value(oracle_bf16_from_double(v - ej));
+        }
+    }
+}
+
+/* Down half on one row: out_m = bf16(sum_j h_j W2_mj); with bound non-NULL
+ * also the bound on |fp32 evaluation of the sum - exact sum|: for h values
+ * shared by both sides (spread == NULL) G(H) sum|h w2|; for h values that
+ * may each lie spread_j away on the fp32 side, as derived above. */
+static void down_row(int d, int H, const double *h, const double *spread, const uint16_t *w2,
+                     uint16_t *out, double *bound)
+{
+    for (int m = 0; m < d; ++m) {
+        double o = 0.0, ao = 0.0, so = 0.0, s2 = 0.0;
+        for (int j = 0; j < H; ++j) {
+            const double w = bf16_value(w2[(size_t)m * H + j]);
+            o += h[j] * w;
+            if (bound) {
+                ao += fabs(h[j] * w);
+                if (spread) {
+                    so += spread[j] * fabs(w);
+                    s2 += spread[j] * w * spread[j] * w;
+                }
+            }
+        }
+        out[m] = oracle_bf16_from_double(o);
+        if (bound)
+            bound[m] = BOUND_L * sqrt(s2) + gamma_n(H) * (ao + so);
+    }
+}
+
+/* The row's values: bf16 (codes == NULL) or [F8] E4M3 codes times the row's
+ * scale (exact in double). */
+static void row_values(int d, int r, const uint16_t *rows, const uint8_t *codes,
+                       const float *scales, double *xr)
+{
+    for (int i = 0; i < d; ++i)
+        xr[i] = codes ? oracle_fp8_value(codes[(size_t)r * d + i]) * (double)scales[r]
+                      : bf16_value(rows[(size_t)r * d + i]);
+}
+
+/* The whole expert on n rows; bound: the end-to-end bound derived above. */
 static void expert_ffn_rows(int n, int d, int H, const uint16_t *rows, const uint8_t *codes,
                             const float *scales, const uint16_t *w1, const uint16_t *w3,
-                            const uint16_t *w2, uint16_t *out)
+                            const uint16_t *w2, uint16_t *out, double *bound)
+{
+#pragma omp parallel
+    {
+        double *xr = malloc((size_t)d * sizeof *xr);
+        double *h = malloc((size_t)H * sizeof *h);
+        double *sp = bound ? malloc((size_t)H * sizeof *sp) : NULL;
+#pragma omp for schedule(dynamic, 1)
+        for (int r = 0; r < n; ++r) {
+            row_values(d, r, rows, codes, scales, xr);
+            gate_up_row(d, H, xr, w1, w3, h, NULL, sp);
+            down_row(d, H, h, sp, w2, out + (size_t)r * d, bound ? bound + (size_t)r * d : NULL);
+        }
+        free(xr);
+        free(h);
+        free(sp);
+    }
+}
+
+void oracle_expert_ffn(int n, int d, int H, const uint16_t *rows, const uint16_t *w1,
+                       const uint16_t *w3, const uint16_t *w2, uint16_t *out, double *bound)
+{
+    expert_ffn_rows(n, d, H, rows, NULL, NULL, w1, w3, w2, out, bound);
+}
+
+/* The same FFN on FP8 rows (codes [n, d], scales [n]).          [F8]  */
+void oracle_expert_ffn_fp8(int n, int d, int H, const uint8_t *codes, const float *scales,
+                           const uint16_t *w1, const uint16_t *w3, const uint16_t *w2,
+                           uint16_t *out, double *bound)
+{
+    expert_ffn_rows(n, d, H, NULL, codes, scales, w1, w3, w2, out, bound);
+}
+
+/* The two halves apart (stage checks on identical inputs).  Gate/up: rows
+ * [n, d] bf16 (codes == NULL) or E4M3 codes + scales -> h [n, H] bf16, and
+ * bound_h [n, H] (optional): e_j above.  Down: h [n, H] bf16 -> out [n, d],
+ * and bound [n, d] (optional): G(H) sum|h w2|.  down(gate_up(x)) is the
+ * expert above, bit for bit. */
+static void expert_gate_up_rows(int n, int d, int H, const uint16_t *rows, const uint8_t *codes,
+                                const float *scales, const uint16_t *w1, const uint16_t *w3,
+                                uint16_t *h_out, double *bound_h)
 {
 #pragma omp parallel
     {
@@ -550,42 +690,43 @@ static void expert_ffn_rows(int n, int d, int H, const uint16_t *rows, const uin
         double *h = malloc((size_t)H * sizeof *h);
 #pragma omp for schedule(dynamic, 1)
         for (int r = 0; r < n; ++r) {
-            for (int i = 0; i < d; ++i)
-                xr[i] = codes ? oracle_fp8_value(codes[(size_t)r * d + i]) * (double)scales[r]
-                              : bf16_value(rows[(size_t)r * d + i]);
-            for (int j = 0; j < H; ++j) {
-                double g = 0.0, u = 0.0;
-                for (int i = 0; i < d; ++i) {
-                    g += xr[i] * bf16_value(w1[(size_t)j * d + i]);
-                    u += xr[i] * bf16_value(w3[(size_t)j * d + i]);
-                }
-                double silu = g / (1.0 + exp(-g));
-                h[j] = bf16_value(oracle_bf16_from_double(silu * u));
-            }
-            for (int m = 0; m < d; ++m) {
-                double o = 0.0;
-                for (int j = 0; j < H; ++j)
-                    o += h[j] * bf16_value(w2[(size_t)m * H + j]);
-                out[(size_t)r * d + m] = oracle_bf16_from_double(o);
-            }
+            row_values(d, r, rows, codes, scales, xr);
+            gate_up_row(d, H, xr, w1, w3, h, bound_h ? bound_h + (size_t)r * H : NULL, NULL);
+            for (int j = 0; j < H; ++j)
+                h_out[(size_t)r * H + j] = oracle_bf16_from_double(h[j]);
         }
         free(xr);
         free(h);
     }
 }
 
-void oracle_expert_ffn(int n, int d, int H, const uint16_t *rows, const uint16_t *w1,
-                       const uint16_t *w3, const uint16_t *w2, uint16_t *out)
+void oracle_expert_gate_up(int n, int d, int H, const uint16_t *rows, const uint16_t *w1,
+                           const uint16_t *w3, uint16_t *h, double *bound_h)
 {
-    expert_ffn_rows(n, d, H, rows, NULL, NULL, w1, w3, w2, out);
+    expert_gate_up_rows(n, d, H, rows, NULL, NULL, w1, w3, h, bound_h);
 }
 
-/* The same FFN on FP8 rows (codes [n, d], scales [n]).          [F8]  */
-void oracle_expert_ffn_fp8(int n, int d, int H, const uint8_t *codes, const float *scales,
-                           const uint16_t *w1, const uint16_t *w3, const uint16_t *w2,
-                           uint16_t *out)
+void oracle_expert_gate_up_fp8(int n, int d, int H, const uint8_t *codes, const float *scales,
+                               const uint16_t *w1, const uint16_t *w3, uint16_t *h,
+                               double *bound_h)
 {
-    expert_ffn_rows(n, d, H, NULL, codes, scales, w1, w3, w2, out);
+    expert_gate_up_rows(n, d, H, NULL, codes, scales, w1, w3, h, bound_h);
+}
+
+void oracle_expert_down(int n, int d, int H, const uint16_t *h, const uint16_t *w2,
+                        uint16_t *out, double *bound)
+{
+#pragma omp parallel
+    {
+        double *hr = malloc((size_t)H * sizeof *hr);
+#pragma omp for schedule(dynamic, 1)
+        for (int r = 0; r < n; ++r) {
+            for (int j = 0; j < H; ++j)
+                hr[j] = bf16_value(h[(size_t)r * H + j]);
+            down_row(d, H, hr, NULL, w2, out + (size_t)r * d, bound ? bound + (size_t)r * d : NULL);
+        }
+        free(hr);
+    }
 }
 
 /* ------------------------------------------------------------------ */

@@ -508,6 +508,137 @@ def test_expert_ffn_zero_up_projection_gives_zero():
     W2 = bf16_bits(torch.from_numpy(rng.standard_normal((32, 16))).to(torch.bfloat16))
     out = oracle.expert_ffn(X, W1, W3, W2)
     assert np.all(_f(out) == 0)
+    # nothing is rounded on the way (v = 0 exactly): the fp32-evaluation bound is 0
+    _, bnd = oracle.expert_ffn(X, W1, W3, W2, bound=True)
+    assert np.all(bnd == 0)
+
+
+# ---------------------------------------------------------------------------
+# The bound on an fp32 evaluation of the expert (test infrastructure the GPU
+# parity checks use as their per-element floor): checked against independent
+# fp32 evaluations in numpy, in two summation orders, and on a hidden value
+# placed on a bf16 rounding midpoint.
+# ---------------------------------------------------------------------------
+
+def _bf16_of_f32(v32):
+    return bf16_bits(torch.from_numpy(np.ascontiguousarray(v32, np.float32)).to(torch.bfloat16))
+
+
+def _fp32_gate_up(x, w1, w3, scale=None, order="blas"):
+    """An fp32 evaluation of the gate/up half: x [n, d] float64 values (exact
+    in fp32), weights as bf16 bits; fp32 sums (BLAS order, or one term at a
+    time), the row scale (E4M3 rows) on the fp32 sums, SiLU in fp32;
+    returns the unrounded fp32 v = SiLU(g) u."""
+    f32 = np.float32
+    X = x.astype(f32)
+    A1, A3 = (_f(w).astype(f32) for w in (w1, w3))
+    g, u = _fp32_mm(X, A1, order), _fp32_mm(X, A3, order)
+    if scale is not None:
+        g = (g * scale[:, None].astype(f32)).astype(f32)
+        u = (u * scale[:, None].astype(f32)).astype(f32)
+    return (g / (f32(1) + np.exp(-g)) * u).astype(f32)
+
+
+def _fp32_mm(a, b, order):
+    f32 = np.float32
+    if order == "blas":
+        return (a @ b.T).astype(f32)
+    acc = np.zeros((a.shape[0], b.shape[0]), f32)
+    for i in range(a.shape[1]):
+        acc = (acc + a[:, i:i + 1] * b[:, i][None, :]).astype(f32)
+    return acc
+
+
+def _fp32_expert(x, w1, w3, w2, scale=None, order="blas"):
+    """The whole expert in fp32 (h rounded to bf16); unrounded fp32 output."""
+    h = _f(_bf16_of_f32(_fp32_gate_up(x, w1, w3, scale, order))).astype(np.float32)
+    return _fp32_mm(h, _f(w2).astype(np.float32), order)
+
+
+def _ffn_case(fp8, seed):
+    rng = np.random.default_rng(seed)
+    n, d, H = 24, 256, 96
+    mk = lambda *s, sc: bf16_bits(torch.from_numpy(rng.standard_normal(s) * sc).to(torch.bfloat16))
+    w1, w3, w2 = mk(H, d, sc=0.08), mk(H, d, sc=0.08), mk(d, H, sc=0.1)
+    if fp8:
+        q, scales = oracle.fp8_quantize_rows(mk(n, d, sc=1.0))
+        return dict(codes=q, scales=scales), oracle.fp8_values(q), scales, (w1, w3, w2)
+    rows = mk(n, d, sc=1.0)
+    return dict(rows=rows), _f(rows), None, (w1, w3, w2)
+
+
+def _ffn(src, w, bound):
+    if "codes" in src:
+        return oracle.expert_ffn_fp8(src["codes"], src["scales"], *w, bound=bound)
+    return oracle.expert_ffn(src["rows"], *w, bound=bound)
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_expert_ffn_bound_covers_fp32_evaluations(fp8):
+    """End to end: an fp32 evaluation (h rounded to bf16 on its own) lands
+    within 2e-2 |ref| + bound of the oracle's expert output."""
+    src, x, scale, w = _ffn_case(fp8, 21 + fp8)
+    out, bnd = _ffn(src, w, bound=True)
+    ref = _f(out)
+    for order in ("blas", "sequential"):
+        got = _f(_bf16_of_f32(_fp32_expert(x, *w, scale, order)))
+        assert np.all(np.abs(got - ref) <= 2e-2 * np.abs(ref) + 1.01 * bnd + 2.0 ** -126), order
+    assert np.all(bnd >= 0) and bnd.max() > 0
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_expert_stage_bounds_cover_fp32_evaluations(fp8):
+    """Stage by stage: the gate/up half's h against an fp32 evaluation on the
+    same rows, the down half's output against an fp32 evaluation on the same
+    h; both stage floors are far below the output's rms."""
+    src, x, scale, (w1, w3, w2) = _ffn_case(fp8, 31 + fp8)
+    h, bh = oracle.expert_gate_up(src.get("rows"), w1, w3, codes=src.get("codes"),
+                                  scales=src.get("scales"), bound=True)
+    hr = _f(h)
+    o, bo = oracle.expert_down(h, w2, bound=True)
+    orr = _f(o)
+    for order in ("blas", "sequential"):
+        hg = _f(_bf16_of_f32(_fp32_gate_up(x, w1, w3, scale, order)))
+        assert np.all(np.abs(hg - hr) <= 2e-2 * np.abs(hr) + 1.01 * bh + 2.0 ** -126), order
+        og = _f(_bf16_of_f32(_fp32_mm(hr.astype(np.float32), _f(w2).astype(np.float32), order)))
+        assert np.all(np.abs(og - orr) <= 2e-2 * np.abs(orr) + 1.01 * bo + 2.0 ** -126), order
+    assert np.all(bh >= 0) and np.all(bo > 0)
+    assert bh.max() < 2e-3 * np.sqrt(np.mean(hr * hr))
+    assert bo.max() < 2e-3 * np.sqrt(np.mean(orr * orr))
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_expert_stages_compose_to_the_expert(fp8):
+    """down(gate_up(x)) is the (BLAS-pinned) expert, bit for bit."""
+    src, _, _, (w1, w3, w2) = _ffn_case(fp8, 41 + fp8)
+    h = oracle.expert_gate_up(src.get("rows"), w1, w3, codes=src.get("codes"),
+                              scales=src.get("scales"))
+    np.testing.assert_array_equal(oracle.expert_down(h, w2), _ffn(src, (w1, w3, w2), False))
+
+
+def test_expert_ffn_bound_covers_a_hidden_value_on_a_rounding_midpoint():
+    """g = 32 makes SiLU(g) = 32 - 4e-13 exactly (fp64 resolves it) but 32 in
+    fp32 (1 + e^-32 rounds to 1), and u = 1 + 3 * 2^-8 puts v = SiLU(g) u
+    just below the bf16 midpoint 32.375: the exact h is 32.25, an fp32
+    evaluation's h is 32.5 (the tie goes to even).  The end-to-end bound must
+    cover that one-spacing (0.25) flip times |W2|, and the gate/up stage
+    bound must cover the fp32 h."""
+    d, H = 8, 4
+    bf = lambda a: bf16_bits(torch.tensor(a, dtype=torch.float32).to(torch.bfloat16))
+    rows = bf([[1.0, 1.0] + [0.0] * (d - 2)])
+    w1 = bf([[32.0] + [0.0] * (d - 1)] * H)
+    w3 = bf([[1.0, 3 * 2.0 ** -8] + [0.0] * (d - 2)] + [[0.0] * d] * (H - 1))
+    w2 = bf([[1.0, 0.0, 0.0, 0.0]] + [[0.25, 0.0, 0.0, 0.0]] * (d - 1))
+    out, bnd = oracle.expert_ffn(rows, w1, w3, w2, bound=True)
+    assert _f(out)[0, 0] == 32.25                  # the exact h, rounded once
+    assert bnd[0, 0] >= 0.25 and bnd[0, 1] >= 0.0625  # one bf16 spacing of h times |W2|
+    got = _f(_bf16_of_f32(_fp32_expert(_f(rows), w1, w3, w2)))
+    assert got[0, 0] == 32.5                       # the fp32 evaluation took the other side
+    assert np.all(np.abs(got - _f(out)) <= 2e-2 * np.abs(_f(out)) + 1.01 * bnd)
+    h, bh = oracle.expert_gate_up(rows, w1, w3, bound=True)
+    hg = _f(_bf16_of_f32(_fp32_gate_up(_f(rows), w1, w3)))
+    assert _f(h)[0, 0] == 32.25 and hg[0, 0] == 32.5
+    assert np.all(np.abs(hg - _f(h)) <= 2e-2 * np.abs(_f(h)) + 1.01 * bh)
 
 
 # ---------------------------------------------------------------------------
