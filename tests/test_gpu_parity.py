@@ -8,8 +8,10 @@ Acceptance:
     are within 1e-5 of each other;
   * counts, offsets, slots, per-rank rows, counters and the send buffer
     bit-exact (fed the same routing);
-  * bf16 outputs within 2e-2 * (|ref| + rms(ref)) elementwise and 5e-3
-    relative Frobenius.
+  * bf16 outputs within 2e-2 |ref| + F elementwise, F a per-element floor
+    derived from the fp32 arithmetic (parity_util), and 5e-3 relative
+    Frobenius; each stage is checked on the GPU's own inputs for it, and the
+    whole path against the oracle's own intermediate values.
 """
 from __future__ import annotations
 
@@ -23,8 +25,8 @@ import torch
 import oracle
 from expert_token_routing_moe_amd import api
 from expert_token_routing_moe_amd.inputs import CONFIGS, MoEConfig, bf16_bits, make_inputs
-from parity_util import (GAP, assert_bf16_close, bits_to_f64, logit_tolerance, routing_mismatch,
-                         t2f)
+from parity_util import (GAP, assert_bf16_close, bits_to_f64, check_expert_rows, combine_floor,
+                         expert_dev, gate_rel, logit_tolerance, routing_mismatch, t2f)
 
 pytestmark = pytest.mark.gpu
 INF = math.inf
@@ -99,8 +101,8 @@ def test_router_logits_and_selection(case):
     assert not bad.any(), f"routing differs beyond near-ties for tokens {np.nonzero(bad)[0][:8]}"
 
 
-# Router launch shapes: several K slices (partial sums; the last workgroup
-# of a token tile selects), several expert tiles per token tile (E > 256),
+# Router launch shapes: several K slices (partial sums, summed and selected
+# by the second launch), several expert tiles per token tile (E > 256),
 # 256-, 128- and 64-expert tiles, a non-power-of-two slice count, W_g rows
 # that are not a multiple of 8 experts (padded copy), a group limit, a bias,
 # one token.  (T, d, E, k, G, M, bias)
@@ -128,7 +130,7 @@ def test_router_launch_shapes(T, d, E, k, G, M, with_bias):
     lg = torch.empty(T, E, dtype=torch.float32, device=DEV)
     idx = torch.empty(T, k, dtype=torch.int32, device=DEV)
     w = torch.empty(T, k, dtype=torch.float32, device=DEV)
-    # a workspace full of arbitrary bytes: the arrival counters need no clearing
+    # a workspace full of arbitrary bytes: nothing in it needs clearing
     ws = torch.randint(0, 256, (ws_bytes,), dtype=torch.uint8, generator=g, device=DEV)
     api.moe_route(shape, x, wg, bias, lg, idx, w, ws)
     torch.cuda.synchronize()
@@ -186,6 +188,37 @@ def _assert_dispatch_equal(buf, r, send_rows):
     assert api.stats_dict(buf.stats) == r["stats"]
     if r["send_buf"] is not None and send_rows:
         np.testing.assert_array_equal(bf16_bits(buf.send_buf[:send_rows]), r["send_buf"])
+
+
+def _gpu_h(shape, send, scale, off, kept, w1, w3, workspace=None):
+    """The GPU's SwiGLU hidden values for a send buffer (the gate/up half)."""
+    hg = torch.zeros(send.shape[0], shape.H, dtype=torch.bfloat16, device=DEV)
+    api.moe_expert_gate_up(shape, send, scale, off, kept, w1, w3, hg, workspace=workspace)
+    torch.cuda.synchronize()
+    return bf16_bits(hg)
+
+
+def _check_layer_y(buf, r, w, h, fp8=False, shared_ref=None, grel=0.0):
+    """y of a layer call, on the GPU's routing r/w: the combine stage on the
+    GPU's own expert (and shared) outputs, then end to end against the
+    oracle's own expert outputs.  shared_ref: (bits, end-to-end bound)."""
+    eg = bf16_bits(buf.expert_out)
+    sg = bf16_bits(buf.shared_out) if shared_ref is not None else None
+    y = t2f(buf.y)
+    assert_bf16_close(y, bits_to_f64(oracle.combine(eg, r["slot"], w, sg)), "y (combine)",
+                      combine_floor(bits_to_f64(eg), r["slot"], w,
+                                    None if sg is None else bits_to_f64(sg)))
+    eo, eb = oracle.expert_ffn_all(r["send_buf"], r["expert_offset"], r["expert_kept"], h["w1"],
+                                   h["w3"], h["w2"], send_scale=r["send_scale"] if fp8 else None,
+                                   bound=True)
+    so, sb = shared_ref if shared_ref is not None else (None, None)
+    yref = oracle.combine(eo, r["slot"], w, so)
+    assert_bf16_close(y, bits_to_f64(yref), "y (end to end)",
+                      combine_floor(bits_to_f64(eo), r["slot"], w,
+                                    None if so is None else bits_to_f64(so),
+                                    o_dev=expert_dev(eo, eb),
+                                    shared_dev=None if so is None else expert_dev(so, sb),
+                                    gate_rel=grel))
 
 
 def test_dispatch_bit_exact(case):
@@ -264,13 +297,19 @@ def test_expert_ffn_stage(case):
     out = torch.zeros_like(send)
     api.moe_expert_ffn(shape, send, None, off, kept, inp["w1"], inp["w3"], inp["w2"], out,
                        buf.workspace)
+    # the two halves apart, so each is checked on its own inputs
+    hg = torch.zeros(send.shape[0], cfg.H, dtype=torch.bfloat16, device=DEV)
+    out2 = torch.zeros_like(send)
+    api.moe_expert_gate_up(shape, send, None, off, kept, inp["w1"], inp["w3"], hg)
+    api.moe_expert_down(shape, hg, off, kept, inp["w2"], out2)
     torch.cuda.synchronize()
-    got = bf16_bits(out)
+    got, hb = bf16_bits(out), bf16_bits(hg)
+    assert np.array_equal(got, bf16_bits(out2))
     for e in range(cfg.E):
         lo, n = int(ref["expert_offset"][e]), int(ref["expert_kept"][e])
         if n:
-            assert_bf16_close(bits_to_f64(got[lo:lo + n]),
-                              bits_to_f64(ref["expert_out"][lo:lo + n]), f"expert {e}")
+            check_expert_rows(f"expert {e}", h["w1"][e], h["w3"][e], h["w2"][e],
+                              hb[lo:lo + n], got[lo:lo + n], rows=ref["send_buf"][lo:lo + n])
 
 
 def test_combine_stage(case):
@@ -280,7 +319,9 @@ def test_combine_stage(case):
     api.moe_combine(shape, eo, _i32(ref["slot"]), _f32(ref["topk_w"]), None, y)
     torch.cuda.synchronize()
     got, want = t2f(y), bits_to_f64(ref["y"])
-    res = assert_bf16_close(got, want, "combine")
+    res = assert_bf16_close(got, want, "combine",
+                            combine_floor(bits_to_f64(ref["expert_out"]), ref["slot"],
+                                          ref["topk_w"]))
     # same inputs, fp32 vs double accumulation: at most one bf16 ulp apart
     ulp = np.ldexp(1.0, np.frexp(np.abs(want))[1] - 8)
     assert np.all(np.abs(got - want) <= np.maximum(ulp, 2.0 ** -133))
@@ -295,18 +336,26 @@ def test_layer_fwd_end_to_end(case):
     idx = buf.topk_idx.cpu().numpy()
     flips = np.any(idx != ref["topk_idx"], axis=1)
     assert not routing_mismatch(idx, ref["topk_idx"], ref["logits"], ref["gap"]).any()
+    w = buf.topk_w.cpu().numpy()
     if flips.any():
         # a legitimate near-tie flip: check the rest on the GPU's own routing
-        w = buf.topk_w.cpu().numpy()
         r = oracle.dispatch(h["x"], idx, T=cfg.T, d=cfg.d, E=cfg.E, D=cfg.D,
                             my_rank=cfg.my_rank, cf=cfg.cf)
-        eo = oracle.expert_ffn_all(r["send_buf"], r["expert_offset"], r["expert_kept"],
-                                   h["w1"], h["w3"], h["w2"])
-        yref = oracle.combine(eo, r["slot"], w)
+        eo, eb = oracle.expert_ffn_all(r["send_buf"], r["expert_offset"], r["expert_kept"],
+                                       h["w1"], h["w3"], h["w2"], bound=True)
+        yref, grel = oracle.combine(eo, r["slot"], w), 0.0
     else:
-        r, yref = ref, ref["y"]
+        r, yref, eo, eb, grel = ref, ref["y"], ref["expert_out"], ref["expert_out_bound"], \
+            gate_rel(cfg.k)
     _assert_dispatch_equal(buf, r, r["stats"]["send_rows"])
-    assert_bf16_close(t2f(buf.y), bits_to_f64(yref), "y")
+    # the combine on the GPU's own expert outputs and gates
+    eg = bf16_bits(buf.expert_out)
+    assert_bf16_close(t2f(buf.y), bits_to_f64(oracle.combine(eg, r["slot"], w)), "y (combine)",
+                      combine_floor(bits_to_f64(eg), r["slot"], w))
+    # end to end, every step by the oracle
+    assert_bf16_close(t2f(buf.y), bits_to_f64(yref), "y (end to end)",
+                      combine_floor(bits_to_f64(eo), r["slot"], w, o_dev=expert_dev(eo, eb),
+                                    gate_rel=grel))
     # determinism: a second run is bitwise identical
     y1 = buf.y.clone()
     eo1 = buf.expert_out.clone()
@@ -406,10 +455,7 @@ def test_layer_fwd_by_gate_end_to_end(name):
     r = oracle.dispatch(h["x"], idx, T=cfg.T, d=cfg.d, E=cfg.E, D=cfg.D, cf=cfg.cf,
                         drop_policy=1, topk_w=w)
     _assert_dispatch_equal(buf, r, r["stats"]["send_rows"])
-    eo = oracle.expert_ffn_all(r["send_buf"], r["expert_offset"], r["expert_kept"], h["w1"],
-                               h["w3"], h["w2"])
-    yref = oracle.combine(eo, r["slot"], w)
-    assert_bf16_close(t2f(buf.y), bits_to_f64(yref), "y")
+    _check_layer_y(buf, r, w, h)
 
 
 # ---------------------------------------------------------------------------
@@ -489,17 +535,17 @@ def test_expert_ffn_fp8_stage(case):
     scale = _f32(r["send_scale"])
     out = torch.zeros(send.shape, dtype=torch.bfloat16, device=DEV)
     ws = api.LayerBuffers.allocate(sh8, DEV).workspace
-    api.moe_expert_ffn(sh8, send, scale, _i32(r["expert_offset"]), _i32(r["expert_kept"]),
-                       inp["w1"], inp["w3"], inp["w2"], out, ws)
+    off, kept = _i32(r["expert_offset"]), _i32(r["expert_kept"])
+    api.moe_expert_ffn(sh8, send, scale, off, kept, inp["w1"], inp["w3"], inp["w2"], out, ws)
     torch.cuda.synchronize()
     got = bf16_bits(out)
-    want = oracle.expert_ffn_all(r["send_buf"], r["expert_offset"], r["expert_kept"], h["w1"],
-                                 h["w3"], h["w2"], send_scale=r["send_scale"])
+    hb = _gpu_h(sh8, send, scale, off, kept, inp["w1"], inp["w3"], ws)
     for e in range(cfg.E):
         lo, n = int(r["expert_offset"][e]), int(r["expert_kept"][e])
         if n:
-            assert_bf16_close(bits_to_f64(got[lo:lo + n]), bits_to_f64(want[lo:lo + n]),
-                              f"fp8 expert {e}")
+            check_expert_rows(f"fp8 expert {e}", h["w1"][e], h["w3"][e], h["w2"][e],
+                              hb[lo:lo + n], got[lo:lo + n], codes=r["send_buf"][lo:lo + n],
+                              scales=r["send_scale"][lo:lo + n])
 
 
 # Expert row counts that reach every per-wave slice count (0..8) of a 256-row
@@ -525,21 +571,22 @@ def test_expert_ffn_every_tile_shape(fp8):
     if fp8:
         q, sc = oracle.fp8_quantize_rows(x)
         send, scale = torch.from_numpy(q).to(DEV), _f32(sc)
-        want = oracle.expert_ffn_all(q, off, counts, w1, w3, w2, send_scale=sc)
     else:
         send, scale = inp["x"], None
-        want = oracle.expert_ffn_all(x, off, counts, w1, w3, w2)
     out = torch.zeros(n, cfg.d, dtype=torch.bfloat16, device=DEV)
     ws = api.LayerBuffers.allocate(shape, DEV).workspace
     api.moe_expert_ffn(shape, send, scale, _i32(off), _i32(counts), inp["w1"], inp["w3"],
                        inp["w2"], out, ws)
     torch.cuda.synchronize()
     got = bf16_bits(out)
+    hb = _gpu_h(shape, send, scale, _i32(off), _i32(counts), inp["w1"], inp["w3"], ws)
     for e in range(E):
         lo, m = int(off[e]), int(counts[e])
         if m:
-            assert_bf16_close(bits_to_f64(got[lo:lo + m]), bits_to_f64(want[lo:lo + m]),
-                              f"expert {e} ({m} rows)")
+            rows = dict(codes=q[lo:lo + m], scales=sc[lo:lo + m]) if fp8 else \
+                dict(rows=x[lo:lo + m])
+            check_expert_rows(f"expert {e} ({m} rows)", w1[e], w3[e], w2[e], hb[lo:lo + m],
+                              got[lo:lo + m], **rows)
 
 
 def test_fp8_widened_gate_up_matches_register_path():
@@ -571,13 +618,12 @@ def test_fp8_widened_gate_up_matches_register_path():
         lo, m = int(off[e]), int(kept[e])
         assert torch.equal(hw[lo:lo + m].view(torch.int16), hr[lo:lo + m].view(torch.int16)), e
     w1, w3, w2 = (bf16_bits(inp[k]) for k in ("w1", "w3", "w2"))
-    want = oracle.expert_ffn_all(buf.send_buf.cpu().numpy(), off, kept, w1, w3, w2,
-                                 send_scale=buf.send_scale.cpu().numpy())
-    got = bf16_bits(buf.expert_out)
+    codes, scales = buf.send_buf.cpu().numpy(), buf.send_scale.cpu().numpy()
+    got, hb = bf16_bits(buf.expert_out), bf16_bits(hw)
     for e in range(cfg.E):
         lo, m = int(off[e]), int(kept[e])
-        assert_bf16_close(bits_to_f64(got[lo:lo + m]), bits_to_f64(want[lo:lo + m]),
-                          f"fp8 widened expert {e}")
+        check_expert_rows(f"fp8 widened expert {e}", w1[e], w3[e], w2[e], hb[lo:lo + m],
+                          got[lo:lo + m], codes=codes[lo:lo + m], scales=scales[lo:lo + m])
 
 
 @pytest.mark.parametrize("name", list(SMALL))
@@ -594,10 +640,7 @@ def test_layer_fwd_fp8_end_to_end(name):
     r = oracle.dispatch(h["x"], idx, T=cfg.T, d=cfg.d, E=cfg.E, D=cfg.D, cf=cfg.cf, fp8=True)
     n = r["stats"]["send_rows"]
     np.testing.assert_array_equal(buf.send_buf[:n].cpu().numpy(), r["send_buf"])
-    eo = oracle.expert_ffn_all(r["send_buf"], r["expert_offset"], r["expert_kept"], h["w1"],
-                               h["w3"], h["w2"], send_scale=r["send_scale"])
-    yref = oracle.combine(eo, r["slot"], w)
-    assert_bf16_close(t2f(buf.y), bits_to_f64(yref), "y (fp8 dispatch)")
+    _check_layer_y(buf, r, w, h, fp8=True)
 
 
 # ---------------------------------------------------------------------------
@@ -657,14 +700,24 @@ def test_layer_fwd_grouped_and_shared_end_to_end(name):
     # downstream on the GPU's own routing
     r = oracle.dispatch(h["x"], idx, T=cfg.T, d=cfg.d, E=cfg.E, D=cfg.D, cf=cfg.cf)
     _assert_dispatch_equal(buf, r, r["stats"]["send_rows"])
-    eo = oracle.expert_ffn_all(r["send_buf"], r["expert_offset"], r["expert_kept"], h["w1"],
-                               h["w3"], h["w2"])
-    so = None
+    shared_ref = None
     if cfg.shared_H:
-        so = oracle.expert_ffn(h["x"], h["w1s"], h["w3s"], h["w2s"])
-        assert_bf16_close(t2f(buf.shared_out), bits_to_f64(so), "shared expert")
-    yref = oracle.combine(eo, r["slot"], w, so)
-    assert_bf16_close(t2f(buf.y), bits_to_f64(yref), "y")
+        _check_shared(cfg, inp, h, buf.shared_out)
+        shared_ref = oracle.expert_ffn(h["x"], h["w1s"], h["w3s"], h["w2s"], bound=True)
+    _check_layer_y(buf, r, w, h, shared_ref=shared_ref)
+
+
+def _check_shared(cfg, inp, h, shared_out, toks=None):
+    """The shared expert's output against the oracle, stage by stage: its
+    hidden values come from the gate/up half run as one group of all T
+    tokens (the kernels moe_shared_expert uses)."""
+    sh = api.Shape(T=cfg.T, d=cfg.d, E=1, k=1, H=cfg.shared_H)
+    off, cnt = _i32([0, cfg.T]), _i32([cfg.T])
+    hb = _gpu_h(sh, inp["x"], None, off, cnt, inp["w1s"], inp["w3s"])
+    so = bf16_bits(shared_out)
+    toks = np.arange(cfg.T) if toks is None else toks
+    check_expert_rows("shared expert", h["w1s"], h["w3s"], h["w2s"], hb[toks], so[toks],
+                      rows=h["x"][toks])
 
 
 def test_shared_expert_and_combine_stages():
@@ -676,8 +729,8 @@ def test_shared_expert_and_combine_stages():
     api.moe_shared_expert(shape, inp["x"], inp["w1s"], inp["w3s"], inp["w2s"], buf.shared_out,
                           buf.workspace)
     torch.cuda.synchronize()
+    _check_shared(cfg, inp, h, buf.shared_out)
     so = oracle.expert_ffn(h["x"], h["w1s"], h["w3s"], h["w2s"])
-    assert_bf16_close(t2f(buf.shared_out), bits_to_f64(so), "shared expert")
     # combine on identical inputs: within one bf16 ulp of the oracle
     ref = oracle.layer_fwd(h["x"], h["w_gate"], h["w1"], h["w3"], h["w2"], k=cfg.k, D=cfg.D,
                            cf=cfg.cf)
@@ -867,67 +920,84 @@ def test_full_size_config(name):
         for e in rng.choice(cfg.E, min(cfg.E, 8), replace=False):
             pads = buf.send_buf[e * C + kept[e]:(e + 1) * C]
             assert torch.count_nonzero(pads) == 0
-    # expert FFN: sampled experts (busiest, quietest non-empty, one more), sampled rows
+    # expert FFN, stage by stage on the GPU's own hidden values: the busiest,
+    # the quietest non-empty and another expert; all their rows where the
+    # oracle's work stays near 10 G multiply-adds per expert, else a sample
     eo = bf16_bits(buf.expert_out)
     sb = buf.send_buf.cpu().numpy() if fp8 else bf16_bits(buf.send_buf)
     ss = buf.send_scale.cpu().numpy() if fp8 else None
     kept = r["expert_kept"]
+    hb = _gpu_h(shape, buf.send_buf, buf.send_scale, buf.expert_offset, buf.expert_kept,
+                inp["w1"], inp["w3"], buf.workspace)
     nz = np.nonzero(kept)[0]
-    experts = sorted({int(nz[np.argmax(kept[nz])]), int(nz[np.argmin(kept[nz])]),
-                      int(rng.choice(nz))})
-    max_rows = 48 if cfg.d * cfg.H > 20e6 else 160
+    picks = [int(nz[np.argmax(kept[nz])]), int(nz[np.argmin(kept[nz])])]
+    picks += [int(e) for e in rng.permutation(nz) if e not in picks][:1]
+    experts = sorted(set(picks))
+    max_rows = max(32, int(1e10 // (3 * cfg.d * cfg.H)))
     for e in experts:
         lo, n = int(r["expert_offset"][e]), int(kept[e])
-        rows = np.sort(rng.choice(n, min(n, max_rows), replace=False)) + lo
-        got = (oracle.expert_ffn_fp8(sb[rows], ss[rows], *_expert_weights(inp, e)) if fp8
-               else oracle.expert_ffn(sb[rows], *_expert_weights(inp, e)))
-        assert_bf16_close(bits_to_f64(eo[rows]), bits_to_f64(got), f"{name} expert {e}")
+        rows = (np.arange(lo, lo + n) if n <= max_rows else
+                np.sort(rng.choice(n, max_rows, replace=False)) + lo)
+        src = dict(codes=sb[rows], scales=ss[rows]) if fp8 else dict(rows=sb[rows])
+        check_expert_rows(f"{name} expert {e} ({len(rows)} of {n} rows)",
+                          *_expert_weights(inp, e), hb[rows], eo[rows], **src)
+    del hb
     # shared expert: sampled tokens
     toks = np.sort(rng.choice(cfg.T, min(cfg.T, 256), replace=False))
-    so = None
+    so = so_e2e = None
     if cfg.shared_H:
-        ws_ = tuple(bf16_bits(inp[n]) for n in ("w1s", "w3s", "w2s"))
-        so_gpu = bf16_bits(buf.shared_out)
-        so_ref = oracle.expert_ffn(x[toks[:48]], *ws_)
-        assert_bf16_close(bits_to_f64(so_gpu[toks[:48]]), bits_to_f64(so_ref), "shared expert")
-        so = so_gpu[toks]
+        hx = dict(x=x, **{n: bf16_bits(inp[n]) for n in ("w1s", "w3s", "w2s")})
+        _check_shared(cfg, inp, hx, buf.shared_out, toks[:48])
+        so = bf16_bits(buf.shared_out)[toks]
     # combine: sampled tokens on the GPU's expert outputs (stage parity)
     yref = oracle.combine(eo, slot[toks], w[toks], so)
     y = bf16_bits(buf.y)
-    assert_bf16_close(bits_to_f64(y[toks]), bits_to_f64(yref), f"{name} combine")
+    assert_bf16_close(bits_to_f64(y[toks]), bits_to_f64(yref), f"{name} combine",
+                      combine_floor(bits_to_f64(eo), slot[toks], w[toks],
+                                    None if so is None else bits_to_f64(so)))
     # end to end for a few tokens, every step by the oracle from x
     for t in toks[:2]:
-        acc = []
+        outs, bnds = [], []
         for s in range(cfg.k):
-            if slot[t, s] < 0:
-                continue
             e = int(idx[t, s])
             if fp8:
                 q, sc = oracle.fp8_quantize_rows(x[t:t + 1])
-                o = oracle.expert_ffn_fp8(q, sc, *_expert_weights(inp, e))
+                o, ob = oracle.expert_ffn_fp8(q, sc, *_expert_weights(inp, e), bound=True)
             else:
-                o = oracle.expert_ffn(x[t:t + 1], *_expert_weights(inp, e))
-            acc.append((float(w[t, s]), o))
-        yt = np.zeros(cfg.d)
-        for g, o in acc:
-            yt += g * bits_to_f64(o[0])
+                o, ob = oracle.expert_ffn(x[t:t + 1], *_expert_weights(inp, e), bound=True)
+            outs.append(o[0])
+            bnds.append(ob[0])
+        eo_t, eb_t = np.stack(outs), np.stack(bnds)
+        slot_t = np.where(slot[t:t + 1] >= 0, np.arange(cfg.k)[None, :], -1).astype(np.int32)
+        so_t = sb_t = None
         if cfg.shared_H:
-            yt += bits_to_f64(oracle.expert_ffn(x[t:t + 1], *ws_)[0])
-        ref_row = np.array([oracle.bf16_from_double(v) for v in yt], np.uint16)
-        assert_bf16_close(bits_to_f64(y[t]), bits_to_f64(ref_row), f"{name} token {t}")
+            so_t, sb_t = oracle.expert_ffn(x[t:t + 1], hx["w1s"], hx["w3s"], hx["w2s"],
+                                           bound=True)
+        ref_row = oracle.combine(eo_t, slot_t, w[t:t + 1], so_t)
+        assert_bf16_close(bits_to_f64(y[t:t + 1]), bits_to_f64(ref_row), f"{name} token {t}",
+                          combine_floor(bits_to_f64(eo_t), slot_t, w[t:t + 1],
+                                        None if so_t is None else bits_to_f64(so_t),
+                                        o_dev=expert_dev(eo_t, eb_t),
+                                        shared_dev=None if so_t is None else
+                                        expert_dev(so_t, sb_t)))
     del inp, buf
     torch.cuda.empty_cache()
 
 
-def test_rank_local_expert_share():
+@pytest.mark.parametrize("fp8", [False, True])
+def test_rank_local_expert_share(fp8):
     """The expert GEMMs on one rank's share under 8-way expert parallelism:
     8 * 4096 DeepSeek-V3-shaped tokens are routed and dispatched, and the two
     grouped GEMMs run with E/D = 32 experts on the rows of experts 0..31
-    (about 1024 each, several full 256-row tiles).  Sampled rows match the
-    oracle; rows of other experts are left untouched."""
-    base = CONFIGS["dsv3_prefill"]
+    (about 1024 each, several full 256-row tiles).  Rows of at least three
+    distinct experts match the oracle stage by stage; rows of other experts
+    are left untouched.  With E4M3 rows the share ends well before the send
+    buffer does, and the gate/up GEMM's widened path (a workspace holding a
+    non-zero pattern) gives the register path's bits on every kept row."""
+    base = CONFIGS["dsv3_prefill"].with_(dispatch_fp8=int(fp8))
     cfg = base.with_(T=base.T * base.D)
-    print(f"\n[rank-local] T={cfg.T} d={cfg.d} E={cfg.E} k={cfg.k} H={cfg.H}", flush=True)
+    print(f"\n[rank-local] fp8={fp8} T={cfg.T} d={cfg.d} E={cfg.E} k={cfg.k} H={cfg.H}",
+          flush=True)
     inp = make_inputs(cfg, DEV, experts=False)
     el = cfg.E // cfg.D
     w = make_inputs(base.with_(E=el, T=1), DEV)  # weights of experts 0..31
@@ -941,23 +1011,40 @@ def test_rank_local_expert_share():
     off = buf.expert_offset.cpu().numpy()
     rows = int(off[el])
     assert rows == int(kept[:el].sum()) and kept[:el].max() > 256
-    loc = api.Shape(cfg.T, cfg.d, el, cfg.k, cfg.H, 1, 0, INF)
+    loc = api.Shape(cfg.T, cfg.d, el, cfg.k, cfg.H, 1, 0, INF, dispatch_fp8=int(fp8))
     h = torch.empty(buf.send_buf.shape[0], cfg.H, dtype=torch.bfloat16, device=DEV)
     out = torch.full(buf.send_buf.shape, 0x1234, dtype=torch.int16, device=DEV)
-    api.moe_expert_gate_up(loc, buf.send_buf, None, buf.expert_offset, buf.expert_kept, w["w1"],
-                           w["w3"], h)
+    ws = None
+    if fp8:
+        _, _, ws_bytes = api.moe_query(loc)
+        ws = torch.full((ws_bytes,), 0x5A, dtype=torch.uint8, device=DEV)
+    api.moe_expert_gate_up(loc, buf.send_buf, buf.send_scale, buf.expert_offset, buf.expert_kept,
+                           w["w1"], w["w3"], h, workspace=ws)
+    if fp8:
+        hr = torch.empty_like(h)
+        api.moe_expert_gate_up(loc, buf.send_buf, buf.send_scale, buf.expert_offset,
+                               buf.expert_kept, w["w1"], w["w3"], hr)
     api.moe_expert_down(loc, h, buf.expert_offset, buf.expert_kept, w["w2"],
                         out.view(torch.bfloat16))
     torch.cuda.synchronize()
+    if fp8:
+        assert rows < buf.send_buf.shape[0] // 2
+        assert torch.equal(h[:rows].view(torch.int16), hr[:rows].view(torch.int16))
+        del hr
     tail = out[rows:rows + 4096]
     assert torch.all(tail == 0x1234), "rows past the share were written"
     rng = np.random.default_rng(1)
-    sb = bf16_bits(buf.send_buf[:rows])
+    sb = buf.send_buf[:rows].cpu().numpy() if fp8 else bf16_bits(buf.send_buf[:rows])
+    ss = buf.send_scale[:rows].cpu().numpy() if fp8 else None
     eo = bf16_bits(out[:rows].view(torch.bfloat16))
-    for e in sorted({int(np.argmax(kept[:el])), int(np.argmin(kept[:el])), int(rng.integers(el))}):
+    hb = bf16_bits(h[:rows])
+    picks = [int(np.argmax(kept[:el])), int(np.argmin(kept[:el]))]
+    picks += [int(e) for e in rng.permutation(el) if e not in picks][:2]
+    assert len(set(picks)) >= 3
+    for e in sorted(set(picks)):
         lo, n = int(off[e]), int(kept[e])
         r = np.sort(rng.choice(n, min(n, 48), replace=False)) + lo
-        got = oracle.expert_ffn(sb[r], *_expert_weights(w, e))
-        assert_bf16_close(bits_to_f64(eo[r]), bits_to_f64(got), f"rank-local expert {e}")
-    del inp, w, buf, h, out
+        src = dict(codes=sb[r], scales=ss[r]) if fp8 else dict(rows=sb[r])
+        check_expert_rows(f"rank-local expert {e}", *_expert_weights(w, e), hb[r], eo[r], **src)
+    del inp, w, buf, h, out, ws
     torch.cuda.empty_cache()
