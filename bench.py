@@ -15,6 +15,10 @@ timed on one rank's share under D-way expert parallelism (E/D experts, the
 rows of D batches), where the grouped GEMM is bound by the matrix cores
 rather than by streaming the weights.
 
+Before every timed step a 512 MiB buffer is read, so the 256 MB last-level
+cache holds nothing of the previous step (--no-flush-mall turns that off);
+the step time is then the sum of the stages' event times.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -118,10 +122,50 @@ def cpu_baseline(cfg, inp, budget_s):
         spent += time.perf_counter() - t0
         done += tb
         log(f"  cpu oracle: {done} tokens in {spent:.1f} s")
-    return dict(value=done / spent, unit="tokens/s", cores=oracle.num_threads(), kind="oracle",
+    return dict(value=done / spent, unit="tokens/s", cores=oracle.num_threads(),
+                cpu_model=cpu_model(), kind="oracle",
                 sample=f"first {done} of {cfg.T} tokens of the {cfg.name} workload, in batches "
                        f"of {batch}: route, dispatch, SwiGLU experts and combine in fp64 "
                        f"({spent:.1f} s of oracle compute)")
+
+
+def cpu_model():
+    """The host CPU's model name, from /proc/cpuinfo."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def vendor_gemm_reference(cfg, dev, steps):
+    """The vendor GEMM library (torch.nn.functional.linear -> hipBLASLt) on one
+    expert's two GEMMs at this workload's expert-parallel rank-local shape
+    (about D*T*k/E rows per expert), for scale: TFLOP/s and fraction of the
+    bf16 matrix-core peak."""
+    import torch
+
+    rows = max(1, cfg.D * cfg.T * cfg.k // cfg.E)
+    out = {"rows_per_expert": rows}
+    for name, (n, kdim) in {"gate_up": (2 * cfg.H, cfg.d), "down": (cfg.d, cfg.H)}.items():
+        a = torch.randn(rows, kdim, device=dev).to(torch.bfloat16)
+        w = torch.randn(n, kdim, device=dev).to(torch.bfloat16)
+        for _ in range(3):
+            torch.nn.functional.linear(a, w)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            torch.nn.functional.linear(a, w)
+        e1.record()
+        e1.synchronize()
+        t = e0.elapsed_time(e1) / steps / 1e3
+        tf = 2 * rows * n * kdim / t / 1e12
+        out[name] = dict(us=round(t * 1e6, 1), tflops=round(tf, 1),
+                         mfma_util=round(tf / MFMA_BF16_PEAK_TFLOPS, 4))
+    return out
 
 
 def pct(v, q):
@@ -247,10 +291,14 @@ def main():
                     help="skip the expert-parallel rank-local GEMM measurement")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (scale reference for HBM counters)")
-    ap.add_argument("--flush-mall", action="store_true",
-                    help="read a 512 MiB buffer before every timed step, so the 256 MB "
-                         "last-level cache holds nothing of the previous step; the step time "
-                         "is then the sum of the stages' event times, without the read")
+    ap.add_argument("--no-flush-mall", dest="flush_mall", action="store_false",
+                    help="do not read a 512 MiB buffer before every timed step (by default "
+                         "the 256 MB last-level cache then holds nothing of the previous "
+                         "step, and the step time is the sum of the stages' event times, "
+                         "without the read)")
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="also time the vendor GEMM library on one expert's GEMMs at the "
+                         "rank-local shape, for scale")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU's share of the MoE layer; the library has no "
@@ -414,6 +462,9 @@ def main():
     if cfg.D > 1 and cfg.cf == float("inf") and not args.no_rank_local:
         log(f"bench: rank-local expert GEMMs ({cfg.E // cfg.D} experts, {cfg.D}x tokens routed)")
         out["grouped_gemm_rank_local"] = rank_local_gemm(cfg, inp, dev, args.steps, args.warmup)
+    if args.vendor_gemm:
+        log("bench: vendor GEMM reference at the rank-local expert shape")
+        out["vendor_gemm_reference"] = vendor_gemm_reference(cfg, dev, args.steps)
     if args.copy_calibration:
         # a plain device copy of known size: its FETCH_SIZE / WRITE_SIZE counter
         # readings give the scale factor for the counters of the kernels above

@@ -136,6 +136,26 @@ def _p(t: torch.Tensor | None, dtype=None):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _need(shape, **tensors):
+    """Raise ValueError, before anything reaches the library, if a tensor
+    holds fewer elements than the shape makes the call read or write.  Each
+    keyword names a tensor (or None) and its required element count as
+    (tensor, count); counts come from the shape and moe_query."""
+    for name, (t, n) in tensors.items():
+        if t is not None and t.numel() < n:
+            raise ValueError(f"{name}: {t.numel()} elements, the shape needs {n}")
+
+
+def _sizes(shape):
+    """Element counts of the layer's tensors for this shape."""
+    send_rows, _, _ = moe_query(shape)
+    T, d, E, k, H, D = shape.T, shape.d, shape.E, shape.k, shape.H, shape.D
+    return dict(x=T * d, w_gate=d * E, bias=E, logits=T * E, tk=T * k, send=send_rows * d,
+                scale=send_rows, h=send_rows * H, E=E, E1=E + 1, D=D, stats=len(STAT_NAMES),
+                w13=E * H * d, w2=E * d * H, y=T * d, ws13=shape.shared_H * d,
+                ws2=d * shape.shared_H)
+
+
 def _stream(stream) -> ctypes.c_void_p:
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -161,6 +181,10 @@ def moe_query(shape: Shape):
 
 def moe_route(shape, x, w_gate, logit_bias, logits_out, topk_idx, topk_w, workspace,
               stream=None):
+    z = _sizes(shape)
+    _need(shape, x=(x, z["x"]), w_gate=(w_gate, z["w_gate"]), logit_bias=(logit_bias, z["bias"]),
+          logits_out=(logits_out, z["logits"]), topk_idx=(topk_idx, z["tk"]),
+          topk_w=(topk_w, z["tk"]))
     s = shape.c()
     _check("moe_route", lib().moe_route(
         ctypes.byref(s), _p(x, BF16), _p(w_gate, BF16), _p(logit_bias, F32),
@@ -169,6 +193,9 @@ def moe_route(shape, x, w_gate, logit_bias, logits_out, topk_idx, topk_w, worksp
 
 
 def moe_topk_from_logits(shape, logits, topk_idx, topk_w, stream=None):
+    z = _sizes(shape)
+    _need(shape, logits=(logits, z["logits"]), topk_idx=(topk_idx, z["tk"]),
+          topk_w=(topk_w, z["tk"]))
     s = shape.c()
     _check("moe_topk_from_logits", lib().moe_topk_from_logits(
         ctypes.byref(s), _p(logits, F32), _p(topk_idx, I32), _p(topk_w, F32), _stream(stream)))
@@ -178,6 +205,12 @@ def moe_dispatch(shape, x, topk_idx, topk_w, send_buf, send_scale, slot, expert_
                  expert_kept, expert_offset, rank_rows, stats, workspace, stream=None):
     """topk_w is read only by drop policy 1 in capacity mode; send_scale only
     under FP8 dispatch; either may be None otherwise."""
+    z = _sizes(shape)
+    _need(shape, x=(x, z["x"]), topk_idx=(topk_idx, z["tk"]), topk_w=(topk_w, z["tk"]),
+          send_buf=(send_buf, z["send"]), send_scale=(send_scale, z["scale"]),
+          slot=(slot, z["tk"]), expert_count=(expert_count, z["E"]),
+          expert_kept=(expert_kept, z["E"]), expert_offset=(expert_offset, z["E1"]),
+          rank_rows=(rank_rows, z["D"]), stats=(stats, z["stats"]))
     s = shape.c()
     _check("moe_dispatch", lib().moe_dispatch(
         ctypes.byref(s), _p(x, BF16), _p(topk_idx, I32), _p(topk_w, F32), _send(shape, send_buf),
@@ -192,6 +225,12 @@ def moe_dispatch_noalloc(shape, x, topk_idx, topk_w, send_buf, send_scale, slot,
     """moe_dispatch without a workspace: the library's static per-GPU scratch
     holds the dispatch's intermediates (no allocation; overlapping calls on
     one GPU race)."""
+    z = _sizes(shape)
+    _need(shape, x=(x, z["x"]), topk_idx=(topk_idx, z["tk"]), topk_w=(topk_w, z["tk"]),
+          send_buf=(send_buf, z["send"]), send_scale=(send_scale, z["scale"]),
+          slot=(slot, z["tk"]), expert_count=(expert_count, z["E"]),
+          expert_kept=(expert_kept, z["E"]), expert_offset=(expert_offset, z["E1"]),
+          rank_rows=(rank_rows, z["D"]), stats=(stats, z["stats"]))
     s = shape.c()
     _check("moe_dispatch_noalloc", lib().moe_dispatch_noalloc(
         ctypes.byref(s), _p(x, BF16), _p(topk_idx, I32), _p(topk_w, F32), _send(shape, send_buf),
@@ -202,6 +241,11 @@ def moe_dispatch_noalloc(shape, x, topk_idx, topk_w, send_buf, send_scale, slot,
 
 def moe_expert_ffn(shape, send_buf, send_scale, expert_offset, expert_kept, w1, w3, w2,
                    expert_out, workspace, stream=None):
+    z = _sizes(shape)
+    _need(shape, send_buf=(send_buf, z["send"]), send_scale=(send_scale, z["scale"]),
+          expert_offset=(expert_offset, z["E1"]), expert_kept=(expert_kept, z["E"]),
+          w1=(w1, z["w13"]), w3=(w3, z["w13"]), w2=(w2, z["w2"]),
+          expert_out=(expert_out, z["send"]))
     s = shape.c()
     _check("moe_expert_ffn", lib().moe_expert_ffn(
         ctypes.byref(s), _send(shape, send_buf), _p(send_scale, F32), _p(expert_offset, I32),
@@ -214,6 +258,10 @@ def moe_expert_gate_up(shape, send_buf, send_scale, expert_offset, expert_kept, 
                        stream=None, workspace=None):
     """workspace (optional, uint8 of moe_query's size): lets E4M3 rows be
     widened to bf16 in one pass before the GEMM on MFMA-bound shapes."""
+    z = _sizes(shape)
+    _need(shape, send_buf=(send_buf, z["send"]), send_scale=(send_scale, z["scale"]),
+          expert_offset=(expert_offset, z["E1"]), expert_kept=(expert_kept, z["E"]),
+          w1=(w1, z["w13"]), w3=(w3, z["w13"]), h=(h, z["h"]))
     s = shape.c()
     _check("moe_expert_gate_up", lib().moe_expert_gate_up(
         ctypes.byref(s), _send(shape, send_buf), _p(send_scale, F32), _p(expert_offset, I32),
@@ -224,6 +272,10 @@ def moe_expert_gate_up(shape, send_buf, send_scale, expert_offset, expert_kept, 
 
 
 def moe_expert_down(shape, h, expert_offset, expert_kept, w2, expert_out, stream=None):
+    z = _sizes(shape)
+    _need(shape, h=(h, z["h"]), expert_offset=(expert_offset, z["E1"]),
+          expert_kept=(expert_kept, z["E"]), w2=(w2, z["w2"]),
+          expert_out=(expert_out, z["send"]))
     s = shape.c()
     _check("moe_expert_down", lib().moe_expert_down(
         ctypes.byref(s), _p(h, BF16), _p(expert_offset, I32), _p(expert_kept, I32),
@@ -232,6 +284,9 @@ def moe_expert_down(shape, h, expert_offset, expert_kept, w2, expert_out, stream
 
 def moe_combine(shape, expert_out, slot, topk_w, shared_out, y, stream=None):
     """shared_out: the shared expert's [T, d] output, added with weight 1, or None."""
+    z = _sizes(shape)
+    _need(shape, expert_out=(expert_out, z["send"]), slot=(slot, z["tk"]),
+          topk_w=(topk_w, z["tk"]), shared_out=(shared_out, z["y"]), y=(y, z["y"]))
     s = shape.c()
     _check("moe_combine", lib().moe_combine(
         ctypes.byref(s), _p(expert_out, BF16), _p(slot, I32), _p(topk_w, F32),
@@ -239,6 +294,9 @@ def moe_combine(shape, expert_out, slot, topk_w, shared_out, y, stream=None):
 
 
 def moe_shared_expert(shape, x, w1s, w3s, w2s, shared_out, workspace, stream=None):
+    z = _sizes(shape)
+    _need(shape, x=(x, z["x"]), w1s=(w1s, z["ws13"]), w3s=(w3s, z["ws13"]),
+          w2s=(w2s, z["ws2"]), shared_out=(shared_out, z["y"]))
     s = shape.c()
     _check("moe_shared_expert", lib().moe_shared_expert(
         ctypes.byref(s), _p(x, BF16), _p(w1s, BF16), _p(w3s, BF16), _p(w2s, BF16),
@@ -249,6 +307,18 @@ def moe_shared_expert(shape, x, w1s, w3s, w2s, shared_out, workspace, stream=Non
 def moe_layer_fwd(shape, x, w_gate, logit_bias, w1, w3, w2, buf: "LayerBuffers", stream=None,
                   shared=None):
     """shared: (w1s, w3s, w2s) of the shared expert when shape.shared_H > 0."""
+    z = _sizes(shape)
+    w1s_, w3s_, w2s_ = shared if shared is not None else (None, None, None)
+    _need(shape, x=(x, z["x"]), w_gate=(w_gate, z["w_gate"]), logit_bias=(logit_bias, z["bias"]),
+          w1=(w1, z["w13"]), w3=(w3, z["w13"]), w2=(w2, z["w2"]), w1s=(w1s_, z["ws13"]),
+          w3s=(w3s_, z["ws13"]), w2s=(w2s_, z["ws2"]), y=(buf.y, z["y"]),
+          logits=(buf.logits, z["logits"]), topk_idx=(buf.topk_idx, z["tk"]),
+          topk_w=(buf.topk_w, z["tk"]), send_buf=(buf.send_buf, z["send"]),
+          send_scale=(buf.send_scale, z["scale"]), slot=(buf.slot, z["tk"]),
+          expert_count=(buf.expert_count, z["E"]), expert_kept=(buf.expert_kept, z["E"]),
+          expert_offset=(buf.expert_offset, z["E1"]), rank_rows=(buf.rank_rows, z["D"]),
+          stats=(buf.stats, z["stats"]), expert_out=(buf.expert_out, z["send"]),
+          shared_out=(buf.shared_out, z["y"] if shape.shared_H else 0))
     s = shape.c()
     w1s, w3s, w2s = shared if shared is not None else (None, None, None)
     _check("moe_layer_fwd", lib().moe_layer_fwd(
@@ -265,6 +335,9 @@ def moe_layer_fwd(shape, x, w_gate, logit_bias, w1, w3, w2, buf: "LayerBuffers",
 def moe_fp8_rows_to_bf16(codes, scales, out, stream=None):
     """out = bf16(E4M3 value of codes * row scale), the expert GEMM's decode."""
     rows, d = codes.shape
+    if scales.numel() < rows or out.numel() < rows * d:
+        raise ValueError(f"scales/out hold {scales.numel()}/{out.numel()} elements, "
+                         f"the codes need {rows}/{rows * d}")
     _check("moe_fp8_rows_to_bf16", lib().moe_fp8_rows_to_bf16(
         _p(codes, torch.uint8), _p(scales, F32), rows, d, _p(out, BF16), _stream(stream)))
 

@@ -26,11 +26,10 @@
  *   [DP] same page, "Capacity semantics decide what crosses the wire" and its
  *        question on the capacity factor: with a capacity factor set, tokens
  *        beyond an expert's capacity are dropped by selected probability.
- *   [MC] same page, the DeepSpeed paragraph: a minimum capacity per expert
- *        regardless of the capacity factor.
- *   [F8] same page, "What the bounds omit": FP8 dispatch sends token rows in
- *        FP8 instead of BF16 (half the dispatch row, plus scale tensors),
- *        while the combine path may stay wider.
+ *   [MC] same page, the DeepSpeed paragraph: C raised to a floor,
+ *        min_capacity, whatever the capacity factor gives.
+ *   [F8] same page, "What the bounds omit": FP8 rows on dispatch, bf16 on
+ *        combine; per-row scales added to the traffic.
  *   [GL] same page, the traffic bounds: at most 4 nodes per token
  *        (DeepSeek-V3), exposed by Megatron as group-limited routing.
  *   [SE] same page, the token-assignment worksheet: the shared expert is

@@ -79,9 +79,9 @@ def _load():
     lib.oracle_logits.argtypes = [i32, i32, i32, P, P, P, P]
     lib.oracle_logits.restype = None
     lib.oracle_topk.argtypes = [i32, i32, i32, P, P, P, P]
-    lib.oracle_topk.restype = None
+    lib.oracle_topk.restype = ctypes.c_int
     lib.oracle_topk_grouped.argtypes = [i32, i32, i32, i32, i32, P, P, P, P]
-    lib.oracle_topk_grouped.restype = None
+    lib.oracle_topk_grouped.restype = ctypes.c_int
     lib.oracle_capacity.argtypes = [i32, i32, i32, ctypes.c_double, i32]
     lib.oracle_capacity.restype = ctypes.c_int64
     lib.oracle_dispatch.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.c_double, i32, i32,
@@ -151,14 +151,14 @@ def topk(lg: np.ndarray, k: int, groups: int = 1, group_limit: int = 1):
     groups with the largest best logit may be chosen (group-limited routing)."""
     lg = _c(lg, np.float32)
     T, E = lg.shape
-    assert 1 <= k <= E and E <= 4096 and groups <= 1024
-    if groups > 1 and group_limit < groups:
-        assert E % groups == 0 and k <= group_limit * (E // groups)
-    idx = np.empty((T, k), np.int32)
-    w = np.empty((T, k), np.float32)
+    idx = np.empty((T, max(k, 0)), np.int32)
+    w = np.empty((T, max(k, 0)), np.float32)
     gap = np.empty((T,), np.float64)
-    _load().oracle_topk_grouped(T, E, k, groups, group_limit, _ptr(lg), _ptr(idx), _ptr(w),
-                                _ptr(gap))
+    rc = _load().oracle_topk_grouped(T, E, k, groups, group_limit, _ptr(lg), _ptr(idx), _ptr(w),
+                                     _ptr(gap))
+    if rc != 0:
+        raise ValueError(f"oracle top-k: unsupported shape E={E} k={k} groups={groups} "
+                         f"limit={group_limit}")
     return idx, w, gap
 
 

@@ -41,12 +41,10 @@
  *        its question on the capacity factor: with a capacity factor set,
  *        the tokens beyond an expert's capacity are dropped by their
  *        selected (gate) probability, the default strategy drops nothing.
- *   [MC] same page, the DeepSpeed paragraph: a minimum capacity per expert
- *        that holds regardless of the capacity factor.
- *   [F8] same page, "What the bounds omit": FP8 dispatch sends the token
- *        rows in FP8 instead of BF16, halving the dispatch row, while the
- *        combine path may stay wider; quantization scale tensors travel
- *        with it.
+ *   [MC] same page, the DeepSpeed paragraph: C raised to a floor,
+ *        min_capacity, whatever the capacity factor gives.
+ *   [F8] same page, "What the bounds omit": FP8 rows on dispatch, bf16 on
+ *        combine; per-row scales added to the traffic.
  *   [GL] same page, the traffic bounds: DeepSeek-V3 dispatches each token
  *        to at most 4 nodes, which Megatron exposes as group-limited
  *        routing.
@@ -164,11 +162,21 @@ void oracle_logits(int T, int d, int E, const uint16_t *x, const uint16_t *w_gat
 /* gap[t] = h_(k) - h_(k+1) among the allowed experts (+inf when all   */
 /* are kept), and under a group limit also at most s_(M) - s_(M+1):    */
 /* the distance to the nearest change of the selection.                */
+/* Returns 0, or -1 (nothing written) for a shape beyond the per-token  */
+/* scratch arrays (E > 4096, G > 1024) or without a valid selection    */
+/* (k outside [1, E]; under a group limit E % G != 0, M < 1, or fewer  */
+/* than k experts in M groups).                                        */
 /* ------------------------------------------------------------------ */
-void oracle_topk_grouped(int T, int E, int k, int G, int M, const float *logits,
-                         int32_t *topk_idx, float *topk_w, double *gap)
+#define TOPK_MAX_E 4096
+#define TOPK_MAX_G 1024
+int oracle_topk_grouped(int T, int E, int k, int G, int M, const float *logits,
+                        int32_t *topk_idx, float *topk_w, double *gap)
 {
+    if (E < 1 || E > TOPK_MAX_E || G > TOPK_MAX_G || k < 1 || k > E)
+        return -1;
     const int limited = G > 1 && M < G;
+    if (limited && (E % G != 0 || M < 1 || (long)M * (E / G) < k))
+        return -1;
     const int per = limited ? E / G : E;
 #pragma omp parallel for schedule(static)
     for (int t = 0; t < T; ++t) {
@@ -177,11 +185,11 @@ void oracle_topk_grouped(int T, int E, int k, int G, int M, const float *logits,
         int have_rejected = 0;
         double group_gap = INFINITY;
         /* allowed[e]: expert e's group is among the M best */
-        char allowed[4096];
+        char allowed[TOPK_MAX_E];
         for (int e = 0; e < E; ++e)
             allowed[e] = 1;
         if (limited) {
-            float score[1024];
+            float score[TOPK_MAX_G];
             for (int g = 0; g < G; ++g) {
                 score[g] = h[g * per];
                 for (int e = g * per + 1; e < (g + 1) * per; ++e)
@@ -232,12 +240,13 @@ void oracle_topk_grouped(int T, int E, int k, int G, int M, const float *logits,
             gap[t] = g_e < group_gap ? g_e : group_gap;
         }
     }
+    return 0;
 }
 
-void oracle_topk(int T, int E, int k, const float *logits, int32_t *topk_idx,
-                 float *topk_w, double *gap)
+int oracle_topk(int T, int E, int k, const float *logits, int32_t *topk_idx,
+                float *topk_w, double *gap)
 {
-    oracle_topk_grouped(T, E, k, 1, 1, logits, topk_idx, topk_w, gap);
+    return oracle_topk_grouped(T, E, k, 1, 1, logits, topk_idx, topk_w, gap);
 }
 
 /* ------------------------------------------------------------------ */

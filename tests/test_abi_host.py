@@ -249,3 +249,29 @@ def test_binding_refuses_cpu_tensors():
     with pytest.raises(ValueError):
         api.moe_combine(shape, x, torch.zeros(4, 1, dtype=torch.int32),
                         torch.zeros(4, 1), None, x)
+
+
+def test_binding_rejects_undersized_tensors():
+    """The binding checks every tensor against the element count the shape
+    needs before anything reaches the library (whose C ABI sees only
+    pointers): a send buffer, a gate array or a workspace-side h sized for
+    another shape is refused."""
+    import torch
+
+    shape = api.Shape(T=64, d=128, E=8, k=2, H=64, D=2, capacity_factor=1.25)
+    send_rows, _, _ = api.moe_query(shape)
+    z = lambda *s, dt=torch.bfloat16: torch.zeros(*s, dtype=dt)
+    i32 = lambda *s: z(*s, dt=torch.int32)
+    with pytest.raises(ValueError, match="send_buf"):
+        api.moe_dispatch(shape, z(64, 128), i32(64, 2), None, z(send_rows - 1, 128), None,
+                         i32(64, 2), i32(8), i32(8), i32(9), i32(2), z(12, dt=torch.int64),
+                         z(1 << 20, dt=torch.uint8))
+    with pytest.raises(ValueError, match="topk_w"):
+        api.moe_combine(shape, z(send_rows, 128), i32(64, 2), z(64, 1, dt=torch.float32), None,
+                        z(64, 128))
+    with pytest.raises(ValueError, match="expert_offset"):
+        api.moe_expert_down(shape, z(send_rows, 64), i32(8), i32(8), z(8, 128, 64),
+                            z(send_rows, 128))
+    with pytest.raises(ValueError, match="h"):
+        api.moe_expert_gate_up(shape, z(send_rows, 128), None, i32(9), i32(8), z(8, 64, 128),
+                               z(8, 64, 128), z(send_rows, 32))

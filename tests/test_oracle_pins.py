@@ -118,6 +118,25 @@ def test_topk_brute_force_with_ties(E, k):
         assert gap[t] == (srt[k - 1] - srt[k] if k < E else INF)
 
 
+@pytest.mark.parametrize("E,k,G,M", [(4097, 2, 1, 1), (2048, 2, 2048, 4), (8, 0, 1, 1),
+                                     (8, 9, 1, 1), (12, 2, 5, 2), (16, 9, 4, 2)])
+def test_topk_rejects_shapes_it_cannot_hold(E, k, G, M):
+    """Beyond the per-token scratch (E > 4096, more than 1024 groups) or
+    without a valid selection, the oracle returns an error and writes
+    nothing, rather than relying on its caller's checks."""
+    import ctypes
+    lg = np.zeros((3, E), np.float32)
+    idx = np.full((3, max(k, 1)), -7, np.int32)
+    w = np.full((3, max(k, 1)), -7.0, np.float32)
+    gap = np.full(3, -7.0)
+    p = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    rc = oracle._load().oracle_topk_grouped(3, E, k, G, M, p(lg), p(idx), p(w), p(gap))
+    assert rc == -1
+    assert np.all(idx == -7) and np.all(w == -7.0) and np.all(gap == -7.0)
+    with pytest.raises(ValueError):
+        oracle.topk(lg, k, G, M)
+
+
 def test_softmax_closed_forms():
     rng = np.random.default_rng(3)
     lg = rng.standard_normal((500, 6)).astype(np.float32) * 3
