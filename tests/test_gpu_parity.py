@@ -247,6 +247,28 @@ def test_dispatch_invalid_and_repeated_entries(case):
     _assert_dispatch_equal(buf, r, r["stats"]["send_rows"])
 
 
+# Shapes past the one-workgroup count-and-scan (more than 32 chunks of 256
+# tokens, or chunks x experts beyond its LDS bitmaps): the count kernel per
+# chunk, then the scan kernel.  Random distinct experts per token, some
+# entries invalid or repeated.
+@pytest.mark.parametrize("T,E,k,cf", [(9000, 64, 2, 1.25), (5000, 256, 8, INF),
+                                      (8300, 8, 2, 1.0)])
+def test_dispatch_count_then_scan_path(T, E, k, cf):
+    rng = np.random.default_rng(T + E)
+    idx = np.argsort(rng.random((T, E)), axis=1)[:, :k].astype(np.int32)
+    idx[::97, 0] = -1
+    idx[5::101, k - 1] = idx[5::101, 0]
+    idx[7::89, 0] = E + 5
+    d = 64
+    x = torch.randn(T, d, device=DEV).to(torch.bfloat16)
+    shape = api.Shape(T=T, d=d, E=E, k=k, H=64, D=4, capacity_factor=cf)
+    buf = api.LayerBuffers.allocate(shape, DEV)
+    _run_dispatch(shape, x, _i32(idx), buf)
+    r = oracle.dispatch(bf16_bits(x), idx, T=T, d=d, E=E, D=4, cf=cf)
+    _assert_dispatch_equal(buf, r, r["stats"]["send_rows"])
+    assert r["stats"]["invalid_index"] > 0
+
+
 @pytest.mark.parametrize("k,cf", [(12, INF), (12, 1.0), (20, INF), (20, 0.75)])
 def test_dispatch_and_combine_large_k(k, cf):
     """k above 8 (the count kernel's 16-slot and generic paths, the combine's
