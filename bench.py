@@ -8,7 +8,10 @@ entry point on one stream.  HIP events recorded on that stream around every
 stage give per-stage durations over the timed region; the dominant kernel's
 roofline is computed from its algorithmic bytes and flops.  Each stage's
 byte rate is also given as a fraction of this device's own streaming-read
-rate, measured after the timed steps with moe_stream_read.
+rate (read_frac), and as device_frac: the stage's reads at that rate plus
+its writes at the device's streaming-store rate, over the stage's time.
+Both rates are measured after the timed steps (moe_stream_read and
+moe_stream_write, the non-temporal 16-byte accesses of the kernels).
 
 For a dropless workload spread over D > 1 ranks, the expert GEMMs are also
 timed on one rank's share under D-way expert parallelism (E/D experts, the
@@ -44,22 +47,29 @@ def log(msg):
 
 
 def stage_traffic(cfg, st, touched):
-    """Algorithmic HBM bytes and flops of each stage for one call."""
+    """Algorithmic HBM bytes (read and written) and flops of each stage for one call."""
     T, d, E, k, H = cfg.T, cfg.d, cfg.E, cfg.k, cfg.H
     kept, send_rows = st["kept"], st["send_rows"]
     row = d + 4 if cfg.dispatch_fp8 else d * 2   # a dispatched row: E4M3 + scale, or bf16
-    return {
-        "route": dict(bytes=T * d * 2 + d * E * 2 + T * k * 8, flops=2 * T * d * E),
-        "dispatch": dict(bytes=T * d * 2 + send_rows * row + T * k * 8, flops=0),
-        "gate_up": dict(bytes=touched * 2 * H * d * 2 + kept * row + kept * H * 2,
+    sH = cfg.shared_H
+    rec = {
+        # x and W_g read; top-k indices and weights written
+        "route": dict(read=T * d * 2 + d * E * 2, write=T * k * 8, flops=2 * T * d * E),
+        # x and the top-k indices read; send rows and slots written
+        "dispatch": dict(read=T * d * 2 + T * k * 4, write=send_rows * row + T * k * 4, flops=0),
+        "gate_up": dict(read=touched * 2 * H * d * 2 + kept * row, write=kept * H * 2,
                         flops=4 * kept * d * H),
-        "down": dict(bytes=touched * d * H * 2 + kept * H * 2 + kept * d * 2,
+        "down": dict(read=touched * d * H * 2 + kept * H * 2, write=kept * d * 2,
                      flops=2 * kept * d * H),
-        "combine": dict(bytes=kept * d * 2 + T * d * 2 + T * k * 8
-                        + (T * d * 2 if cfg.shared_H else 0), flops=0),
-        "shared": dict(bytes=3 * cfg.shared_H * d * 2 + T * d * 2 * 2 + T * cfg.shared_H * 2 * 2,
-                       flops=6 * T * d * cfg.shared_H),
+        # expert outputs, slots and gates (and the shared expert's output) read; y written
+        "combine": dict(read=kept * d * 2 + T * k * 8 + (T * d * 2 if sH else 0),
+                        write=T * d * 2, flops=0),
+        "shared": dict(read=3 * sH * d * 2 + T * d * 2 + T * sH * 2,
+                       write=T * sH * 2 + T * d * 2, flops=6 * T * d * sH),
     }
+    for v in rec.values():
+        v["bytes"] = v["read"] + v["write"]
+    return rec
 
 
 def kernel_source_digest():
@@ -242,29 +252,213 @@ def rank_local_gemm(cfg, inp, dev, steps, warmup):
     return res
 
 
-def device_read_rate(dev, stream):
-    """Streaming-read rate of this device, GB/s: the best of five reads of a
-    2 GiB buffer through moe_stream_read (the expert GEMMs' non-temporal
-    16-byte loads), timed with events on the given stream."""
+def _best_ms(fn, stream, reps=5):
+    import torch
+
+    fn()  # warm-up
+    best = float("inf")
+    for _ in range(reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        e1.synchronize()
+        best = min(best, e0.elapsed_time(e1))
+    return best
+
+
+def device_rates(dev, stream):
+    """Streaming rates of this device, GB/s: the best of five reads of a 2 GiB
+    buffer through moe_stream_read (the expert GEMMs' non-temporal 16-byte
+    loads) and the best of five fills of it through moe_stream_write (the
+    permute's and the GEMM epilogues' non-temporal 16-byte stores), timed
+    with events on the given stream."""
     import torch
 
     from expert_token_routing_moe_amd import api
 
     n = 1 << 31
-    src = torch.ones(n // 4, dtype=torch.int32, device=dev)
+    buf = torch.ones(n // 4, dtype=torch.int32, device=dev)
     sink = torch.zeros(4, dtype=torch.int32, device=dev)
-    api.moe_stream_read(src, sink, stream)  # warm-up
-    best = float("inf")
-    for _ in range(5):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        api.moe_stream_read(src, sink, stream)
-        e1.record(stream)
-        e1.synchronize()
-        best = min(best, e0.elapsed_time(e1))
-    del src
-    return n / (best / 1e3) / 1e9
+    rd = _best_ms(lambda: api.moe_stream_read(buf, sink, stream), stream)
+    wr = _best_ms(lambda: api.moe_stream_write(buf, 1, stream), stream)
+    del buf
+    return n / (rd / 1e3) / 1e9, n / (wr / 1e3) / 1e9
+
+
+# ---------------------------------------------------------------------------
+# rocprofv3 summaries: the committed tables under profiles/ are made from the
+# CSV output of the commands they list, by the function below.
+# ---------------------------------------------------------------------------
+
+def _kernel_label(name):
+    name = name.replace("void ", "", 1).replace("(anonymous namespace)::", "")
+    depth, out = 0, []
+    for ch in name:  # drop the argument list, keep the template arguments
+        if ch == "(" and depth == 0:
+            break
+        depth += ch == "<"
+        depth -= ch == ">"
+        out.append(ch)
+    return "".join(out).strip()
+
+
+def _gemm_stage(label):
+    """'gate_up' or 'down' for a grouped GEMM kernel label (its DUAL argument)."""
+    args = label[label.index("<") + 1:label.rindex(">")].split(",")
+    dual = args[-1].strip() if "stream" in label else args[7].strip()
+    return "gate_up" if dual == "true" else "down"
+
+
+def _stage_of(label):
+    if "route_" in label or "pad_wg" in label or "topk_softmax" in label:
+        return "route"
+    if "count" in label or "scan_kernel" in label or "permute" in label or "widen" in label:
+        return "dispatch"
+    if "grouped_gemm" in label:
+        return _gemm_stage(label)
+    if "combine" in label:
+        return "combine"
+    return None
+
+
+def summarize_rocprof(out_dir, workload):
+    """Markdown summary of the rocprofv3 runs of one workload (sub-folders
+    trace/, fetch/, write/ and mfma/ of out_dir, with the bench JSON lines of
+    the traced run in trace.json), and the grouped GEMMs' counter bytes per
+    launch for profiles/hbm_traffic.json."""
+    import csv
+    import statistics as stt
+
+    def rows(sub, name):
+        path = os.path.join(out_dir, sub, name)
+        return list(csv.DictReader(open(path))) if os.path.exists(path) else []
+
+    with open(os.path.join(out_dir, "trace.json")) as f:
+        bj = json.loads(f.read().strip().splitlines()[-1])
+    # kernel trace: durations per (kernel, grid), first dispatch order kept
+    groups, first_grid = {}, {}
+    for r in rows("trace", "run_kernel_trace.csv"):
+        lab = _kernel_label(r["Kernel_Name"])
+        if not lab.startswith("moe::"):
+            continue
+        grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+        first_grid.setdefault(lab, grid)
+        groups.setdefault((lab, grid), []).append(
+            (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+
+    def counters(sub):
+        per = {}
+        copies = []
+        for r in rows(sub, "run_counter_collection.csv"):
+            lab = _kernel_label(r["Kernel_Name"])
+            if lab == "__amd_rocclr_copyBuffer":
+                copies.append((int(r["Dispatch_Id"]), float(r["Counter_Value"])))
+                continue
+            if not lab.startswith("moe::"):
+                continue
+            key = (lab, int(r["Grid_Size"]))
+            per.setdefault(key, {}).setdefault(r["Dispatch_Id"], {})[r["Counter_Name"]] = \
+                float(r["Counter_Value"])
+        # the calibration copies are the run's last three copies
+        return per, [v for _, v in sorted(copies)[-3:]]
+
+    fetch, fcopy = counters("fetch")
+    write, wcopy = counters("write")
+    mfma, _ = counters("mfma")
+    cal = bj.get("copy_calibration_bytes", 1 << 30)
+    fscale = (cal / 1024) / stt.mean(fcopy) if fcopy else float("nan")
+    wscale = (cal / 1024) / stt.mean(wcopy) if wcopy else float("nan")
+
+    def mb(per, key, counter, scale):
+        d = per.get(key)
+        if not d:
+            return float("nan")
+        return stt.mean(v[counter] for v in d.values()) * scale * 1024 / 1e6
+
+    cfg = bj["config"]
+    dev = bj.get("device") or {"read_gbs": bj["roofline"].get("device_read_gbs"),
+                               "write_gbs": bj["roofline"].get("device_write_gbs")}
+    lines = [f"| kernel | grid (work-items) | calls | avg us | median us | min us | max us "
+             f"| HBM read MB | HBM write MB |", "|---|---|---|---|---|---|---|---|---|"]
+    traffic = {}
+    stage_counter = {}
+    for (lab, grid), ts in groups.items():
+        rd = mb(fetch, (lab, grid), "FETCH_SIZE", fscale)
+        wr = mb(write, (lab, grid), "WRITE_SIZE", wscale)
+        lines.append(f"| `{lab}` | {grid} | {len(ts)} | {stt.mean(ts):.1f} | {stt.median(ts):.1f} "
+                     f"| {min(ts):.1f} | {max(ts):.1f} | {rd:.1f} | {wr:.1f} |")
+        st = _stage_of(lab)
+        layer = grid == first_grid[lab]
+        if st and layer:
+            acc = stage_counter.setdefault(st, [0.0, 0.0])
+            acc[0] += stt.mean(ts)
+            acc[1] += rd + wr
+        if "grouped_gemm" in lab:
+            key = _gemm_stage(lab) + ("" if layer else "_rank_local")
+            traffic[key] = dict(kernel=lab, grid=grid, fetch_bytes=round(rd * 1e6),
+                                write_bytes=round(wr * 1e6), bytes_per_launch=round((rd + wr) * 1e6),
+                                avg_us=round(stt.mean(ts), 2), source_digest=kernel_source_digest())
+    stage_lines = ["| stage | event ms (bench) | kernels' avg us (sum) | algorithmic MB "
+                   "| counter MB (read + write) | counter / algorithmic |", "|---|---|---|---|---|---|"]
+    for st, v in bj["stages"].items():
+        alg = v["gbs"] * v["ms"]  # GB/s x ms = MB
+        ks, cm = stage_counter.get(st, [float("nan"), float("nan")])
+        stage_lines.append(f"| {st} | {v['ms']:.4f} | {ks:.1f} | {alg:.1f} | {cm:.1f} "
+                           f"| {cm / alg if alg else float('nan'):.3f} |")
+    mf_lines = []
+    if mfma:
+        mf_lines = ["| kernel | grid | launches | SQ_INSTS_MFMA | algorithmic | ratio "
+                    "| MFMA busy cycles | busy fraction |", "|---|---|---|---|---|---|---|---|"]
+        rl = bj.get("grouped_gemm_rank_local")
+        for (lab, grid), d in mfma.items():
+            if "grouped_gemm" not in lab:
+                continue
+            st = _gemm_stage(lab)
+            layer = grid == first_grid.get(lab, grid)
+            per = 4 if st == "gate_up" else 2
+            if layer:
+                alg = bj["stages"][st]["tflops"] * bj["stages"][st]["ms"] * 1e9 / 16384
+            elif rl:
+                alg = per * rl["rows"] * cfg["d"] * cfg["H"] / 16384
+            else:
+                alg = float("nan")
+            inst = stt.mean(v["SQ_INSTS_MFMA"] for v in d.values())
+            busy = stt.mean(v["SQ_VALU_MFMA_BUSY_CYCLES"] for v in d.values())
+            act = stt.mean(v["GRBM_GUI_ACTIVE"] for v in d.values())
+            mf_lines.append(f"| `{lab}`{'' if layer else ' (rank-local share)'} | {grid} | {len(d)} "
+                            f"| {inst:.4g} | {alg:.4g} | {inst / alg:.3f} | {busy:.4g} "
+                            f"| {busy / (1024 * act / 8):.3f} |")
+    R = "$R"
+    cmd = f"python3 {R}/bench.py --workload {workload}"
+    md = [f"# rocprofv3 summary: MoE layer kernels, {workload} workload", "",
+          "Commands (run from /tmp with TMPDIR=/tmp; $R is the repository root, OUT an output folder):", "",
+          f"    rocprofv3 --kernel-trace --stats --output-format csv -d OUT/trace -o run -- {cmd} --no-cpu-baseline > OUT/trace.json",
+          f"    rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/fetch -o run -- {cmd} --steps 3 --warmup 1 --no-cpu-baseline --copy-calibration",
+          f"    rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/write -o run -- {cmd} --steps 3 --warmup 1 --no-cpu-baseline --copy-calibration",
+          f"    rocprofv3 --pmc SQ_INSTS_MFMA SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES GRBM_GUI_ACTIVE --output-format csv -d OUT/mfma -o run -- {cmd} --steps 3 --warmup 1 --no-cpu-baseline",
+          f"    python3 {R}/bench.py --summarize-rocprof OUT --workload {workload}", "",
+          "Durations are from the kernel trace (every dispatch of the traced command, warmup",
+          "included), grouped by kernel and grid size: the layer's launches come first; other grids",
+          "of the same kernels are the rank-local expert-parallel share or the device-rate probes.",
+          "",
+          f"Counter scale: the counter runs copy a {cal >> 20} MiB device buffer three times "
+          f"(`--copy-calibration`); FETCH_SIZE reads {stt.mean(fcopy) if fcopy else float('nan'):.0f} KiB "
+          f"per copy (scale x{fscale:.4f}), WRITE_SIZE {stt.mean(wcopy) if wcopy else float('nan'):.0f} KiB "
+          f"(scale x{wscale:.4f}); the MB below are scaled, per launch.", "",
+          f"Traced bench line: {bj['ms_per_step']} ms/step, {bj['value']} tokens/s; device streaming "
+          f"read {dev.get('read_gbs')} GB/s, store {dev.get('write_gbs')} GB/s.",
+          "", *lines, "",
+          "Per stage (the layer's launches only): HIP-event time of the stage in the traced bench",
+          "run, the kernel-trace average of its kernels, its algorithmic bytes, and the counters.", "",
+          *stage_lines, ""]
+    if mf_lines:
+        md += ["Grouped-GEMM matrix-core counters per launch. Algorithmic MFMA instructions = flops / 16384",
+               "(one `v_mfma_f32_16x16x32_bf16` is 16x16x32 multiply-adds); busy fraction =",
+               "SQ_VALU_MFMA_BUSY_CYCLES over 1024 SIMDs x GRBM_GUI_ACTIVE / 8 (GRBM_GUI_ACTIVE read as",
+               "summed over the 8 XCDs).", "", *mf_lines, ""]
+    return "\n".join(md), traffic
 
 
 def main():
@@ -296,6 +490,10 @@ def main():
                          "the 256 MB last-level cache then holds nothing of the previous "
                          "step, and the step time is the sum of the stages' event times, "
                          "without the read)")
+    ap.add_argument("--summarize-rocprof", metavar="OUT", default=None,
+                    help="print the markdown summary of the rocprofv3 runs in OUT for --workload "
+                         "(no GPU use) and record the grouped GEMMs' counter bytes in "
+                         "profiles/hbm_traffic.json")
     ap.add_argument("--vendor-gemm", action="store_true",
                     help="also time the vendor GEMM library on one expert's GEMMs at the "
                          "rank-local shape, for scale")
@@ -305,6 +503,17 @@ def main():
               "multi-GPU path (the expert-parallel exchange is not implemented); use --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
+    if args.summarize_rocprof:
+        md, traffic = summarize_rocprof(args.summarize_rocprof, args.workload)
+        print(md)
+        path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+        rec = json.load(open(path)) if os.path.exists(path) else {}
+        if traffic:
+            rec[args.workload] = traffic
+            with open(path, "w") as f:
+                json.dump(rec, f, indent=1)
+                f.write("\n")
+        return
 
     import torch
 
@@ -390,8 +599,8 @@ def main():
     st = api.stats_dict(buf.stats)
     touched = int((buf.expert_kept > 0).sum().item())
     traffic = stage_traffic(cfg, st, touched)
-    read_gbs = device_read_rate(dev, stream)
-    log(f"bench: streaming read on this device {read_gbs:.0f} GB/s")
+    read_gbs, write_gbs = device_rates(dev, stream)
+    log(f"bench: streaming read on this device {read_gbs:.0f} GB/s, store {write_gbs:.0f} GB/s")
     per_stage = {}
     for s in stages:
         t = stage_ms[s] / 1e3
@@ -402,6 +611,10 @@ def main():
                             gbs=round(traffic[s]["bytes"] / t / 1e9, 1),
                             hbm_frac=round(traffic[s]["bytes"] / t / 1e9 / HBM_PEAK_GBS, 4),
                             read_frac=round(traffic[s]["bytes"] / t / 1e9 / read_gbs, 4),
+                            # the stage's reads at the device's streaming-read rate plus
+                            # its writes at the streaming-store rate, over its time
+                            device_frac=round((traffic[s]["read"] / (read_gbs * 1e9)
+                                               + traffic[s]["write"] / (write_gbs * 1e9)) / t, 4),
                             tflops=round(traffic[s]["flops"] / t / 1e12, 2))
     dom = max(("gate_up", "down"), key=lambda s: stage_ms[s])
     t_dom = stage_ms[dom] / 1e3
@@ -417,6 +630,7 @@ def main():
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     if roof["bound"] == "hbm":  # against what this device's reads reach
         roof["device_read_gbs"] = round(read_gbs, 1)
+        roof["device_write_gbs"] = round(write_gbs, 1)
         roof["frac_of_device_read"] = round(roof["achieved"] / read_gbs, 4)
     roof["traffic"] = measured_traffic(dom, cfg.name)
     roof["kernel"] = f"grouped_gemm {dom}"
@@ -456,6 +670,7 @@ def main():
                          "mfma_util": round(gemm_flops / gemm_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
                          "touched_experts": touched},
         "stages": per_stage,
+        "device": {"read_gbs": round(read_gbs, 1), "write_gbs": round(write_gbs, 1)},
         "counts": counts,
         "roofline": roof,
     }

@@ -76,6 +76,7 @@ def lib():
         "moe_layer_fwd": [S] + [P] * 24 + [SZ, P],
         "moe_fp8_rows_to_bf16": [P, P, ctypes.c_int64, ctypes.c_int32, P, P],
         "moe_stream_read": [P, SZ, P, P],
+        "moe_stream_write": [P, SZ, ctypes.c_uint32, P],
     }
     for name, argtypes in sig.items():
         f = getattr(L, name)
@@ -351,6 +352,14 @@ def moe_stream_read(src, sink, stream=None):
     by a reading lane whose XOR of the words it read equals the mark."""
     _check("moe_stream_read", lib().moe_stream_read(
         _p(src), src.numel() * src.element_size(), _p(sink, I32), _stream(stream)))
+
+
+def moe_stream_write(dst, value, stream=None):
+    """Fill dst with the 32-bit value, once, with the permute's non-temporal
+    16-byte stores (a probe of the device's streaming-store rate)."""
+    _check("moe_stream_write", lib().moe_stream_write(
+        _p(dst), dst.numel() * dst.element_size(), ctypes.c_uint32(value & 0xFFFFFFFF),
+        _stream(stream)))
 
 
 @dataclass

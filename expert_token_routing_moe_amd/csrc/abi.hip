@@ -473,6 +473,13 @@ MOE_EXPORT int moe_stream_read(const void *src, size_t bytes, uint32_t *sink, vo
     return hip_status(launch_stream_read(src, bytes, sink, static_cast<hipStream_t>(stream)));
 }
 
+MOE_EXPORT int moe_stream_write(void *dst, size_t bytes, uint32_t value, void *stream)
+{
+    if (bytes % 16 != 0 || bad_ptr(dst, (long long)(bytes / 16)))
+        return MOE_EINVAL;
+    return hip_status(launch_stream_write(dst, bytes, value, static_cast<hipStream_t>(stream)));
+}
+
 MOE_EXPORT const char *moe_status_str(int status)
 {
     switch (status) {

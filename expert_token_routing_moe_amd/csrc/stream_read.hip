@@ -2,6 +2,8 @@
 // loads that the expert GEMMs use for their weights: the read rate that
 // this device reaches, measured beside the kernels, for reading their
 // HBM fractions against the device as well as against the data sheet.
+// Its mirror, a streaming fill with the non-temporal 16-byte stores that
+// the permute and the GEMM epilogues write with, gives the store rate.
 //
 // Each lane keeps 8 loads in flight per pass (grid-stride over the buffer)
 // and folds every 32-bit word it reads into an XOR.  A lane whose fold
@@ -38,7 +40,33 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const uint4 *__restric
         *sink = acc;
 }
 
+// Every lane stores 8 pieces of 16 bytes per pass (grid-stride), the same
+// value in every 32-bit word.
+__global__ __launch_bounds__(256) void stream_write_kernel(uint4 *__restrict__ dst, size_t n16,
+                                                           uint32_t value)
+{
+    const uint4 v = make_uint4(value, value, value, value);
+    const size_t stride = (size_t)gridDim.x * 256 * kReadUnroll;
+    for (size_t i = (size_t)blockIdx.x * 256 * kReadUnroll + threadIdx.x; i < n16; i += stride) {
+#pragma unroll
+        for (int u = 0; u < kReadUnroll; ++u)
+            if (i + (size_t)u * 256 < n16)
+                store_nt(dst + i + (size_t)u * 256, v);
+    }
+}
+
 } // namespace
+
+hipError_t launch_stream_write(void *dst, size_t bytes, uint32_t value, hipStream_t st)
+{
+    const size_t n16 = bytes / 16;
+    if (n16 == 0)
+        return hipSuccess;
+    const size_t per_block = (size_t)256 * kReadUnroll;
+    const unsigned blocks = (unsigned)std::min<size_t>(2048, (n16 + per_block - 1) / per_block);
+    stream_write_kernel<<<blocks, 256, 0, st>>>(static_cast<uint4 *>(dst), n16, value);
+    return hipGetLastError();
+}
 
 hipError_t launch_stream_read(const void *src, size_t bytes, uint32_t *sink, hipStream_t st)
 {

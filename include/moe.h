@@ -336,6 +336,15 @@ int moe_fp8_rows_to_bf16(const void *codes, const float *scales, int64_t rows, i
 #define MOE_STREAM_READ_MARK 0x9E3779B9u
 int moe_stream_read(const void *src, size_t bytes, uint32_t *sink, void *stream);
 
+/* Diagnostic, not a step of the layer: writes value to every 32-bit word of
+ * the bytes of device memory at dst, once, with the non-temporal 16-byte
+ * stores that the permute and the expert GEMMs' epilogues write with, so
+ * that a caller can time this device's streaming-store rate beside the
+ * layer's kernels.
+ *   dst   device, 16-byte aligned, caller-owned; bytes % 16 == 0 (0: no launch)
+ * Returns MOE_EINVAL for a bad pointer or size, MOE_EHIP on a launch error. */
+int moe_stream_write(void *dst, size_t bytes, uint32_t value, void *stream);
+
 /* Static string naming a status code (never NULL). */
 const char *moe_status_str(int status);
 

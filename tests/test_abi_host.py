@@ -235,6 +235,18 @@ def test_stream_read_rejects_bad_arguments():
     assert _raw("moe_stream_read", None, ctypes.c_size_t(0), good, None) == api.MOE_OK
 
 
+def test_stream_write_rejects_bad_arguments():
+    P = ctypes.c_void_p
+    good = P(1 << 20)
+    v = ctypes.c_uint32(7)
+    assert _raw("moe_stream_write", None, ctypes.c_size_t(16), v, None) == api.MOE_EINVAL
+    assert _raw("moe_stream_write", good, ctypes.c_size_t(24), v, None) == api.MOE_EINVAL
+    assert _raw("moe_stream_write", P((1 << 20) + 8), ctypes.c_size_t(16), v,
+                None) == api.MOE_EINVAL
+    # nothing to write: accepted, nothing enqueued
+    assert _raw("moe_stream_write", None, ctypes.c_size_t(0), v, None) == api.MOE_OK
+
+
 def test_status_strings():
     L = api.lib()
     for st in (0, -1, -2, -3, -4, -5, 7):

@@ -512,6 +512,21 @@ def test_stream_read_reads_every_word(nbytes):
     assert int(sink[0].item()) == 0
 
 
+@pytest.mark.parametrize("nbytes", [16, 4099 * 16, 3 << 20, 64 << 20])
+def test_stream_write_fills_every_word(nbytes):
+    """The store-rate probe writes its value to every word once (ragged
+    tails, one to 2048 workgroups) and nothing past the buffer's end."""
+    n = nbytes // 4
+    pad = 64
+    buf = torch.zeros(n + pad, dtype=torch.int32, device=DEV)
+    value = 0x5A5A1234
+    api.moe_stream_write(buf[:n], value)
+    torch.cuda.synchronize()
+    got = buf.cpu().numpy()
+    assert (got[:n] == value).all()
+    assert (got[n:] == 0).all()
+
+
 def test_fp8_decode_every_code():
     """The expert GEMM's E4M3 -> bf16 decode, through the diagnostic entry
     point: all 256 codes at unit and power-of-two scales, bit-exact."""
