@@ -711,8 +711,8 @@ def test_layer_fwd_tiny_end_to_end_invariants():
 
 # ---------------------------------------------------------------------------
 # FP8 dispatch payload ("MoE Expert Parallelism Sizing: Traffic, Capacity,
-# Fabric", "What the bounds omit": FP8 dispatch halves the dispatch row, the
-# combine may stay wider, scale tensors travel with it).  Format: OCP E4M3.
+# Fabric", "What the bounds omit": 8-bit rows on dispatch, the combine in
+# bf16, per-row scales sent beside the rows).  Format: OCP E4M3.
 # ---------------------------------------------------------------------------
 
 def _torch_e4m3_decode():
