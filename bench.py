@@ -307,8 +307,7 @@ def _kernel_label(name):
 def _gemm_stage(label):
     """'gate_up' or 'down' for a grouped GEMM kernel label (its DUAL argument)."""
     args = label[label.index("<") + 1:label.rindex(">")].split(",")
-    dual = args[-1].strip() if "stream" in label else args[7].strip()
-    return "gate_up" if dual == "true" else "down"
+    return "gate_up" if args[7].strip() == "true" else "down"
 
 
 def _stage_of(label):
