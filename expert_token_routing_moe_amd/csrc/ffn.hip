@@ -35,6 +35,7 @@
 // layout into 8-byte row pieces, converted to bf16 by v_cvt_pk_bf16_f32; they
 // are gathered in LDS (the ring is free by then) and leave as 16-byte
 // non-temporal stores (the next kernel is the only reader).
+#include <algorithm>
 #include <type_traits>
 
 #include "moe_internal.hpp"
@@ -631,12 +632,27 @@ __global__ __launch_bounds__(256) void widen_e4m3_kernel(const uint4 *__restrict
     }
 }
 
+// Launches of fewer tiles than the chip has CUs (small layers: a few
+// experts, narrow d or H) take 64-column tiles, so more workgroups stream
+// the weights at once.  The estimate of M tiles is the larger of the
+// experts that can hold rows and the full tiles the rows need.  Every
+// output's K sum runs in one wave in the same order whatever the tile width,
+// so the results are the same bits.
+constexpr long long kNarrowBelow = 256;
+static bool few_tiles(const Dims &dm, int N, int BN, int BM)
+{
+    const long long mt = std::max<long long>(std::min<long long>(dm.E, dm.send_rows),
+                                             (dm.send_rows + BM - 1) / BM);
+    return mt * (N / BN) < kNarrowBelow;
+}
+
 template <bool A8>
 static void launch_gate_up_t(const Dims &dm, const GemmArgs &a, long long mtiles_max,
                              hipStream_t st)
 {
     constexpr int threads = kWM1 * kWN1 * 64;
-    if (dm.H % kBN1 == 0) // H is a multiple of 64; the wide tile needs a multiple of kBN1
+    if (dm.H % kBN1 == 0 && !few_tiles(dm, dm.H, kBN1, kBM1))
+        // H is a multiple of 64; the wide tile needs a multiple of kBN1
         grouped_gemm_kernel<kBM1, kBN1, kBK, kRing1, kMinB1, kWM1, kWN1, true, A8>
             <<<xcd_grid((int)(mtiles_max * (dm.H / kBN1))), threads, 0, st>>>(a);
     else
@@ -684,7 +700,7 @@ hipError_t launch_down(const Dims &dm, const uint16_t *h, const int32_t *expert_
     GemmArgs a{h, nullptr, expert_offset, expert_kept, w2, nullptr, expert_out, dm.E, dm.d, dm.H,
                MOE_GEMM_ROT_DN ? rotate_k(dm.H) : 0};
     constexpr int threads = kWM2 * kWN2 * 64;
-    if (dm.d % kBN2 == 0)
+    if (dm.d % kBN2 == 0 && !few_tiles(dm, dm.d, kBN2, kBM2))
         grouped_gemm_kernel<kBM2, kBN2, kBK, kRing2, kMinB2, kWM2, kWN2, false, false>
             <<<xcd_grid((int)(mtiles_max * (dm.d / kBN2))), threads, 0, st>>>(a);
     else
