@@ -33,49 +33,58 @@ namespace moe {
 
 int router_epad(int E) { return (E + 63) / 64 * 64; }
 
-// Experts per logit tile: all 256 of a multiple of 256 (one workgroup per
-// CU, eight waves), else 128 or 64 (two workgroups per CU, four waves).
-static int router_be(int E)
-{
-    const int epad = router_epad(E);
-    return epad % 256 == 0 ? 256 : epad % 128 == 0 ? 128 : 64;
-}
-
 // W_g row length as the router reads it: E when E % 8 == 0 (the caller's
 // tensor), else E rounded up to 8 (a zero-padded copy in the workspace).
 int router_ldw(int E) { return (E + 7) / 8 * 8; }
 
-// Launch shape of the logit GEMM: 64-token tiles, and K cut into S slices
-// when the token tiles alone leave the chip short of workgroups (one or two
-// per CU): enough slices to fill it, at least four K steps each, at most 32.
-// (128-token tiles with twice the slices measured the same time at the
-// DeepSeek-V3 prefill shape for twice the partial-sum bytes.)  T = 0:
-// nothing to split.
-void router_plan(int T, int E, int d, int *bt, int *sk)
+// Launch shape of the logit GEMM: 64-token tiles of BE experts, and K cut
+// into S slices when the tiles alone leave the chip short of workgroups
+// (one per CU for BE = 256, eight waves; two per CU for BE = 128 or 64, four
+// waves): enough slices to fill it, at least four K steps each, at most 32.
+// BE is the widest of 256, 128, 64 (dividing E rounded up to 64) whose
+// launch fills the chip; when none does (few tokens: DeepSeek-V3 decode has
+// one token tile and 28 slices), the one with the most workgroups, so that
+// more CUs stream W_g.  The K slices do not depend on BE, so neither do the
+// logits' bits.  (128-token tiles with twice the slices measured the same
+// time at the DeepSeek-V3 prefill shape for twice the partial-sum bytes.)
+// T = 0: nothing to split.
+struct RouterPlan {
+    int be, sk;
+};
+static RouterPlan router_plan(int T, int E, int d)
 {
-    const int be = router_be(E), n_et = router_epad(E) / be;
-    const int target = be == 256 ? 256 : 512;
+    const int epad = router_epad(E);
     const int steps = d / 64;
-    *bt = 64;
-    *sk = 1;
-    const int tiles = ((T + 63) / 64) * n_et;
-    if (T == 0 || tiles >= target)
-        return;
-    int s = (target + tiles - 1) / tiles;
-    s = std::min(s, std::max(1, steps / 4));
-    *sk = std::max(1, std::min(s, 32));
+    RouterPlan best{64, 1};
+    long long best_wg = -1;
+    for (int be = 256; be >= 64; be /= 2) {
+        if (epad % be != 0)
+            continue;
+        const int target = be == 256 ? 256 : 512;
+        const long long tiles = (long long)((T + 63) / 64) * (epad / be);
+        int sk = 1;
+        if (T > 0 && tiles < target) {
+            int s = (int)((target + tiles - 1) / tiles);
+            s = std::min(s, std::max(1, steps / 4));
+            sk = std::max(1, std::min(s, 32));
+        }
+        const long long wg = tiles * sk;
+        if (T == 0 || wg >= target)
+            return RouterPlan{be, sk};
+        if (wg > best_wg) {
+            best_wg = wg;
+            best = RouterPlan{be, sk};
+        }
+    }
+    return best;
 }
 
-int router_ksplit(int T, int E, int d)
-{
-    int bt, sk;
-    router_plan(T, E, d, &bt, &sk);
-    return sk;
-}
+int router_ksplit(int T, int E, int d) { return router_plan(T, E, d).sk; }
 
 bool router_partials(int T, int E, int d)
 {
-    return T > 0 && router_ksplit(T, E, d) * (router_epad(E) / router_be(E)) > 1;
+    const RouterPlan p = router_plan(T, E, d);
+    return T > 0 && p.sk * (router_epad(E) / p.be) > 1;
 }
 
 namespace {
@@ -636,10 +645,10 @@ hipError_t launch_route(const Dims &dm, const uint16_t *x, const uint16_t *w_gat
     a.k = dm.k;
     a.G = dm.n_groups;
     a.M = dm.group_limit;
-    const int be = router_be(E);
-    int bt;
-    router_plan(T, E, d, &bt, &a.S);
-    a.n_tt = (T + bt - 1) / bt;
+    const RouterPlan plan = router_plan(T, E, d);
+    const int be = plan.be;
+    a.S = plan.sk;
+    a.n_tt = (T + 63) / 64;
     a.n_et = a.epad / be;
     a.total = a.n_tt * a.n_et * a.S;
     if (be == 256)
