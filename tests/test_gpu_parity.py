@@ -106,14 +106,21 @@ def test_router_logits_and_selection(case):
 # 256-, 128- and 64-expert tiles, a non-power-of-two slice count, W_g rows
 # that are not a multiple of 8 experts (padded copy), a group limit, a bias,
 # one token.  (T, d, E, k, G, M, bias)
+# (T, d, E, k, G, M, bias): the launch plan each shape gets (expert tile
+# width BE, expert tiles, K slices) in the comment
 ROUTE_CASES = [
-    (200, 1024, 512, 8, 0, 0, False),   # 2 expert tiles of 256, 4 slices
-    (100, 512, 384, 6, 0, 0, True),     # 3 expert tiles of 128, 2 slices
-    (333, 2048, 256, 8, 8, 4, True),    # 8 slices, group limit
-    (70, 768, 64, 2, 0, 0, False),      # 64-expert tile, 3 slices
-    (129, 512, 12, 3, 0, 0, True),      # E % 8 != 0
-    (1, 4096, 256, 8, 0, 0, False),     # one token, 8 slices
-    (64, 7168, 1024, 16, 0, 0, False),  # 4 expert tiles of 256, 8 slices, 16-token chunks
+    (200, 1024, 512, 8, 0, 0, False),     # BE 64: 8 expert tiles, 4 slices
+    (100, 512, 384, 6, 0, 0, True),       # BE 64: 6 expert tiles, 2 slices
+    (333, 2048, 256, 8, 8, 4, True),      # BE 64: 4 expert tiles, 8 slices, group limit
+    (70, 768, 64, 2, 0, 0, False),        # BE 64: one expert tile, 3 slices
+    (129, 512, 12, 3, 0, 0, True),        # E % 8 != 0 (padded W_g copy), 2 slices
+    (1, 4096, 256, 8, 0, 0, False),       # one token: BE 64, 4 expert tiles, 16 slices
+    (64, 7168, 1024, 16, 0, 0, False),    # BE 64: 16 expert tiles, 28 slices
+    (64, 7168, 256, 8, 0, 0, True),       # DeepSeek-V3 decode: BE 64, 4 expert tiles, 28 slices
+    (2048, 1024, 512, 8, 0, 0, False),    # BE 256: 2 expert tiles, 4 slices
+    (2048, 4096, 128, 4, 0, 0, True),     # BE 128: one expert tile, 16 slices
+    (16384, 128, 256, 8, 0, 0, False),    # BE 256, one slice: top-k inside the logit kernel
+    (16384, 128, 256, 8, 8, 4, True),     # the same with a group limit
 ]
 
 
