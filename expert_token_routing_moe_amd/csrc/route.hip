@@ -12,10 +12,10 @@
 // products are exact in fp32 and accumulate in fp32
 // (v_mfma_f32_16x16x32_bf16).
 //
-// Selection, one wavefront per token: k rounds of a wave-wide arg-max on
-// order-preserving 64-bit keys (value bits, then E-1-e, so a tie goes to the
-// lower expert index), a softmax over the kept logits, optionally within the
-// token's best expert groups.
+// Selection, one wavefront per token: k rounds of a wave-wide maximum of
+// order-preserving 32-bit value images, the winner being the lowest expert
+// index that holds the maximum (ballots), a softmax over the kept logits,
+// optionally within the token's best expert groups.
 //
 // One launch when a token tile's logits fit one workgroup (one slice, one
 // expert tile): it selects from its own tile.  Otherwise every slice stores
@@ -107,18 +107,15 @@ __device__ __forceinline__ int swzb(int r)
     return s;
 }
 
-// Order-preserving key of a finite fp32 logit and its expert index: larger
-// key = larger logit; equal logits -> the lower index has the larger key.
-__device__ __forceinline__ uint64_t topk_key(float v, int e, int E)
+// Order-preserving 32-bit image of a finite fp32 logit: larger image =
+// larger logit, -0 and +0 equal, and every image of a real value above 0.
+__device__ __forceinline__ uint32_t value_key(float v)
 {
     uint32_t u = __float_as_uint(v == 0.f ? 0.f : v); // -0 and +0 compare equal
-    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-    return ((uint64_t)u << 32) | (uint32_t)(E - 1 - e);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
-
-__device__ __forceinline__ float key_value(uint64_t key)
+__device__ __forceinline__ float key_value(uint32_t u)
 {
-    uint32_t u = (uint32_t)(key >> 32);
     u = (u & 0x80000000u) ? (u & 0x7fffffffu) : ~u;
     return __uint_as_float(u);
 }
@@ -180,11 +177,13 @@ __device__ __forceinline__ void topk_softmax_token(const float (&h)[V], int E, i
                                                    float *__restrict__ w_row)
 {
     const int lane = threadIdx.x & 63;
-    uint64_t key[V];
+    // order-preserving 32-bit image of each logit; 0 (below every real
+    // value) marks experts past E and retired ones
+    uint32_t vk[V];
 #pragma unroll
     for (int j = 0; j < V; ++j) {
         const int e = lane + 64 * j;
-        key[j] = e < E ? topk_key(h[j], e, E) : 0ull; // 0 sorts below every real key
+        vk[j] = e < E ? value_key(h[j]) : 0u;
     }
     if (G > 1 && M < G) {
         const int per = E / G;
@@ -197,7 +196,7 @@ __device__ __forceinline__ void topk_softmax_token(const float (&h)[V], int E, i
         for (int j = 0; j < V; ++j) {
             const int e = lane + 64 * j;
             if (e < E)
-                atomicMax(&gs[e / per], (uint32_t)(key[j] >> 32));
+                atomicMax(&gs[e / per], vk[j]);
         }
         lds_wait();
         for (int r = 0; r < M; ++r) {
@@ -217,26 +216,35 @@ __device__ __forceinline__ void topk_softmax_token(const float (&h)[V], int E, i
         for (int j = 0; j < V; ++j) {
             const int e = lane + 64 * j;
             if (e < E && !allow[e / per])
-                key[j] = 0;
+                vk[j] = 0;
         }
     }
     float hmax = 0.f, denom = 0.f;
-    // k rounds of a wave-wide arg-max; the winner's key is retired.  Lane s
-    // keeps rank s's index and unnormalised weight (ranks past 64: lane
-    // s % 64 stores them and rereads them to normalise).
+    // k rounds: the wave-wide maximum of the values, then the lowest expert
+    // holding it (ties to the lower index), found with one ballot per
+    // register of values (expert e = lane + 64 j: the first j with a match,
+    // its lowest lane); the winner is retired.  Lane s keeps rank s's index
+    // and unnormalised weight (ranks past 64: lane s % 64 stores them and
+    // rereads them to normalise).
     int my_e = 0;
     float my_p = 0.f;
     for (int s = 0; s < k; ++s) {
-        uint64_t best = 0;
+        uint32_t best = 0;
 #pragma unroll
         for (int j = 0; j < V; ++j)
-            best = key[j] > best ? key[j] : best;
-        const uint64_t win = wave_max_u64(best);
+            best = vk[j] > best ? vk[j] : best;
+        const uint32_t win = wave_max_u32(best);
+        int e = -1;
+#pragma unroll
+        for (int j = 0; j < V; ++j) {
+            const uint64_t b = __ballot(vk[j] == win);
+            if (e < 0 && b != 0)
+                e = 64 * j + (int)__builtin_ctzll(b);
+        }
 #pragma unroll
         for (int j = 0; j < V; ++j)
-            if (key[j] == win)
-                key[j] = 0;
-        const int e = E - 1 - (int)(uint32_t)(win & 0xffffffffu);
+            if (64 * j + lane == e)
+                vk[j] = 0;
         const float v = key_value(win);
         if (s == 0)
             hmax = v;
