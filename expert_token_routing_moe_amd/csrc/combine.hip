@@ -2,9 +2,11 @@
 // at the token's home device ("Mixture-of-Experts (MoE) Architecture and
 // Expert Parallelism", section 2; "EP Math -- Expert Parallelism (MoE)",
 // "The combine all-to-all").  A dropped assignment (slot -1) adds nothing
-// ("Token drop").  With a shared expert (replicated on every rank, "MoE
-// Expert Parallelism Sizing: Traffic, Capacity, Fabric", token-assignment
-// worksheet) its bf16 output row is added last, with weight 1.
+// ("Token drop"), and so does a slot past the send buffer's rows (a
+// caller's slot array that moe_dispatch did not write).  With a shared
+// expert (replicated on every rank, "MoE Expert Parallelism Sizing: Traffic,
+// Capacity, Fabric", token-assignment worksheet) its bf16 output row is
+// added last, with weight 1.
 //
 // A wavefront per token.  Its slots and gates are read once into scalar
 // registers; for every 16-byte piece of the row, the lane issues all k
@@ -33,7 +35,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict
                                                       const float *__restrict__ topk_w,
                                                       const uint16_t *__restrict__ shared_out,
                                                       uint16_t *__restrict__ y, int T, int d,
-                                                      int k)
+                                                      int k, long long rows_max)
 {
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -44,7 +46,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict
     float g[KM];
 #pragma unroll
     for (int s = 0; s < KM; ++s) {
-        rows[s] = s < k ? __builtin_amdgcn_readfirstlane(slot[(size_t)t * k + s]) : -1;
+        const int r = s < k ? __builtin_amdgcn_readfirstlane(slot[(size_t)t * k + s]) : -1;
+        rows[s] = r >= 0 && r < rows_max ? r : -1; // a slot past the rows adds nothing
         g[s] = s < k ? __int_as_float(__builtin_amdgcn_readfirstlane(
                                __float_as_int(topk_w[(size_t)t * k + s])))
                          : 0.f;
@@ -80,7 +83,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict
 __global__ __launch_bounds__(256) void combine_kernel_any_k(
     const uint16_t *__restrict__ expert_out, const int32_t *__restrict__ slot,
     const float *__restrict__ topk_w, const uint16_t *__restrict__ shared_out,
-    uint16_t *__restrict__ y, int T, int d, int k)
+    uint16_t *__restrict__ y, int T, int d, int k, long long rows_max)
 {
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -94,7 +97,7 @@ __global__ __launch_bounds__(256) void combine_kernel_any_k(
         float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
         for (int s = 0; s < k; ++s) {
             const int r = sl[s];
-            if (r < 0)
+            if (r < 0 || r >= rows_max)
                 continue;
             const float g = gw[s];
             const uint4 v = load_nt(reinterpret_cast<const uint4 *>(expert_out + (size_t)r * d) + c);
@@ -123,16 +126,16 @@ hipError_t launch_combine(const Dims &dm, const uint16_t *expert_out, const int3
     const int blocks = (dm.T + 3) / 4;
     if (dm.k <= 2)
         combine_kernel<2><<<blocks, 256, 0, st>>>(expert_out, slot, topk_w, shared_out, y, dm.T,
-                                                             dm.d, dm.k);
+                                                             dm.d, dm.k, dm.send_rows);
     else if (dm.k <= 4)
         combine_kernel<4><<<blocks, 256, 0, st>>>(expert_out, slot, topk_w, shared_out, y, dm.T,
-                                                             dm.d, dm.k);
+                                                             dm.d, dm.k, dm.send_rows);
     else if (dm.k <= 8)
         combine_kernel<8><<<blocks, 256, 0, st>>>(expert_out, slot, topk_w, shared_out, y, dm.T,
-                                                             dm.d, dm.k);
+                                                             dm.d, dm.k, dm.send_rows);
     else
         combine_kernel_any_k<<<blocks, 256, 0, st>>>(expert_out, slot, topk_w, shared_out, y,
-                                                     dm.T, dm.d, dm.k);
+                                                     dm.T, dm.d, dm.k, dm.send_rows);
     return hipGetLastError();
 }
 

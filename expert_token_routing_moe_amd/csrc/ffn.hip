@@ -55,23 +55,25 @@ struct GemmArgs {
     uint16_t *out;              // [rows, N]
     int E, N, K;
     int rot;                    // 1: each N tile starts its K walk at its own offset
+    long long rows;             // rows of A and out: no tile reaches past them
 };
+
 
 // Tile work of expert e is ceil(rows_e / BM) * (N / BN) tiles.  Wave 0 of the
 // workgroup scans all experts (lane l owns experts [l*V, (l+1)*V)), maps the
 // block to a work index with the XCD remap, and publishes (expert, local
 // index) in LDS; e = -1 marks a surplus block.
 template <int BM>
-__device__ __forceinline__ void decode_work(const int32_t *__restrict__ rows, int E, int nN,
-                                            int *s_e, int *s_local)
+__device__ __forceinline__ void decode_work(const GemmArgs &g, int nN, int *s_e, int *s_local)
 {
     const int lane = threadIdx.x & 63;
+    const int E = g.E;
     const int V = (E + 63) >> 6;
     int sum = 0;
     for (int j = 0; j < V; ++j) {
         const int e = lane * V + j;
         if (e < E)
-            sum += (rows[e] + BM - 1) / BM * nN;
+            sum += (max(g.row_count[e], 0) + BM - 1) / BM * nN;
     }
     int incl = sum;
 #pragma unroll
@@ -90,7 +92,7 @@ __device__ __forceinline__ void decode_work(const int32_t *__restrict__ rows, in
             const int e = lane * V + j;
             if (e >= E)
                 break;
-            const int t = (rows[e] + BM - 1) / BM * nN;
+            const int t = (max(g.row_count[e], 0) + BM - 1) / BM * nN;
             if (w < acc + t) {
                 *s_e = e;
                 *s_local = w - acc;
@@ -162,7 +164,7 @@ __global__ __launch_bounds__(WM * WN * 64, MINB) void grouped_gemm_kernel(GemmAr
     __shared__ int s_e, s_local;
 
     if (threadIdx.x < 64)
-        decode_work<BM>(g.row_count, g.E, g.N / BN, &s_e, &s_local);
+        decode_work<BM>(g, g.N / BN, &s_e, &s_local);
     __syncthreads();
     // tile facts are wave-uniform; readfirstlane lets the compiler keep them in
     // scalar registers and branch on them without exec masking
@@ -170,7 +172,7 @@ __global__ __launch_bounds__(WM * WN * 64, MINB) void grouped_gemm_kernel(GemmAr
     if (e < 0)
         return;
     const int local = __builtin_amdgcn_readfirstlane(s_local);
-    const int cnt = __builtin_amdgcn_readfirstlane(g.row_count[e]);
+    const int cnt = __builtin_amdgcn_readfirstlane(max(g.row_count[e], 0));
     // The expert's rows are cut into mt tiles of (nearly) equal size rather
     // than full tiles plus a remainder: the M tiles that share a weight tile
     // run side by side, and equal tiles keep them in step, so the weights
@@ -179,8 +181,16 @@ __global__ __launch_bounds__(WM * WN * 64, MINB) void grouped_gemm_kernel(GemmAr
     const int n_tile = local / mt, m_tile = local % mt;
     const int tile_rows = (cnt + mt - 1) / mt; // <= BM; the last tile is never empty
     const int m0 = m_tile * tile_rows;
-    const int rows_valid = min(tile_rows, cnt - m0);
-    const size_t row0 = (size_t)__builtin_amdgcn_readfirstlane(g.row_offset[e]) + m0;
+    const int offset = __builtin_amdgcn_readfirstlane(g.row_offset[e]);
+    // Offsets and counts come from the caller: a tile's rows are clipped to
+    // the buffers' rows (as moe_dispatch writes them nothing is clipped), and
+    // a tile left with none, or of an offset below 0, stores nothing.
+    const int rows_valid = offset < 0 ? 0
+                                      : (int)min((long long)min(tile_rows, cnt - m0),
+                                                 g.rows - ((long long)offset + m0));
+    if (rows_valid <= 0)
+        return;
+    const size_t row0 = (size_t)offset + m0;
     const int n0 = n_tile * BN;
     const int N = g.N, K = g.K;
 
@@ -669,7 +679,7 @@ hipError_t launch_gate_up(const Dims &dm, const void *send_buf, const float *sen
         return hipSuccess;
     const long long mtiles_max = (dm.send_rows + kBM1 - 1) / kBM1 + dm.E;
     GemmArgs a{send_buf, dm.fp8 ? send_scale : nullptr, expert_offset, expert_kept, w1, w3, h,
-               dm.E, dm.H, dm.d, MOE_GEMM_ROT_GU ? rotate_k(dm.d) : 0};
+               dm.E, dm.H, dm.d, MOE_GEMM_ROT_GU ? rotate_k(dm.d) : 0, dm.send_rows};
     if (dm.fp8 && dm.fp8_widen && a_wide) {
         // E4M3 values widened to bf16 (exact), row scales applied in the
         // epilogue as in the E4M3 loop: the same products in the same
@@ -698,7 +708,7 @@ hipError_t launch_down(const Dims &dm, const uint16_t *h, const int32_t *expert_
         return hipSuccess;
     const long long mtiles_max = (dm.send_rows + kBM2 - 1) / kBM2 + dm.E;
     GemmArgs a{h, nullptr, expert_offset, expert_kept, w2, nullptr, expert_out, dm.E, dm.d, dm.H,
-               MOE_GEMM_ROT_DN ? rotate_k(dm.H) : 0};
+               MOE_GEMM_ROT_DN ? rotate_k(dm.H) : 0, dm.send_rows};
     constexpr int threads = kWM2 * kWN2 * 64;
     if (dm.d % kBN2 == 0 && !few_tiles(dm, dm.d, kBN2, kBM2))
         grouped_gemm_kernel<kBM2, kBN2, kBK, kRing2, kMinB2, kWM2, kWN2, false, false>

@@ -282,7 +282,8 @@ int moe_expert_down(const moe_shape *shape, const uint16_t *h, const int32_t *ex
  * order, of topk_w[t,s] * expert_out[slot[t,s]], then + shared_out[t]) with
  * fp32 accumulation.  Dropped assignments add nothing; the residual is the
  * caller's to add.
- *   expert_out  [send_rows, d] bf16;  slot, topk_w [T, k];
+ *   expert_out  [send_rows, d] bf16;  slot, topk_w [T, k];  a slot outside
+ *               [0, send_rows) counts as dropped (never read past the rows)
  *   shared_out  [T, d] bf16 (the shared expert's output) or NULL;
  *   y [T, d] bf16 out */
 int moe_combine(const moe_shape *shape, const uint16_t *expert_out, const int32_t *slot,

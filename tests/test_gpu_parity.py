@@ -317,6 +317,41 @@ def test_dispatch_and_combine_large_k(k, cf):
     assert np.all(np.abs(got - want) <= np.maximum(ulp, 2.0 ** -133) + (k + 1) * 2.0 ** -24 * mag)
 
 
+@pytest.mark.parametrize("k", [2, 8, 12])
+def test_combine_treats_slots_outside_the_rows_as_dropped(k):
+    """A caller's slot array with values at or past send_rows (and -1s): the
+    combine reads only rows that exist and counts the others as dropped,
+    through the k <= 2, k <= 8 and any-k kernels."""
+    T, d, E = 300, 256, 16
+    shape = api.Shape(T=T, d=d, E=E, k=k, H=64, D=2)
+    n, _, _ = api.moe_query(shape)
+    rng = np.random.default_rng(100 + k)
+    slot = rng.integers(0, n, (T, k)).astype(np.int32)
+    pick = rng.random((T, k))
+    slot[pick < 0.1] = -1
+    # past the rows, but inside the (padded) buffer: a missing bound would
+    # read the padding's large values, not fault
+    slot[pick >= 0.8] = n + rng.integers(0, 64, int((pick >= 0.8).sum()))
+    w = rng.random((T, k)).astype(np.float32)
+    eo_bits = bf16_bits(torch.randn(n, d).to(torch.bfloat16))
+    pad = np.full((64, d), np.float32(1e4).view(np.uint32) >> 16, np.uint16)
+    eo = torch.from_numpy(np.concatenate([eo_bits, pad]).view(np.int16)).view(
+        torch.bfloat16).to(DEV)
+    y = torch.empty(T, d, dtype=torch.bfloat16, device=DEV)
+    api.moe_combine(shape, eo, _i32(slot), _f32(w), None, y)
+    torch.cuda.synchronize()
+    kept = np.where((slot >= 0) & (slot < n), slot, -1)
+    want = bits_to_f64(oracle.combine(eo_bits, kept, w))
+    got = t2f(y)
+    rows = bits_to_f64(eo_bits)
+    mag = np.zeros((T, d))
+    for s in range(k):
+        m = kept[:, s] >= 0
+        mag[m] += np.abs(w[m, s, None].astype(np.float64) * rows[kept[m, s]])
+    ulp = np.ldexp(1.0, np.frexp(np.abs(want))[1] - 8)
+    assert np.all(np.abs(got - want) <= np.maximum(ulp, 2.0 ** -133) + (k + 1) * 2.0 ** -24 * mag)
+
+
 def test_expert_ffn_stage(case):
     cfg, inp, h, bias, ref, shape, buf = case
     # feed the oracle's dispatch so both sides see identical rows
@@ -631,6 +666,45 @@ def test_expert_ffn_every_tile_shape(fp8):
                 dict(rows=x[lo:lo + m])
             check_expert_rows(f"expert {e} ({m} rows)", w1[e], w3[e], w2[e], hb[lo:lo + m],
                               got[lo:lo + m], **rows)
+
+
+def test_expert_ffn_clips_rows_outside_the_buffers():
+    """Caller-given offsets and counts that reach past the send buffer's rows:
+    each expert's rows are clipped to [0, send_rows), an expert whose offset
+    lies past them has none, and no row past send_rows is read or written.
+    The buffers carry 64 padding rows, so a missing clip would show in them
+    (never as an access outside an allocation)."""
+    counts = np.array([40, 0, 300, 17, 64, 90], np.int32)
+    E, n = len(counts), int(counts.sum())
+    cfg = MoEConfig("clip_rows", T=n, d=256, E=E, k=1, H=128, cf=INF, D=1, x_std=1.0,
+                    wg_std=0.1, w_std=0.05, seed=23)
+    inp = make_inputs(cfg, DEV)
+    shape = api.Shape.from_config(cfg)
+    assert api.moe_query(shape)[0] == n
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    kept = counts.copy()
+    kept[5] += 30                       # 30 rows past the end: clipped
+    off_in = off.copy()
+    off_in[1], kept[1] = n + 5, 10      # starts past the end: no rows
+    pad = 64
+    x = bf16_bits(inp["x"])
+    w1, w3, w2 = (bf16_bits(inp[k]) for k in ("w1", "w3", "w2"))
+    big = np.float32(1e4).view(np.uint32) >> 16
+    send_np = np.concatenate([x, np.full((pad, cfg.d), big, np.uint16)])
+    send = torch.from_numpy(send_np.view(np.int16)).view(torch.bfloat16).to(DEV)
+    sentinel = -12345
+    h = torch.full((n + pad, cfg.H), sentinel, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    out = torch.full((n + pad, cfg.d), sentinel, dtype=torch.int16,
+                     device=DEV).view(torch.bfloat16)
+    api.moe_expert_gate_up(shape, send, None, _i32(off_in), _i32(kept), inp["w1"], inp["w3"], h)
+    api.moe_expert_down(shape, h, _i32(off_in), _i32(kept), inp["w2"], out)
+    torch.cuda.synchronize()
+    hb, ob = bf16_bits(h), bf16_bits(out)
+    assert np.all(hb[n:].view(np.int16) == sentinel) and np.all(ob[n:].view(np.int16) == sentinel)
+    for e in (0, 2, 3, 4, 5):
+        lo, m = int(off[e]), int(counts[e])   # clipped: expert 5 ends at n
+        check_expert_rows(f"expert {e} ({m} rows)", w1[e], w3[e], w2[e], hb[lo:lo + m],
+                          ob[lo:lo + m], rows=x[lo:lo + m])
 
 
 def test_fp8_widened_gate_up_matches_register_path():
