@@ -248,7 +248,9 @@ int moe_dispatch_noalloc(const moe_shape *shape, const uint16_t *x, const int32_
  *   send_scale     [send_rows] fp32 row scales under FP8 dispatch, may be
  *                  NULL otherwise; the expert's input row is code * scale
  *   expert_offset  [E+1] int32, expert_kept [E] int32 (as moe_dispatch
- *                  writes them; kept rows must lie inside send_buf)
+ *                  writes them); an expert's rows [offset, offset + kept)
+ *                  are clipped to [0, send_rows), a negative offset or count
+ *                  gives none
  *   w1, w3         [E, H, d] bf16;  w2 [E, d, H] bf16
  *   expert_out     [send_rows, d] bf16 out; only kept rows are written
  *   workspace      device, >= moe_query's size (holds h) */
