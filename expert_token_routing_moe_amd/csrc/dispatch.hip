@@ -281,57 +281,47 @@ __global__ __launch_bounds__(kMaxExperts) void scan_kernel(
 
 // Count and scan in one workgroup of 1024 threads, for small shapes whose
 // chunk bitmaps all fit in LDS (nchunks * E <= kFusedCells) and whose routing
-// entries fit in registers (T <= 1024 * TPT, k <= KM): the count kernel's
-// per-chunk token bitmaps for every chunk at once (thread i takes tokens
-// i, i + 1024, ..., and loads all their entries before using any), their
-// popcounts as the chunk counts, the scan, then the in-chunk positions.
-// Same outputs as count_kernel + scan_kernel, in one launch.
+// entries fit in registers (T <= 1024, k <= KM: thread t takes token t and
+// loads all its entries before using any): the count kernel's per-chunk
+// token bitmaps for every chunk at once, their popcounts as the chunk
+// counts, the scan, then the in-chunk positions.  Same outputs as
+// count_kernel + scan_kernel, in one launch.
 constexpr int kFusedCells = 4096;
-template <int KM, int TPT>
+template <int KM>
 __global__ __launch_bounds__(1024) void count_scan_kernel(
     const int32_t *__restrict__ topk_idx, int T, int k, int E, int D, int my_rank, int d,
     int fp8, long long C, int nchunks, int32_t *__restrict__ pos_in_chunk, ScanOut o)
 {
     __shared__ uint32_t s_bm[kFusedCells * kWords]; // [nchunks][E][kWords]
     __shared__ int32_t s_cnt[kFusedCells];          // [nchunks][E]
-    const int tid = threadIdx.x;
+    const int t = threadIdx.x;
     const int cells = nchunks * E;
-    int32_t ids[TPT][KM];
-    bool ok[TPT][KM];
+    int32_t ids[KM];
+    bool ok[KM];
 #pragma unroll
-    for (int j = 0; j < TPT; ++j) {
-        const int t = tid + 1024 * j;
-#pragma unroll
-        for (int s = 0; s < KM; ++s)
-            ids[j][s] = (t < T && s < k) ? topk_idx[(size_t)t * k + s] : -1;
-    }
-    for (int w = tid; w < cells * kWords; w += 1024)
+    for (int s = 0; s < KM; ++s)
+        ids[s] = (t < T && s < k) ? topk_idx[(size_t)t * k + s] : -1;
+    for (int w = t; w < cells * kWords; w += 1024)
         s_bm[w] = 0u;
     int invalid = 0;
 #pragma unroll
-    for (int j = 0; j < TPT; ++j) {
-        const int t = tid + 1024 * j;
+    for (int s = 0; s < KM; ++s) {
+        ok[s] = ids[s] >= 0 && ids[s] < E;
 #pragma unroll
-        for (int s = 0; s < KM; ++s) {
-            ok[j][s] = ids[j][s] >= 0 && ids[j][s] < E;
-#pragma unroll
-            for (int s2 = 0; s2 < s; ++s2)
-                ok[j][s] = ok[j][s] && ids[j][s2] != ids[j][s];
-            invalid += (t < T && s < k && !ok[j][s]) ? 1 : 0;
-        }
+        for (int s2 = 0; s2 < s; ++s2)
+            ok[s] = ok[s] && ids[s2] != ids[s];
+        invalid += (t < T && s < k && !ok[s]) ? 1 : 0;
     }
     __syncthreads();
-#pragma unroll
-    for (int j = 0; j < TPT; ++j) {
-        const int t = tid + 1024 * j;
+    {
         uint32_t *bm = s_bm + (size_t)(t / kChunk) * E * kWords + ((t % kChunk) >> 5);
 #pragma unroll
         for (int s = 0; s < KM; ++s)
-            if (ok[j][s])
-                atomicOr(bm + ids[j][s] * kWords, 1u << (t & 31));
+            if (ok[s])
+                atomicOr(bm + ids[s] * kWords, 1u << (t & 31));
     }
     __syncthreads();
-    for (int c = tid; c < cells; c += 1024) {
+    for (int c = t; c < cells; c += 1024) {
         int n = 0;
 #pragma unroll
         for (int w = 0; w < kWords; ++w)
@@ -342,27 +332,23 @@ __global__ __launch_bounds__(1024) void count_scan_kernel(
     scan_block(T, k, E, D, my_rank, d, fp8, C, nchunks, s_cnt, invalid, o);
     // in-chunk position of (t, s): earlier tokens of the chunk routed to
     // the same expert
+    if (t >= T)
+        return;
+    const uint32_t bit = 1u << (t & 31);
+    const int wi = (t % kChunk) >> 5;
+    const uint32_t *bm = s_bm + (size_t)(t / kChunk) * E * kWords;
 #pragma unroll
-    for (int j = 0; j < TPT; ++j) {
-        const int t = tid + 1024 * j;
-        if (t >= T)
+    for (int s = 0; s < KM; ++s) {
+        if (s >= k)
             break;
-        const uint32_t bit = 1u << (t & 31);
-        const int wi = (t % kChunk) >> 5;
-        const uint32_t *bm = s_bm + (size_t)(t / kChunk) * E * kWords;
-#pragma unroll
-        for (int s = 0; s < KM; ++s) {
-            if (s >= k)
-                break;
-            int p = -1;
-            if (ok[j][s]) {
-                const uint32_t *m = bm + ids[j][s] * kWords;
-                p = __popc(m[wi] & (bit - 1u));
-                for (int w = 0; w < wi; ++w)
-                    p += __popc(m[w]);
-            }
-            pos_in_chunk[(size_t)t * k + s] = p;
+        int p = -1;
+        if (ok[s]) {
+            const uint32_t *m = bm + ids[s] * kWords;
+            p = __popc(m[wi] & (bit - 1u));
+            for (int w = 0; w < wi; ++w)
+                p += __popc(m[w]);
         }
+        pos_in_chunk[(size_t)t * k + s] = p;
     }
 }
 
@@ -724,16 +710,16 @@ hipError_t launch_dispatch(const Dims &dm, const uint16_t *x, const int32_t *top
     // 60.8 us against 9.0 + 7.6 us for the two kernels).
     const bool fused = dm.T <= 1024 && dm.k <= 8 && (long long)dm.nchunks * dm.E <= kFusedCells;
     if (fused) {
-#define MOE_COUNT_SCAN(KM, TPT)                                                              \
-    count_scan_kernel<KM, TPT><<<1, 1024, 0, st>>>(topk_idx, dm.T, dm.k, dm.E, dm.D,          \
-                                                   dm.my_rank, dm.d, dm.fp8,                  \
-                                                   (long long)dm.capacity, dm.nchunks, slot, so)
+#define MOE_COUNT_SCAN(KM)                                                                   \
+    count_scan_kernel<KM><<<1, 1024, 0, st>>>(topk_idx, dm.T, dm.k, dm.E, dm.D, dm.my_rank,   \
+                                              dm.d, dm.fp8, (long long)dm.capacity,           \
+                                              dm.nchunks, slot, so)
         if (dm.k <= 2)
-            MOE_COUNT_SCAN(2, 1);
+            MOE_COUNT_SCAN(2);
         else if (dm.k <= 4)
-            MOE_COUNT_SCAN(4, 1);
+            MOE_COUNT_SCAN(4);
         else
-            MOE_COUNT_SCAN(8, 1);
+            MOE_COUNT_SCAN(8);
 #undef MOE_COUNT_SCAN
     } else {
         const size_t lds = (size_t)dm.E * kWords * sizeof(uint32_t);
