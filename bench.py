@@ -153,12 +153,14 @@ def cpu_model():
 
 def vendor_gemm_reference(cfg, dev, steps):
     """The vendor GEMM library (torch.nn.functional.linear -> hipBLASLt) on one
-    expert's two GEMMs at this workload's expert-parallel rank-local shape
-    (about D*T*k/E rows per expert), for scale: TFLOP/s and fraction of the
-    bf16 matrix-core peak."""
+    expert's two GEMMs, for scale: TFLOP/s and fraction of the bf16
+    matrix-core peak.  Rows per expert as in the grouped GEMM it is set
+    beside: the expert-parallel rank-local share (D*T*k/E) where bench.py
+    times one, else the layer's T*k/E."""
     import torch
 
-    rows = max(1, cfg.D * cfg.T * cfg.k // cfg.E)
+    rank_local = cfg.D > 1 and cfg.cf == float("inf")
+    rows = max(1, (cfg.D if rank_local else 1) * cfg.T * cfg.k // cfg.E)
     out = {"rows_per_expert": rows}
     for name, (n, kdim) in {"gate_up": (2 * cfg.H, cfg.d), "down": (cfg.d, cfg.H)}.items():
         a = torch.randn(rows, kdim, device=dev).to(torch.bfloat16)
