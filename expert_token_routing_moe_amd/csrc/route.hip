@@ -17,13 +17,14 @@
 // index that holds the maximum (ballots), a softmax over the kept logits,
 // optionally within the token's best expert groups.
 //
-// One launch when a token tile's logits fit one workgroup (one slice, one
-// expert tile): it selects from its own tile.  Otherwise every slice stores
-// its fp32 partial tile and a second launch, one wavefront per token, sums
-// the partials in slice order (a fixed order: deterministic), adds the bias
-// and selects.  The kernel boundary is the device-wide barrier: on this
-// eight-XCD part a release inside the kernel means an L2 write-back per
-// workgroup, which measured slower than the second launch.
+// Every workgroup stores its fp32 partial tile; a second launch, one
+// wavefront per token, sums a token's partials in slice order (a fixed
+// order: deterministic), adds the bias and selects.  The kernel boundary is
+// the device-wide barrier: on this eight-XCD part a release inside the
+// kernel means an L2 write-back per workgroup, which measured slower than
+// the second launch.  (Selecting inside the logit kernel when one workgroup
+// holds whole logit rows measured slower too: its 8 waves select 64 tokens
+// one after another, where the second launch gives every token a wave.)
 #include <type_traits>
 
 #include "moe_internal.hpp"
@@ -81,11 +82,8 @@ static RouterPlan router_plan(int T, int E, int d)
 
 int router_ksplit(int T, int E, int d) { return router_plan(T, E, d).sk; }
 
-bool router_partials(int T, int E, int d)
-{
-    const RouterPlan p = router_plan(T, E, d);
-    return T > 0 && p.sk * (router_epad(E) / p.be) > 1;
-}
+// The logit kernel always stores partial sums (any T > 0).
+bool router_partials(int T, int, int) { return T > 0; }
 
 namespace {
 
@@ -298,62 +296,17 @@ struct RouteArgs {
     float *logits_out;        // [T, E] or null
     int32_t *topk_idx;        // [T, k]
     float *topk_w;            // [T, k]
-    float *partial;           // [S, T, E_pad] fp32 partial logits (S * n_et > 1)
+    float *partial;           // [S, T, E_pad] fp32 partial logits
     int T, d, E, ldw, epad, k, G, M;
     int n_tt, n_et, S, total;
 };
 
-// Logits of tokens [t0, t0 + TC) and all E_pad experts sit in LDS (row pitch
-// ldl floats, bias included); each wavefront selects for tokens wave,
-// wave + NW, ...
-template <int V, int NW>
-__device__ __forceinline__ void select_rows(const RouteArgs &a, const float *L, int ldl, int t0,
-                                            int TC, char *gscratch)
-{
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    uint32_t *gs = reinterpret_cast<uint32_t *>(gscratch) + wave * kMaxExperts;
-    uint8_t *allow = reinterpret_cast<uint8_t *>(gscratch + NW * kMaxExperts * 4) +
-                     wave * kMaxExperts;
-    for (int tl = wave; tl < TC; tl += NW) {
-        const int t = t0 + tl;
-        if (t >= a.T)
-            break;
-        float h[V];
-#pragma unroll
-        for (int j = 0; j < V; ++j) {
-            const int e = lane + 64 * j;
-            h[j] = e < a.E ? L[tl * ldl + e] : 0.f;
-        }
-        topk_softmax_token<V>(h, a.E, a.k, a.G, a.M, gs, allow, a.topk_idx + (size_t)t * a.k,
-                              a.topk_w + (size_t)t * a.k);
-    }
-}
-
-template <int NW>
-__device__ __forceinline__ void select_dispatch(const RouteArgs &a, const float *L, int ldl,
-                                                int t0, int TC, char *gscratch)
-{
-    const int V = a.epad / 64;
-    if (V <= 1)
-        select_rows<1, NW>(a, L, ldl, t0, TC, gscratch);
-    else if (V <= 2)
-        select_rows<2, NW>(a, L, ldl, t0, TC, gscratch);
-    else if (V <= 4)
-        select_rows<4, NW>(a, L, ldl, t0, TC, gscratch);
-    else if (V <= 8)
-        select_rows<8, NW>(a, L, ldl, t0, TC, gscratch);
-    else
-        select_rows<16, NW>(a, L, ldl, t0, TC, gscratch);
-}
-
-// The logit GEMM.  BT tokens x BE experts x one K slice per workgroup; with
-// one slice and one expert tile (S * n_et == 1, so BE == E_pad) it selects
-// from its own tile, else it stores the fp32 partial tile.
+// The logit GEMM.  BT tokens x BE experts x one K slice per workgroup, stored
+// as an fp32 partial tile.
 template <int BT, int RBK, int BE, int RRING, int MINB, int WM, int WN>
 __global__ __launch_bounds__(WM * WN * 64, MINB) void route_logits_kernel(RouteArgs a)
 {
     constexpr int NW = WM * WN;                  // waves per workgroup
-    constexpr int NT = NW * 64;
     constexpr int RC = RBK / 8, RPI = 64 / RC;   // x: pieces per row, rows per load
     constexpr int A_PW = BT / RPI / NW;          // x loads per wave per stage
     constexpr int BPR = BE / 8;                  // W_g: pieces per tile row
@@ -365,9 +318,6 @@ __global__ __launch_bounds__(WM * WN * 64, MINB) void route_logits_kernel(RouteA
     static_assert(NS >= 2, "two stages fit");
     constexpr int WTT = BT / WM, WTE = BE / WN;  // wave tile
     constexpr int RT = WTT / 16, CT = WTE / 16;
-    constexpr int LDC = BE + 4;                  // epilogue tile pitch (floats)
-    static_assert(BT * LDC * 4 <= RRING, "epilogue tile fits in the ring");
-    constexpr int GSCR = NW * kMaxExperts * 5;   // selection scratch (group limit)
     __shared__ __attribute__((aligned(1024))) char smem[RRING];
 
     const int w = xcd_remap(blockIdx.x, a.total);
@@ -486,52 +436,20 @@ __global__ __launch_bounds__(WM * WN * 64, MINB) void route_logits_kernel(RouteA
 
     // D layout of a 16x16 MFMA tile: lane holds rows 4*(lane/16)+q, column
     // lane%16.
-    if (a.S * a.n_et > 1) {
-        // partial tile -> [sk, t, e0 .. e0 + BE) of the [S, T, E_pad] sums,
-        // 64-byte row pieces straight from the accumulators
-        float *out = a.partial + (size_t)sk * T * a.epad;
-#pragma unroll
-        for (int i = 0; i < RT; ++i)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int t = t0 + wt * WTT + i * 16 + 4 * (lane >> 4) + q;
-                if (t < T)
-#pragma unroll
-                    for (int j = 0; j < CT; ++j)
-                        out[(size_t)t * a.epad + e0 + we * WTE + j * 16 + (lane & 15)] =
-                            acc[i][j][q];
-            }
-        return;
-    }
-    // one slice, one expert tile (64-token tiles only: the planner uses
-    // 128-token tiles with partial sums): the tile goes to LDS and straight
-    // to selection
-    if constexpr (BT * LDC * 4 + GSCR <= RRING) {
-    __syncthreads(); // every wave is done with the ring
-    float *C = reinterpret_cast<float *>(smem);
+    // partial tile -> [sk, t, e0 .. e0 + BE) of the [S, T, E_pad] sums,
+    // 64-byte row pieces straight from the accumulators
+    float *out = a.partial + (size_t)sk * T * a.epad;
 #pragma unroll
     for (int i = 0; i < RT; ++i)
 #pragma unroll
-        for (int j = 0; j < CT; ++j)
+        for (int q = 0; q < 4; ++q) {
+            const int t = t0 + wt * WTT + i * 16 + 4 * (lane >> 4) + q;
+            if (t < T)
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                C[(wt * WTT + i * 16 + 4 * (lane >> 4) + q) * LDC + we * WTE + j * 16 +
-                  (lane & 15)] = acc[i][j][q];
-    __syncthreads();
-    for (int c = tid; c < BT * BE; c += NT) {
-        const int r = c / BE, e = c % BE;
-        float v = C[r * LDC + e];
-        if (e < a.E) {
-            if (a.bias)
-                v += a.bias[e];
-            if (a.logits_out && t0 + r < T)
-                a.logits_out[(size_t)(t0 + r) * a.E + e] = v;
+                for (int j = 0; j < CT; ++j)
+                    out[(size_t)t * a.epad + e0 + we * WTE + j * 16 + (lane & 15)] =
+                        acc[i][j][q];
         }
-        C[r * LDC + e] = v;
-    }
-    __syncthreads();
-    select_dispatch<NW>(a, C, LDC, t0, BT, smem + BT * LDC * 4);
-    }
 }
 
 // Sum of the S partial logits of a token in slice order (loads in batches
@@ -666,7 +584,7 @@ hipError_t launch_route(const Dims &dm, const uint16_t *x, const uint16_t *w_gat
     else
         route_logits_kernel<64, 64, 64, 78 * 1024, 2, 2, 2><<<xcd_grid(a.total), 256, 0, st>>>(a);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || a.S * a.n_et == 1)
+    if (e != hipSuccess)
         return e;
     const int blocks = (T + 3) / 4;
     const int V = a.epad / 64;

@@ -113,14 +113,16 @@ ROUTE_CASES = [
     (100, 512, 384, 6, 0, 0, True),       # BE 64: 6 expert tiles, 2 slices
     (333, 2048, 256, 8, 8, 4, True),      # BE 64: 4 expert tiles, 8 slices, group limit
     (70, 768, 64, 2, 0, 0, False),        # BE 64: one expert tile, 3 slices
+    (70, 4096, 64, 2, 0, 0, False),       # BE 64: one expert tile, 16 slices
     (129, 512, 12, 3, 0, 0, True),        # E % 8 != 0 (padded W_g copy), 2 slices
+    (129, 4096, 12, 3, 0, 0, True),       # E % 8 != 0, 16 slices
     (1, 4096, 256, 8, 0, 0, False),       # one token: BE 64, 4 expert tiles, 16 slices
     (64, 7168, 1024, 16, 0, 0, False),    # BE 64: 16 expert tiles, 28 slices
     (64, 7168, 256, 8, 0, 0, True),       # DeepSeek-V3 decode: BE 64, 4 expert tiles, 28 slices
     (2048, 1024, 512, 8, 0, 0, False),    # BE 256: 2 expert tiles, 4 slices
     (2048, 4096, 128, 4, 0, 0, True),     # BE 128: one expert tile, 16 slices
-    (16384, 128, 256, 8, 0, 0, False),    # BE 256, one slice: top-k inside the logit kernel
-    (16384, 128, 256, 8, 8, 4, True),     # the same with a group limit
+    (16384, 128, 256, 8, 0, 0, False),    # BE 256, one slice (tiles alone fill the chip)
+    (16384, 128, 256, 8, 8, 4, True),     # the same with a group limit and bias
 ]
 
 
