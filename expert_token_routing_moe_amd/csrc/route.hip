@@ -50,13 +50,13 @@ int router_ldw(int E) { return (E + 7) / 8 * 8; }
 // time at the DeepSeek-V3 prefill shape for twice the partial-sum bytes.)
 // T = 0: nothing to split.
 struct RouterPlan {
-    int be, sk;
+    int be, sk, bt;
 };
 static RouterPlan router_plan(int T, int E, int d)
 {
     const int epad = router_epad(E);
     const int steps = d / 64;
-    RouterPlan best{64, 1};
+    RouterPlan best{64, 1, 64};
     long long best_wg = -1;
     for (int be = 256; be >= 64; be /= 2) {
         if (epad % be != 0)
@@ -70,11 +70,20 @@ static RouterPlan router_plan(int T, int E, int d)
             sk = std::max(1, std::min(s, 32));
         }
         const long long wg = tiles * sk;
+        // More tiles than the chip needs: taller token tiles (128, and 256
+        // for 256-expert tiles, whose ring holds two of their 64 KB stages)
+        // that still fill it, so each reads W_g for more tokens (at T = 32768
+        // every 64-token tile would read all of W_g, 3.7 MB at DeepSeek-V3
+        // shape)
+        if (T > 0 && be == 256 && tiles >= 4LL * target)
+            return RouterPlan{be, 1, 256};
+        if (T > 0 && tiles >= 2LL * target)
+            return RouterPlan{be, 1, 128};
         if (T == 0 || wg >= target)
-            return RouterPlan{be, sk};
+            return RouterPlan{be, sk, 64};
         if (wg > best_wg) {
             best_wg = wg;
-            best = RouterPlan{be, sk};
+            best = RouterPlan{be, sk, 64};
         }
     }
     return best;
@@ -574,15 +583,27 @@ hipError_t launch_route(const Dims &dm, const uint16_t *x, const uint16_t *w_gat
     const RouterPlan plan = router_plan(T, E, d);
     const int be = plan.be;
     a.S = plan.sk;
-    a.n_tt = (T + 63) / 64;
+    a.n_tt = (T + plan.bt - 1) / plan.bt;
     a.n_et = a.epad / be;
     a.total = a.n_tt * a.n_et * a.S;
-    if (be == 256)
-        route_logits_kernel<64, 64, 256, 156 * 1024, 1, 2, 4><<<xcd_grid(a.total), 512, 0, st>>>(a);
-    else if (be == 128)
-        route_logits_kernel<64, 64, 128, 78 * 1024, 2, 2, 2><<<xcd_grid(a.total), 256, 0, st>>>(a);
-    else
-        route_logits_kernel<64, 64, 64, 78 * 1024, 2, 2, 2><<<xcd_grid(a.total), 256, 0, st>>>(a);
+#define MOE_LOGITS(BT)                                                                       \
+    if (be == 256)                                                                           \
+        route_logits_kernel<BT, 64, 256, 156 * 1024, 1, 2, 4>                                \
+            <<<xcd_grid(a.total), 512, 0, st>>>(a);                                          \
+    else if (be == 128)                                                                      \
+        route_logits_kernel<BT, 64, 128, 78 * 1024, 2, 2, 2>                                 \
+            <<<xcd_grid(a.total), 256, 0, st>>>(a);                                          \
+    else                                                                                     \
+        route_logits_kernel<BT, 64, 64, 78 * 1024, 2, 2, 2><<<xcd_grid(a.total), 256, 0, st>>>(a);
+    if (plan.bt == 256) {
+        route_logits_kernel<256, 64, 256, 156 * 1024, 1, 2, 4>
+            <<<xcd_grid(a.total), 512, 0, st>>>(a);
+    } else if (plan.bt == 128) {
+        MOE_LOGITS(128)
+    } else {
+        MOE_LOGITS(64)
+    }
+#undef MOE_LOGITS
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;

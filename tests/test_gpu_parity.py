@@ -123,6 +123,9 @@ ROUTE_CASES = [
     (2048, 4096, 128, 4, 0, 0, True),     # BE 128: one expert tile, 16 slices
     (16384, 128, 256, 8, 0, 0, False),    # BE 256, one slice (tiles alone fill the chip)
     (16384, 128, 256, 8, 8, 4, True),     # the same with a group limit and bias
+    (32768, 128, 256, 8, 0, 0, False),    # 128-token tiles (twice the tiles needed), BE 256
+    (65536, 64, 64, 2, 0, 0, True),       # 128-token tiles, BE 64
+    (65536, 64, 256, 8, 8, 4, True),      # 256-token tiles, BE 256, group limit
 ]
 
 
