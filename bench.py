@@ -333,21 +333,36 @@ def summarize_rocprof(out_dir, workload):
     import statistics as stt
 
     def rows(sub, name):
+        import gzip
+
         path = os.path.join(out_dir, sub, name)
-        return list(csv.DictReader(open(path))) if os.path.exists(path) else []
+        if os.path.exists(path):
+            return list(csv.DictReader(open(path)))
+        if os.path.exists(path + ".gz"):  # the same, compressed
+            with gzip.open(path + ".gz", "rt") as f:
+                return list(csv.DictReader(f))
+        return []
 
     with open(os.path.join(out_dir, "trace.json")) as f:
         bj = json.loads(f.read().strip().splitlines()[-1])
-    # kernel trace: durations per (kernel, grid), first dispatch order kept
-    groups, first_grid = {}, {}
+    # kernel trace: durations per (kernel, grid).  The layer's launches are
+    # the groups first dispatched before the device-rate probes, which
+    # bench.py runs after the timed steps (the rank-local share comes after)
+    groups, first_start = {}, {}
+    probe_start = None
     for r in rows("trace", "run_kernel_trace.csv"):
         lab = _kernel_label(r["Kernel_Name"])
         if not lab.startswith("moe::"):
             continue
         grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
-        first_grid.setdefault(lab, grid)
-        groups.setdefault((lab, grid), []).append(
-            (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        t0 = int(r["Start_Timestamp"])
+        if "stream_read" in lab:
+            probe_start = t0 if probe_start is None else min(probe_start, t0)
+        first_start[(lab, grid)] = min(first_start.get((lab, grid), t0), t0)
+        groups.setdefault((lab, grid), []).append((int(r["End_Timestamp"]) - t0) / 1e3)
+
+    def is_layer(key):
+        return probe_start is None or first_start.get(key, probe_start) < probe_start
 
     def counters(sub):
         per = {}
@@ -391,7 +406,7 @@ def summarize_rocprof(out_dir, workload):
         lines.append(f"| `{lab}` | {grid} | {len(ts)} | {stt.mean(ts):.1f} | {stt.median(ts):.1f} "
                      f"| {min(ts):.1f} | {max(ts):.1f} | {rd:.1f} | {wr:.1f} |")
         st = _stage_of(lab)
-        layer = grid == first_grid[lab]
+        layer = is_layer((lab, grid))
         if st and layer:
             acc = stage_counter.setdefault(st, [0.0, 0.0])
             acc[0] += stt.mean(ts)
@@ -417,7 +432,7 @@ def summarize_rocprof(out_dir, workload):
             if "grouped_gemm" not in lab:
                 continue
             st = _gemm_stage(lab)
-            layer = grid == first_grid.get(lab, grid)
+            layer = is_layer((lab, grid))
             per = 4 if st == "gate_up" else 2
             if layer:
                 alg = bj["stages"][st]["tflops"] * bj["stages"][st]["ms"] * 1e9 / 16384
