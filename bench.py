@@ -11,7 +11,9 @@ byte rate is also given as a fraction of this device's own streaming-read
 rate (read_frac), and as device_frac: the stage's reads at that rate plus
 its writes at the device's streaming-store rate, over the stage's time.
 Both rates are measured after the timed steps (moe_stream_read and
-moe_stream_write, the non-temporal 16-byte accesses of the kernels).
+moe_stream_write, the non-temporal 16-byte accesses of the kernels), and
+the combine is set beside moe_stream_gather, its own access pattern with
+none of its arithmetic, on the same expert outputs and slots.
 
 For a dropless workload spread over D > 1 ranks, the expert GEMMs are also
 timed on one rank's share under D-way expert parallelism (E/D experts, the
@@ -267,6 +269,31 @@ def _best_ms(fn, stream, reps=5):
         e1.record(stream)
         e1.synchronize()
         best = min(best, e0.elapsed_time(e1))
+    return best
+
+
+def gather_probe_ms(buf, stream, scratch, reps=5):
+    """The combine's access without its arithmetic (moe_stream_gather) on the
+    layer's own expert outputs and slots: best of reps, each after the same
+    last-level-cache flush as a timed step."""
+    import torch
+
+    from expert_token_routing_moe_amd import api
+
+    out = torch.empty_like(buf.y)
+    api.moe_stream_gather(buf.expert_out, buf.slot, out, stream)  # warm-up
+    best = float("inf")
+    for _ in range(reps):
+        if scratch is not None:
+            scratch.sum()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        api.moe_stream_gather(buf.expert_out, buf.slot, out, stream)
+        e1.record(stream)
+        e1.synchronize()
+        best = min(best, e0.elapsed_time(e1))
+    del out
     return best
 
 
@@ -620,6 +647,7 @@ def main():
     traffic = stage_traffic(cfg, st, touched)
     read_gbs, write_gbs = device_rates(dev, stream)
     log(f"bench: streaming read on this device {read_gbs:.0f} GB/s, store {write_gbs:.0f} GB/s")
+    g_ms = gather_probe_ms(buf, stream, scratch)
     per_stage = {}
     for s in stages:
         t = stage_ms[s] / 1e3
@@ -635,6 +663,9 @@ def main():
                             device_frac=round((traffic[s]["read"] / (read_gbs * 1e9)
                                                + traffic[s]["write"] / (write_gbs * 1e9)) / t, 4),
                             tflops=round(traffic[s]["flops"] / t / 1e12, 2))
+    # the combine against its own access pattern with no arithmetic
+    per_stage["combine"]["gather_probe_ms"] = round(g_ms, 5)
+    per_stage["combine"]["of_gather_probe"] = round(g_ms / stage_ms["combine"], 4)
     dom = max(("gate_up", "down"), key=lambda s: stage_ms[s])
     t_dom = stage_ms[dom] / 1e3
     intensity = traffic[dom]["flops"] / traffic[dom]["bytes"]

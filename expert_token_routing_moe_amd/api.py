@@ -77,6 +77,8 @@ def lib():
         "moe_fp8_rows_to_bf16": [P, P, ctypes.c_int64, ctypes.c_int32, P, P],
         "moe_stream_read": [P, SZ, P, P],
         "moe_stream_write": [P, SZ, ctypes.c_uint32, P],
+        "moe_stream_gather": [P, ctypes.c_int64, ctypes.c_int32, P, ctypes.c_int64,
+                              ctypes.c_int32, P, P],
     }
     for name, argtypes in sig.items():
         f = getattr(L, name)
@@ -360,6 +362,18 @@ def moe_stream_write(dst, value, stream=None):
     _check("moe_stream_write", lib().moe_stream_write(
         _p(dst), dst.numel() * dst.element_size(), ctypes.c_uint32(value & 0xFFFFFFFF),
         _stream(stream)))
+
+
+def moe_stream_gather(rows, slot, out, stream=None):
+    """out[t] = XOR over s of rows[slot[t, s]] (16-byte pieces), with the
+    combine's access and none of its arithmetic (a probe of that access's
+    rate).  rows [nrows, d] bf16; slot [T, k] int32; out [T, d] bf16."""
+    nrows, d = rows.shape
+    T, k = slot.shape
+    if tuple(out.shape) != (T, d):
+        raise ValueError(f"moe_stream_gather: out is {tuple(out.shape)}, needs {(T, d)}")
+    _check("moe_stream_gather", lib().moe_stream_gather(
+        _p(rows, BF16), nrows, d, _p(slot, I32), T, k, _p(out, BF16), _stream(stream)))
 
 
 @dataclass

@@ -480,6 +480,18 @@ MOE_EXPORT int moe_stream_write(void *dst, size_t bytes, uint32_t value, void *s
     return hip_status(launch_stream_write(dst, bytes, value, static_cast<hipStream_t>(stream)));
 }
 
+MOE_EXPORT int moe_stream_gather(const void *rows, int64_t nrows, int32_t d, const int32_t *slot,
+                                 int64_t T, int32_t k, void *out, void *stream)
+{
+    if (nrows < 0 || d <= 0 || d % 8 != 0 || T < 0 || T > INT32_MAX || k < 1 ||
+        (long long)T * k > INT32_MAX)
+        return MOE_EINVAL;
+    if (bad_ptr(rows, nrows) || bad_ptr(slot, T) || bad_ptr(out, T))
+        return MOE_EINVAL;
+    return hip_status(launch_stream_gather(rows, nrows, d, slot, (int)T, k, out,
+                                           static_cast<hipStream_t>(stream)));
+}
+
 MOE_EXPORT const char *moe_status_str(int status)
 {
     switch (status) {

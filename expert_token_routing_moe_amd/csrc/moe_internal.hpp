@@ -167,6 +167,8 @@ hipError_t launch_combine(const Dims &dm, const uint16_t *expert_out, const int3
                           hipStream_t st);
 hipError_t launch_stream_read(const void *src, size_t bytes, uint32_t *sink, hipStream_t st);
 hipError_t launch_stream_write(void *dst, size_t bytes, uint32_t value, hipStream_t st);
+hipError_t launch_stream_gather(const void *rows, long long nrows, int d, const int32_t *slot,
+                                int T, int k, void *out, hipStream_t st);
 hipError_t launch_shared_expert(const Dims &dm, const uint16_t *x, const uint16_t *w1s,
                                 const uint16_t *w3s, const uint16_t *w2s, uint16_t *shared_out,
                                 char *ws, const Workspace &wl, hipStream_t st);

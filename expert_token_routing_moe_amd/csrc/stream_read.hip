@@ -3,7 +3,9 @@
 // this device reaches, measured beside the kernels, for reading their
 // HBM fractions against the device as well as against the data sheet.
 // Its mirror, a streaming fill with the non-temporal 16-byte stores that
-// the permute and the GEMM epilogues write with, gives the store rate.
+// the permute and the GEMM epilogues write with, gives the store rate, and
+// a gather with the combine's access and none of its arithmetic gives the
+// rate of that access itself.
 //
 // Each lane keeps 8 loads in flight per pass (grid-stride over the buffer)
 // and folds every 32-bit word it reads into an XOR.  A lane whose fold
@@ -55,7 +57,76 @@ __global__ __launch_bounds__(256) void stream_write_kernel(uint4 *__restrict__ d
     }
 }
 
+// The combine's memory traffic without its arithmetic: out[t] = XOR over
+// s < k of rows[slot[t, s]] (16-byte pieces; a slot outside [0, nrows)
+// adds nothing).  As in the combine: one wavefront per token, its slots
+// read once into scalar registers, every gather of a piece issued before
+// any is used (KM an upper bound on k; larger k one gather at a time),
+// non-temporal gathers, 16-byte stores.
+template <int KM>
+__global__ __launch_bounds__(256) void stream_gather_kernel(const uint4 *__restrict__ rows,
+                                                            const int32_t *__restrict__ slot,
+                                                            int T, int k, int d16,
+                                                            long long nrows,
+                                                            uint4 *__restrict__ out)
+{
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T)
+        return;
+    uint4 *dst = out + (size_t)t * d16;
+    if (k > KM) {
+        for (int c = lane; c < d16; c += 64) {
+            uint4 x = make_uint4(0, 0, 0, 0);
+            for (int s = 0; s < k; ++s) {
+                const int r = slot[(size_t)t * k + s];
+                if (r < 0 || r >= nrows)
+                    continue;
+                const uint4 v = load_nt(rows + (size_t)r * d16 + c);
+                x = make_uint4(x.x ^ v.x, x.y ^ v.y, x.z ^ v.z, x.w ^ v.w);
+            }
+            dst[c] = x;
+        }
+        return;
+    }
+    int rr[KM];
+#pragma unroll
+    for (int s = 0; s < KM; ++s) {
+        const int r = s < k ? __builtin_amdgcn_readfirstlane(slot[(size_t)t * k + s]) : -1;
+        rr[s] = r >= 0 && r < nrows ? r : -1;
+    }
+    for (int c = lane; c < d16; c += 64) {
+        uint4 v[KM];
+#pragma unroll
+        for (int s = 0; s < KM; ++s)
+            v[s] = rr[s] >= 0 ? load_nt(rows + (size_t)rr[s] * d16 + c) : make_uint4(0, 0, 0, 0);
+        uint4 x = v[0];
+#pragma unroll
+        for (int s = 1; s < KM; ++s)
+            x = make_uint4(x.x ^ v[s].x, x.y ^ v[s].y, x.z ^ v[s].z, x.w ^ v[s].w);
+        dst[c] = x;
+    }
+}
+
 } // namespace
+
+hipError_t launch_stream_gather(const void *rows, long long nrows, int d, const int32_t *slot,
+                                int T, int k, void *out, hipStream_t st)
+{
+    if (T == 0)
+        return hipSuccess;
+    const int blocks = (T + 3) / 4;
+    const int d16 = d / 8; // bf16 rows: 8 values per 16-byte piece
+    const uint4 *r = static_cast<const uint4 *>(rows);
+    uint4 *o = static_cast<uint4 *>(out);
+    if (k <= 2)
+        stream_gather_kernel<2><<<blocks, 256, 0, st>>>(r, slot, T, k, d16, nrows, o);
+    else if (k <= 4)
+        stream_gather_kernel<4><<<blocks, 256, 0, st>>>(r, slot, T, k, d16, nrows, o);
+    else
+        stream_gather_kernel<8><<<blocks, 256, 0, st>>>(r, slot, T, k, d16, nrows, o);
+    return hipGetLastError();
+}
 
 hipError_t launch_stream_write(void *dst, size_t bytes, uint32_t value, hipStream_t st)
 {

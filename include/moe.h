@@ -348,6 +348,18 @@ int moe_stream_read(const void *src, size_t bytes, uint32_t *sink, void *stream)
  * Returns MOE_EINVAL for a bad pointer or size, MOE_EHIP on a launch error. */
 int moe_stream_write(void *dst, size_t bytes, uint32_t value, void *stream);
 
+/* Diagnostic, not a step of the layer: the combine's memory traffic without
+ * its arithmetic, out[t] = XOR over s < k of the 16-byte pieces of row
+ * slot[t, s] of rows (a slot outside [0, nrows) adds nothing), with the
+ * combine's access (one wavefront per token, non-temporal 16-byte gathers,
+ * all k of a piece in flight together for k <= 8), so that a caller can
+ * time the rate of that access beside moe_combine.
+ *   rows  [nrows, d] bf16 (device);  slot [T, k] int32 (device)
+ *   out   [T, d] bf16 out (device);  d % 8 == 0, k >= 1
+ * Returns MOE_EINVAL for a bad pointer or size, MOE_EHIP on a launch error. */
+int moe_stream_gather(const void *rows, int64_t nrows, int32_t d, const int32_t *slot,
+                      int64_t T, int32_t k, void *out, void *stream);
+
 /* Static string naming a status code (never NULL). */
 const char *moe_status_str(int status);
 

@@ -247,6 +247,19 @@ def test_stream_write_rejects_bad_arguments():
     assert _raw("moe_stream_write", None, ctypes.c_size_t(0), v, None) == api.MOE_OK
 
 
+def test_stream_gather_rejects_bad_arguments():
+    P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    good = P(1 << 20)
+    ok = (good, I64(10), I32(64), good, I64(4), I32(2), good, None)
+    assert _raw("moe_stream_gather", *ok[:2], I32(60), *ok[3:]) == api.MOE_EINVAL   # d % 8
+    assert _raw("moe_stream_gather", *ok[:5], I32(0), *ok[6:]) == api.MOE_EINVAL    # k < 1
+    assert _raw("moe_stream_gather", *ok[:3], None, *ok[4:]) == api.MOE_EINVAL      # slot
+    assert _raw("moe_stream_gather", *ok[:6], P((1 << 20) + 4), None) == api.MOE_EINVAL
+    assert _raw("moe_stream_gather", *ok[:4], I64(1 << 32), *ok[5:]) == api.MOE_EINVAL
+    # no tokens: accepted, nothing enqueued
+    assert _raw("moe_stream_gather", *ok[:4], I64(0), *ok[5:]) == api.MOE_OK
+
+
 def test_status_strings():
     L = api.lib()
     for st in (0, -1, -2, -3, -4, -5, 7):

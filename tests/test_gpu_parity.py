@@ -574,6 +574,29 @@ def test_stream_write_fills_every_word(nbytes):
     assert (got[n:] == 0).all()
 
 
+@pytest.mark.parametrize("k", [2, 8, 12])
+def test_stream_gather_xors_the_slotted_rows(k):
+    """The combine-pattern probe: out[t] is the XOR of the rows its slots
+    name, a slot outside [0, nrows) adding nothing (those slots point into
+    padding rows, so a missing bound shows as a wrong value)."""
+    T, d, nrows, pad = 300, 512, 700, 64
+    rng = np.random.default_rng(7 + k)
+    rows = rng.integers(-2 ** 15, 2 ** 15, (nrows + pad, d), dtype=np.int64).astype(np.int16)
+    slot = rng.integers(0, nrows, (T, k)).astype(np.int32)
+    pick = rng.random((T, k))
+    slot[pick < 0.1] = -1
+    slot[pick > 0.9] = nrows + rng.integers(0, pad, int((pick > 0.9).sum()))
+    want = np.zeros((T, d), np.int16)
+    for s in range(k):
+        m = (slot[:, s] >= 0) & (slot[:, s] < nrows)
+        want[m] ^= rows[slot[m, s]]
+    r = torch.from_numpy(rows).to(DEV).view(torch.bfloat16)
+    out = torch.empty(T, d, dtype=torch.bfloat16, device=DEV)
+    api.moe_stream_gather(r[:nrows], _i32(slot), out)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(out.view(torch.int16).cpu().numpy(), want)
+
+
 def test_fp8_decode_every_code():
     """The expert GEMM's E4M3 -> bf16 decode, through the diagnostic entry
     point: all 256 codes at unit and power-of-two scales, bit-exact."""
