@@ -38,8 +38,9 @@ int router_epad(int E) { return (E + 63) / 64 * 64; }
 // tensor), else E rounded up to 8 (a zero-padded copy in the workspace).
 int router_ldw(int E) { return (E + 7) / 8 * 8; }
 
-// Launch shape of the logit GEMM: 64-token tiles of BE experts, and K cut
-// into S slices when the tiles alone leave the chip short of workgroups
+// Launch shape of the logit GEMM: 64-token tiles of BE experts (taller ones
+// when there are many, below), and K cut into S slices when the tiles alone
+// leave the chip short of workgroups
 // (one per CU for BE = 256, eight waves; two per CU for BE = 128 or 64, four
 // waves): enough slices to fill it, at least four K steps each, at most 32.
 // BE is the widest of 256, 128, 64 (dividing E rounded up to 64) whose
@@ -95,7 +96,6 @@ int router_ksplit(int T, int E, int d) { return router_plan(T, E, d).sk; }
 bool router_partials(int T, int, int) { return T > 0; }
 
 namespace {
-
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
