@@ -663,13 +663,20 @@ TILE_ROWS = [1, 16, 17, 40, 56, 57, 96, 97, 128, 160, 161, 170, 176, 177, 192, 1
              257, 384, 400, 513, 0, 3]
 
 
-@pytest.mark.parametrize("fp8", [False, True])
-def test_expert_ffn_every_tile_shape(fp8):
+# (d, H, fp8): the launches estimate 24 M tiles (24 experts, 3,774 rows), so
+# d = H = 256 gives both GEMMs fewer tiles than CUs and the 64-column tiles;
+# H = 1408 gives the gate/up GEMM 24 x 11 tiles and its 128-column tiles;
+# d = 2816 gives the down GEMM 24 x 11 tiles and its 256-column tiles.
+TILE_SHAPES = [(256, 256, False), (256, 256, True), (256, 1408, False), (2816, 128, False)]
+
+
+@pytest.mark.parametrize("d,H,fp8", TILE_SHAPES)
+def test_expert_ffn_every_tile_shape(d, H, fp8):
     counts = np.array(TILE_ROWS, np.int32)
     E, n = len(counts), int(counts.sum())
-    cfg = MoEConfig("tile_rows", T=n, d=256, E=E, k=1, H=256, cf=INF, D=1, x_std=1.0,
+    cfg = MoEConfig("tile_rows", T=n, d=d, E=E, k=1, H=H, cf=INF, D=1, x_std=1.0,
                     wg_std=0.1, w_std=0.05, seed=18, dispatch_fp8=int(fp8))
-    print(f"\n[tile rows] fp8={fp8} E={E} rows={n}", flush=True)
+    print(f"\n[tile rows] d={d} H={H} fp8={fp8} E={E} rows={n}", flush=True)
     inp = make_inputs(cfg, DEV)
     shape = api.Shape.from_config(cfg)
     off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
