@@ -663,6 +663,12 @@ def main():
                             device_frac=round((traffic[s]["read"] / (read_gbs * 1e9)
                                                + traffic[s]["write"] / (write_gbs * 1e9)) / t, 4),
                             tflops=round(traffic[s]["flops"] / t / 1e12, 2))
+    # the whole layer against its roofline: each stage at the larger of its
+    # algorithmic bytes at the HBM peak and its flops at the bf16 matrix-core
+    # peak, summed over the stages
+    bound_ms = sum(max(traffic[s]["bytes"] / (HBM_PEAK_GBS * 1e9),
+                       traffic[s]["flops"] / (MFMA_BF16_PEAK_TFLOPS * 1e12)) for s in stages) * 1e3
+    layer_roof = {"bound_ms": round(bound_ms, 4), "frac": round(bound_ms / ms_step, 4)}
     # the combine against its own access pattern with no arithmetic
     per_stage["combine"]["gather_probe_ms"] = round(g_ms, 5)
     per_stage["combine"]["of_gather_probe"] = round(g_ms / stage_ms["combine"], 4)
@@ -723,6 +729,7 @@ def main():
         "device": {"read_gbs": round(read_gbs, 1), "write_gbs": round(write_gbs, 1)},
         "counts": counts,
         "roofline": roof,
+        "layer_roofline": layer_roof,
     }
     if cfg.D > 1 and cfg.cf == float("inf") and not args.no_rank_local:
         log(f"bench: rank-local expert GEMMs ({cfg.E // cfg.D} experts, {cfg.D}x tokens routed)")
