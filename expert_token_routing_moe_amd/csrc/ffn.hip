@@ -134,6 +134,19 @@ __device__ __forceinline__ uint2 quad_transpose_bf16(const float v[4], int c)
     return make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
 }
 
+// SiLU(g) * u ("MoE Expert Parallelism Sizing: Traffic, Capacity, Fabric",
+// the gated three-matrix expert) with the hardware base-2 exponential and
+// reciprocal: g * u / (1 + 2^(-g log2 e)).  Each is within about one unit in
+// the last place of fp32, far below the bf16 rounding of h that follows; the
+// IEEE division and range-reduced exponential took about half of the gate/up
+// epilogue.  Large negative g gives 2^(+inf) = inf and a product of 0, as the
+// exact function does.
+__device__ __forceinline__ float silu_mul(float g, float u)
+{
+    const float t = __builtin_amdgcn_exp2f(-g * 1.4426950408889634f);
+    return g * __builtin_amdgcn_rcpf(1.f + t) * u;
+}
+
 // A8: the A operand is E4M3 codes with one fp32 scale per row (FP8
 // dispatch); its fragments are widened to bf16 (exact) before the MFMA and
 // the row scale multiplies the fp32 sums in the epilogue.
@@ -505,8 +518,7 @@ __global__ __launch_bounds__(WM * WN * 64, MINB) void grouped_gemm_kernel(GemmAr
                 for (int q = 0; q < 4; ++q) {
                     float gt = acc0[i][j][q] * sr[q];
                     if constexpr (DUAL) {
-                        const float up = acc1[i][j][q] * sr[q];
-                        gt = gt / (1.f + expf(-gt)) * up; // SiLU(g) * u
+                        gt = silu_mul(gt, acc1[i][j][q] * sr[q]);
                     }
                     v[q] = gt;
                 }
