@@ -402,8 +402,10 @@ def summarize_rocprof(out_dir, workload):
             if not lab.startswith("moe::"):
                 continue
             key = (lab, int(r["Grid_Size"]))
-            per.setdefault(key, {}).setdefault(r["Dispatch_Id"], {})[r["Counter_Name"]] = \
-                float(r["Counter_Value"])
+            d = per.setdefault(key, {}).setdefault(r["Dispatch_Id"], {})
+            d[r["Counter_Name"]] = float(r["Counter_Value"])
+            if r.get("Start_Timestamp") and r.get("End_Timestamp"):  # ns, this dispatch
+                d["_dur_s"] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e9
         # the calibration copies are the run's last three copies
         return per, [v for _, v in sorted(copies)[-3:]]
 
@@ -453,7 +455,8 @@ def summarize_rocprof(out_dir, workload):
     mf_lines = []
     if mfma:
         mf_lines = ["| kernel | grid | launches | SQ_INSTS_MFMA | algorithmic | ratio "
-                    "| MFMA busy cycles | busy fraction |", "|---|---|---|---|---|---|---|---|"]
+                    "| MFMA busy cycles | busy fraction | clock GHz | PFLOP/s | of peak at that clock |",
+                    "|---|---|---|---|---|---|---|---|---|---|---|"]
         rl = bj.get("grouped_gemm_rank_local")
         for (lab, grid), d in mfma.items():
             if "grouped_gemm" not in lab:
@@ -470,9 +473,17 @@ def summarize_rocprof(out_dir, workload):
             inst = stt.mean(v["SQ_INSTS_MFMA"] for v in d.values())
             busy = stt.mean(v["SQ_VALU_MFMA_BUSY_CYCLES"] for v in d.values())
             act = stt.mean(v["GRBM_GUI_ACTIVE"] for v in d.values())
+            # the clock the chip held: GPU-active cycles of one XCD over the
+            # dispatch's own time; the matrix-core peak at that clock is
+            # 1024 SIMDs x 1024 flop per cycle (2.5 PFLOP/s at 2.4 GHz)
+            durs = [v["_dur_s"] for v in d.values() if v.get("_dur_s")]
+            dur = stt.mean(durs) if durs else float("nan")
+            clk = act / 8 / dur if durs else float("nan")
+            pf = alg * 16384 / dur / 1e15 if durs else float("nan")
             mf_lines.append(f"| `{lab}`{'' if layer else ' (rank-local share)'} | {grid} | {len(d)} "
                             f"| {inst:.4g} | {alg:.4g} | {inst / alg:.3f} | {busy:.4g} "
-                            f"| {busy / (1024 * act / 8):.3f} |")
+                            f"| {busy / (1024 * act / 8):.3f} | {clk / 1e9:.2f} | {pf:.3f} "
+                            f"| {pf * 1e15 / (1024 * 1024 * clk):.3f} |")
     R = "$R"
     cmd = f"python3 {R}/bench.py --workload {workload}"
     md = [f"# rocprofv3 summary: MoE layer kernels, {workload} workload", "",
@@ -500,7 +511,10 @@ def summarize_rocprof(out_dir, workload):
         md += ["Grouped-GEMM matrix-core counters per launch. Algorithmic MFMA instructions = flops / 16384",
                "(one `v_mfma_f32_16x16x32_bf16` is 16x16x32 multiply-adds); busy fraction =",
                "SQ_VALU_MFMA_BUSY_CYCLES over 1024 SIMDs x GRBM_GUI_ACTIVE / 8 (GRBM_GUI_ACTIVE read as",
-               "summed over the 8 XCDs).", "", *mf_lines, ""]
+               "summed over the 8 XCDs); clock = GRBM_GUI_ACTIVE / 8 over the dispatch's own start-to-end",
+               "time in the counter run (the clock the chip held under the kernel); PFLOP/s = algorithmic",
+               "flops over that time; of peak at that clock = PFLOP/s over 1024 SIMDs x 1024 flop x clock.",
+               "", *mf_lines, ""]
     return "\n".join(md), traffic
 
 

@@ -38,15 +38,21 @@ def _write_trace(path):
 
 
 def _write_counters(path, rows, compress=False):
+    """rows: (kernel, grid, counter, value) or (kernel, grid, counter, value,
+    dispatch id, start ns, end ns)."""
     os.makedirs(path)
-    fields = ["Dispatch_Id", "Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value"]
+    fields = ["Dispatch_Id", "Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value",
+              "Start_Timestamp", "End_Timestamp"]
     name = os.path.join(path, "run_counter_collection.csv")
     with (gzip.open(name + ".gz", "wt", newline="") if compress else open(name, "w", newline="")) as f:
         w = csv.DictWriter(f, fields)
         w.writeheader()
-        for i, (kname, grid, counter, value) in enumerate(rows):
-            w.writerow(dict(Dispatch_Id=i + 1, Kernel_Name=kname, Grid_Size=grid,
-                            Counter_Name=counter, Counter_Value=value))
+        for i, row in enumerate(rows):
+            kname, grid, counter, value = row[:4]
+            disp, t0, t1 = row[4:] if len(row) > 4 else (i + 1, 0, 0)
+            w.writerow(dict(Dispatch_Id=disp, Kernel_Name=kname, Grid_Size=grid,
+                            Counter_Name=counter, Counter_Value=value,
+                            Start_Timestamp=t0, End_Timestamp=t1))
 
 
 def test_summary_tables(tmp_path):
@@ -60,12 +66,18 @@ def test_summary_tables(tmp_path):
     _write_counters(str(out / "write"),
                     [(ROUTE, 1024, "WRITE_SIZE", 100.0), (GEMM_GU, 4096, "WRITE_SIZE", 200.0)]
                     + [(COPY, 65536, "WRITE_SIZE", 1048576.0)] * 3)
+    # matrix-core counters of one gate/up dispatch lasting 2 ms: 8 XCDs x
+    # 3.6e6 active cycles -> 1.8 GHz; busy 1024 SIMDs x 1.8e6 cycles -> 0.5
+    _write_counters(str(out / "mfma"),
+                    [(GEMM_GU, 4096, c, v, 7, 10_000_000, 12_000_000)
+                     for c, v in (("SQ_INSTS_MFMA", 1.25e8), ("SQ_VALU_MFMA_BUSY_CYCLES", 1024 * 1.8e6),
+                                  ("SQ_BUSY_CYCLES", 1.0e7), ("GRBM_GUI_ACTIVE", 8 * 3.6e6))])
     line = {"ms_per_step": 2.0, "value": 2048000.0, "config": {"d": 64, "H": 64},
             "copy_calibration_bytes": 1 << 30,
             "device": {"read_gbs": 7000.0, "write_gbs": 5000.0},
             "roofline": {},
             "stages": {"route": {"ms": 0.03, "gbs": 100.0, "tflops": 0.0},
-                       "gate_up": {"ms": 2.0, "gbs": 4.0, "tflops": 1.0}}}
+                       "gate_up": {"ms": 2.0, "gbs": 4.0, "tflops": 1000.0}}}
     (out / "trace.json").write_text("progress line\n" + json.dumps(line) + "\n")
     md, traffic = bench.summarize_rocprof(str(out), "tiny")
     # per-launch scaled megabytes: FETCH x2 (the copies read half), WRITE x1
@@ -82,3 +94,11 @@ def test_summary_tables(tmp_path):
     assert traffic["gate_up"]["write_bytes"] == 200 * 1024
     assert set(traffic) == {"gate_up"}                              # the router is no GEMM
     assert traffic["gate_up"]["source_digest"] == bench.kernel_source_digest()
+    # matrix cores: algorithmic instructions = 1 PFLOP/s x 2 ms / 16384 =
+    # 1.2207e8; 1 PFLOP/s over 1024 x 1024 flop x 1.8 GHz = 0.530
+    mrow = [r for r in md.splitlines() if r.startswith("| `moe::grouped_gemm") and r.count("|") == 12]
+    assert len(mrow) == 1, md
+    cells = [c.strip() for c in mrow[0].split("|")][1:-1]
+    assert cells[4] == "1.221e+08" and cells[5] == "1.024"
+    assert cells[7] == "0.500" and cells[8] == "1.80" and cells[9] == "1.000"
+    assert cells[10] == "0.530"
