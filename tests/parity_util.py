@@ -47,7 +47,11 @@ def gamma_p(m: int) -> float:
 
 
 def bits_to_f64(bits: np.ndarray) -> np.ndarray:
-    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    # any 16-bit pattern is accepted: rows a kernel leaves unwritten (padding
+    # past an expert's rows) may hold signalling NaNs, whose widening would
+    # otherwise raise numpy's invalid-value warning
+    with np.errstate(invalid="ignore"):
+        return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
 def t2f(t: torch.Tensor) -> np.ndarray:
