@@ -111,7 +111,8 @@ static int make_dims(const moe_shape *s, Dims *dm)
     // rows an expert is expected to hold: C, or the mean T*k/E when dropless
     const int64_t per_expert =
         C >= 0 ? C : ((int64_t)s->T * s->k + s->E - 1) / s->E;
-    dm->fp8_widen = s->dispatch_fp8 == 1 && per_expert >= kFp8WidenRows;
+    dm->mfma_bound = per_expert >= kMfmaBoundRows;
+    dm->fp8_widen = s->dispatch_fp8 == 1 && dm->mfma_bound;
     dm->nchunks = (s->T + kChunk - 1) / kChunk;
     return MOE_OK;
 }

@@ -557,6 +557,264 @@ __global__ __launch_bounds__(WM * WN * 64, MINB) void grouped_gemm_kernel(GemmAr
     }
 }
 
+// Ping-pong grouped GEMM, for shapes bound by the matrix cores (experts of
+// hundreds of rows and more).  The tile is 256 rows x 256 weight rows (gate/up:
+// 128 columns of W1 and of W3; down: 256 columns), as in the kernel above, and
+// each output's K sum runs in the same order, so the results are the same
+// bits.
+//
+// The eight waves form two groups of four, one wave of each on every SIMD;
+// group g owns rows [128g, 128g + 128), and wave q of a group owns the weight
+// columns 32q.. of W1 and of W3 (gate/up) or 64q.. (down).  The K walk goes in
+// units of 32, each two phases separated by workgroup barriers:
+//   X_u: group 0 multiplies unit u, group 1 reads unit u's fragments;
+//   Y_u: group 0 reads unit u + 1's fragments, group 1 multiplies unit u.
+// So on every SIMD one wave keeps the matrix cores busy while the other reads
+// LDS.  The direct-to-LDS loads go out from the reading group only: a load
+// issued between a wave's MFMAs held that wave up (a probe of this loop: 0.87
+// of the matrix-core peak at the held clock this way, 0.74 with the loads
+// spread between the MFMAs, 0.75 for the kernel above).
+//
+// LDS (all 160 KB): the weights in three 64-deep stages (128-byte row pieces,
+// as HBM wants them; 32 KB each), loaded by group 0; the tile's rows in four
+// 32-deep units (16 KB each), loaded by group 1.  Each phase then carries 16 KB
+// of loads, issued by the group that reads in it (a probe took longer phases
+// where 32 KB went out in one).  Weight stage s + 3 goes into stage s's slot,
+// half at the start of Y_{2s+1} (once both groups have read unit 2s + 1) and
+// half at the start of Y_{2s+2}; row unit u + 3 goes into unit u - 1's slot at
+// the start of X_u.
+__device__ __forceinline__ void pp_barrier()
+{
+    // keeps the compiler from moving any instruction across the phase boundary
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int BN, bool DUAL>
+__global__ __launch_bounds__(512, 1) void grouped_gemm_pp_kernel(GemmArgs g)
+{
+    constexpr int BM = 256;
+    constexpr int NB = DUAL ? 2 * BN : BN;      // weight rows per tile
+    static_assert(NB == 256, "256 weight rows per tile");
+    constexpr int B_STAGE = NB * 64 * 2;        // 32 KB: 64-deep weight stage
+    constexpr int A_UNIT = BM * 32 * 2;         // 16 KB: 32-deep row unit
+    constexpr int A_BASE = 3 * B_STAGE;         // row units after the three weight stages
+    constexpr int RING = A_BASE + 4 * A_UNIT;   // 160 KB: the whole LDS
+    constexpr int LDC = BN + 16;                // epilogue row pitch (elements)
+    constexpr int SMEM = RING > BM * LDC * 2 ? RING : BM * LDC * 2;
+    constexpr int CT = DUAL ? 2 : 4;            // 16-column tiles per wave and matrix
+    __shared__ __attribute__((aligned(1024))) char smem[SMEM];
+    // the decoded tile lives in the ring's first bytes until every wave has it
+    int *s_tile = reinterpret_cast<int *>(smem);
+
+    if (threadIdx.x < 64)
+        decode_work<BM>(g, g.N / BN, s_tile, s_tile + 1);
+    __syncthreads();
+    const int e = __builtin_amdgcn_readfirstlane(s_tile[0]);
+    const int local = __builtin_amdgcn_readfirstlane(s_tile[1]);
+    __syncthreads();
+    if (e < 0)
+        return;
+    const int cnt = __builtin_amdgcn_readfirstlane(max(g.row_count[e], 0));
+    const int mt = (cnt + BM - 1) / BM;
+    const int n_tile = local / mt, m_tile = local % mt;
+    const int tile_rows = (cnt + mt - 1) / mt;
+    const int m0 = m_tile * tile_rows;
+    const int offset = __builtin_amdgcn_readfirstlane(g.row_offset[e]);
+    const int rows_valid = offset < 0 ? 0
+                                      : (int)min((long long)min(tile_rows, cnt - m0),
+                                                 g.rows - ((long long)offset + m0));
+    if (rows_valid <= 0)
+        return;
+    const size_t row0 = (size_t)offset + m0;
+    const int n0 = n_tile * BN;
+    const int N = g.N, K = g.K;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave >> 2, q = wave & 3;
+
+    // Loads of wave q of its group, load l: L = 4 l + q.
+    //  group 0, weight stage (l < 8): rows [8 L, 8 L + 8), lane i writes piece
+    //    i % 8 of row i / 8 (source piece (i % 8) ^ swz<8>(row));
+    //  group 1, row unit (l < 4): rows [16 L, 16 L + 16), lane i writes piece
+    //    i % 4 of row i / 4 (source piece (i % 4) ^ swz<4>(row)); rows past the
+    //    tile's end read row 0 of the tile (never stored).
+    const char *src[8];
+#pragma unroll
+    for (int l = 0; l < 8; ++l) {
+        const int L = 4 * l + q;
+        if (grp == 0) {
+            const int r = 8 * L + lane / 8;
+            const int piece = (lane % 8) ^ swz<8>(r);
+            const uint16_t *base = (DUAL && r >= BN) ? g.B1 : g.B0;
+            const int rr = (DUAL && r >= BN) ? r - BN : r;
+            src[l] = reinterpret_cast<const char *>(base + ((size_t)e * N + n0 + rr) * K + piece * 8);
+        } else {
+            const int r = 16 * (L & 15) + lane / 4;
+            const int piece = (lane % 4) ^ swz<4>(r);
+            const int rr = r < rows_valid ? r : 0;
+            src[l] = reinterpret_cast<const char *>(
+                reinterpret_cast<const uint16_t *>(g.A) + (row0 + rr) * K + piece * 8);
+        }
+    }
+    // the K walk, rotated as in the kernel above (in 64-deep steps)
+    const int S = K / 64, U = 2 * S;
+    const int krot = g.rot ? (n_tile * 5) % S : 0;
+    const uint32_t lds_base = (uint32_t)(uintptr_t)(LDS_AS char *)smem;
+    auto issue_b = [&](int s, int half) { // group 0: half (0, 1) of weight stage s
+        const int ks = s + krot < S ? s + krot : s + krot - S;
+        const uint32_t st = lds_base + (s % 3) * B_STAGE;
+#pragma unroll
+        for (int l = 4 * half; l < 4 * half + 4; ++l)
+            dma16<true>(src[l] + (size_t)ks * 128, st + (4 * l + q) * 1024);
+    };
+    auto issue_a = [&](int u) { // group 1: row unit u
+        const int s = u >> 1, ks = s + krot < S ? s + krot : s + krot - S;
+        const uint32_t st = lds_base + A_BASE + (u & 3) * A_UNIT;
+#pragma unroll
+        for (int l = 0; l < 4; ++l)
+            dma16(src[l] + (size_t)ks * 128 + (u & 1) * 64, st + (4 * l + q) * 1024);
+    };
+
+    // fragments: rows 128 grp + 16 i + (lane & 15) and weight rows nb(j) +
+    // (lane & 15); the swizzles depend on the lane only
+    const int a_lane = A_BASE + (128 * grp + (lane & 15)) * 64 +
+                       (((lane >> 4) ^ swz<4>(lane & 15)) << 4);
+    const int b_lane = (lane & 15) * 128;
+    auto b_row = [&](int j) { // first weight row of fragment j of this wave
+        return DUAL ? (j < 2 ? 32 * q + 16 * j : BN + 32 * q + 16 * (j - 2)) : 64 * q + 16 * j;
+    };
+    bf16x8 af[8], bf[4];
+    floatx4 acc[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+    // read: issue the fragment reads of unit u (waited on with read_wait, so
+    // that the phase's loads can go out while they are in flight)
+    auto read = [&](int u) {
+        const char *As = smem + a_lane + (u & 3) * A_UNIT;
+        const char *Bs = smem + b_lane + ((u >> 1) % 3) * B_STAGE +
+                         (((4 * (u & 1) + (lane >> 4)) ^ (lane & 7)) << 4);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            af[i] = *reinterpret_cast<const bf16x8 *>(As + i * 16 * 64);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            bf[j] = *reinterpret_cast<const bf16x8 *>(Bs + b_row(j) * 128);
+    };
+    auto read_wait = [&]() {
+        __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8)); // lgkmcnt(0)
+    };
+    auto mult = [&]() {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+    };
+
+    // prologue: weight stages 0..2, row units 0..3; unit 0 in place
+    if (grp == 0) {
+        for (int t = 0; t < 3 && t < S; ++t) {
+            issue_b(t, 0);
+            issue_b(t, 1);
+        }
+        wait_vmcnt(8 * (min(S, 3) - 1));
+    } else {
+        for (int u = 0; u < 4 && u < U; ++u)
+            issue_a(u);
+        wait_vmcnt(4 * (min(U, 4) - 1));
+    }
+    pp_barrier();
+    if (grp == 0) {
+        read(0);
+        read_wait();
+    }
+    pp_barrier();
+    // The groups run separate loops with the same sequence of barriers, so
+    // that no fragment set is merged across branches.
+    if (grp == 0) {
+        for (int u = 0; u < U; ++u) {
+            mult(); // X_u
+            if (u & 1) // weight stage s + 1 = (u + 1) / 2 for unit u + 1; s + 2 may be in flight
+                wait_vmcnt((u >> 1) + 2 < S ? 8 : 0);
+            pp_barrier();
+            // Y_u: the fragment reads of unit u + 1 go out first, then the
+            // loads: first half of stage s + 3 (u = 2s + 1), second half of
+            // stage s + 2 (u = 2s, s >= 1)
+            if (u + 1 < U)
+                read(u + 1);
+            if ((u & 1) && (u >> 1) + 3 < S)
+                issue_b((u >> 1) + 3, 0);
+            else if (!(u & 1) && u >= 2 && (u >> 1) + 2 < S)
+                issue_b((u >> 1) + 2, 1);
+            read_wait();
+            pp_barrier();
+        }
+    } else {
+        for (int u = 0; u < U; ++u) {
+            read(u); // X_u, then unit u + 3 into unit u - 1's slot
+            if (u >= 1 && u + 3 < U)
+                issue_a(u + 3);
+            read_wait();
+            const int later = min(U - 1, u + 3) - (u + 1); // row unit u + 1 in place
+            if (later >= 2)
+                wait_vmcnt(8);
+            else if (later == 1)
+                wait_vmcnt(4);
+            else
+                wait_vmcnt(0);
+            pp_barrier();
+            mult(); // Y_u
+            pp_barrier();
+        }
+    }
+
+    // Epilogue through LDS (the ring is free: every unit has been read), as
+    // in the kernel above.
+    __syncthreads();
+    uint16_t *Cs = reinterpret_cast<uint16_t *>(smem);
+    const int c4 = lane & 3;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int mq = 128 * grp + 16 * i + 4 * (lane >> 4); // row of q = 0
+        float sr[4] = {1.f, 1.f, 1.f, 1.f};
+        if (g.a_scale) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                sr[r] = mq + r < rows_valid ? g.a_scale[row0 + mq + r] : 0.f;
+        }
+        const int m = mq + c4;
+#pragma unroll
+        for (int j = 0; j < CT; ++j) {
+            float v[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float gt = acc[i][j][r] * sr[r];
+                if constexpr (DUAL)
+                    gt = silu_mul(gt, acc[i][2 + j][r] * sr[r]);
+                v[r] = gt;
+            }
+            const uint2 o = quad_transpose_bf16(v, c4);
+            const int n = (DUAL ? 32 * q : 64 * q) + 16 * j + 4 * ((lane & 15) >> 2);
+            *reinterpret_cast<uint2 *>(Cs + m * LDC + n) = o;
+        }
+    }
+    __syncthreads();
+    constexpr int CPR = BN / 8; // 16-byte pieces per output row
+    for (int c = tid; c < rows_valid * CPR; c += 512) {
+        const int r = c / CPR, cc = c % CPR;
+        store_nt(reinterpret_cast<uint4 *>(g.out + (row0 + r) * N + n0 + cc * 8),
+                 *reinterpret_cast<const uint4 *>(Cs + r * LDC + cc * 8));
+    }
+}
+
 #ifndef MOE_GEMM_BK
 #define MOE_GEMM_BK 64
 #endif
@@ -668,12 +926,25 @@ static bool few_tiles(const Dims &dm, int N, int BN, int BM)
     return mt * (N / BN) < kNarrowBelow;
 }
 
+#ifndef MOE_GEMM_PP
+#define MOE_GEMM_PP 1
+#endif
+// The ping-pong kernel takes the bf16 launches of shapes bound by the matrix
+// cores whose tiles fill the chip.
+static bool use_pp(const Dims &dm, int N, int BN)
+{
+    return MOE_GEMM_PP && dm.mfma_bound && N % BN == 0 && !few_tiles(dm, N, BN, 256);
+}
+
 template <bool A8>
 static void launch_gate_up_t(const Dims &dm, const GemmArgs &a, long long mtiles_max,
                              hipStream_t st)
 {
     constexpr int threads = kWM1 * kWN1 * 64;
-    if (dm.H % kBN1 == 0 && !few_tiles(dm, dm.H, kBN1, kBM1))
+    if (!A8 && use_pp(dm, dm.H, 128))
+        grouped_gemm_pp_kernel<128, true>
+            <<<xcd_grid((int)(mtiles_max * (dm.H / 128))), 512, 0, st>>>(a);
+    else if (dm.H % kBN1 == 0 && !few_tiles(dm, dm.H, kBN1, kBM1))
         // H is a multiple of 64; the wide tile needs a multiple of kBN1
         grouped_gemm_kernel<kBM1, kBN1, kBK, kRing1, kMinB1, kWM1, kWN1, true, A8>
             <<<xcd_grid((int)(mtiles_max * (dm.H / kBN1))), threads, 0, st>>>(a);
@@ -722,7 +993,10 @@ hipError_t launch_down(const Dims &dm, const uint16_t *h, const int32_t *expert_
     GemmArgs a{h, nullptr, expert_offset, expert_kept, w2, nullptr, expert_out, dm.E, dm.d, dm.H,
                MOE_GEMM_ROT_DN ? rotate_k(dm.H) : 0, dm.send_rows};
     constexpr int threads = kWM2 * kWN2 * 64;
-    if (dm.d % kBN2 == 0 && !few_tiles(dm, dm.d, kBN2, kBM2))
+    if (use_pp(dm, dm.d, 256))
+        grouped_gemm_pp_kernel<256, false>
+            <<<xcd_grid((int)(mtiles_max * (dm.d / 256))), 512, 0, st>>>(a);
+    else if (dm.d % kBN2 == 0 && !few_tiles(dm, dm.d, kBN2, kBM2))
         grouped_gemm_kernel<kBM2, kBN2, kBK, kRing2, kMinB2, kWM2, kWN2, false, false>
             <<<xcd_grid((int)(mtiles_max * (dm.d / kBN2))), threads, 0, st>>>(a);
     else
@@ -758,6 +1032,7 @@ hipError_t launch_shared_expert(const Dims &dm, const uint16_t *x, const uint16_
     ds.send_rows = dm.T;
     ds.fp8 = 0;
     ds.fp8_widen = false;
+    ds.mfma_bound = dm.T >= kMfmaBoundRows;
     hipError_t e = launch_gate_up(ds, x, nullptr, rows, rows + 2, w1s, w3s, hs, nullptr, st);
     if (e == hipSuccess)
         e = launch_down(ds, hs, rows, rows + 2, w2s, shared_out, st);

@@ -112,13 +112,16 @@ struct Dims {
     int64_t capacity;  // C, or -1 when dropless
     int64_t send_rows; // E*C or T*k
     int nchunks;       // ceil(T / kChunk)
+    // An expert is expected to hold at least kMfmaBoundRows rows: the
+    // grouped GEMMs are then bound by the matrix cores and take the
+    // ping-pong kernel.
+    bool mfma_bound;
     // E4M3 rows are widened to bf16 in a separate pass before the gate/up
-    // GEMM (given a workspace) when an expert is expected to hold at least
-    // kFp8WidenRows rows: there the GEMM is bound by the matrix cores, and
-    // the bf16 loop runs faster than the loop that widens in registers.
+    // GEMM (given a workspace) on such shapes: the bf16 loop runs faster
+    // than the loop that widens in registers.
     bool fp8_widen;
 };
-constexpr int64_t kFp8WidenRows = 512;
+constexpr int64_t kMfmaBoundRows = 512;
 
 // Byte offsets of each region inside the caller's workspace.
 struct Workspace {
