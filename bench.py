@@ -334,9 +334,12 @@ def _kernel_label(name):
 
 
 def _gemm_stage(label):
-    """'gate_up' or 'down' for a grouped GEMM kernel label (its DUAL argument)."""
+    """'gate_up' or 'down' for a grouped GEMM kernel label (its DUAL argument:
+    the eighth of the ring kernel's template arguments, the second of the
+    ping-pong kernel's)."""
     args = label[label.index("<") + 1:label.rindex(">")].split(",")
-    return "gate_up" if args[7].strip() == "true" else "down"
+    dual = args[1] if "grouped_gemm_pp_kernel" in label else args[7]
+    return "gate_up" if dual.strip() == "true" else "down"
 
 
 def _stage_of(label):

@@ -55,6 +55,15 @@ def _write_counters(path, rows, compress=False):
                             Start_Timestamp=t0, End_Timestamp=t1))
 
 
+def test_gemm_stage_of_both_kernels():
+    assert bench._gemm_stage(GEMM_GU) == "gate_up"
+    assert bench._gemm_stage(GEMM_GU.replace("true, false>", "false, false>")) == "down"
+    pp = "void moe::(anonymous namespace)::grouped_gemm_pp_kernel<{}, {}>(moe::(anonymous namespace)::GemmArgs)"
+    assert bench._gemm_stage(bench._kernel_label(pp.format(128, "true"))) == "gate_up"
+    assert bench._gemm_stage(bench._kernel_label(pp.format(256, "false"))) == "down"
+    assert bench._stage_of(bench._kernel_label(pp.format(256, "false"))) == "down"
+
+
 def test_summary_tables(tmp_path):
     out = tmp_path / "run"
     os.makedirs(out)
