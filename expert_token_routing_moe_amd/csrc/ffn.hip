@@ -688,123 +688,145 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_pp_kernel(GemmArgs g)
     auto b_row = [&](int j) { // first weight row of fragment j of this wave
         return DUAL ? (j < 2 ? 32 * q + 16 * j : BN + 32 * q + 16 * (j - 2)) : 64 * q + 16 * j;
     };
-    bf16x8 af[8], bf[4];
-    floatx4 acc[8][4];
+    uint16_t *Cs = reinterpret_cast<uint16_t *>(smem); // the epilogue's staging
+    // The loop and the epilogue's first half for a wave whose group holds NA
+    // non-empty 16-row slices (a compile-time value, so no MFMA or fragment
+    // read sits under a branch); slices past NA are neither read nor
+    // multiplied.  The sequence of barriers does not depend on NA.
+    auto body = [&](auto na_const) {
+        constexpr int NA = decltype(na_const)::value;
+        bf16x8 af[NA > 0 ? NA : 1], bf[4];
+        floatx4 acc[NA > 0 ? NA : 1][4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-    // read: issue the fragment reads of unit u (waited on with read_wait, so
-    // that the phase's loads can go out while they are in flight)
-    auto read = [&](int u) {
-        const char *As = smem + a_lane + (u & 3) * A_UNIT;
-        const char *Bs = smem + b_lane + ((u >> 1) % 3) * B_STAGE +
-                         (((4 * (u & 1) + (lane >> 4)) ^ (lane & 7)) << 4);
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            af[i] = *reinterpret_cast<const bf16x8 *>(As + i * 16 * 64);
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            bf[j] = *reinterpret_cast<const bf16x8 *>(Bs + b_row(j) * 128);
-    };
-    auto read_wait = [&]() {
-        __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8)); // lgkmcnt(0)
-    };
-    auto mult = [&]() {
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
+        for (int i = 0; i < NA; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
-    };
-
-    // prologue: weight stages 0..2, row units 0..3; unit 0 in place
-    if (grp == 0) {
-        for (int t = 0; t < 3 && t < S; ++t) {
-            issue_b(t, 0);
-            issue_b(t, 1);
-        }
-        wait_vmcnt(8 * (min(S, 3) - 1));
-    } else {
-        for (int u = 0; u < 4 && u < U; ++u)
-            issue_a(u);
-        wait_vmcnt(4 * (min(U, 4) - 1));
-    }
-    pp_barrier();
-    if (grp == 0) {
-        read(0);
-        read_wait();
-    }
-    pp_barrier();
-    // The groups run separate loops with the same sequence of barriers, so
-    // that no fragment set is merged across branches.
-    if (grp == 0) {
-        for (int u = 0; u < U; ++u) {
-            mult(); // X_u
-            if (u & 1) // weight stage s + 1 = (u + 1) / 2 for unit u + 1; s + 2 may be in flight
-                wait_vmcnt((u >> 1) + 2 < S ? 8 : 0);
-            pp_barrier();
-            // Y_u: the fragment reads of unit u + 1 go out first, then the
-            // loads: first half of stage s + 3 (u = 2s + 1), second half of
-            // stage s + 2 (u = 2s, s >= 1)
-            if (u + 1 < U)
-                read(u + 1);
-            if ((u & 1) && (u >> 1) + 3 < S)
-                issue_b((u >> 1) + 3, 0);
-            else if (!(u & 1) && u >= 2 && (u >> 1) + 2 < S)
-                issue_b((u >> 1) + 2, 1);
-            read_wait();
-            pp_barrier();
-        }
-    } else {
-        for (int u = 0; u < U; ++u) {
-            read(u); // X_u, then unit u + 3 into unit u - 1's slot
-            if (u >= 1 && u + 3 < U)
-                issue_a(u + 3);
-            read_wait();
-            const int later = min(U - 1, u + 3) - (u + 1); // row unit u + 1 in place
-            if (later >= 2)
-                wait_vmcnt(8);
-            else if (later == 1)
-                wait_vmcnt(4);
-            else
-                wait_vmcnt(0);
-            pp_barrier();
-            mult(); // Y_u
-            pp_barrier();
-        }
-    }
-
-    // Epilogue through LDS (the ring is free: every unit has been read), as
-    // in the kernel above.
-    __syncthreads();
-    uint16_t *Cs = reinterpret_cast<uint16_t *>(smem);
-    const int c4 = lane & 3;
+                acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+        // read: issue the fragment reads of unit u (waited on with read_wait,
+        // so that the phase's loads can go out while they are in flight)
+        auto read = [&](int u) {
+            if constexpr (NA > 0) {
+                const char *As = smem + a_lane + (u & 3) * A_UNIT;
+                const char *Bs = smem + b_lane + ((u >> 1) % 3) * B_STAGE +
+                                 (((4 * (u & 1) + (lane >> 4)) ^ (lane & 7)) << 4);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int mq = 128 * grp + 16 * i + 4 * (lane >> 4); // row of q = 0
-        float sr[4] = {1.f, 1.f, 1.f, 1.f};
-        if (g.a_scale) {
+                for (int i = 0; i < NA; ++i)
+                    af[i] = *reinterpret_cast<const bf16x8 *>(As + i * 16 * 64);
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                sr[r] = mq + r < rows_valid ? g.a_scale[row0 + mq + r] : 0.f;
-        }
-        const int m = mq + c4;
-#pragma unroll
-        for (int j = 0; j < CT; ++j) {
-            float v[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                float gt = acc[i][j][r] * sr[r];
-                if constexpr (DUAL)
-                    gt = silu_mul(gt, acc[i][2 + j][r] * sr[r]);
-                v[r] = gt;
+                for (int j = 0; j < 4; ++j)
+                    bf[j] = *reinterpret_cast<const bf16x8 *>(Bs + b_row(j) * 128);
             }
-            const uint2 o = quad_transpose_bf16(v, c4);
-            const int n = (DUAL ? 32 * q : 64 * q) + 16 * j + 4 * ((lane & 15) >> 2);
-            *reinterpret_cast<uint2 *>(Cs + m * LDC + n) = o;
+        };
+        auto read_wait = [&]() {
+            __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8)); // lgkmcnt(0)
+        };
+        auto mult = [&]() {
+#pragma unroll
+            for (int i = 0; i < NA; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] =
+                        __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+        };
+        // prologue: weight stages 0..2, row units 0..3; unit 0 in place
+        if (grp == 0) {
+            for (int t = 0; t < 3 && t < S; ++t) {
+                issue_b(t, 0);
+                issue_b(t, 1);
+            }
+            wait_vmcnt(8 * (min(S, 3) - 1));
+        } else {
+            for (int u = 0; u < 4 && u < U; ++u)
+                issue_a(u);
+            wait_vmcnt(4 * (min(U, 4) - 1));
         }
+        pp_barrier();
+        if (grp == 0) {
+            read(0);
+            read_wait();
+        }
+        pp_barrier();
+        // The groups run separate loops with the same sequence of barriers, so
+        // that no fragment set is merged across branches.
+        if (grp == 0) {
+            for (int u = 0; u < U; ++u) {
+                mult(); // X_u
+                if (u & 1) // weight stage s + 1 = (u + 1) / 2 for unit u + 1; s + 2 may be in flight
+                    wait_vmcnt((u >> 1) + 2 < S ? 8 : 0);
+                pp_barrier();
+                // Y_u: the fragment reads of unit u + 1 go out first, then the
+                // loads: first half of stage s + 3 (u = 2s + 1), second half of
+                // stage s + 2 (u = 2s, s >= 1)
+                if (u + 1 < U)
+                    read(u + 1);
+                if ((u & 1) && (u >> 1) + 3 < S)
+                    issue_b((u >> 1) + 3, 0);
+                else if (!(u & 1) && u >= 2 && (u >> 1) + 2 < S)
+                    issue_b((u >> 1) + 2, 1);
+                read_wait();
+                pp_barrier();
+            }
+        } else {
+            for (int u = 0; u < U; ++u) {
+                read(u); // X_u, then unit u + 3 into unit u - 1's slot
+                if (u >= 1 && u + 3 < U)
+                    issue_a(u + 3);
+                read_wait();
+                const int later = min(U - 1, u + 3) - (u + 1); // row unit u + 1 in place
+                if (later >= 2)
+                    wait_vmcnt(8);
+                else if (later == 1)
+                    wait_vmcnt(4);
+                else
+                    wait_vmcnt(0);
+                pp_barrier();
+                mult(); // Y_u
+                pp_barrier();
+            }
+        }
+
+        // Epilogue through LDS (the ring is free: every unit has been read), as
+        // in the kernel above.
+        __syncthreads();
+        const int c4 = lane & 3;
+#pragma unroll
+        for (int i = 0; i < NA; ++i) {
+            const int mq = 128 * grp + 16 * i + 4 * (lane >> 4); // row of q = 0
+            float sr[4] = {1.f, 1.f, 1.f, 1.f};
+            if (g.a_scale) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    sr[r] = mq + r < rows_valid ? g.a_scale[row0 + mq + r] : 0.f;
+            }
+            const int m = mq + c4;
+#pragma unroll
+            for (int j = 0; j < CT; ++j) {
+                float v[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float gt = acc[i][j][r] * sr[r];
+                    if constexpr (DUAL)
+                        gt = silu_mul(gt, acc[i][2 + j][r] * sr[r]);
+                    v[r] = gt;
+                }
+                const uint2 o = quad_transpose_bf16(v, c4);
+                const int n = (DUAL ? 32 * q : 64 * q) + 16 * j + 4 * ((lane & 15) >> 2);
+                *reinterpret_cast<uint2 *>(Cs + m * LDC + n) = o;
+            }
+        }
+    };
+    // non-empty slices of this wave's group
+    const int g_rows = min(max(rows_valid - 128 * grp, 0), 128);
+    switch ((g_rows + 15) / 16) {
+    case 0: body(std::integral_constant<int, 0>{}); break;
+    case 1: body(std::integral_constant<int, 1>{}); break;
+    case 2: body(std::integral_constant<int, 2>{}); break;
+    case 3: body(std::integral_constant<int, 3>{}); break;
+    case 4: body(std::integral_constant<int, 4>{}); break;
+    case 5: body(std::integral_constant<int, 5>{}); break;
+    case 6: body(std::integral_constant<int, 6>{}); break;
+    case 7: body(std::integral_constant<int, 7>{}); break;
+    default: body(std::integral_constant<int, 8>{}); break;
     }
     __syncthreads();
     constexpr int CPR = BN / 8; // 16-byte pieces per output row

@@ -703,22 +703,23 @@ def test_expert_ffn_every_tile_shape(d, H, fp8):
                               got[lo:lo + m], **rows)
 
 
-# Expert rows for the two grouped-GEMM kernels: an empty expert, one row (the
-# second row group of its tile empty), 255/256/257 rows, and experts cut into
-# 3 and 8 equal M tiles (513, 700 and 2,018 rows); 4,000 rows in all.
-PP_ROWS = [0, 1, 255, 256, 257, 513, 700, 2018]
+# Expert rows for the two grouped-GEMM kernels: an empty expert; tiles whose
+# second 128-row group holds 0..8 non-empty 16-row slices (1, 40, 145, 177,
+# 193, 209, 255, 256 rows, and 257 rows cut into two tiles of 129); experts cut
+# into 3 and 8 equal M tiles (513, 700 and 2,018 rows); 4,764 rows in all.
+PP_ROWS = [0, 1, 40, 145, 177, 193, 209, 255, 256, 257, 513, 700, 2018]
 
 
 def test_pingpong_gemm_matches_the_ring_kernel():
     """The ping-pong kernel (shapes where an expert is expected to hold >= 512
     rows) and the ring kernel give the same bits on the same rows: a shape of
-    4,096 tokens (512 per expert) takes the first, one of 4,000 tokens (500
-    per expert) the second, on the same send buffer, offsets and counts.  The
-    down GEMM's K walk is rotated (H = 2048, a 4 KB weight-row pitch).  Three
+    6,656 tokens (512 per expert) takes the first, one of 4,764 tokens (367 per
+    expert) the second, on the same send buffer, offsets and counts.  The down
+    GEMM's K walk is rotated (H = 2048, a 4 KB weight-row pitch).  Three
     experts are also checked against the oracle."""
     counts = np.array(PP_ROWS, np.int32)
     E, n = len(counts), int(counts.sum())
-    cfg = MoEConfig("pingpong", T=4096, d=4096, E=E, k=1, H=2048, cf=INF, D=1, x_std=1.0,
+    cfg = MoEConfig("pingpong", T=512 * E, d=4096, E=E, k=1, H=2048, cf=INF, D=1, x_std=1.0,
                     wg_std=0.1, w_std=0.02, seed=29)
     print(f"\n[pingpong] d={cfg.d} H={cfg.H} E={E} rows={n}", flush=True)
     inp = make_inputs(cfg, DEV)
@@ -740,7 +741,7 @@ def test_pingpong_gemm_matches_the_ring_kernel():
     x = bf16_bits(inp["x"])
     w1, w3, w2 = (bf16_bits(inp[k]) for k in ("w1", "w3", "w2"))
     rng = np.random.default_rng(5)
-    for e in (1, 4, 7):
+    for e in (1, 5, 12):
         lo, m = int(off[e]), int(counts[e])
         r = np.sort(rng.choice(m, min(m, 24), replace=False)) + lo
         check_expert_rows(f"expert {e} ({m} rows)", w1[e], w3[e], w2[e], hp[r], op[r],
