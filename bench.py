@@ -74,11 +74,22 @@ def stage_traffic(cfg, st, touched):
     return rec
 
 
+def _code_only(text):
+    """Source text without comments and blank space: what the compiler sees."""
+    import re
+
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_digest():
+    """Digest of the grouped GEMM's sources, comments left out, so that the
+    stored counter bytes stay valid across comment edits."""
     h = hashlib.sha256()
     for name in ("ffn.hip", "moe_internal.hpp", "ring.hpp"):
-        with open(os.path.join(ROOT, "expert_token_routing_moe_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "expert_token_routing_moe_amd", "csrc", name)) as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -35,6 +35,10 @@
 // layout into 8-byte row pieces, converted to bf16 by v_cvt_pk_bf16_f32; they
 // are gathered in LDS (the ring is free by then) and leave as 16-byte
 // non-temporal stores (the next kernel is the only reader).
+//
+// Shapes bound by the matrix cores (experts of hundreds of rows) take a
+// second kernel with the same tiles and the same bits, whose two wave groups
+// alternate between fragment reads and MFMAs (grouped_gemm_pp_kernel below).
 #include <algorithm>
 #include <type_traits>
 

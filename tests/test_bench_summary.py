@@ -111,3 +111,10 @@ def test_summary_tables(tmp_path):
     assert cells[4] == "1.221e+08" and cells[5] == "1.024"
     assert cells[7] == "0.500" and cells[8] == "1.80" and cells[9] == "1.000"
     assert cells[10] == "0.530"
+
+
+def test_source_digest_ignores_comments():
+    code = "int f(int a) { return a + 1; }\n"
+    commented = "// what f does\nint f(int a) /* one more */ { return a + 1; } // trailing\n"
+    assert bench._code_only(code) == bench._code_only(commented)
+    assert bench._code_only(code) != bench._code_only(code.replace("+ 1", "+ 2"))
