@@ -12,10 +12,11 @@
 // products are exact in fp32 and accumulate in fp32
 // (v_mfma_f32_16x16x32_bf16).
 //
-// Selection, one wavefront per token: k rounds of a wave-wide maximum of
-// order-preserving 32-bit value images, the winner being the lowest expert
-// index that holds the maximum (ballots), a softmax over the kept logits,
-// optionally within the token's best expert groups.
+// Selection, one wavefront per token, each lane holding a run of
+// consecutive experts: k rounds of a wave-wide maximum of order-preserving
+// 32-bit value images, the winner being the lowest expert index that holds
+// the maximum (one ballot and one lane read), then a softmax over the kept
+// logits, optionally within the token's best expert groups.
 //
 // Every workgroup stores its fp32 partial tile; a second launch, one
 // wavefront per token, sums a token's partials in slice order (a fixed
@@ -128,11 +129,13 @@ __device__ __forceinline__ float key_value(uint32_t u)
 }
 
 // v = max(v, v of the lane that DPP control CTRL selects), for the rows in
-// ROW_MASK; a lane without a source keeps its own value.
+// ROW_MASK; a lane outside them, or without a source, takes 0 from the move,
+// which leaves its own value (0 is the identity of the unsigned maximum, so
+// the move folds into one DPP maximum instruction).
 template <int CTRL, int ROW_MASK>
 __device__ __forceinline__ uint32_t max_dpp(uint32_t v)
 {
-    const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, ROW_MASK, 0xF, false);
+    const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xF, true);
     return o > v ? o : v;
 }
 
@@ -169,14 +172,15 @@ __device__ __forceinline__ void lds_wait()
 }
 
 // KeepTopK + softmax of one token by one wavefront.  Lane l holds the
-// logits (bias included) of experts l, l+64, ... in h[0..V); experts >= E
-// are ignored.  Group limit ("MoE Expert Parallelism Sizing: Traffic,
-// Capacity, Fabric": at most M nodes per token, Megatron's group-limited
-// routing), when G > 1 and M < G: the E experts form G contiguous groups;
-// each group's score is its best logit (LDS atomic max of the
-// order-preserving key), the M best groups are picked by M wave arg-max
-// rounds (ties to the lower group), and the other groups' experts are
-// retired before KeepTopK.  gs/allow: this wave's LDS scratch (G entries).
+// logits (bias included) of the V consecutive experts l*V .. l*V+V-1 in
+// h[0..V); experts >= E are ignored.  Group limit ("MoE Expert Parallelism
+// Sizing: Traffic, Capacity, Fabric": at most M nodes per token, Megatron's
+// group-limited routing), when G > 1 and M < G: the E experts form G
+// contiguous groups; each group's score is its best logit (LDS atomic max
+// of the order-preserving key), the M best groups are picked by M wave
+// arg-max rounds (ties to the lower group), and the other groups' experts
+// are retired before KeepTopK.  gs/allow: this wave's LDS scratch (G
+// entries).
 template <int V>
 __device__ __forceinline__ void topk_softmax_token(const float (&h)[V], int E, int k, int G,
                                                    int M, uint32_t *gs, uint8_t *allow,
@@ -189,7 +193,7 @@ __device__ __forceinline__ void topk_softmax_token(const float (&h)[V], int E, i
     uint32_t vk[V];
 #pragma unroll
     for (int j = 0; j < V; ++j) {
-        const int e = lane + 64 * j;
+        const int e = lane * V + j;
         vk[j] = e < E ? value_key(h[j]) : 0u;
     }
     if (G > 1 && M < G) {
@@ -201,7 +205,7 @@ __device__ __forceinline__ void topk_softmax_token(const float (&h)[V], int E, i
         lds_wait();
 #pragma unroll
         for (int j = 0; j < V; ++j) {
-            const int e = lane + 64 * j;
+            const int e = lane * V + j;
             if (e < E)
                 atomicMax(&gs[e / per], vk[j]);
         }
@@ -221,58 +225,97 @@ __device__ __forceinline__ void topk_softmax_token(const float (&h)[V], int E, i
         }
 #pragma unroll
         for (int j = 0; j < V; ++j) {
-            const int e = lane + 64 * j;
+            const int e = lane * V + j;
             if (e < E && !allow[e / per])
                 vk[j] = 0;
         }
     }
-    float hmax = 0.f, denom = 0.f;
-    // k rounds: the wave-wide maximum of the values, then the lowest expert
-    // holding it (ties to the lower index), found with one ballot per
-    // register of values (expert e = lane + 64 j: the first j with a match,
-    // its lowest lane); the winner is retired.  Lane s keeps rank s's index
-    // and unnormalised weight (ranks past 64: lane s % 64 stores them and
-    // rereads them to normalise).
-    int my_e = 0;
-    float my_p = 0.f;
+    // k rounds: the wave-wide maximum of the lanes' best values; the lowest
+    // lane holding it holds the lowest expert with that value (lanes own
+    // consecutive experts), and within the lane the lowest register holding
+    // it (ties to the lower index); the winner is retired.  Rank s's expert
+    // and logit stay in lane s % 64, register s / 64, until the end.
+    int my_e[V];
+    float my_v[V];
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+        my_e[j] = 0;
+        my_v[j] = 0.f;
+    }
+    float hmax = 0.f;
+    // one round: the winner's expert e and logit v; the winner retired
+    auto select_one = [&](int &e, float &v) {
+        uint32_t head = vk[0];
+#pragma unroll
+        for (int j = 1; j < V; ++j)
+            head = vk[j] > head ? vk[j] : head;
+        const uint32_t win = wave_max_u32(head);
+        const int wl = (int)__builtin_ctzll(__ballot(head == win));
+        int jpos = V - 1;
+#pragma unroll
+        for (int j = V - 2; j >= 0; --j)
+            jpos = vk[j] == win ? j : jpos;
+        const int jw = __builtin_amdgcn_readlane(jpos, wl);
+        const bool mine = lane == wl;
+#pragma unroll
+        for (int j = 0; j < V; ++j)
+            if (j == jw)
+                vk[j] = mine ? 0u : vk[j];
+        e = wl * V + jw;
+        v = key_value(win);
+    };
+    if (k <= 64) {
+        for (int s = 0; s < k; ++s) {
+            int e;
+            float v;
+            select_one(e, v);
+            if (s == 0)
+                hmax = v;
+            const bool rec = lane == s;
+            my_e[0] = rec ? e : my_e[0];
+            my_v[0] = rec ? v : my_v[0];
+        }
+    } else {
+        for (int s = 0; s < k; ++s) {
+            int e;
+            float v;
+            select_one(e, v);
+            if (s == 0)
+                hmax = v;
+            const bool rec = lane == (s & 63);
+            const int r = s >> 6;
+#pragma unroll
+            for (int j = 0; j < V; ++j)
+                if (j == r) {
+                    my_e[j] = rec ? e : my_e[j];
+                    my_v[j] = rec ? v : my_v[j];
+                }
+        }
+    }
+    // softmax over the kept logits, max-subtracted: every lane takes the
+    // exponentials of its ranks, the denominator sums them in rank order
+    float p[V];
+#pragma unroll
+    for (int j = 0; j < V; ++j)
+        p[j] = (j * 64 < k && j * 64 + lane < k) ? expf(my_v[j] - hmax) : 0.f;
+    float denom = 0.f;
     for (int s = 0; s < k; ++s) {
-        uint32_t best = 0;
+        const int r = s >> 6;
+        float ps = 0.f;
 #pragma unroll
         for (int j = 0; j < V; ++j)
-            best = vk[j] > best ? vk[j] : best;
-        const uint32_t win = wave_max_u32(best);
-        int e = -1;
+            if (j == r)
+                ps = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p[j]), s & 63));
+        denom += ps;
+    }
 #pragma unroll
-        for (int j = 0; j < V; ++j) {
-            const uint64_t b = __ballot(vk[j] == win);
-            if (e < 0 && b != 0)
-                e = 64 * j + (int)__builtin_ctzll(b);
-        }
-#pragma unroll
-        for (int j = 0; j < V; ++j)
-            if (64 * j + lane == e)
-                vk[j] = 0;
-        const float v = key_value(win);
-        if (s == 0)
-            hmax = v;
-        const float p = expf(v - hmax);
-        denom += p; // same order in every lane
-        if (lane == (s & 63)) {
-            if (s < 64) {
-                my_e = e;
-                my_p = p;
-            } else {
-                idx_row[s] = e;
-                w_row[s] = p;
-            }
+    for (int j = 0; j < V; ++j) {
+        const int s = j * 64 + lane;
+        if (j * 64 < k && s < k) {
+            idx_row[s] = my_e[j];
+            w_row[s] = p[j] / denom;
         }
     }
-    if (lane < k) {
-        idx_row[lane] = my_e;
-        w_row[lane] = my_p / denom;
-    }
-    for (int s = lane + 64; s < k; s += 64)
-        w_row[s] = w_row[s] / denom;
 }
 
 // Selection on caller-given logits: one wavefront per token.
@@ -291,7 +334,7 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(const float *__restri
     float h[V];
 #pragma unroll
     for (int j = 0; j < V; ++j) {
-        const int e = lane + 64 * j;
+        const int e = lane * V + j;
         h[j] = e < E ? logits[(size_t)t * E + e] : 0.f;
     }
     topk_softmax_token<V>(h, E, k, G, M, s_gscore[wave], s_allow[wave], topk_idx + (size_t)t * k,
@@ -475,18 +518,30 @@ __global__ __launch_bounds__(256) void route_select_kernel(RouteArgs a)
     if (t >= a.T)
         return;
     const int S = a.S, E = a.E, epad = a.epad;
+    // lane l sums experts l*V .. l*V+V-1: V consecutive floats of each
+    // slice's row (16-byte loads when V >= 4; every row holds E_pad = 64 V)
     float h[V];
     for (int s0 = 0; s0 < S; s0 += SB) {
         float pv[SB][V];
 #pragma unroll
-        for (int u = 0; u < SB; ++u)
+        for (int u = 0; u < SB; ++u) {
+            const float *src = a.partial + ((size_t)(s0 + u) * a.T + t) * epad + lane * V;
+            if constexpr (V % 4 == 0) {
 #pragma unroll
-            for (int j = 0; j < V; ++j) {
-                const int e = lane + 64 * j;
-                pv[u][j] = (s0 + u < S && e < E)
-                               ? a.partial[((size_t)(s0 + u) * a.T + t) * epad + e]
-                               : 0.f;
+                for (int q = 0; q < V / 4; ++q) {
+                    const float4 f = s0 + u < S ? reinterpret_cast<const float4 *>(src)[q]
+                                                : make_float4(0.f, 0.f, 0.f, 0.f);
+                    pv[u][4 * q] = f.x;
+                    pv[u][4 * q + 1] = f.y;
+                    pv[u][4 * q + 2] = f.z;
+                    pv[u][4 * q + 3] = f.w;
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < V; ++j)
+                    pv[u][j] = s0 + u < S ? src[j] : 0.f;
             }
+        }
 #pragma unroll
         for (int u = 0; u < SB; ++u)
 #pragma unroll
@@ -496,7 +551,7 @@ __global__ __launch_bounds__(256) void route_select_kernel(RouteArgs a)
     }
 #pragma unroll
     for (int j = 0; j < V; ++j) {
-        const int e = lane + 64 * j;
+        const int e = lane * V + j;
         if (e < E) {
             if (a.bias)
                 h[j] += a.bias[e];
