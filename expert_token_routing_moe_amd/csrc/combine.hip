@@ -8,11 +8,17 @@
 // Capacity, Fabric", token-assignment worksheet) its bf16 output row is
 // added last, with weight 1.
 //
-// A wavefront per token.  Its slots and gates are read once into scalar
-// registers; for every 16-byte piece of the row, the lane issues all k
-// gathers before using any of them, accumulates G * row in fp32 in rank
-// order, and stores the bf16 result (round to nearest even).  The gathers are
-// non-temporal loads: every expert_out row is read once.
+// A wavefront per token, or W of them when there are few tokens (fewer than
+// 4096: DeepSeek-V3 decode has 64), wave h of a token then owning the
+// contiguous pieces [h n / W, (h+1) n / W) of its row (n 16-byte pieces).
+// The token's slots and gates are read once into scalar registers; for
+// every piece the lane issues all k gathers before using any of them,
+// accumulates G * row in fp32 in rank order, and stores the bf16 result
+// (round to nearest even).  The gathers are non-temporal loads: every
+// expert_out row is read once.  (Splitting the rows of 4096 or more tokens
+// measured no faster at DeepSeek-V3 prefill shape and slower on the
+// Mixtral-shaped and skewed layers; at 64 tokens one wave each leaves the
+// chip all but idle.)
 #include "moe_internal.hpp"
 
 namespace moe {
@@ -35,13 +41,15 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict
                                                       const float *__restrict__ topk_w,
                                                       const uint16_t *__restrict__ shared_out,
                                                       uint16_t *__restrict__ y, int T, int d,
-                                                      int k, long long rows_max)
+                                                      int k, long long rows_max, int W)
 {
     const int lane = threadIdx.x & 63;
-    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int gwave = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int t = gwave / W, h = gwave % W;
     if (t >= T)
         return;
     const int nvec = d / 8;
+    const int c_lo = (int)((long long)h * nvec / W), c_hi = (int)((long long)(h + 1) * nvec / W);
     int rows[KM];
     float g[KM];
 #pragma unroll
@@ -53,7 +61,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict
                          : 0.f;
     }
     uint4 *dst = reinterpret_cast<uint4 *>(y + (size_t)t * d);
-    for (int c = lane; c < nvec; c += 64) {
+    for (int c = c_lo + lane; c < c_hi; c += 64) {
         uint4 v[KM];
 #pragma unroll
         for (int s = 0; s < KM; ++s)
@@ -83,17 +91,19 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict
 __global__ __launch_bounds__(256) void combine_kernel_any_k(
     const uint16_t *__restrict__ expert_out, const int32_t *__restrict__ slot,
     const float *__restrict__ topk_w, const uint16_t *__restrict__ shared_out,
-    uint16_t *__restrict__ y, int T, int d, int k, long long rows_max)
+    uint16_t *__restrict__ y, int T, int d, int k, long long rows_max, int W)
 {
     const int lane = threadIdx.x & 63;
-    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int gwave = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int t = gwave / W, h = gwave % W;
     if (t >= T)
         return;
     const int nvec = d / 8;
+    const int c_lo = (int)((long long)h * nvec / W), c_hi = (int)((long long)(h + 1) * nvec / W);
     const int32_t *sl = slot + (size_t)t * k;
     const float *gw = topk_w + (size_t)t * k;
     uint4 *dst = reinterpret_cast<uint4 *>(y + (size_t)t * d);
-    for (int c = lane; c < nvec; c += 64) {
+    for (int c = c_lo + lane; c < c_hi; c += 64) {
         float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
         for (int s = 0; s < k; ++s) {
             const int r = sl[s];
@@ -123,19 +133,21 @@ hipError_t launch_combine(const Dims &dm, const uint16_t *expert_out, const int3
 {
     if (dm.T == 0)
         return hipSuccess;
-    const int blocks = (dm.T + 3) / 4;
+    const int W = combine_waves_per_token(dm.T, dm.d);
+    const long long waves = (long long)dm.T * W;
+    const unsigned blocks = (unsigned)((waves + 3) / 4);
+#define MOE_COMBINE(KERNEL)                                                                 \
+    KERNEL<<<blocks, 256, 0, st>>>(expert_out, slot, topk_w, shared_out, y, dm.T, dm.d, dm.k, \
+                                   dm.send_rows, W)
     if (dm.k <= 2)
-        combine_kernel<2><<<blocks, 256, 0, st>>>(expert_out, slot, topk_w, shared_out, y, dm.T,
-                                                             dm.d, dm.k, dm.send_rows);
+        MOE_COMBINE(combine_kernel<2>);
     else if (dm.k <= 4)
-        combine_kernel<4><<<blocks, 256, 0, st>>>(expert_out, slot, topk_w, shared_out, y, dm.T,
-                                                             dm.d, dm.k, dm.send_rows);
+        MOE_COMBINE(combine_kernel<4>);
     else if (dm.k <= 8)
-        combine_kernel<8><<<blocks, 256, 0, st>>>(expert_out, slot, topk_w, shared_out, y, dm.T,
-                                                             dm.d, dm.k, dm.send_rows);
+        MOE_COMBINE(combine_kernel<8>);
     else
-        combine_kernel_any_k<<<blocks, 256, 0, st>>>(expert_out, slot, topk_w, shared_out, y,
-                                                     dm.T, dm.d, dm.k, dm.send_rows);
+        MOE_COMBINE(combine_kernel_any_k);
+#undef MOE_COMBINE
     return hipGetLastError();
 }
 

@@ -545,16 +545,22 @@ __global__ __launch_bounds__(256) void permute_kernel(
     int32_t *__restrict__ slot, const int32_t *__restrict__ chunk_base,
     const int32_t *__restrict__ expert_offset, const int32_t *__restrict__ expert_kept,
     void *__restrict__ send_buf_v, float *__restrict__ send_scale, int T, int d, int k, int E,
-    long long C, int tok_blocks, int pad_parts, int pos_final)
+    long long C, int tok_blocks, int pad_parts, int pos_final, int W)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int nvec = d / 8;                    // 16-byte pieces of an x row
     const size_t row_bytes = (size_t)d * (FP8 ? 1 : 2);
     char *send_buf = reinterpret_cast<char *>(send_buf_v);
     if ((int)blockIdx.x < tok_blocks) {
-        const int t = blockIdx.x * 4 + wave;
-        if (t >= T)
-            return;
+        // W waves per token (1, 2 or 4: a token's waves share a workgroup);
+        // wave h copies the contiguous pieces [h n / W, (h+1) n / W)
+        const int gw = blockIdx.x * 4 + wave;
+        const int h = gw % W;
+        const bool valid = gw / W < T;
+        if (!valid && W == 1)
+            return; // (W > 1: every wave reaches the workgroup barriers)
+        const int t = valid ? gw / W : T - 1; // a wave past T mirrors the last token, writes nothing
+        const int c_lo = (int)((long long)h * nvec / W), c_hi = (int)((long long)(h + 1) * nvec / W);
         const int32_t *row = topk_idx + (size_t)t * k;
         const int32_t *base = chunk_base + (size_t)(t / kChunk) * E;
         const uint4 *src = reinterpret_cast<const uint4 *>(x + (size_t)t * d);
@@ -583,9 +589,14 @@ __global__ __launch_bounds__(256) void permute_kernel(
                 const int off = __builtin_amdgcn_readfirstlane(expert_offset[e]);
                 dst[q] = (pq[q] >= 0 && (C < 0 || pos < C)) ? off + (int)pos : -1;
             }
-            // every lane has read the positions before lane 0 overwrites them
+            // every lane (and every wave of the token) has read the
+            // positions before lane 0 of wave 0 overwrites them
             __builtin_amdgcn_wave_barrier();
-            if (lane < kSlotGroup && s0 + lane < k) {
+            if (W > 1)
+                __syncthreads();
+            if (!valid)
+                continue;
+            if (h == 0 && lane < kSlotGroup && s0 + lane < k) {
                 int v = dst[0];
 #pragma unroll
                 for (int q = 1; q < kSlotGroup; ++q)
@@ -597,11 +608,11 @@ __global__ __launch_bounds__(256) void permute_kernel(
             }
             // four row pieces in flight per lane before their stores; the
             // stores are non-temporal (the rows are read by the GEMM only)
-            for (int c0 = lane; c0 < nvec; c0 += 256) {
+            for (int c0 = c_lo + lane; c0 < c_hi; c0 += 256) {
                 uint4 v[4];
 #pragma unroll
                 for (int u = 0; u < 4; ++u)
-                    v[u] = (c0 + 64 * u < nvec) ? src[c0 + 64 * u] : make_uint4(0, 0, 0, 0);
+                    v[u] = (c0 + 64 * u < c_hi) ? src[c0 + 64 * u] : make_uint4(0, 0, 0, 0);
                 if constexpr (FP8) {
                     uint2 q8[4];
 #pragma unroll
@@ -614,7 +625,7 @@ __global__ __launch_bounds__(256) void permute_kernel(
                         uint2 *out = reinterpret_cast<uint2 *>(send_buf + (size_t)dst[q] * row_bytes);
 #pragma unroll
                         for (int u = 0; u < 4; ++u)
-                            if (c0 + 64 * u < nvec)
+                            if (c0 + 64 * u < c_hi)
                                 store_nt(out + c0 + 64 * u, q8[u]);
                     }
                 } else {
@@ -625,7 +636,7 @@ __global__ __launch_bounds__(256) void permute_kernel(
                         uint4 *out = reinterpret_cast<uint4 *>(send_buf + (size_t)dst[q] * row_bytes);
 #pragma unroll
                         for (int u = 0; u < 4; ++u)
-                            if (c0 + 64 * u < nvec)
+                            if (c0 + 64 * u < c_hi)
                                 store_nt(out + c0 + 64 * u, v[u]);
                     }
                 }
@@ -748,7 +759,10 @@ hipError_t launch_dispatch(const Dims &dm, const uint16_t *x, const int32_t *top
         gate_select_kernel<<<dm.E, 1024, 0, st>>>(by_expert, all_offset, expert_count, topk_w,
                                                    (long long)dm.capacity, slot);
     }
-    const int tok_blocks = (dm.T + 3) / 4;
+    // waves per token: one when the tokens give the launch 4096 wavefronts
+    // (16 per CU), else two or four (DeepSeek-V3 decode: 64 tokens)
+    const int pw = dm.T >= 4096 ? 1 : dm.T >= 2048 ? 2 : 4;
+    const int tok_blocks = (int)(((long long)dm.T * pw + 3) / 4);
     int pad_parts = 0;
     long long pad_blocks = 0;
     if (dm.capacity > 0) {
@@ -766,12 +780,12 @@ hipError_t launch_dispatch(const Dims &dm, const uint16_t *x, const int32_t *top
             permute_kernel<true><<<(unsigned)blocks, 256, 0, st>>>(
                 x, topk_idx, slot, chunk_base, expert_offset, expert_kept, send_buf, send_scale,
                 dm.T, dm.d, dm.k, dm.E, (long long)dm.capacity, tok_blocks, pad_parts,
-                by_gate ? 1 : 0);
+                by_gate ? 1 : 0, pw);
         else
             permute_kernel<false><<<(unsigned)blocks, 256, 0, st>>>(
                 x, topk_idx, slot, chunk_base, expert_offset, expert_kept, send_buf, nullptr,
                 dm.T, dm.d, dm.k, dm.E, (long long)dm.capacity, tok_blocks, pad_parts,
-                by_gate ? 1 : 0);
+                by_gate ? 1 : 0, pw);
     }
     return hipGetLastError();
 }

@@ -196,4 +196,16 @@ __device__ __forceinline__ int xcd_remap(int b, int total)
 
 inline int xcd_grid(int total) { return ((total + 7) / 8) * 8; }
 
+// Wavefronts that share one token's row in the combine (and its gather
+// probe): one per token when the tokens alone give the launch 4096
+// wavefronts (16 per CU), else enough to reach that, each keeping at least
+// 64 of the row's 16-byte pieces (one per lane), at most 16.
+inline int combine_waves_per_token(int T, int d)
+{
+    const int most = d / 8 / 64 < 16 ? d / 8 / 64 : 16;
+    const int want = T > 0 ? (4096 + T - 1) / T : 1;
+    const int w = want < most ? want : most;
+    return w < 1 ? 1 : w;
+}
+
 } // namespace moe

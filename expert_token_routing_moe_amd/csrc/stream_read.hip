@@ -59,24 +59,27 @@ __global__ __launch_bounds__(256) void stream_write_kernel(uint4 *__restrict__ d
 
 // The combine's memory traffic without its arithmetic: out[t] = XOR over
 // s < k of rows[slot[t, s]] (16-byte pieces; a slot outside [0, nrows)
-// adds nothing).  As in the combine: one wavefront per token, its slots
-// read once into scalar registers, every gather of a piece issued before
-// any is used (KM an upper bound on k; larger k one gather at a time),
-// non-temporal gathers, 16-byte stores.
+// adds nothing).  As in the combine: W wavefronts per token, each over its
+// contiguous share of the row's pieces, the slots read once into scalar
+// registers, every gather of a piece issued before any is used (KM an upper
+// bound on k; larger k one gather at a time), non-temporal gathers, 16-byte
+// stores.
 template <int KM>
 __global__ __launch_bounds__(256) void stream_gather_kernel(const uint4 *__restrict__ rows,
                                                             const int32_t *__restrict__ slot,
                                                             int T, int k, int d16,
                                                             long long nrows,
-                                                            uint4 *__restrict__ out)
+                                                            uint4 *__restrict__ out, int W)
 {
     const int lane = threadIdx.x & 63;
-    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int gwave = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int t = gwave / W, h = gwave % W;
     if (t >= T)
         return;
+    const int c_lo = (int)((long long)h * d16 / W), c_hi = (int)((long long)(h + 1) * d16 / W);
     uint4 *dst = out + (size_t)t * d16;
     if (k > KM) {
-        for (int c = lane; c < d16; c += 64) {
+        for (int c = c_lo + lane; c < c_hi; c += 64) {
             uint4 x = make_uint4(0, 0, 0, 0);
             for (int s = 0; s < k; ++s) {
                 const int r = slot[(size_t)t * k + s];
@@ -95,7 +98,7 @@ __global__ __launch_bounds__(256) void stream_gather_kernel(const uint4 *__restr
         const int r = s < k ? __builtin_amdgcn_readfirstlane(slot[(size_t)t * k + s]) : -1;
         rr[s] = r >= 0 && r < nrows ? r : -1;
     }
-    for (int c = lane; c < d16; c += 64) {
+    for (int c = c_lo + lane; c < c_hi; c += 64) {
         uint4 v[KM];
 #pragma unroll
         for (int s = 0; s < KM; ++s)
@@ -115,16 +118,17 @@ hipError_t launch_stream_gather(const void *rows, long long nrows, int d, const 
 {
     if (T == 0)
         return hipSuccess;
-    const int blocks = (T + 3) / 4;
+    const int W = combine_waves_per_token(T, d);
+    const unsigned blocks = (unsigned)(((long long)T * W + 3) / 4);
     const int d16 = d / 8; // bf16 rows: 8 values per 16-byte piece
     const uint4 *r = static_cast<const uint4 *>(rows);
     uint4 *o = static_cast<uint4 *>(out);
     if (k <= 2)
-        stream_gather_kernel<2><<<blocks, 256, 0, st>>>(r, slot, T, k, d16, nrows, o);
+        stream_gather_kernel<2><<<blocks, 256, 0, st>>>(r, slot, T, k, d16, nrows, o, W);
     else if (k <= 4)
-        stream_gather_kernel<4><<<blocks, 256, 0, st>>>(r, slot, T, k, d16, nrows, o);
+        stream_gather_kernel<4><<<blocks, 256, 0, st>>>(r, slot, T, k, d16, nrows, o, W);
     else
-        stream_gather_kernel<8><<<blocks, 256, 0, st>>>(r, slot, T, k, d16, nrows, o);
+        stream_gather_kernel<8><<<blocks, 256, 0, st>>>(r, slot, T, k, d16, nrows, o, W);
     return hipGetLastError();
 }
 
