@@ -322,6 +322,55 @@ def test_dispatch_and_combine_large_k(k, cf):
     assert np.all(np.abs(got - want) <= np.maximum(ulp, 2.0 ** -133) + (k + 1) * 2.0 ** -24 * mag)
 
 
+# Token counts below 4096, where the permute gives a token two or four
+# wavefronts (an odd T leaves the last workgroup half past T) and the combine
+# gives it up to 16 (row shares of 64 pieces or more, ragged against the
+# 64 lanes): dispatch bit-exact, combine within the fp32 bound of the
+# oracle's, FP8 rows and scales bit-exact too.
+@pytest.mark.parametrize("T,d,E,k,cf,fp8", [
+    (2049, 128, 16, 2, INF, 0),     # permute: 2 waves, odd T; combine: 1 wave
+    (333, 1344, 32, 8, INF, 0),     # permute: 4 waves; combine: 2 waves of 84 pieces
+    (64, 7168, 256, 8, 1.0, 0),     # DSV3 decode width, capacity drops; combine: 14 waves
+    (1000, 2112, 40, 12, INF, 0),   # k > 8: two slot groups per token, any-k combine, 4 waves
+    (777, 1024, 24, 4, 1.25, 1),    # E4M3 rows: every wave takes the whole row's scale
+    (3001, 512, 8, 3, 0.8, 0),      # permute: 2 waves, odd T, drops; combine: 1 wave
+])
+def test_dispatch_and_combine_wave_split(T, d, E, k, cf, fp8):
+    rng = np.random.default_rng(T * 7 + d)
+    idx = np.argsort(rng.random((T, E)), axis=1)[:, :k].astype(np.int32)
+    idx[3::53, 0] = -1
+    w = rng.random((T, k)).astype(np.float32)
+    x = torch.randn(T, d, device=DEV).to(torch.bfloat16)
+    shape = api.Shape(T=T, d=d, E=E, k=k, H=64, D=4, capacity_factor=cf, dispatch_fp8=fp8)
+    buf = api.LayerBuffers.allocate(shape, DEV)
+    _run_dispatch(shape, x, _i32(idx), buf)
+    r = oracle.dispatch(bf16_bits(x), idx, T=T, d=d, E=E, D=4, cf=cf, fp8=bool(fp8))
+    n = r["stats"]["send_rows"]
+    if fp8:
+        for key in ("expert_count", "expert_kept", "expert_offset", "rank_rows", "slot"):
+            np.testing.assert_array_equal(getattr(buf, key).cpu().numpy(), r[key], err_msg=key)
+        assert api.stats_dict(buf.stats) == r["stats"]
+        np.testing.assert_array_equal(buf.send_buf[:n].cpu().numpy(), r["send_buf"])
+        np.testing.assert_array_equal(buf.send_scale[:n].cpu().numpy(), r["send_scale"])
+    else:
+        _assert_dispatch_equal(buf, r, n)
+    eo_bits = bf16_bits(torch.randn(max(n, 1), d).to(torch.bfloat16))[:n]
+    eo = torch.from_numpy(eo_bits.view(np.int16)).view(torch.bfloat16).to(DEV)
+    y = torch.empty(T, d, dtype=torch.bfloat16, device=DEV)
+    api.moe_combine(shape, eo, _i32(r["slot"]), _f32(w), None, y)
+    torch.cuda.synchronize()
+    want = bits_to_f64(oracle.combine(eo_bits, r["slot"], w))
+    rows = bits_to_f64(eo_bits)
+    mag = np.zeros((T, d))
+    for s_ in range(k):
+        sl = r["slot"][:, s_]
+        m = sl >= 0
+        mag[m] += np.abs(w[m, s_, None].astype(np.float64) * rows[sl[m]])
+    ulp = np.ldexp(1.0, np.frexp(np.abs(want))[1] - 8)
+    got = t2f(y)
+    assert np.all(np.abs(got - want) <= np.maximum(ulp, 2.0 ** -133) + (k + 1) * 2.0 ** -24 * mag)
+
+
 @pytest.mark.parametrize("k", [2, 8, 12])
 def test_combine_treats_slots_outside_the_rows_as_dropped(k):
     """A caller's slot array with values at or past send_rows (and -1s): the
