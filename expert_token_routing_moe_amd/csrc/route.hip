@@ -505,14 +505,13 @@ __global__ __launch_bounds__(WM * WN * 64, MINB) void route_logits_kernel(RouteA
 }
 
 // Sum of the S partial logits of a token in slice order (loads in batches
-// of 8 slices, every load of a batch in flight together), plus the bias,
+// of SB slices, every load of a batch in flight together), plus the bias,
 // then selection: one wavefront per token.
-template <int V>
+template <int V, int SB>
 __global__ __launch_bounds__(256) void route_select_kernel(RouteArgs a)
 {
     __shared__ uint32_t s_gscore[4][kMaxExperts];
     __shared__ uint8_t s_allow[4][kMaxExperts];
-    constexpr int SB = 8;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int t = blockIdx.x * 4 + wave;
     if (t >= a.T)
@@ -664,17 +663,21 @@ hipError_t launch_route(const Dims &dm, const uint16_t *x, const uint16_t *w_gat
         return e;
     const int blocks = (T + 3) / 4;
     const int V = a.epad / 64;
-#define MOE_SEL(VV) route_select_kernel<VV><<<blocks, 256, 0, st>>>(a)
+    // every slice's loads in flight together when the slices are many (up
+    // to 32: DeepSeek-V3 decode has 28) and a lane's experts few; else
+    // batches of 8
+    const bool one_batch = a.S > 8 && V <= 4;
+#define MOE_SEL(VV, SB) route_select_kernel<VV, SB><<<blocks, 256, 0, st>>>(a)
     if (V <= 1)
-        MOE_SEL(1);
+        one_batch ? MOE_SEL(1, 32) : MOE_SEL(1, 8);
     else if (V <= 2)
-        MOE_SEL(2);
+        one_batch ? MOE_SEL(2, 32) : MOE_SEL(2, 8);
     else if (V <= 4)
-        MOE_SEL(4);
+        one_batch ? MOE_SEL(4, 32) : MOE_SEL(4, 8);
     else if (V <= 8)
-        MOE_SEL(8);
+        MOE_SEL(8, 8);
     else
-        MOE_SEL(16);
+        MOE_SEL(16, 8);
 #undef MOE_SEL
     return hipGetLastError();
 }
