@@ -63,9 +63,25 @@ struct GemmArgs {
 };
 
 
+// Inclusive prefix sum over the wavefront: within each 16-lane row by DPP
+// row shifts of 1, 2, 4 and 8 (a lane without a source adds 0), then the
+// totals of rows 0 and 2 into rows 1 and 3 (row broadcast of lane 15) and
+// the total of rows 0-1 into rows 2 and 3 (row broadcast of lane 31).
+__device__ __forceinline__ int wave_incl_scan(int v)
+{
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true); // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true); // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true); // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true); // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false); // row_bcast:15
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false); // row_bcast:31
+    return v;
+}
+
 // Tile work of expert e is ceil(rows_e / BM) * (N / BN) tiles.  Wave 0 of the
-// workgroup scans all experts (lane l owns experts [l*V, (l+1)*V)), maps the
-// block to a work index with the XCD remap, and publishes (expert, local
+// workgroup scans all experts (lane l owns the V = ceil(E / 64) experts
+// [l*V, (l+1)*V), their counts loaded together: E <= 1024, so V <= 16), maps
+// the block to a work index with the XCD remap, and publishes (expert, local
 // index) in LDS; e = -1 marks a surplus block.
 template <int BM>
 __device__ __forceinline__ void decode_work(const GemmArgs &g, int nN, int *s_e, int *s_local)
@@ -73,36 +89,35 @@ __device__ __forceinline__ void decode_work(const GemmArgs &g, int nN, int *s_e,
     const int lane = threadIdx.x & 63;
     const int E = g.E;
     const int V = (E + 63) >> 6;
-    int sum = 0;
-    for (int j = 0; j < V; ++j) {
-        const int e = lane * V + j;
-        if (e < E)
-            sum += (max(g.row_count[e], 0) + BM - 1) / BM * nN;
-    }
-    int incl = sum;
+    // every load in bounds (clamped to expert E-1), none under a branch, so
+    // that all sixteen are in flight together; the ones past the lane's
+    // experts are discarded
+    int t[16];
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int o = __shfl_up(incl, off, 64);
-        if (lane >= off)
-            incl += o;
+    for (int j = 0; j < 16; ++j)
+        t[j] = g.row_count[min(lane * V + j, E - 1)];
+    int sum = 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const int e = lane * V + j;
+        t[j] = (j < V && e < E) ? (max(t[j], 0) + BM - 1) / BM * nN : 0;
+        sum += t[j];
     }
-    const int W = __shfl(incl, 63, 64);
+    const int incl = wave_incl_scan(sum);
+    const int W = __builtin_amdgcn_readlane(incl, 63);
     const int w = xcd_remap(blockIdx.x, W);
     if (lane == 0)
         *s_e = -1;
     if (w >= 0 && w >= incl - sum && w < incl) {
         int acc = incl - sum;
-        for (int j = 0; j < V; ++j) {
-            const int e = lane * V + j;
-            if (e >= E)
-                break;
-            const int t = (max(g.row_count[e], 0) + BM - 1) / BM * nN;
-            if (w < acc + t) {
-                *s_e = e;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            // the tile ranges are disjoint: exactly one (lane, j) holds w
+            if (w >= acc && w < acc + t[j]) {
+                *s_e = lane * V + j;
                 *s_local = w - acc;
-                break;
             }
-            acc += t;
+            acc += t[j];
         }
     }
 }
