@@ -351,8 +351,9 @@ int moe_stream_write(void *dst, size_t bytes, uint32_t value, void *stream);
 /* Diagnostic, not a step of the layer: the combine's memory traffic without
  * its arithmetic, out[t] = XOR over s < k of the 16-byte pieces of row
  * slot[t, s] of rows (a slot outside [0, nrows) adds nothing), with the
- * combine's access (one wavefront per token, non-temporal 16-byte gathers,
- * all k of a piece in flight together for k <= 8), so that a caller can
+ * combine's access (a wavefront per token, or several sharing its row when
+ * there are fewer than 4096 tokens; non-temporal 16-byte gathers, all k of
+ * a piece in flight together for k <= 8), so that a caller can
  * time the rate of that access beside moe_combine.
  *   rows  [nrows, d] bf16 (device);  slot [T, k] int32 (device)
  *   out   [T, d] bf16 out (device);  d % 8 == 0, k >= 1
