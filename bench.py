@@ -541,6 +541,9 @@ def main():
     # the steady state
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="dsv3_prefill")
+    ap.add_argument("--tokens", type=int, default=None, metavar="T",
+                    help="tokens per layer call instead of the workload's (the same seeded "
+                         "inputs, drawn for T tokens)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--drop-policy", type=int, default=None, choices=(0, 1),
@@ -595,6 +598,8 @@ def main():
     from expert_token_routing_moe_amd.inputs import CONFIGS, make_inputs
 
     cfg = CONFIGS[args.workload]
+    if args.tokens is not None:
+        cfg = cfg.with_(T=args.tokens)
     if args.drop_policy is not None:
         cfg = cfg.with_(drop_policy=args.drop_policy)
     if args.min_capacity is not None:

@@ -43,11 +43,15 @@ int router_ldw(int E) { return (E + 7) / 8 * 8; }
 // when there are many, below), and K cut into S slices when the tiles alone
 // leave the chip short of workgroups
 // (one per CU for BE = 256, eight waves; two per CU for BE = 128 or 64, four
-// waves): enough slices to fill it, at least four K steps each, at most 32.
-// BE is the widest of 256, 128, 64 (dividing E rounded up to 64) whose
-// launch fills the chip; when none does (few tokens: DeepSeek-V3 decode has
-// one token tile and 28 slices), the one with the most workgroups, so that
-// more CUs stream W_g.  The K slices do not depend on BE, so neither do the
+// waves): as many slices as the chip holds in one round of workgroups, at
+// least four K steps each, at most 32 (a launch just past one round would
+// run a second round for a few workgroups: at 3072 tokens of DeepSeek-V3
+// shape 6 slices made 288 workgroups, 5 make 240).  BE is the widest of
+// 256, 128, 64 (dividing E rounded up to 64) whose launch fills the chip,
+// or at least half of it in one round when the slice count is not at its
+// cap; when none does (few tokens: DeepSeek-V3 decode has one token tile
+// and 28 slices), the one with the most workgroups, so that more CUs
+// stream W_g.  The K slices do not depend on BE, so neither do the
 // logits' bits.  (128-token tiles with twice the slices measured the same
 // time at the DeepSeek-V3 prefill shape for twice the partial-sum bytes.)
 // T = 0: nothing to split.
@@ -66,10 +70,12 @@ static RouterPlan router_plan(int T, int E, int d)
         const int target = be == 256 ? 256 : 512;
         const long long tiles = (long long)((T + 63) / 64) * (epad / be);
         int sk = 1;
+        bool capped = false; // fewer slices than one round would hold
         if (T > 0 && tiles < target) {
-            int s = (int)((target + tiles - 1) / tiles);
-            s = std::min(s, std::max(1, steps / 4));
-            sk = std::max(1, std::min(s, 32));
+            const int fit = (int)(target / tiles);
+            const int cap = std::max(1, std::min(steps / 4, 32));
+            sk = std::max(1, std::min(fit, cap));
+            capped = fit > cap;
         }
         const long long wg = tiles * sk;
         // More tiles than the chip needs: taller token tiles (128, and 256
@@ -81,7 +87,7 @@ static RouterPlan router_plan(int T, int E, int d)
             return RouterPlan{be, 1, 256};
         if (T > 0 && tiles >= 2LL * target)
             return RouterPlan{be, 1, 128};
-        if (T == 0 || wg >= target)
+        if (T == 0 || wg >= target || (!capped && 2 * wg >= target))
             return RouterPlan{be, sk, 64};
         if (wg > best_wg) {
             best_wg = wg;
