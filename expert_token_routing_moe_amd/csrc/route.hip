@@ -78,14 +78,14 @@ static RouterPlan router_plan(int T, int E, int d)
             capped = fit > cap;
         }
         const long long wg = tiles * sk;
-        // More tiles than the chip needs: taller token tiles (128, and 256
-        // for 256-expert tiles, whose ring holds two of their 64 KB stages)
-        // that still fill it, so each reads W_g for more tokens (at T = 32768
-        // every 64-token tile would read all of W_g, 3.7 MB at DeepSeek-V3
-        // shape)
-        if (T > 0 && be == 256 && tiles >= 4LL * target)
+        // More tiles than one round of workgroups: taller token tiles (128,
+        // and 256 for 256-expert tiles, whose ring holds two of their 64 KB
+        // stages), so each reads W_g for more tokens (at T = 32768 every
+        // 64-token tile would read all of W_g, 3.7 MB at DeepSeek-V3 shape)
+        // and fewer rounds run
+        if (T > 0 && be == 256 && tiles > 2LL * target)
             return RouterPlan{be, 1, 256};
-        if (T > 0 && tiles >= 2LL * target)
+        if (T > 0 && tiles > target)
             return RouterPlan{be, 1, 128};
         if (T == 0 || wg >= target || (!capped && 2 * wg >= target))
             return RouterPlan{be, sk, 64};
