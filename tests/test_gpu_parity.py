@@ -126,6 +126,10 @@ ROUTE_CASES = [
     (32768, 128, 256, 8, 0, 0, False),    # 128-token tiles (twice the tiles needed), BE 256
     (65536, 64, 64, 2, 0, 0, True),       # 128-token tiles, BE 64
     (65536, 64, 256, 8, 8, 4, True),      # 256-token tiles, BE 256, group limit
+    (3072, 2048, 256, 8, 0, 0, True),     # BE 256, 5 slices (one round: 240 workgroups)
+    (6144, 1024, 256, 8, 8, 4, False),    # BE 256, 2 slices, group limit
+    (20480, 128, 256, 8, 0, 0, False),    # 128-token tiles (64-token ones: 320, past one round)
+    (40960, 128, 256, 8, 0, 0, True),     # 256-token tiles (128-token ones: 320)
 ]
 
 
