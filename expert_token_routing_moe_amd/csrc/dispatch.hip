@@ -18,7 +18,8 @@
 //  2. scan: one workgroup scans the chunk counts of every expert (giving the
 //     chunk bases and n_e), applies the capacity, forms the expert offsets,
 //     the per-rank rows and the counters.
-//  3. permute: a wavefront per token turns positions into slots, reads the
+//  3. permute: a wavefront per token (two or four, each over a share of the
+//     row, when there are few tokens) turns positions into slots, reads the
 //     token row once and writes it to each kept slot with 16-byte stores;
 //     extra workgroups zero the pad rows of capacity mode.
 //
