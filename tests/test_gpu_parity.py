@@ -627,12 +627,14 @@ def test_stream_write_fills_every_word(nbytes):
     assert (got[n:] == 0).all()
 
 
-@pytest.mark.parametrize("k", [2, 8, 12])
-def test_stream_gather_xors_the_slotted_rows(k):
+@pytest.mark.parametrize("k,T,d", [(2, 300, 512), (8, 300, 512), (12, 300, 512),
+                                   (8, 64, 7168), (3, 301, 2112), (12, 33, 1536)])
+def test_stream_gather_xors_the_slotted_rows(k, T, d):
     """The combine-pattern probe: out[t] is the XOR of the rows its slots
     name, a slot outside [0, nrows) adding nothing (those slots point into
-    padding rows, so a missing bound shows as a wrong value)."""
-    T, d, nrows, pad = 300, 512, 700, 64
+    padding rows, so a missing bound shows as a wrong value).  The wide
+    rows at few tokens split a token over 14, 4 and 3 wavefronts."""
+    nrows, pad = 700, 64
     rng = np.random.default_rng(7 + k)
     rows = rng.integers(-2 ** 15, 2 ** 15, (nrows + pad, d), dtype=np.int64).astype(np.int16)
     slot = rng.integers(0, nrows, (T, k)).astype(np.int32)
